@@ -1,0 +1,201 @@
+"""ctypes binding of the CPU oracle (oracle/sbf_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  The oracle is the plain per-k-mer definition of the
+Super Bloom filter of "cuSBF: A Minimizer-Aware Bloom Filter for Genomic
+Sequence Data on Modern GPUs"; the GPU library is checked against it.  Only
+the tests, the smoke entry point and the benchmark's CPU-baseline leg may
+import this module.  It imports nothing from the GPU package.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "sbf_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+KIND_SBF = 0
+KIND_BBF = 1
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, no vectorisation flags)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+                               "-Wall", "-Werror", "-o", tmp, SRC])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(LIB)
+        u64, u32, p = ctypes.c_uint64, ctypes.c_uint, ctypes.c_void_p
+        L.osbf_code.argtypes = [ctypes.c_ubyte]
+        L.osbf_code.restype = ctypes.c_int
+        for name in ("osbf_hmin", "osbf_mix", "osbf_hs"):
+            getattr(L, name).argtypes = [u64]
+            getattr(L, name).restype = u64
+        L.osbf_bitaddr.argtypes = [u64, u32, u32]
+        L.osbf_bitaddr.restype = u32
+        L.osbf_probe_kmer.argtypes = [u64, u64, u32]
+        L.osbf_probe_kmer.restype = u64
+        L.osbf_pack_kmer.argtypes = [ctypes.c_char_p, u32, ctypes.POINTER(u64)]
+        L.osbf_pack_kmer.restype = ctypes.c_int
+        L.osbf_subwindow.argtypes = [u64, u32, u32, u32]
+        L.osbf_subwindow.restype = u64
+        L.osbf_minimizer_hash.argtypes = [u64, u32, u32]
+        L.osbf_minimizer_hash.restype = u64
+        L.osbf_create.argtypes = [ctypes.c_int, u32, u32, u32, u32, u64]
+        L.osbf_create.restype = p
+        L.osbf_destroy.argtypes = [p]
+        L.osbf_destroy.restype = None
+        L.osbf_num_shards.argtypes = [p]
+        L.osbf_num_shards.restype = u64
+        L.osbf_words.argtypes = [p]
+        L.osbf_words.restype = ctypes.POINTER(u64)
+        L.osbf_shard_of.argtypes = [p, u64]
+        L.osbf_shard_of.restype = u64
+        L.osbf_insert_kmer.argtypes = [p, u64]
+        L.osbf_insert_kmer.restype = None
+        L.osbf_query_kmer.argtypes = [p, u64]
+        L.osbf_query_kmer.restype = ctypes.c_int
+        L.osbf_insert_seq.argtypes = [p, p, u64]
+        L.osbf_insert_seq.restype = None
+        L.osbf_query_seq.argtypes = [p, p, u64, p]
+        L.osbf_query_seq.restype = None
+        L.osbf_query_positions.argtypes = [p, p, u64, p, u64, p]
+        L.osbf_query_positions.restype = None
+        L.osbf_fpr_probe.argtypes = [p, u64, u64]
+        L.osbf_fpr_probe.restype = u64
+        _lib = L
+    return _lib
+
+
+def _buf(seq):
+    """Return (numpy uint8 array, pointer) for bytes / str / uint8 arrays."""
+    if isinstance(seq, str):
+        seq = seq.encode("ascii")
+    if isinstance(seq, (bytes, bytearray)):
+        arr = np.frombuffer(bytes(seq), dtype=np.uint8)
+    else:
+        arr = np.ascontiguousarray(seq, dtype=np.uint8)
+    return arr, arr.ctypes.data
+
+
+# ---- primitives ------------------------------------------------------------
+
+def code(c) -> int:
+    if isinstance(c, str):
+        c = ord(c)
+    return lib().osbf_code(c)
+
+
+def hmin(v: int) -> int:
+    return lib().osbf_hmin(v & (2**64 - 1))
+
+
+def mix(z: int) -> int:
+    return lib().osbf_mix(z & (2**64 - 1))
+
+
+def hs(v: int) -> int:
+    return lib().osbf_hs(v & (2**64 - 1))
+
+
+def bitaddr(h: int, t: int, H: int) -> int:
+    return lib().osbf_bitaddr(h, t, H)
+
+
+def probe_kmer(seed: int, i: int, k: int) -> int:
+    return lib().osbf_probe_kmer(seed & (2**64 - 1), i, k)
+
+
+def pack_kmer(s) -> int | None:
+    if isinstance(s, str):
+        s = s.encode("ascii")
+    x = ctypes.c_uint64(0)
+    rc = lib().osbf_pack_kmer(s, len(s), ctypes.byref(x))
+    return None if rc != 0 else x.value
+
+
+def subwindow(x: int, k: int, i: int, w: int) -> int:
+    return lib().osbf_subwindow(x, k, i, w)
+
+
+def minimizer_hash(x: int, k: int, m: int) -> int:
+    return lib().osbf_minimizer_hash(x, k, m)
+
+
+# ---- filter ----------------------------------------------------------------
+
+class OracleFilter:
+    """A Super Bloom filter (kind=KIND_SBF) or per-k-mer blocked Bloom filter
+    (kind=KIND_BBF) held in host memory by the C oracle."""
+
+    def __init__(self, k, m, s, H, bits, kind=KIND_SBF):
+        self.k, self.m, self.s, self.H, self.kind = k, m, s, H, kind
+        self._h = lib().osbf_create(kind, k, m, s, H, bits)
+        if not self._h:
+            raise ValueError("oracle: invalid parameters (k=%d m=%d s=%d H=%d bits=%d)"
+                             % (k, m, s, H, bits))
+
+    def close(self):
+        if self._h:
+            lib().osbf_destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    @property
+    def num_shards(self) -> int:
+        return lib().osbf_num_shards(self._h)
+
+    def words(self) -> np.ndarray:
+        """Copy of the filter: uint64[4 * num_shards]."""
+        n = 4 * self.num_shards
+        ptr = lib().osbf_words(self._h)
+        return np.ctypeslib.as_array(ptr, shape=(n,)).copy()
+
+    def shard_of(self, x: int) -> int:
+        return lib().osbf_shard_of(self._h, x)
+
+    def insert_kmer(self, x: int):
+        lib().osbf_insert_kmer(self._h, x)
+
+    def query_kmer(self, x: int) -> bool:
+        return bool(lib().osbf_query_kmer(self._h, x))
+
+    def insert_seq(self, seq):
+        arr, ptr = _buf(seq)
+        lib().osbf_insert_seq(self._h, ptr, arr.size)
+
+    def query_seq(self, seq) -> np.ndarray:
+        """uint64 bit words, bit p = answer for the k-mer starting at p."""
+        arr, ptr = _buf(seq)
+        nk = max(0, arr.size - self.k + 1)
+        out = np.zeros((nk + 63) // 64, dtype=np.uint64)
+        if nk:
+            lib().osbf_query_seq(self._h, ptr, arr.size, out.ctypes.data)
+        return out
+
+    def query_positions(self, seq, positions) -> np.ndarray:
+        arr, ptr = _buf(seq)
+        pos = np.ascontiguousarray(positions, dtype=np.uint64)
+        out = np.zeros(pos.size, dtype=np.uint8)
+        lib().osbf_query_positions(self._h, ptr, arr.size, pos.ctypes.data, pos.size,
+                                   out.ctypes.data)
+        return out
+
+    def fpr_probe(self, n: int, seed: int) -> int:
+        return lib().osbf_fpr_probe(self._h, n, seed & (2**64 - 1))

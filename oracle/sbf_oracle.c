@@ -1,0 +1,277 @@
+/*
+ * sbf_oracle.c -- plain, single-threaded CPU oracle of the Super Bloom filter.
+ *
+ * TEST INFRASTRUCTURE ONLY (see sbf_oracle.h).  Slow on purpose: every k-mer
+ * is packed, minimized, hashed and tested from scratch.
+ *
+ * Source: [cuSBF] = "cuSBF: A Minimizer-Aware Bloom Filter for Genomic
+ * Sequence Data on Modern GPUs" (Dortmann, Vieth, Schmidt).
+ *
+ * Readings fixed here where [cuSBF] leaves a step open:
+ *  - Codes: A/a=0, C/c=1, G/g=2, T/t=3; any other byte is an invalid symbol
+ *    ([cuSBF] §IV-A names the 2-bit DNA alphabet, not the code order).
+ *  - A k-mer is packed with its first base in the most significant bits
+ *    (shift-left-and-OR of [cuSBF] §IV-C / §IV-E); sub-window i is the
+ *    window starting at base i of the k-mer.
+ *  - h_min(v) = u ^ (u >> 32) with u = (v + G) * C1 mod 2^64: one
+ *    multiplicative mix ([cuSBF] §IV-G, role-specialized hashing), folded so
+ *    the low bits used for the shard depend on every base.
+ *  - h_s(v) = mix(v + G), mix = the SplitMix64 finalizer (two multiplies and
+ *    three xorshifts): the "stronger mix" of [cuSBF] §IV-G, SplitMix-style as
+ *    the CPU reference of [cuSBF] §V-D.
+ *    G  = 0x9E3779B97F4A7C15 (2^64 / golden ratio),
+ *    C1 = 0xBF58476D1CE4E5B9, C2 = 0x94D049BB133111EB (SplitMix64).
+ *  - Bit address: for H <= 10, slice t of width floor(64/H), its low 6 bits
+ *    ([cuSBF] §IV-G bit-slicing); for H > 10, the top 6 bits of
+ *    hs * ((2t+1) * G) (the golden-ratio salted fallback of §IV-G).
+ *  - Shard count: the smallest power of two >= ceil(bits/256), at least 1
+ *    ([cuSBF] §IV-B).  Hash index t lives in word t mod 4 of the shard.
+ *  - Invalid k-mers (any non-ACGT base) insert nothing and query false
+ *    ([cuSBF] Algorithms 1 and 2, §IV-F).
+ *  - Probe k-mers: the i-th output of the SplitMix64 stream seeded with
+ *    `seed`, mix(seed + (i+1) * G), shifted right by 64-2k
+ *    ([cuSBF] §V-D measures the FPR on uniformly random k-mers).
+ */
+#include "sbf_oracle.h"
+
+#include <stdlib.h>
+#include <string.h>
+
+#define GOLDEN 0x9E3779B97F4A7C15ull
+#define SM_C1 0xBF58476D1CE4E5B9ull
+#define SM_C2 0x94D049BB133111EBull
+
+struct osbf {
+    int kind;
+    unsigned k, m, s, H;
+    uint64_t num_shards;
+    uint64_t* words;
+};
+
+/* [cuSBF] §IV-A: DNA, 4 symbols, 2 bits each. */
+int osbf_code(unsigned char c)
+{
+    switch (c) {
+    case 'A': case 'a': return 0;
+    case 'C': case 'c': return 1;
+    case 'G': case 'g': return 2;
+    case 'T': case 't': return 3;
+    default: return -1;
+    }
+}
+
+/* [cuSBF] §IV-G: the minimizer hash is a single multiplicative mix. */
+uint64_t osbf_hmin(uint64_t v)
+{
+    uint64_t u = (v + GOLDEN) * SM_C1;
+    return u ^ (u >> 32);
+}
+
+/* SplitMix64 output function (Steele, Lea, Flood 2014). */
+uint64_t osbf_mix(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * SM_C1;
+    z = (z ^ (z >> 27)) * SM_C2;
+    return z ^ (z >> 31);
+}
+
+/* [cuSBF] §IV-G: the s-mer hash is a stronger mix with extra xorshifts. */
+uint64_t osbf_hs(uint64_t v)
+{
+    return osbf_mix(v + GOLDEN);
+}
+
+/* [cuSBF] §IV-G, bit-slicing and the salted fallback. */
+unsigned osbf_bitaddr(uint64_t hs, unsigned t, unsigned H)
+{
+    if (H <= 10) {
+        unsigned width = 64u / H;
+        return (unsigned)((hs >> (t * width)) & 63u);
+    }
+    uint64_t salt = (2ull * t + 1ull) * GOLDEN;
+    return (unsigned)((hs * salt) >> 58);
+}
+
+/* [cuSBF] §V-D: uniformly random k-mers, drawn from SplitMix64. */
+uint64_t osbf_probe_kmer(uint64_t seed, uint64_t i, unsigned k)
+{
+    uint64_t r = osbf_mix(seed + (i + 1ull) * GOLDEN);
+    return r >> (64u - 2u * k);
+}
+
+static uint64_t low_mask(unsigned nbases)
+{
+    return nbases >= 32 ? ~0ull : ((1ull << (2u * nbases)) - 1ull);
+}
+
+/* [cuSBF] §IV-C: pack k symbols into one 64-bit word by shift-and-OR. */
+int osbf_pack_kmer(const char* seq, unsigned k, uint64_t* x)
+{
+    uint64_t v = 0;
+    for (unsigned j = 0; j < k; ++j) {
+        int c = osbf_code((unsigned char)seq[j]);
+        if (c < 0)
+            return -1;
+        v = (v << 2) | (uint64_t)c;
+    }
+    *x = v;
+    return 0;
+}
+
+/* Window of w bases starting at base i of a packed k-mer. */
+uint64_t osbf_subwindow(uint64_t x, unsigned k, unsigned i, unsigned w)
+{
+    return (x >> (2u * (k - w - i))) & low_mask(w);
+}
+
+/* [cuSBF] §II-B-1 and Algorithm 1: the minimizer is the m-mer of least hash;
+ * the shard only needs that least hash value. */
+uint64_t osbf_minimizer_hash(uint64_t x, unsigned k, unsigned m)
+{
+    uint64_t best = ~0ull;
+    for (unsigned i = 0; i + m <= k; ++i) {
+        uint64_t h = osbf_hmin(osbf_subwindow(x, k, i, m));
+        if (h < best)
+            best = h;
+    }
+    return best;
+}
+
+osbf* osbf_create(int kind, unsigned k, unsigned m, unsigned s, unsigned H, uint64_t bits)
+{
+    if (kind != OSBF_KIND_SBF && kind != OSBF_KIND_BBF)
+        return NULL;
+    if (k < 1 || k > 32 || H < 1 || H > 64 || bits < 1)
+        return NULL;
+    if (kind == OSBF_KIND_SBF && (m < 1 || m > k || s < 1 || s > k))
+        return NULL;
+    /* [cuSBF] §IV-B: shard count rounded up to a power of two. */
+    uint64_t need = bits / 256u + (bits % 256u != 0);
+    uint64_t n = 1;
+    while (n < need)
+        n <<= 1;
+    osbf* f = (osbf*)calloc(1, sizeof(osbf));
+    if (!f)
+        return NULL;
+    f->words = (uint64_t*)calloc(4u * n, sizeof(uint64_t));
+    if (!f->words) {
+        free(f);
+        return NULL;
+    }
+    f->kind = kind;
+    f->k = k;
+    f->m = m;
+    f->s = s;
+    f->H = H;
+    f->num_shards = n;
+    return f;
+}
+
+void osbf_destroy(osbf* f)
+{
+    if (!f)
+        return;
+    free(f->words);
+    free(f);
+}
+
+uint64_t osbf_num_shards(const osbf* f) { return f->num_shards; }
+uint64_t* osbf_words(osbf* f) { return f->words; }
+
+/* SBF: [cuSBF] Algorithm 1, shard = minimizer hash & (N-1).
+ * BBF: [cuSBF] §II-A / Fig. 1b, one hash of the whole key picks the block. */
+uint64_t osbf_shard_of(const osbf* f, uint64_t x)
+{
+    if (f->kind == OSBF_KIND_BBF)
+        return osbf_hs(x) & (f->num_shards - 1u);
+    return osbf_minimizer_hash(x, f->k, f->m) & (f->num_shards - 1u);
+}
+
+/* [cuSBF] §IV-B: hash index t sets one bit in word t mod 4 of the shard. */
+static void set_bits(uint64_t* shard, uint64_t hs, unsigned H)
+{
+    for (unsigned t = 0; t < H; ++t)
+        shard[t % 4u] |= 1ull << osbf_bitaddr(hs, t, H);
+}
+
+static int test_bits(const uint64_t* shard, uint64_t hs, unsigned H)
+{
+    for (unsigned t = 0; t < H; ++t)
+        if (!((shard[t % 4u] >> osbf_bitaddr(hs, t, H)) & 1u))
+            return 0;
+    return 1;
+}
+
+/* [cuSBF] §II-B-2 (Findere) and Algorithm 1: every one of the k-s+1 s-mers
+ * sets its H bits in the k-mer's shard.  The BBF keys its bits on a second
+ * hash of the k-mer's block hash. */
+void osbf_insert_kmer(osbf* f, uint64_t x)
+{
+    uint64_t* shard = f->words + 4u * osbf_shard_of(f, x);
+    if (f->kind == OSBF_KIND_BBF) {
+        set_bits(shard, osbf_hs(osbf_hs(x)), f->H);
+        return;
+    }
+    for (unsigned j = 0; j + f->s <= f->k; ++j)
+        set_bits(shard, osbf_hs(osbf_subwindow(x, f->k, j, f->s)), f->H);
+}
+
+/* [cuSBF] §II-B-2 and Algorithm 2 (Contains): present only if every s-mer
+ * finds all of its H bits. */
+int osbf_query_kmer(const osbf* f, uint64_t x)
+{
+    const uint64_t* shard = f->words + 4u * osbf_shard_of(f, x);
+    if (f->kind == OSBF_KIND_BBF)
+        return test_bits(shard, osbf_hs(osbf_hs(x)), f->H);
+    for (unsigned j = 0; j + f->s <= f->k; ++j)
+        if (!test_bits(shard, osbf_hs(osbf_subwindow(x, f->k, j, f->s)), f->H))
+            return 0;
+    return 1;
+}
+
+/* [cuSBF] §IV-D / §IV-F: every k-mer start; invalid k-mers are skipped. */
+void osbf_insert_seq(osbf* f, const char* seq, uint64_t len)
+{
+    if (len < f->k)
+        return;
+    for (uint64_t p = 0; p + f->k <= len; ++p) {
+        uint64_t x;
+        if (osbf_pack_kmer(seq + p, f->k, &x) == 0)
+            osbf_insert_kmer(f, x);
+    }
+}
+
+/* [cuSBF] §IV-E: one answer per k-mer start, invalid k-mers answer false. */
+void osbf_query_seq(const osbf* f, const char* seq, uint64_t len, uint64_t* out)
+{
+    if (len < f->k)
+        return;
+    uint64_t nk = len - f->k + 1u;
+    memset(out, 0, ((nk + 63u) / 64u) * sizeof(uint64_t));
+    for (uint64_t p = 0; p < nk; ++p) {
+        uint64_t x;
+        if (osbf_pack_kmer(seq + p, f->k, &x) == 0 && osbf_query_kmer(f, x))
+            out[p / 64u] |= 1ull << (p % 64u);
+    }
+}
+
+void osbf_query_positions(const osbf* f, const char* seq, uint64_t len,
+                          const uint64_t* pos, uint64_t n, uint8_t* out)
+{
+    for (uint64_t i = 0; i < n; ++i) {
+        uint64_t x;
+        uint64_t p = pos[i];
+        out[i] = 0;
+        if (p + f->k <= len && osbf_pack_kmer(seq + p, f->k, &x) == 0)
+            out[i] = (uint8_t)osbf_query_kmer(f, x);
+    }
+}
+
+/* [cuSBF] §V-D: count positives among n random k-mers. */
+uint64_t osbf_fpr_probe(const osbf* f, uint64_t n, uint64_t seed)
+{
+    uint64_t hits = 0;
+    for (uint64_t i = 0; i < n; ++i)
+        hits += (uint64_t)osbf_query_kmer(f, osbf_probe_kmer(seed, i, f->k));
+    return hits;
+}

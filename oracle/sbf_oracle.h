@@ -1,0 +1,88 @@
+/*
+ * sbf_oracle.h -- plain, single-threaded CPU oracle of the Super Bloom filter.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, obviously correct definition
+ * that the GPU library is checked against.  Only the test suite, the smoke
+ * entry point and the benchmark's CPU-baseline leg may load it.  It shares no
+ * code, header, table or constant generator with the HIP library.
+ *
+ * Source: "cuSBF: A Minimizer-Aware Bloom Filter for Genomic Sequence Data
+ * on Modern GPUs" (Dortmann, Vieth, Schmidt), referred to below as [cuSBF].
+ *
+ * Every operation is written per k-mer, straight from its definition: no
+ * sliding windows, no run grouping, no batching.  Insert is a set union and
+ * query a pure function of (k-mer, filter), so this per-k-mer loop fixes the
+ * one correct result for any input.
+ *
+ * Fixed readings where [cuSBF] is silent (hash constants, code order, bit
+ * order) are listed at the top of sbf_oracle.c.
+ */
+#ifndef SBF_ORACLE_H
+#define SBF_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* kind of filter */
+#define OSBF_KIND_SBF 0 /* Super Bloom filter (minimizer shard + Findere s-mers) */
+#define OSBF_KIND_BBF 1 /* per-k-mer blocked Bloom filter with the same shard layout */
+
+typedef struct osbf osbf;
+
+/* ---- primitives (exposed for the pins) ---------------------------------- */
+
+/* 2-bit code of one base, or -1 if the byte is not a DNA base. */
+int osbf_code(unsigned char c);
+/* minimizer hash h_min and s-mer hash h_s; mix is the SplitMix64 finalizer */
+uint64_t osbf_hmin(uint64_t v);
+uint64_t osbf_mix(uint64_t z);
+uint64_t osbf_hs(uint64_t v);
+/* bit position (0..63) of hash index t of an s-mer hash, for H hashes */
+unsigned osbf_bitaddr(uint64_t hs, unsigned t, unsigned H);
+/* i-th probe k-mer (0-based) of the stream started at `seed` */
+uint64_t osbf_probe_kmer(uint64_t seed, uint64_t i, unsigned k);
+
+/* Pack k bases starting at seq into a k-mer value, first base most
+ * significant.  Returns 0 and sets *x if every base is valid, else -1. */
+int osbf_pack_kmer(const char* seq, unsigned k, uint64_t* x);
+/* value of the i-th sub-window of length w of a packed k-mer (0 = first) */
+uint64_t osbf_subwindow(uint64_t x, unsigned k, unsigned i, unsigned w);
+/* minimizer hash of a packed k-mer: min over its k-m+1 m-mers of h_min */
+uint64_t osbf_minimizer_hash(uint64_t x, unsigned k, unsigned m);
+
+/* ---- filter ------------------------------------------------------------- */
+
+/* Returns NULL on invalid parameters or allocation failure. */
+osbf* osbf_create(int kind, unsigned k, unsigned m, unsigned s, unsigned H, uint64_t bits);
+void osbf_destroy(osbf* f);
+uint64_t osbf_num_shards(const osbf* f);
+/* the filter: 4 * num_shards words, shard j is words 4j..4j+3 */
+uint64_t* osbf_words(osbf* f);
+
+/* shard a packed k-mer maps to */
+uint64_t osbf_shard_of(const osbf* f, uint64_t x);
+/* insert / test one packed k-mer */
+void osbf_insert_kmer(osbf* f, uint64_t x);
+int osbf_query_kmer(const osbf* f, uint64_t x);
+
+/* Insert every valid k-mer of an ASCII sequence. */
+void osbf_insert_seq(osbf* f, const char* seq, uint64_t len);
+/* Query every k-mer start of an ASCII sequence.  out receives
+ * ceil((len-k+1)/64) words; bit p (LSB-first within word p/64) is the answer
+ * for the k-mer starting at p; invalid k-mers and tail bits are 0.
+ * Nothing is written when len < k. */
+void osbf_query_seq(const osbf* f, const char* seq, uint64_t len, uint64_t* out);
+/* Query the k-mers starting at the given positions; out[i] = 0/1. */
+void osbf_query_positions(const osbf* f, const char* seq, uint64_t len,
+                          const uint64_t* pos, uint64_t n, uint8_t* out);
+/* Number of positives among n probe k-mers from the stream at `seed`. */
+uint64_t osbf_fpr_probe(const osbf* f, uint64_t n, uint64_t seed);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,68 @@
+"""Pure-Python helpers for the tests: independent routes to facts the oracle
+must agree with, written from the definitions in "cuSBF: A Minimizer-Aware
+Bloom Filter for Genomic Sequence Data on Modern GPUs" (§II-B, §IV-B..E).
+
+They work on strings, not on packed k-mers: every sub-window is cut out of the
+text and packed on its own, so a wrong shift, mask or index in the oracle's
+integer arithmetic shows up as a mismatch.  They only call the oracle's hash
+primitives, which are pinned separately (published SplitMix64 outputs and an
+inverse of h_min).
+"""
+import math
+
+import numpy as np
+
+from oracle import oracle as O
+
+CODE = {"A": 0, "C": 1, "G": 2, "T": 3, "a": 0, "c": 1, "g": 2, "t": 3}
+
+
+def pack_str(s: str) -> int:
+    """Base-4 number with the first base most significant."""
+    v = 0
+    for ch in s:
+        v = v * 4 + CODE[ch]
+    return v
+
+
+def valid_str(s: str) -> bool:
+    return all(ch in CODE for ch in s)
+
+
+def minimizer_hash_str(kmer: str, m: int) -> int:
+    return min(O.hmin(pack_str(kmer[i:i + m])) for i in range(len(kmer) - m + 1))
+
+
+def kmer_bits_str(kmer: str, s: int, H: int):
+    """{(sector, bit)} that the k-mer's s-mers set, from the text."""
+    out = set()
+    for j in range(len(kmer) - s + 1):
+        h = O.hs(pack_str(kmer[j:j + s]))
+        for t in range(H):
+            out.add((t % 4, O.bitaddr(h, t, H)))
+    return out
+
+
+def num_shards(bits: int) -> int:
+    need = -(-bits // 256)
+    n = 1
+    while n < need:
+        n *= 2
+    return n
+
+
+def random_dna(rng: np.random.Generator, n: int, alphabet=b"ACGT") -> bytes:
+    return np.frombuffer(alphabet, dtype=np.uint8)[rng.integers(0, len(alphabet), n)].tobytes()
+
+
+def bits_of(words: np.ndarray, n: int) -> np.ndarray:
+    """First n bits of LSB-first uint64 words as a 0/1 array."""
+    b = np.unpackbits(np.ascontiguousarray(words, dtype="<u8").view(np.uint8), bitorder="little")
+    return b[:n]
+
+
+def binom_ok(hits: int, n: int, p: float, z: float = 3.5) -> bool:
+    """hits within z standard deviations of Binomial(n, p) (normal approx.)."""
+    mu = n * p
+    sd = math.sqrt(max(n * p * (1 - p), 1e-12))
+    return abs(hits - mu) <= z * sd + 1.0

@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Source of the method: "cuSBF: A Minimizer-Aware Bloom Filter for Genomic
+Sequence Data on Modern GPUs" (sections cited per test).  Each pin is chosen so
+that a plausible slip in the oracle (dropped term, wrong shift or index, wrong
+sector, a missing fold) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tests import helpers as T
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+M64 = 2**64 - 1
+GAMMA = 0x9E3779B97F4A7C15
+C1 = 0xBF58476D1CE4E5B9
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---- hash primitives --------------------------------------------------------
+
+def test_splitmix64_published_stream():
+    """mix and the golden-ratio increment reproduce the published SplitMix64
+    outputs; h_s(v) is the SplitMix64 output for state v and the probe stream
+    is the SplitMix64 stream itself."""
+    g = _gold("splitmix64_seed1234567.json")
+    seed, outs = g["seed"], g["outputs"]
+    for i, want in enumerate(outs):
+        assert O.mix((seed + (i + 1) * GAMMA) & M64) == want
+        assert O.hs((seed + i * GAMMA) & M64) == want
+        assert O.probe_kmer(seed, i, 32) == want
+        assert O.probe_kmer(seed, i, 31) == want >> 2
+        assert O.probe_kmer(seed, i, 9) == want >> 46
+
+
+def test_hmin_inverts():
+    """h_min(v) = fold((v + G) * C1): undo it with the modular inverse of C1
+    (the fold x ^ (x >> 32) is its own inverse)."""
+    inv = pow(C1, -1, 2**64)
+    rng = np.random.default_rng(11)
+    vals = [0, 1, 2**32 - 1, 2**62, M64] + [int(x) for x in rng.integers(0, 2**63, 200, dtype=np.uint64)]
+    for v in vals:
+        h = O.hmin(v)
+        u = h ^ (h >> 32)
+        assert ((u * inv) - GAMMA) & M64 == v
+    assert O.hmin(0) != 0  # the offset keeps poly-A off zero
+
+
+def test_hmin_low_bits_depend_on_every_base():
+    """§IV-B takes the shard from the low hash bits.  m-mers that share their
+    last three bases must still spread over the low 6 bits (a chi-square
+    test); without the fold they would all land on one value."""
+    rng = np.random.default_rng(12)
+    n = 64 * 200
+    tail = 0b101101
+    counts = np.zeros(64)
+    for r in rng.integers(0, 2**26, n):
+        counts[O.hmin((int(r) << 6) | tail) & 63] += 1
+    chi2 = float(((counts - n / 64) ** 2 / (n / 64)).sum())
+    assert chi2 < 120  # 63 dof, p ~ 1e-5
+
+
+def test_bitaddr_slices():
+    """§IV-G bit-slicing: for H <= 10 hash index t reads the low 6 bits of
+    slice t of width floor(64/H); for H > 10 the salted multiply's top bits."""
+    h = 0x0123456789ABCDEF
+    for H in range(1, 11):
+        w = 64 // H
+        for t in range(H):
+            assert O.bitaddr(h, t, H) == (h >> (t * w)) & 63
+    # H = 4: the four 16-bit slices of 0x0123456789ABCDEF end in
+    # 0xCDEF, 0x89AB, 0x4567, 0x0123 -> low 6 bits 0x2F, 0x2B, 0x27, 0x23
+    assert [O.bitaddr(h, t, 4) for t in range(4)] == [0x2F, 0x2B, 0x27, 0x23]
+    for t in range(12):
+        salt = ((2 * t + 1) * GAMMA) & M64
+        assert O.bitaddr(h, t, 12) == ((h * salt) & M64) >> 58
+
+
+# ---- encoding and packing ---------------------------------------------------
+
+def test_code_table_exhaustive():
+    """§IV-A: four DNA symbols; every other byte is invalid."""
+    want = {ord(c): v for c, v in T.CODE.items()}
+    for b in range(256):
+        assert O.code(b) == want.get(b, -1)
+
+
+def test_pack_known_answers():
+    assert O.pack_kmer("ACGT") == 0x1B
+    assert O.pack_kmer("A") == 0 and O.pack_kmer("T") == 3
+    assert O.pack_kmer("T" * 32) == M64
+    assert O.pack_kmer("acgt") == 0x1B
+    assert O.pack_kmer("ACNT") is None
+    rng = np.random.default_rng(13)
+    for _ in range(50):
+        k = int(rng.integers(1, 33))
+        s = T.random_dna(rng, k).decode()
+        assert O.pack_kmer(s) == T.pack_str(s)
+
+
+def test_fig2b_smer_enumeration():
+    """Fig. 2b: k = 9, s = 6 gives four s-mers, in order, cut from the k-mer."""
+    g = _gold("cusbf_fig2.json")["fig2b"]
+    x = O.pack_kmer(g["kmer"])
+    k, s = len(g["kmer"]), g["s"]
+    assert k - s + 1 == len(g["smers"]) == 4
+    assert [O.subwindow(x, k, j, s) for j in range(4)] == [T.pack_str(t) for t in g["smers"]]
+
+
+def test_fig2a_kmers_share_the_mmer():
+    """Fig. 2a: the k-mers shown are consecutive 9-mers of the sequence and
+    all contain the m-mer the figure marks as their shared minimizer."""
+    g = _gold("cusbf_fig2.json")["fig2a"]
+    seq, k, m = g["sequence"], g["k"], g["m"]
+    kmers = [seq[p:p + k] for p in range(len(seq) - k + 1)]
+    assert len(kmers) == 4 and kmers[1:] == g["kmers_shown"]
+    mm = T.pack_str(g["shared_minimizer"])
+    for km in g["kmers_shown"]:
+        x = O.pack_kmer(km)
+        assert mm in [O.subwindow(x, k, i, m) for i in range(k - m + 1)]
+
+
+# ---- minimizer and shard ----------------------------------------------------
+
+def test_minimizer_brute_force():
+    """§II-B-1 / Algorithm 1: min over every m-mer cut from the text."""
+    rng = np.random.default_rng(14)
+    for _ in range(300):
+        k = int(rng.integers(1, 33))
+        m = int(rng.integers(1, k + 1))
+        km = T.random_dna(rng, k).decode()
+        assert O.minimizer_hash(O.pack_kmer(km), k, m) == T.minimizer_hash_str(km, m)
+
+
+def test_minimizer_density():
+    """§II-B-1: random minimizers on random text have density about 2/(w+1);
+    for k = 31, m = 16 the mean super-k-mer is (w+1)/2 = 8.5 k-mers."""
+    rng = np.random.default_rng(15)
+    k, m = 31, 16
+    w = k - m + 1
+    seq = T.random_dna(rng, 60000)
+    xs = [O.pack_kmer(seq[p:p + k]) for p in range(len(seq) - k + 1)]
+    mh = np.array([O.minimizer_hash(x, k, m) for x in xs], dtype=np.uint64)
+    changes = int((mh[1:] != mh[:-1]).sum())
+    density = changes / (len(mh) - 1)
+    assert abs(density - 2 / (w + 1)) < 0.06 * 2 / (w + 1)
+    assert abs(1 / density - (w + 1) / 2) < 0.6
+
+
+def test_shard_uniformity():
+    f = O.OracleFilter(31, 16, 28, 4, 64 * 256)
+    assert f.num_shards == 64
+    rng = np.random.default_rng(16)
+    counts = np.zeros(64)
+    n = 64 * 150
+    for x in rng.integers(0, 2**62, n, dtype=np.uint64):
+        counts[f.shard_of(int(x))] += 1
+    chi2 = float(((counts - n / 64) ** 2 / (n / 64)).sum())
+    assert chi2 < 120
+
+
+def test_shard_count_rounding():
+    """§IV-B: shard count rounded up to a power of two, 256-bit shards."""
+    for bits, n in [(1, 1), (256, 1), (257, 2), (2**20, 4096), (2**20 + 1, 8192), (3 * 256, 4)]:
+        f = O.OracleFilter(31, 16, 28, 4, bits)
+        assert f.num_shards == n == T.num_shards(bits)
+
+
+# ---- single k-mer bit layout ------------------------------------------------
+
+@pytest.mark.parametrize("k,m,s,H", [(31, 16, 28, 4), (9, 5, 6, 3), (31, 12, 24, 6), (20, 20, 20, 2), (16, 4, 10, 1), (31, 16, 28, 12)])
+def test_single_kmer_bits(k, m, s, H):
+    """§IV-B / Algorithm 1: one k-mer touches one shard; hash index t sets a
+    bit in word t mod 4; the set bits are exactly those of its s-mers."""
+    rng = np.random.default_rng(17 + k + m + s + H)
+    for _ in range(20):
+        f = O.OracleFilter(k, m, s, H, 2**14)
+        km = T.random_dna(rng, k).decode()
+        x = O.pack_kmer(km)
+        f.insert_kmer(x)
+        w = f.words().reshape(-1, 4)
+        nz = np.nonzero(w.any(axis=1))[0]
+        assert list(nz) == [f.shard_of(x)]
+        assert f.shard_of(x) == T.minimizer_hash_str(km, m) % f.num_shards
+        got = {(q, b) for q in range(4) for b in range(64) if (int(w[nz[0], q]) >> b) & 1}
+        assert got == T.kmer_bits_str(km, s, H)
+        assert 1 <= len(got) <= (k - s + 1) * H
+        for q in range(H, 4):
+            assert w[nz[0], q] == 0
+        assert f.query_kmer(x)
+
+
+def test_bbf_single_key():
+    """Blocked Bloom comparator (§II-A, Fig. 1b): one hash of the key picks the
+    block, H bits from a second hash of it."""
+    f = O.OracleFilter(31, 0, 0, 4, 2**14, kind=O.KIND_BBF)
+    x = O.pack_kmer("ACGTACGTACGTACGTACGTACGTACGTACG")
+    f.insert_kmer(x)
+    w = f.words().reshape(-1, 4)
+    blk = O.hs(x) % f.num_shards
+    assert list(np.nonzero(w.any(axis=1))[0]) == [blk]
+    hb = O.hs(O.hs(x))
+    want = np.zeros(4, dtype=np.uint64)
+    for t in range(4):
+        want[t % 4] |= np.uint64(1 << O.bitaddr(hb, t, 4))
+    assert (w[blk] == want).all()
+
+
+# ---- sequences ---------------------------------------------------------------
+
+def test_no_false_negatives_and_invalid():
+    """§II-A: a Bloom filter has no false negatives; §IV-F: a k-mer holding a
+    separator is invalid and queries false."""
+    rng = np.random.default_rng(18)
+    k = 31
+    seq = bytearray(T.random_dna(rng, 3000))
+    for p in rng.integers(0, len(seq), 12):
+        seq[p] = ord("N")
+    seq = bytes(seq)
+    f = O.OracleFilter(k, 16, 28, 4, 2**16)
+    f.insert_seq(seq)
+    nk = len(seq) - k + 1
+    got = T.bits_of(f.query_seq(seq), nk)
+    want = np.array([T.valid_str(seq[p:p + k].decode()) for p in range(nk)], dtype=np.uint8)
+    assert (got == want).all()
+    tail = f.query_seq(seq)
+    assert tail[-1] >> np.uint64(nk % 64) == 0 if nk % 64 else True
+
+
+def test_query_seq_matches_per_kmer():
+    rng = np.random.default_rng(19)
+    k = 21
+    f = O.OracleFilter(k, 11, 19, 3, 2**12)
+    f.insert_seq(T.random_dna(rng, 4000))
+    q = T.random_dna(rng, 2000, alphabet=b"ACGTN" + b"ACGT" * 10)
+    got = T.bits_of(f.query_seq(q), len(q) - k + 1)
+    for p in range(len(q) - k + 1):
+        km = q[p:p + k].decode()
+        want = T.valid_str(km) and f.query_kmer(T.pack_str(km))
+        assert got[p] == want
+    pos = rng.integers(0, len(q), 300)
+    qp = f.query_positions(q, pos)
+    for i, p in enumerate(pos):
+        assert qp[i] == (got[p] if p + k <= len(q) else 0)
+
+
+def test_insert_is_a_union():
+    """Insert is a set union: order-free, idempotent, and records joined by a
+    separator insert exactly the k-mers of each record (§IV-F)."""
+    rng = np.random.default_rng(20)
+    a, b = T.random_dna(rng, 700), T.random_dna(rng, 500)
+    args = (31, 16, 28, 4, 2**13)
+    f1, f2, f3, f4 = (O.OracleFilter(*args) for _ in range(4))
+    f1.insert_seq(a); f1.insert_seq(b)
+    f2.insert_seq(b); f2.insert_seq(a)
+    f3.insert_seq(a + b"N" + b)
+    f4.insert_seq(a + b"N" + b); f4.insert_seq(a + b"N" + b)
+    w = f1.words()
+    for g in (f2, f3, f4):
+        assert (g.words() == w).all()
+    assert w.any()
+
+
+def test_short_and_empty_sequences():
+    f = O.OracleFilter(31, 16, 28, 4, 2**12)
+    for L in (0, 1, 30):
+        f.insert_seq(b"A" * L)
+        assert f.query_seq(b"A" * L).size == 0
+    assert not f.words().any()
+    f.insert_seq(b"A" * 31)
+    assert f.words().any()
+    assert T.bits_of(f.query_seq(b"A" * 31), 1)[0] == 1
+
+
+# ---- false-positive rate -----------------------------------------------------
+
+def test_single_word_bloom_eq1():
+    """Textbook reduction of Eq. (1): one 256-bit shard (bits = 256), s = m = k
+    and H = 1 make word 0 a 64-bit Bloom filter with one hash.  After n
+    distinct keys the chance that a random key hits is 1 - (1 - 1/64)^n,
+    whose large-m form is Eq. (1)."""
+    rng = np.random.default_rng(21)
+    k, n, trials, probes = 31, 40, 60, 2000
+    hits = 0
+    for tr in range(trials):
+        f = O.OracleFilter(k, k, k, 1, 256)
+        for x in rng.choice(2**62, n, replace=False):
+            f.insert_kmer(int(x))
+        hits += f.fpr_probe(probes, 1000 + tr)
+    p = 1 - (1 - 1 / 64) ** n
+    assert T.binom_ok(hits, trials * probes, p, z=4.5)
+    assert abs(p - (1 - math.exp(-n / 64))) < 0.01  # Eq. (1) with H = 1
+
+
+def test_sector_independence():
+    """With H = 4 and one shard, the four hash indices fill four separate
+    words from separate hash slices: a random key hits with probability
+    prod_q fill_q (fill measured on the filter itself)."""
+    rng = np.random.default_rng(22)
+    hits, expect, total = 0, 0.0, 0
+    for tr in range(40):
+        f = O.OracleFilter(31, 31, 31, 4, 256)
+        for x in rng.choice(2**62, 30, replace=False):
+            f.insert_kmer(int(x))
+        w = f.words()
+        p = float(np.prod([bin(int(v)).count("1") / 64 for v in w]))
+        n = 3000
+        hits += f.fpr_probe(n, 5000 + tr)
+        expect += n * p
+        total += n
+    assert abs(hits - expect) <= 4.5 * math.sqrt(expect) + 2
+
+
+@pytest.mark.parametrize("k,m,s,H", [(31, 16, 28, 4), (31, 16, 24, 2), (21, 11, 19, 3)])
+def test_fpr_fill_based(k, m, s, H):
+    """Eq. (2) refined by the actual shard loads: a random alien k-mer lands in
+    a uniform shard and each of its k-s+1 s-mers must hit H bits, so
+    P(hit) = mean over shards of prod_q (fill_q)^(c_q (k-s+1)), c_q the number
+    of hash indices in word q."""
+    rng = np.random.default_rng(23 + s)
+    f = O.OracleFilter(k, m, s, H, 2**14)
+    f.insert_seq(T.random_dna(rng, 6000))
+    w = f.words().reshape(-1, 4)
+    fill = np.array([[bin(int(v)).count("1") / 64 for v in row] for row in w])
+    c = [sum(1 for t in range(H) if t % 4 == q) for q in range(4)]
+    z1 = k - s + 1
+    p = float(np.mean(np.prod([fill[:, q] ** (c[q] * z1) for q in range(4)], axis=0)))
+    n = 200000
+    hits = f.fpr_probe(n, 0x5EED)
+    assert p > 1e-4
+    assert T.binom_ok(hits, n, p, z=4.5)
+
+
+def test_findere_suppresses_aliens():
+    """§II-B-2: k-mers one substitution away from inserted ones share k-s of
+    their s-mers and hit far more often than random aliens."""
+    rng = np.random.default_rng(24)
+    k = 31
+    f = O.OracleFilter(k, 16, 28, 4, 2**16)
+    seq = T.random_dna(rng, 3000)
+    f.insert_seq(seq)
+    near = 0
+    trials = 1500
+    for _ in range(trials):
+        p = int(rng.integers(0, len(seq) - k))
+        km = bytearray(seq[p:p + k])
+        j = int(rng.integers(0, k))
+        km[j] = ord("ACGT"[(T.CODE[chr(km[j])] + int(rng.integers(1, 4))) % 4])
+        near += f.query_kmer(T.pack_str(km.decode()))
+    alien = f.fpr_probe(trials * 20, 77)
+    assert near / trials > 5 * (alien / (trials * 20) + 1e-4)
