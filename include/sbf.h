@@ -1,0 +1,183 @@
+/*
+ * sbf.h -- C ABI of the MI355X (gfx950) Super Bloom filter library, libsbf.so.
+ *
+ * The method is that of "cuSBF: A Minimizer-Aware Bloom Filter for Genomic
+ * Sequence Data on Modern GPUs" (Dortmann, Vieth, Schmidt), cited as [cuSBF]:
+ * DNA is 2-bit packed; the minimizer hash of each k-mer picks one 256-bit
+ * shard (§II-B-1, §IV-B); each of the k-mer's k-s+1 overlapping s-mers sets
+ * or tests H bits inside that shard, hash index t in 64-bit word t mod 4
+ * (Findere, §II-B-2; §IV-B); a k-mer is present only if all of its s-mers
+ * hit (Algorithm 2).  Hash functions and bit orders are fixed as follows:
+ *
+ *   codes        A/a=0 C/c=1 G/g=2 T/t=3, every other byte is invalid
+ *   k-mer value  first base in the most significant bits (§IV-C)
+ *   h_min(v)     u ^ (u >> 32), u = (v + G) * C1 mod 2^64       (§IV-G)
+ *   h_s(v)       SplitMix64 finalizer of v + G                   (§IV-G)
+ *   bit of hash t: H <= 10: bits [t*floor(64/H), +6) of h_s;
+ *                  H > 10 : top 6 bits of h_s * ((2t+1) * G)     (§IV-G)
+ *   shard        min over the k-m+1 m-mers of h_min, & (N-1)     (Algorithm 1)
+ *   N            smallest power of two >= ceil(bits / 256)       (§IV-B)
+ *   G = 0x9E3779B97F4A7C15, C1 = 0xBF58476D1CE4E5B9, C2 = 0x94D049BB133111EB
+ *
+ * Conventions
+ *  - Every call returns SBF_OK (0) or a negative SBF_E* code and never aborts.
+ *    A failing call leaves no partial allocation behind; the text of the last
+ *    error of the calling thread is returned by sbf_last_error().
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Calls flagged SBF_HOST take host pointers and synchronize before they
+ *    return; calls flagged SBF_DEVICE (and the *_packed / *_device calls) take
+ *    device pointers and are asynchronous on `stream` ([cuSBF] §IV-A: host
+ *    entry points synchronize, device entry points leave ordering to the
+ *    caller).
+ *  - Concurrent inserts into one filter are safe (bitwise OR is idempotent and
+ *    commutative), but calls on one handle share its staging buffers: issue
+ *    the *_seq calls of one handle on one stream, or serialize them.
+ *
+ * Packed sequence layout (device memory), for a sequence of `len` bases:
+ *  - codes: uint32_t[ceil(len/16)]; base j occupies bits 31-2r..30-2r of word
+ *    j/16, r = j mod 16 (the first base of a word is in its top bits).
+ *  - valid: uint32_t[ceil(len/32)]; bit j mod 32 of word j/32 is 1 iff base j
+ *    is one of ACGTacgt.  Bits at or beyond len must be 0 (sbf_pack writes
+ *    them so); k-mers that would reach past len are never valid.
+ * Query output: uint64_t[ceil((len-k+1)/64)]; bit p mod 64 of word p/64 is the
+ * answer for the k-mer starting at base p (LSB first); invalid k-mers and the
+ * bits past len-k+1 are 0.  Nothing is written when len < k.
+ */
+#ifndef SBF_H
+#define SBF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define SBF_OK 0
+#define SBF_EINVAL (-1)       /* bad argument (parameter range, NULL pointer, size) */
+#define SBF_EUNSUPPORTED (-2) /* reserved: parameter combination not available */
+#define SBF_ENOMEM (-3)       /* device or host allocation failed */
+#define SBF_EDEVICE (-4)      /* a HIP runtime call or kernel launch failed */
+
+/* filter kinds */
+#define SBF_KIND_SBF 0 /* Super Bloom filter */
+#define SBF_KIND_BBF 1 /* per-k-mer blocked Bloom filter, same shard layout */
+
+/* where the pointers of a *_seq / copy call live */
+#define SBF_HOST 1u
+#define SBF_DEVICE 2u
+
+typedef struct sbf_handle sbf_t;
+
+typedef struct sbf_info {
+    uint32_t k, m, s, H; /* m = s = 0 for a blocked Bloom filter */
+    uint32_t kind;       /* SBF_KIND_* */
+    uint32_t specialized; /* 1 if a compile-time specialized kernel set serves it */
+    uint64_t num_shards;  /* N, a power of two */
+    uint64_t filter_bytes; /* 32 * N */
+} sbf_info_t;
+
+/*
+ * Create an empty Super Bloom filter ([cuSBF] §IV-A: k, s, m, H fix the
+ * method, the filter size in bits is the only run-time input; §IV-B layout).
+ * Requires 1 <= m <= k <= 32, 1 <= s <= k, 1 <= H <= 64, 1 <= bits <= 2^40.
+ * The device filter (uint64_t[4N], zeroed) is owned by the handle; *out is
+ * set only on success.  Errors: SBF_EINVAL, SBF_ENOMEM, SBF_EDEVICE.
+ */
+int sbf_create(sbf_t** out, uint32_t k, uint32_t m, uint32_t s, uint32_t H, uint64_t bits);
+
+/*
+ * Create an empty per-k-mer blocked Bloom filter ([cuSBF] §II-A, Fig. 1b):
+ * block = h_s(x) & (N-1), hash t sets bit t of h_s(h_s(x)) (sliced as above)
+ * in word t mod 4 of the block.  Same shard layout and calls as the SBF.
+ * Requires 1 <= k <= 32, 1 <= H <= 64, 1 <= bits <= 2^40.
+ */
+int sbf_create_bbf(sbf_t** out, uint32_t k, uint32_t H, uint64_t bits);
+
+/* Free a filter and its buffers (synchronizes the device). NULL is a no-op. */
+int sbf_destroy(sbf_t* h);
+
+/* Zero the filter, asynchronously on `stream`. */
+int sbf_clear(sbf_t* h, void* stream);
+
+/* Parameters and sizes of a filter into a caller-owned struct. */
+int sbf_info(const sbf_t* h, sbf_info_t* out);
+
+/*
+ * Copy the raw filter words (uint64_t[4N], shard j = words 4j..4j+3) to dst.
+ * flags = SBF_HOST: dst is host memory, synchronizes; SBF_DEVICE: device
+ * memory, asynchronous on `stream`.  SBF_EINVAL if bytes < 32 * N.
+ */
+int sbf_copy_filter(const sbf_t* h, void* dst, uint64_t bytes, uint32_t flags, void* stream);
+
+/*
+ * Device pointer to the filter words (owned by the handle, valid until
+ * sbf_destroy), or NULL for a NULL handle.
+ */
+const uint64_t* sbf_filter_device_ptr(const sbf_t* h);
+
+/* Number of uint32_t words of the packed codes and validity of len bases. */
+void sbf_packed_words(uint64_t len, uint64_t* code_words, uint64_t* valid_words);
+
+/*
+ * Pack an ASCII sequence held in device memory into the layout above
+ * ([cuSBF] §IV-A 2-bit DNA alphabet, §IV-F: any non-ACGT byte -- an 'N'
+ * separator between records, a newline -- is invalid).  Asynchronous.  The
+ * caller allocates both outputs (sbf_packed_words).  len = 0 is a no-op.
+ */
+int sbf_pack(const char* d_ascii, uint64_t len, uint32_t* d_codes, uint32_t* d_valid, void* stream);
+
+/*
+ * Insert every valid k-mer of a packed device sequence ([cuSBF] §IV-D,
+ * Algorithm 1).  Asynchronous on `stream`; len < k is a no-op.
+ */
+int sbf_insert_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid,
+                      uint64_t len, void* stream);
+
+/*
+ * Query every k-mer start of a packed device sequence ([cuSBF] §IV-E,
+ * Algorithm 2) into d_out (device, ceil((len-k+1)/64) words, fully
+ * overwritten).  Asynchronous.  len < k is a no-op.
+ */
+int sbf_query_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid,
+                     uint64_t len, uint64_t* d_out, void* stream);
+
+/*
+ * Sequence-native insert ([cuSBF] §IV-A input forms, §IV-F records joined by
+ * an invalid separator).  flags = SBF_HOST: `seq` is host memory; it is staged
+ * to the device, packed and inserted, and the call synchronizes.
+ * SBF_DEVICE: `seq` is device memory; packing goes to the handle's staging
+ * buffer and the call is asynchronous on `stream`.  The staging buffer grows
+ * on demand; growing synchronizes `stream` first.
+ */
+int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void* stream);
+
+/*
+ * Sequence-native query: one bit per k-mer start into out_bits
+ * (ceil((len-k+1)/64) uint64_t words, fully overwritten), which lives where
+ * `flags` says (SBF_HOST: synchronizes; SBF_DEVICE: asynchronous).
+ */
+int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits,
+                  uint32_t flags, void* stream);
+
+/*
+ * False-positive probe ([cuSBF] §V-D): query n k-mers drawn on the device
+ * from the SplitMix64 stream seeded with `seed` (k-mer i = output i shifted
+ * right by 64-2k) and store the number of positives in *hits (host).
+ * Synchronizes.
+ */
+int sbf_fpr_probe(sbf_t* h, uint64_t n, uint64_t seed, uint64_t* hits);
+
+/* As sbf_fpr_probe, asynchronous: the count lands in *d_hits (device). */
+int sbf_fpr_probe_device(sbf_t* h, uint64_t n, uint64_t seed, uint64_t* d_hits, void* stream);
+
+/* Static text for a return code. */
+const char* sbf_strerror(int code);
+
+/* Text of the calling thread's last error ("" if none). */
+const char* sbf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SBF_H */

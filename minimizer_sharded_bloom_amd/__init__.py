@@ -1,0 +1,200 @@
+"""MI355X (gfx950) Super Bloom filter: Python binding of libsbf.so.
+
+The method is that of "cuSBF: A Minimizer-Aware Bloom Filter for Genomic
+Sequence Data on Modern GPUs": a k-mer's minimizer hash picks a 256-bit shard,
+its k-s+1 s-mers set or test H bits inside it, and a query answers present
+only if every s-mer hits.  The functions and methods here marshal arguments
+to the C ABI of include/sbf.h; PyTorch provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import SBF_DEVICE, SBF_HOST, SbfError, check
+
+__all__ = ["SuperBloomFilter", "pack", "packed_words", "SbfError", "lib"]
+
+
+def lib():
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream) -> int | None:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _is_device_tensor(x) -> bool:
+    try:
+        torch = _torch()
+    except ImportError:
+        return False
+    return isinstance(x, torch.Tensor) and x.is_cuda
+
+
+def _host_bytes(seq) -> np.ndarray:
+    if isinstance(seq, str):
+        seq = seq.encode("ascii")
+    if isinstance(seq, (bytes, bytearray, memoryview)):
+        return np.frombuffer(bytes(seq), dtype=np.uint8)
+    if _is_device_tensor(seq):
+        raise TypeError("expected host data")
+    if hasattr(seq, "numpy"):
+        seq = seq.numpy()
+    return np.ascontiguousarray(seq, dtype=np.uint8).reshape(-1)
+
+
+def packed_words(length: int) -> tuple[int, int]:
+    """(code words, validity words) of the packed layout of `length` bases."""
+    cw, vw = ctypes.c_uint64(), ctypes.c_uint64()
+    lib().sbf_packed_words(length, ctypes.byref(cw), ctypes.byref(vw))
+    return cw.value, vw.value
+
+
+def pack(ascii_dev, stream=None):
+    """Pack a device uint8 tensor of ASCII bases into (codes, valid) int32
+    device tensors in the layout of include/sbf.h.  Asynchronous."""
+    torch = _torch()
+    if not _is_device_tensor(ascii_dev) or ascii_dev.dtype != torch.uint8:
+        raise TypeError("pack expects a CUDA uint8 tensor")
+    a = ascii_dev.contiguous().view(-1)
+    cw, vw = packed_words(a.numel())
+    codes = torch.empty(max(cw, 1), dtype=torch.int32, device=a.device)
+    valid = torch.empty(max(vw, 1), dtype=torch.int32, device=a.device)
+    check(lib().sbf_pack(a.data_ptr(), a.numel(), codes.data_ptr(), valid.data_ptr(), _stream_ptr(stream)), "sbf_pack")
+    return codes, valid
+
+
+class SuperBloomFilter:
+    """A Super Bloom filter (or, with `blocked()`, the per-k-mer blocked Bloom
+    comparator) living in device memory."""
+
+    def __init__(self, k: int, m: int, s: int, H: int, bits: int, *, _kind: int = _lib.SBF_KIND_SBF):
+        h = ctypes.c_void_p()
+        if _kind == _lib.SBF_KIND_BBF:
+            check(lib().sbf_create_bbf(ctypes.byref(h), k, H, bits), "sbf_create_bbf")
+        else:
+            check(lib().sbf_create(ctypes.byref(h), k, m, s, H, bits), "sbf_create")
+        self._h = h
+        inf = _lib.SbfInfo()
+        check(lib().sbf_info(self._h, ctypes.byref(inf)), "sbf_info")
+        self.k, self.m, self.s, self.H = inf.k, inf.m, inf.s, inf.H
+        self.kind = inf.kind
+        self.specialized = bool(inf.specialized)
+        self.num_shards = inf.num_shards
+        self.filter_bytes = inf.filter_bytes
+
+    @classmethod
+    def blocked(cls, k: int, H: int, bits: int) -> "SuperBloomFilter":
+        return cls(k, 0, 0, H, bits, _kind=_lib.SBF_KIND_BBF)
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            check(lib().sbf_destroy(self._h), "sbf_destroy")
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    @property
+    def handle(self) -> int:
+        return self._h.value
+
+    def num_answer_words(self, length: int) -> int:
+        return 0 if length < self.k else (length - self.k + 1 + 63) // 64
+
+    # ---- filter state ------------------------------------------------------
+    def clear(self, stream=None):
+        check(lib().sbf_clear(self._h, _stream_ptr(stream)), "sbf_clear")
+
+    def words(self) -> np.ndarray:
+        """Host copy of the filter words (uint64[4N]); synchronizes."""
+        out = np.empty(4 * self.num_shards, dtype=np.uint64)
+        check(lib().sbf_copy_filter(self._h, out.ctypes.data, out.nbytes, SBF_HOST, None), "sbf_copy_filter")
+        return out
+
+    def words_device(self, stream=None):
+        """Device copy of the filter words as an int64 tensor (asynchronous)."""
+        torch = _torch()
+        out = torch.empty(4 * self.num_shards, dtype=torch.int64, device="cuda")
+        check(lib().sbf_copy_filter(self._h, out.data_ptr(), out.numel() * 8, SBF_DEVICE, _stream_ptr(stream)),
+              "sbf_copy_filter")
+        return out
+
+    # ---- sequence-native calls ----------------------------------------------
+    def insert_seq(self, seq, stream=None):
+        """Insert every valid k-mer of an ASCII sequence: a CUDA uint8 tensor
+        (asynchronous) or host bytes / str / numpy (synchronizes)."""
+        if _is_device_tensor(seq):
+            a = seq.contiguous().view(-1)
+            check(lib().sbf_insert_seq(self._h, a.data_ptr(), a.numel(), SBF_DEVICE, _stream_ptr(stream)),
+                  "sbf_insert_seq")
+        else:
+            a = _host_bytes(seq)
+            check(lib().sbf_insert_seq(self._h, a.ctypes.data, a.size, SBF_HOST, _stream_ptr(stream)), "sbf_insert_seq")
+
+    def query_seq(self, seq, out=None, stream=None):
+        """One answer bit per k-mer start.  Device input gives an int64 CUDA
+        tensor of bit words (asynchronous); host input a numpy uint64 array."""
+        if _is_device_tensor(seq):
+            torch = _torch()
+            a = seq.contiguous().view(-1)
+            nw = self.num_answer_words(a.numel())
+            if out is None:
+                out = torch.empty(max(nw, 1), dtype=torch.int64, device=a.device)
+            if nw:
+                check(lib().sbf_query_seq(self._h, a.data_ptr(), a.numel(), out.data_ptr(), SBF_DEVICE,
+                                          _stream_ptr(stream)), "sbf_query_seq")
+            return out[:nw]
+        a = _host_bytes(seq)
+        nw = self.num_answer_words(a.size)
+        res = np.zeros(nw, dtype=np.uint64)
+        if nw:
+            check(lib().sbf_query_seq(self._h, a.ctypes.data, a.size, res.ctypes.data, SBF_HOST, _stream_ptr(stream)),
+                  "sbf_query_seq")
+        return res
+
+    # ---- packed (device-resident) calls ---------------------------------------
+    def insert_packed(self, codes, valid, length: int, stream=None):
+        check(lib().sbf_insert_packed(self._h, codes.data_ptr(), valid.data_ptr(), length, _stream_ptr(stream)),
+              "sbf_insert_packed")
+
+    def query_packed(self, codes, valid, length: int, out=None, stream=None):
+        torch = _torch()
+        nw = self.num_answer_words(length)
+        if out is None:
+            out = torch.empty(max(nw, 1), dtype=torch.int64, device=codes.device)
+        if nw:
+            check(lib().sbf_query_packed(self._h, codes.data_ptr(), valid.data_ptr(), length, out.data_ptr(),
+                                         _stream_ptr(stream)), "sbf_query_packed")
+        return out[:nw]
+
+    # ---- false-positive probe ---------------------------------------------------
+    def fpr_probe(self, n: int, seed: int) -> int:
+        hits = ctypes.c_uint64()
+        check(lib().sbf_fpr_probe(self._h, n, seed & (2**64 - 1), ctypes.byref(hits)), "sbf_fpr_probe")
+        return hits.value
+
+    def fpr_probe_device(self, n: int, seed: int, out, stream=None):
+        check(lib().sbf_fpr_probe_device(self._h, n, seed & (2**64 - 1), out.data_ptr(), _stream_ptr(stream)),
+              "sbf_fpr_probe_device")
+        return out

@@ -1,0 +1,517 @@
+// sbf_api.cpp -- the extern "C" surface of libsbf.so (declared in
+// include/sbf.h): argument checks, filter ownership, staging buffers and
+// dispatch to the specialized or generic kernel sets.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/sbf.h"
+#include "sbf_internal.hpp"
+
+namespace sbf {
+const SpecEntry* spec_table_m12(size_t* n);
+const SpecEntry* spec_table_m16(size_t* n);
+const SpecEntry* spec_table_m20(size_t* n);
+const SpecEntry* spec_table_extra(size_t* n);
+
+bool find_specialized(const Params& p, KernelSet* out)
+{
+    typedef const SpecEntry* (*TableFn)(size_t*);
+    static const TableFn tables[] = {spec_table_m12, spec_table_m16, spec_table_m20, spec_table_extra};
+    for (TableFn fn : tables) {
+        size_t n = 0;
+        const SpecEntry* t = fn(&n);
+        for (size_t i = 0; i < n; ++i) {
+            if (t[i].kind == p.kind && t[i].k == p.k && t[i].m == p.m && t[i].s == p.s && t[i].H == p.H) {
+                *out = t[i].make();
+                return true;
+            }
+        }
+    }
+    return false;
+}
+}  // namespace sbf
+
+struct sbf_handle {
+    sbf::Params P;
+    uint64_t num_shards;
+    uint64_t* d_filter;
+    sbf::KernelSet ks;
+    int device;
+    // staging: ASCII bytes, packed codes, validity, probe counter
+    char* d_ascii;
+    uint64_t ascii_cap;
+    uint32_t* d_codes;
+    uint32_t* d_valid;
+    uint64_t packed_cap;  // bases
+    uint64_t* d_out;      // query bits for host-facing queries
+    uint64_t out_cap;     // words
+    unsigned long long* d_hits;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* what)
+{
+    g_last_error = what;
+    return code;
+}
+
+int fail_hip(hipError_t e, const char* what)
+{
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return e == hipErrorOutOfMemory ? SBF_ENOMEM : SBF_EDEVICE;
+}
+
+void ok() { g_last_error.clear(); }
+
+uint64_t code_words(uint64_t len) { return (len + 15) / 16; }
+uint64_t valid_words(uint64_t len) { return (len + 31) / 32; }
+uint64_t out_words(uint64_t len, uint32_t k) { return len < k ? 0 : (len - k + 1 + 63) / 64; }
+
+int set_device(const sbf_t* h)
+{
+    hipError_t e = hipSetDevice(h->device);
+    return e == hipSuccess ? SBF_OK : fail_hip(e, "hipSetDevice");
+}
+
+int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
+{
+    if (!out)
+        return fail(SBF_EINVAL, "out is NULL");
+    if (P.k < 1 || P.k > 32)
+        return fail(SBF_EINVAL, "k must be in 1..32");
+    if (P.kind == SBF_KIND_SBF && (P.m < 1 || P.m > P.k))
+        return fail(SBF_EINVAL, "m must be in 1..k");
+    if (P.kind == SBF_KIND_SBF && (P.s < 1 || P.s > P.k))
+        return fail(SBF_EINVAL, "s must be in 1..k");
+    if (P.H < 1 || P.H > 64)
+        return fail(SBF_EINVAL, "H must be in 1..64");
+    if (bits < 1 || bits > (1ull << 40))
+        return fail(SBF_EINVAL, "bits must be in 1..2^40");
+    const uint64_t need = (bits + 255) / 256;
+    uint64_t n = 1;
+    while (n < need)
+        n <<= 1;
+
+    sbf_t* h = new (std::nothrow) sbf_t();
+    if (!h)
+        return fail(SBF_ENOMEM, "host allocation failed");
+    h->P = P;
+    h->num_shards = n;
+    if (!sbf::find_specialized(P, &h->ks))
+        h->ks = sbf::generic_kernels();
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) {
+        delete h;
+        return fail_hip(e, "hipGetDevice");
+    }
+    e = hipMalloc(reinterpret_cast<void**>(&h->d_filter), 32 * n);
+    if (e != hipSuccess) {
+        delete h;
+        return fail_hip(e, "hipMalloc(filter)");
+    }
+    e = hipMalloc(reinterpret_cast<void**>(&h->d_hits), sizeof(unsigned long long));
+    if (e != hipSuccess) {
+        (void)hipFree(h->d_filter);
+        delete h;
+        return fail_hip(e, "hipMalloc(counter)");
+    }
+    e = sbf::launch_fill_zero(h->d_filter, 4 * n, nullptr);
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(h->d_filter);
+        (void)hipFree(h->d_hits);
+        delete h;
+        return fail_hip(e, "zeroing the filter");
+    }
+    *out = h;
+    ok();
+    return SBF_OK;
+}
+
+// Grow a device buffer; synchronizes `st` first so no queued work still uses it.
+template <class T>
+int grow(T** buf, uint64_t* cap, uint64_t need, uint64_t elem, hipStream_t st, const char* what)
+{
+    if (*cap >= need)
+        return SBF_OK;
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return fail_hip(e, what);
+    if (*buf)
+        (void)hipFree(*buf);
+    *buf = nullptr;
+    *cap = 0;
+    const uint64_t n = need + need / 4 + 1024;
+    e = hipMalloc(reinterpret_cast<void**>(buf), n * elem);
+    if (e != hipSuccess) {
+        *buf = nullptr;
+        return fail_hip(e, what);
+    }
+    *cap = n;
+    return SBF_OK;
+}
+
+int grow_packed(sbf_t* h, uint64_t len, hipStream_t st)
+{
+    if (h->packed_cap >= len)
+        return SBF_OK;
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return fail_hip(e, "staging");
+    if (h->d_codes)
+        (void)hipFree(h->d_codes);
+    if (h->d_valid)
+        (void)hipFree(h->d_valid);
+    h->d_codes = nullptr;
+    h->d_valid = nullptr;
+    h->packed_cap = 0;
+    const uint64_t n = len + len / 4 + 4096;
+    e = hipMalloc(reinterpret_cast<void**>(&h->d_codes), 4 * code_words(n));
+    if (e == hipSuccess)
+        e = hipMalloc(reinterpret_cast<void**>(&h->d_valid), 4 * valid_words(n));
+    if (e != hipSuccess) {
+        if (h->d_codes)
+            (void)hipFree(h->d_codes);
+        h->d_codes = nullptr;
+        h->d_valid = nullptr;
+        return fail_hip(e, "hipMalloc(packed staging)");
+    }
+    h->packed_cap = n;
+    return SBF_OK;
+}
+
+sbf::SeqArgs seq_args(sbf_t* h, const uint32_t* codes, const uint32_t* valid, uint64_t len, uint64_t* out,
+                      hipStream_t st)
+{
+    sbf::SeqArgs a;
+    a.codes = codes;
+    a.valid = valid;
+    a.ncw = code_words(len);
+    a.nvw = valid_words(len);
+    a.nk = len - h->P.k + 1;
+    a.filter = h->d_filter;
+    a.shard_mask = (uint32_t)(h->num_shards - 1);
+    a.out = out;
+    a.stream = st;
+    return a;
+}
+
+// Stage a sequence (host or device) as packed codes in the handle's buffers.
+int stage_packed(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, hipStream_t st)
+{
+    int rc = grow_packed(h, len, st);
+    if (rc)
+        return rc;
+    const char* d_seq = seq;
+    if (flags == SBF_HOST) {
+        rc = grow(&h->d_ascii, &h->ascii_cap, len, 1, st, "hipMalloc(ascii staging)");
+        if (rc)
+            return rc;
+        hipError_t e = hipMemcpyAsync(h->d_ascii, seq, len, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess)
+            return fail_hip(e, "hipMemcpyAsync(sequence)");
+        d_seq = h->d_ascii;
+    }
+    hipError_t e = sbf::launch_pack(d_seq, len, h->d_codes, h->d_valid, st);
+    return e == hipSuccess ? SBF_OK : fail_hip(e, "pack launch");
+}
+
+int check_flags(uint32_t flags)
+{
+    return (flags == SBF_HOST || flags == SBF_DEVICE) ? SBF_OK : fail(SBF_EINVAL, "flags must be SBF_HOST or SBF_DEVICE");
+}
+
+}  // namespace
+
+extern "C" {
+
+int sbf_create(sbf_t** out, uint32_t k, uint32_t m, uint32_t s, uint32_t H, uint64_t bits)
+{
+    sbf::Params P{SBF_KIND_SBF, k, m, s, H};
+    return create_impl(out, P, bits);
+}
+
+int sbf_create_bbf(sbf_t** out, uint32_t k, uint32_t H, uint64_t bits)
+{
+    sbf::Params P{SBF_KIND_BBF, k, 0, 0, H};
+    return create_impl(out, P, bits);
+}
+
+int sbf_destroy(sbf_t* h)
+{
+    if (!h)
+        return SBF_OK;
+    (void)hipSetDevice(h->device);
+    hipError_t e = hipDeviceSynchronize();
+    (void)hipFree(h->d_filter);
+    (void)hipFree(h->d_hits);
+    if (h->d_ascii)
+        (void)hipFree(h->d_ascii);
+    if (h->d_codes)
+        (void)hipFree(h->d_codes);
+    if (h->d_valid)
+        (void)hipFree(h->d_valid);
+    if (h->d_out)
+        (void)hipFree(h->d_out);
+    delete h;
+    if (e != hipSuccess)
+        return fail_hip(e, "sbf_destroy");
+    ok();
+    return SBF_OK;
+}
+
+int sbf_clear(sbf_t* h, void* stream)
+{
+    if (!h)
+        return fail(SBF_EINVAL, "handle is NULL");
+    int rc = set_device(h);
+    if (rc)
+        return rc;
+    hipError_t e = sbf::launch_fill_zero(h->d_filter, 4 * h->num_shards, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail_hip(e, "clear launch");
+    ok();
+    return SBF_OK;
+}
+
+int sbf_info(const sbf_t* h, sbf_info_t* o)
+{
+    if (!h || !o)
+        return fail(SBF_EINVAL, "NULL argument");
+    o->k = h->P.k;
+    o->m = h->P.m;
+    o->s = h->P.s;
+    o->H = h->P.H;
+    o->kind = h->P.kind;
+    o->specialized = (uint32_t)h->ks.specialized;
+    o->num_shards = h->num_shards;
+    o->filter_bytes = 32 * h->num_shards;
+    ok();
+    return SBF_OK;
+}
+
+int sbf_copy_filter(const sbf_t* h, void* dst, uint64_t bytes, uint32_t flags, void* stream)
+{
+    if (!h || !dst)
+        return fail(SBF_EINVAL, "NULL argument");
+    if (check_flags(flags))
+        return SBF_EINVAL;
+    if (bytes < 32 * h->num_shards)
+        return fail(SBF_EINVAL, "destination smaller than the filter");
+    int rc = set_device(h);
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (flags == SBF_HOST) {
+        e = hipMemcpyAsync(dst, h->d_filter, 32 * h->num_shards, hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(st);
+    } else {
+        e = hipMemcpyAsync(dst, h->d_filter, 32 * h->num_shards, hipMemcpyDeviceToDevice, st);
+    }
+    if (e != hipSuccess)
+        return fail_hip(e, "copy filter");
+    ok();
+    return SBF_OK;
+}
+
+const uint64_t* sbf_filter_device_ptr(const sbf_t* h) { return h ? h->d_filter : nullptr; }
+
+void sbf_packed_words(uint64_t len, uint64_t* cw, uint64_t* vw)
+{
+    if (cw)
+        *cw = code_words(len);
+    if (vw)
+        *vw = valid_words(len);
+}
+
+int sbf_pack(const char* d_ascii, uint64_t len, uint32_t* d_codes, uint32_t* d_valid, void* stream)
+{
+    if (len == 0) {
+        ok();
+        return SBF_OK;
+    }
+    if (!d_ascii || !d_codes || !d_valid)
+        return fail(SBF_EINVAL, "NULL argument");
+    hipError_t e = sbf::launch_pack(d_ascii, len, d_codes, d_valid, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail_hip(e, "pack launch");
+    ok();
+    return SBF_OK;
+}
+
+int sbf_insert_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid, uint64_t len, void* stream)
+{
+    if (!h)
+        return fail(SBF_EINVAL, "handle is NULL");
+    if (len < h->P.k) {
+        ok();
+        return SBF_OK;
+    }
+    if (!d_codes || !d_valid)
+        return fail(SBF_EINVAL, "NULL argument");
+    int rc = set_device(h);
+    if (rc)
+        return rc;
+    const sbf::SeqArgs a = seq_args(h, d_codes, d_valid, len, nullptr, (hipStream_t)stream);
+    hipError_t e = h->ks.insert(a, h->P);
+    if (e != hipSuccess)
+        return fail_hip(e, "insert launch");
+    ok();
+    return SBF_OK;
+}
+
+int sbf_query_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid, uint64_t len, uint64_t* d_out,
+                     void* stream)
+{
+    if (!h)
+        return fail(SBF_EINVAL, "handle is NULL");
+    if (len < h->P.k) {
+        ok();
+        return SBF_OK;
+    }
+    if (!d_codes || !d_valid || !d_out)
+        return fail(SBF_EINVAL, "NULL argument");
+    int rc = set_device(h);
+    if (rc)
+        return rc;
+    const sbf::SeqArgs a = seq_args(h, d_codes, d_valid, len, d_out, (hipStream_t)stream);
+    hipError_t e = h->ks.query(a, h->P);
+    if (e != hipSuccess)
+        return fail_hip(e, "query launch");
+    ok();
+    return SBF_OK;
+}
+
+int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void* stream)
+{
+    if (!h)
+        return fail(SBF_EINVAL, "handle is NULL");
+    if (check_flags(flags))
+        return SBF_EINVAL;
+    if (len < h->P.k) {
+        ok();
+        return SBF_OK;
+    }
+    if (!seq)
+        return fail(SBF_EINVAL, "seq is NULL");
+    int rc = set_device(h);
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    rc = stage_packed(h, seq, len, flags, st);
+    if (rc)
+        return rc;
+    const sbf::SeqArgs a = seq_args(h, h->d_codes, h->d_valid, len, nullptr, st);
+    hipError_t e = h->ks.insert(a, h->P);
+    if (e == hipSuccess && flags == SBF_HOST)
+        e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return fail_hip(e, "insert");
+    ok();
+    return SBF_OK;
+}
+
+int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits, uint32_t flags, void* stream)
+{
+    if (!h)
+        return fail(SBF_EINVAL, "handle is NULL");
+    if (check_flags(flags))
+        return SBF_EINVAL;
+    if (len < h->P.k) {
+        ok();
+        return SBF_OK;
+    }
+    if (!seq || !out_bits)
+        return fail(SBF_EINVAL, "NULL argument");
+    int rc = set_device(h);
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    rc = stage_packed(h, seq, len, flags, st);
+    if (rc)
+        return rc;
+    const uint64_t nw = out_words(len, h->P.k);
+    uint64_t* d_out = out_bits;
+    if (flags == SBF_HOST) {
+        rc = grow(&h->d_out, &h->out_cap, nw, 8, st, "hipMalloc(query staging)");
+        if (rc)
+            return rc;
+        d_out = h->d_out;
+    }
+    const sbf::SeqArgs a = seq_args(h, h->d_codes, h->d_valid, len, d_out, st);
+    hipError_t e = h->ks.query(a, h->P);
+    if (e == hipSuccess && flags == SBF_HOST) {
+        e = hipMemcpyAsync(out_bits, d_out, 8 * nw, hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(st);
+    }
+    if (e != hipSuccess)
+        return fail_hip(e, "query");
+    ok();
+    return SBF_OK;
+}
+
+int sbf_fpr_probe_device(sbf_t* h, uint64_t n, uint64_t seed, uint64_t* d_hits, void* stream)
+{
+    if (!h || !d_hits)
+        return fail(SBF_EINVAL, "NULL argument");
+    int rc = set_device(h);
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = sbf::launch_fill_zero(d_hits, 1, st);
+    if (e == hipSuccess) {
+        sbf::ProbeArgs a;
+        a.filter = h->d_filter;
+        a.shard_mask = (uint32_t)(h->num_shards - 1);
+        a.n = n;
+        a.seed = seed;
+        a.hits = reinterpret_cast<unsigned long long*>(d_hits);
+        a.stream = st;
+        e = h->ks.probe(a, h->P);
+    }
+    if (e != hipSuccess)
+        return fail_hip(e, "probe launch");
+    ok();
+    return SBF_OK;
+}
+
+int sbf_fpr_probe(sbf_t* h, uint64_t n, uint64_t seed, uint64_t* hits)
+{
+    if (!h || !hits)
+        return fail(SBF_EINVAL, "NULL argument");
+    int rc = sbf_fpr_probe_device(h, n, seed, reinterpret_cast<uint64_t*>(h->d_hits), nullptr);
+    if (rc)
+        return rc;
+    hipError_t e = hipMemcpy(hits, h->d_hits, sizeof(uint64_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return fail_hip(e, "probe result");
+    ok();
+    return SBF_OK;
+}
+
+const char* sbf_strerror(int code)
+{
+    switch (code) {
+    case SBF_OK: return "ok";
+    case SBF_EINVAL: return "invalid argument";
+    case SBF_EUNSUPPORTED: return "unsupported parameter combination";
+    case SBF_ENOMEM: return "out of memory";
+    case SBF_EDEVICE: return "device error";
+    default: return "unknown error";
+    }
+}
+
+const char* sbf_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

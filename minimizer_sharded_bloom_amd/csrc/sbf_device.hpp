@@ -1,0 +1,155 @@
+// sbf_device.hpp -- device-side building blocks shared by the gfx950 kernels:
+// hash functions, bit addressing, packed-sequence windows and validity.
+//
+// Method: "cuSBF: A Minimizer-Aware Bloom Filter for Genomic Sequence Data on
+// Modern GPUs" [cuSBF].  Hash choices are fixed in include/sbf.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sbf {
+
+constexpr uint64_t kGolden = 0x9E3779B97F4A7C15ull;  // 2^64 / golden ratio
+constexpr uint64_t kMulA = 0xBF58476D1CE4E5B9ull;    // SplitMix64 multipliers
+constexpr uint64_t kMulB = 0x94D049BB133111EBull;
+
+// [cuSBF] §IV-G role-specialized hashing: one multiplicative mix for the
+// minimizer (folded so the low shard bits see every base) ...
+__device__ __forceinline__ uint64_t hash_min(uint64_t v)
+{
+    const uint64_t u = (v + kGolden) * kMulA;
+    return u ^ (u >> 32);
+}
+
+// ... and a stronger mix for the s-mers (SplitMix64 finalizer of v + G).
+__device__ __forceinline__ uint64_t splitmix_fin(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * kMulA;
+    z = (z ^ (z >> 27)) * kMulB;
+    return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ uint64_t hash_s(uint64_t v) { return splitmix_fin(v + kGolden); }
+
+// [cuSBF] §IV-G bit-slicing (H <= 10) and golden-ratio salted fallback.
+template <int H>
+__device__ __forceinline__ uint32_t bit_addr(uint64_t h, int t)
+{
+    if constexpr (H <= 10) {
+        constexpr int width = 64 / H;
+        return (uint32_t)(h >> (t * width)) & 63u;
+    } else {
+        return (uint32_t)((h * ((2ull * (uint64_t)t + 1ull) * kGolden)) >> 58);
+    }
+}
+
+__device__ __forceinline__ uint32_t bit_addr_rt(uint64_t h, uint32_t t, uint32_t H)
+{
+    if (H <= 10)
+        return (uint32_t)(h >> (t * (64u / H))) & 63u;
+    return (uint32_t)((h * ((2ull * (uint64_t)t + 1ull) * kGolden)) >> 58);
+}
+
+// Top 32 bits of the 64-bit value (a:b) shifted left by r, 0 <= r < 32.
+__device__ __forceinline__ uint32_t funnel_hi(uint32_t a, uint32_t b, uint32_t r)
+{
+    return r == 0 ? a : (uint32_t)((((uint64_t)a << 32) | b) >> (32 - r));
+}
+
+// 64 bits of the packed base stream D starting at base i (i compile-time
+// after unrolling): bases i..i+31, first base in the top bits.
+template <int NDW>
+__device__ __forceinline__ uint64_t stream_window(const uint32_t (&D)[NDW], int i)
+{
+    const int a = i >> 4;
+    const uint32_t r = 2u * (uint32_t)(i & 15);
+    const uint32_t hi = funnel_hi(D[a], D[a + 1], r);
+    const uint32_t lo = funnel_hi(D[a + 1], D[a + 2], r);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Value of the n-base window whose first base is the top of `win` (n <= 32).
+__device__ __forceinline__ uint64_t top_bases(uint64_t win, int n)
+{
+    return n >= 32 ? win : (win >> (64 - 2 * n));
+}
+
+// Read word idx of a uint32 array, 0 past its end.
+__device__ __forceinline__ uint32_t ld_or0(const uint32_t* __restrict__ a, uint64_t n, uint64_t idx)
+{
+    return idx < n ? a[idx] : 0u;
+}
+
+// Validity bits of bases p0 .. p0+63 (bit i = base p0+i), p0 % 16 == 0.
+__device__ __forceinline__ uint64_t valid_window64(const uint32_t* __restrict__ valid, uint64_t nvw, uint64_t p0)
+{
+    const uint64_t w = p0 >> 5;
+    const uint32_t off = (uint32_t)(p0 & 31);
+    const uint64_t v01 = (uint64_t)ld_or0(valid, nvw, w) | ((uint64_t)ld_or0(valid, nvw, w + 1) << 32);
+    uint64_t win = v01 >> off;
+    if (off)
+        win |= (uint64_t)ld_or0(valid, nvw, w + 2) << (64 - off);
+    return win;
+}
+
+// Bit i of the result is 1 iff bits i .. i+k-1 of v are all 1 (k <= 32).
+template <int KK>
+__device__ __forceinline__ uint64_t run_and(uint64_t v)
+{
+    uint64_t a[6];
+    a[0] = v;
+#pragma unroll
+    for (int j = 1; j < 6; ++j)
+        a[j] = a[j - 1] & (a[j - 1] >> (1 << (j - 1)));
+    uint64_t r = ~0ull;
+    int pos = 0;
+#pragma unroll
+    for (int j = 5; j >= 0; --j) {
+        if (KK & (1 << j)) {
+            r &= a[j] >> pos;
+            pos += 1 << j;
+        }
+    }
+    return r;
+}
+
+__device__ __forceinline__ uint64_t run_and_rt(uint64_t v, uint32_t kk)
+{
+    uint64_t r = ~0ull;
+    uint32_t pos = 0;
+    uint64_t a = v;
+    uint64_t levels[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+        levels[j] = a;
+        a = a & (a >> (1 << j));
+    }
+#pragma unroll
+    for (int j = 5; j >= 0; --j) {
+        if (kk & (1u << j)) {
+            r &= levels[j] >> pos;
+            pos += 1u << j;
+        }
+    }
+    return r;
+}
+
+__device__ __forceinline__ void atomic_or_u64(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Load one 256-bit shard (two 128-bit loads).
+__device__ __forceinline__ void load_shard(const uint64_t* __restrict__ filter, uint64_t shard, uint64_t (&w)[4])
+{
+    const ulonglong2* p = reinterpret_cast<const ulonglong2*>(filter + 4 * shard);
+    const ulonglong2 a = p[0];
+    const ulonglong2 b = p[1];
+    w[0] = a.x;
+    w[1] = a.y;
+    w[2] = b.x;
+    w[3] = b.y;
+}
+
+}  // namespace sbf

@@ -1,0 +1,63 @@
+// sbf_internal.hpp -- host-side types shared by the library's translation
+// units: launch arguments, kernel sets and the specialization registry.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sbf {
+
+// Arguments of one insert or query launch over a packed sequence.
+struct SeqArgs {
+    const uint32_t* codes;  // packed bases, 16 per word
+    const uint32_t* valid;  // validity bits, 32 per word
+    uint64_t ncw;           // code words
+    uint64_t nvw;           // validity words
+    uint64_t nk;            // k-mer starts: len - k + 1
+    uint64_t* filter;       // uint64_t[4N]
+    uint32_t shard_mask;    // N - 1
+    uint64_t* out;          // query bits (query only)
+    hipStream_t stream;
+};
+
+// Arguments of one false-positive probe launch.
+struct ProbeArgs {
+    const uint64_t* filter;
+    uint32_t shard_mask;
+    uint64_t n;
+    uint64_t seed;
+    unsigned long long* hits;  // device counter, accumulated into
+    hipStream_t stream;
+};
+
+// Runtime parameters, used by the generic (non-specialized) kernels.
+struct Params {
+    uint32_t kind, k, m, s, H;
+};
+
+typedef hipError_t (*SeqLaunch)(const SeqArgs&, const Params&);
+typedef hipError_t (*ProbeLaunch)(const ProbeArgs&, const Params&);
+
+struct KernelSet {
+    SeqLaunch insert;
+    SeqLaunch query;
+    ProbeLaunch probe;
+    int specialized;
+};
+
+// One row of a specialization table (see sbf_spec_list.hpp).
+struct SpecEntry {
+    uint32_t kind, k, m, s, H;
+    KernelSet (*make)();
+};
+
+// Compile-time specialized kernel sets; false if (kind,k,m,s,H) has none.
+bool find_specialized(const Params& p, KernelSet* out);
+// Kernel set for any valid parameters (one k-mer per lane, runtime loops).
+KernelSet generic_kernels();
+
+// Small utility launches.
+hipError_t launch_pack(const char* ascii, uint64_t len, uint32_t* codes, uint32_t* valid, hipStream_t st);
+hipError_t launch_fill_zero(uint64_t* p, uint64_t nwords, hipStream_t st);
+
+}  // namespace sbf
