@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the Super Bloom filter hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of device-resident
+synthetic input (the method of "cuSBF: A Minimizer-Aware Bloom Filter for
+Genomic Sequence Data on Modern GPUs"):
+    clear the filter
+    pack the genome (ASCII -> 2-bit codes + validity)
+    insert every genome k-mer           (Algorithm 1)
+    pack the reads
+    query every read k-mer              (Algorithm 2)
+    false-positive probe of n random k-mers (§V-D)
+at k=31, m=16, s=28, H=4.  Every launch goes to torch's current stream, so
+the torch events recorded between launches time each kernel on the stream it
+runs on.
+
+Prints one JSON line.  `value` = k-mers processed per second over the step
+(genome k-mer starts + read k-mer starts + probe k-mers) / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+K, M_, S_, H_ = 31, 16, 28, 4
+METRIC = "insert & query Gk-mers/s (k=31,m=16,s=28,H=4) + fraction of HBM/L2 roofline"
+
+# MI355X ALU peak from unit counts and clock: 256 CUs x 4 SIMDs, each SIMD
+# retires 16 lanes of a 3-operand (VOP3-encoded) integer op per clock -- the
+# same rate as an fp64 FMA (78.6 TFLOP/s) -- and 32 lanes of a 2-operand
+# (VOP2) add/xor/shift per clock, the fp32 rate (157.3 TFLOP/s).  Work is
+# counted in VOP3-equivalent lane-ops: VOP3 = 1, VOP2 = 1/2.
+CUS, CLOCK_HZ = 256, 2.4e9
+ALU_PEAK = CUS * 64 * CLOCK_HZ  # 3.93e13 VOP3-equivalent lane-ops/s
+HBM_PEAK = 8.0e12               # bytes/s
+
+
+def alu_ops_per_kmer(kind: str) -> float:
+    """Algorithmic integer work per k-mer start at (k,m,s,H) = (31,16,28,4),
+    in VOP3-equivalent lane-ops, for the sliding formulation: each position
+    contributes one m-mer hash and one s-mer hash; the minimizer is a sliding
+    minimum (3 64-bit min per k-mer); a query tests (k-s+1)*H bits, an insert
+    ORs one new s-mer's H bits into the run's sector masks and re-seeds them at
+    run starts.  Itemised in DESIGN.md ("Roofline")."""
+    window = 2.0            # 64-bit base window at this position: 2 alignbit
+    h_min = 5.5             # +G (2 VOP2), 64x64 multiply (mad_u64 + 2 mul_lo + add3), fold (VOP2)
+    smer = 1.5              # s-mer = window >> (64-2s): alignbit + shift
+    h_s = 16.5              # +G (1), 3 xorshifts (2.5 each), 2 multiplies (4 each)
+    win_min = 6.0           # 3 x (64-bit compare + 2 selects)
+    misc = 1.2              # shard mask, validity, output / run bookkeeping
+    front = window + h_min + smer + h_s + win_min + misc
+    if kind == "query":
+        return front + (K - S_ + 1) * H_ * 2.5   # per bit: extract, 64-bit shift, AND
+    if kind == "insert":
+        masks = H_ * 2 + 4 + 4 + 8 + 1.2       # H addresses + 1<<b, OR new s-mer, select, re-seed ORs, flush
+        return front + masks
+    raise ValueError(kind)
+
+
+def _bytes_per_kmer(kind: str, w: int = K - M_ + 1) -> float:
+    """Algorithmic HBM bytes per k-mer start: packed codes (2 bits) and
+    validity (1 bit) streamed once, plus one 32-byte shard read per run of
+    equal shards (and one 32-byte write-back per run for an insert); a query
+    also writes its answer bit.  Random minimizers give 2/(w+1) runs per k-mer."""
+    runs = 2.0 / (w + 1)
+    seq = 0.25 + 0.125
+    if kind == "query":
+        return seq + 0.125 + 32 * runs
+    return seq + 64 * runs
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4],
+                    help="synthetic configuration (default 2: 8 MiB filter, 5 Mbp genome, 2 M reads)")
+    ap.add_argument("--probe-n", type=int, default=10_000_000)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the single-thread oracle baseline (0 disables it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run one plain 256 MiB device copy (elementwise kernel) whose "
+                         "FETCH_SIZE/WRITE_SIZE counters scale the filter kernels' counters")
+    return ap.parse_args()
+
+
+def cpu_baseline(w: dict, budget_s: float) -> dict:
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    the first genome bases and read bases (about budget_s seconds of work),
+    one thread."""
+    import numpy as np
+    from oracle import oracle as O
+
+    g, reads = w["insert"], w["queries"][0]
+    f = O.OracleFilter(K, M_, S_, H_, w["bits"])
+    # calibrate on a short piece, then size the sample to the budget
+    t0 = time.perf_counter()
+    f.insert_seq(g[:200_000])
+    per = (time.perf_counter() - t0) / max(1, 200_000 - K + 1)
+    f = O.OracleFilter(K, M_, S_, H_, w["bits"])
+    n_ins = int(min(g.size, max(1_000_000, budget_s * 0.3 / per)))
+    n_q = int(min(reads.size, max(1_000_000, budget_s * 0.6 / per)))
+    n_p = int(max(100_000, budget_s * 0.1 / per))
+    t0 = time.perf_counter()
+    f.insert_seq(g[:n_ins])
+    t1 = time.perf_counter()
+    f.query_seq(reads[:n_q])
+    t2 = time.perf_counter()
+    f.fpr_probe(n_p, 0x5EED)
+    t3 = time.perf_counter()
+    kmers = (n_ins - K + 1) + (n_q - K + 1) + n_p
+    return {"value": kmers / (t3 - t0) / 1e9, "unit": "Gk-mers/s", "cores": 1, "kind": "oracle",
+            "sample": "single-thread C oracle: insert of the first %d genome bases, query of the first %d read "
+                      "bases, %d probe k-mers (%.1f s)" % (n_ins, n_q, n_p, t3 - t0),
+            "insert_gkmers_s": (n_ins - K + 1) / (t1 - t0) / 1e9,
+            "query_gkmers_s": (n_q - K + 1) / (t2 - t1) / 1e9}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % a.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import minimizer_sharded_bloom_amd as M
+    from minimizer_sharded_bloom_amd import synthetic as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    lib = M.lib()
+
+    t_gen = time.perf_counter()
+    w = S.workload(a.workload)
+    genome_h, reads_h = w["insert"], w["queries"][-1]
+    gen_s = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    genome = torch.from_numpy(genome_h).to(dev)
+    reads = torch.from_numpy(reads_h).to(dev)
+    LG, LR = genome.numel(), reads.numel()
+    gcw, gvw = M.packed_words(LG)
+    rcw, rvw = M.packed_words(LR)
+    g_codes = torch.empty(gcw, dtype=torch.int32, device=dev)
+    g_valid = torch.empty(gvw, dtype=torch.int32, device=dev)
+    r_codes = torch.empty(rcw, dtype=torch.int32, device=dev)
+    r_valid = torch.empty(rvw, dtype=torch.int32, device=dev)
+    f = M.SuperBloomFilter(K, M_, S_, H_, w["bits"])
+    assert f.specialized
+    out = torch.empty(f.num_answer_words(LR), dtype=torch.int64, device=dev)
+    hits = torch.zeros(1, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    names = ["clear", "pack_genome", "insert", "pack_reads", "query", "probe"]
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record(stream)
+        mark(0)
+        M.check(lib.sbf_clear(f.handle, sp), "clear")
+        mark(1)
+        M.check(lib.sbf_pack(genome.data_ptr(), LG, g_codes.data_ptr(), g_valid.data_ptr(), sp), "pack")
+        mark(2)
+        M.check(lib.sbf_insert_packed(f.handle, g_codes.data_ptr(), g_valid.data_ptr(), LG, sp), "insert")
+        mark(3)
+        M.check(lib.sbf_pack(reads.data_ptr(), LR, r_codes.data_ptr(), r_valid.data_ptr(), sp), "pack")
+        mark(4)
+        M.check(lib.sbf_query_packed(f.handle, r_codes.data_ptr(), r_valid.data_ptr(), LR, out.data_ptr(), sp), "query")
+        mark(5)
+        M.check(lib.sbf_fpr_probe_device(f.handle, a.probe_n, 0x5EED, hits.data_ptr(), sp), "probe")
+        mark(6)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(a.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / a.steps
+    phase = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / a.steps for i, n in enumerate(names)}
+
+    if a.calibrate_copy:
+        src = torch.ones(1 << 25, dtype=torch.int64, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.add(src, 0, out=dst)                                   # elementwise: reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        del src, dst
+
+    nk_g, nk_r = LG - K + 1, LR - K + 1
+    total = nk_g + nk_r + a.probe_n
+    value = total / (ms_step * 1e-3) / 1e9
+    ins_rate = nk_g / (phase["insert"] * 1e-3)
+    q_rate = nk_r / (phase["query"] * 1e-3)
+
+    def roof(kind, rate):
+        alu = rate * alu_ops_per_kmer(kind)
+        mem = rate * _bytes_per_kmer(kind)
+        return ({"bound": "alu", "achieved": alu / 1e12, "peak": ALU_PEAK / 1e12,
+                 "unit": "T int-ops/s", "frac": alu / ALU_PEAK, "traffic": None,
+                 "kernel": kind, "per_kmer_ops": alu_ops_per_kmer(kind)},
+                {"bound": "hbm", "achieved": mem / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                 "frac": mem / HBM_PEAK, "traffic": None, "kernel": kind, "per_kmer_bytes": _bytes_per_kmer(kind)})
+
+    dom = "query" if phase["query"] >= phase["insert"] else "insert"
+    alu, mem = roof(dom, q_rate if dom == "query" else ins_rate)
+    primary, secondary = (alu, mem) if alu["frac"] >= mem["frac"] else (mem, alu)
+
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "Gk-mers/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u64", "data": "synthetic",
+        "config": {"workload": "cfg%d" % a.workload, "k": K, "m": M_, "s": S_, "H": H_, "filter_bits": w["bits"],
+                   "genome_bases": LG, "read_bases": LR, "probe_kmers": a.probe_n,
+                   "kmers_per_step": total},
+        "roofline": primary, "roofline_other": secondary,
+        "insert_gkmers_s": round(ins_rate / 1e9, 3), "query_gkmers_s": round(q_rate / 1e9, 3),
+        "pack_gbases_s": round((LG + LR) / ((phase["pack_genome"] + phase["pack_reads"]) * 1e-3) / 1e9, 3),
+        "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
+        "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},
+        "wall_s_timed": round(wall, 3), "gen_s": round(gen_s, 2),
+    }
+    if a.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
