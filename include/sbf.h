@@ -14,7 +14,8 @@
  *   h_min(v)     u ^ (u >> 32), u = (v + G) * C1 mod 2^64       (§IV-G)
  *   h_s(v)       SplitMix64 finalizer of v + G                   (§IV-G)
  *   bit of hash t: H <= 10: bits [t*floor(64/H), +6) of h_s;
- *                  H > 10 : top 6 bits of h_s * ((2t+1) * G)     (§IV-G)
+ *                  H > 10 : top 6 bits of h_s * S_t,             (§IV-G)
+ *                           S_t = SplitMix64 finalizer of (t+1) * G
  *   shard        min over the k-m+1 m-mers of h_min, & (N-1)     (Algorithm 1)
  *   N            smallest power of two >= ceil(bits / 256)       (§IV-B)
  *   G = 0x9E3779B97F4A7C15, C1 = 0xBF58476D1CE4E5B9, C2 = 0x94D049BB133111EB

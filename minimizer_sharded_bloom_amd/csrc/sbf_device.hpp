@@ -32,6 +32,16 @@ __device__ __forceinline__ uint64_t splitmix_fin(uint64_t z)
 
 __device__ __forceinline__ uint64_t hash_s(uint64_t v) { return splitmix_fin(v + kGolden); }
 
+// Per-hash-index salt of the H > 10 fallback: the t-th SplitMix64 output of
+// seed 0, i.e. the finalizer of (t+1) * G.
+__host__ __device__ constexpr uint64_t salt_of(uint32_t t)
+{
+    uint64_t z = (uint64_t)(t + 1u) * kGolden;
+    z = (z ^ (z >> 30)) * kMulA;
+    z = (z ^ (z >> 27)) * kMulB;
+    return z ^ (z >> 31);
+}
+
 // [cuSBF] §IV-G bit-slicing (H <= 10) and golden-ratio salted fallback.
 template <int H>
 __device__ __forceinline__ uint32_t bit_addr(uint64_t h, int t)
@@ -40,7 +50,7 @@ __device__ __forceinline__ uint32_t bit_addr(uint64_t h, int t)
         constexpr int width = 64 / H;
         return (uint32_t)(h >> (t * width)) & 63u;
     } else {
-        return (uint32_t)((h * ((2ull * (uint64_t)t + 1ull) * kGolden)) >> 58);
+        return (uint32_t)((h * salt_of((uint32_t)t)) >> 58);
     }
 }
 
@@ -48,7 +58,7 @@ __device__ __forceinline__ uint32_t bit_addr_rt(uint64_t h, uint32_t t, uint32_t
 {
     if (H <= 10)
         return (uint32_t)(h >> (t * (64u / H))) & 63u;
-    return (uint32_t)((h * ((2ull * (uint64_t)t + 1ull) * kGolden)) >> 58);
+    return (uint32_t)((h * salt_of(t)) >> 58);
 }
 
 // Top 32 bits of the 64-bit value (a:b) shifted left by r, 0 <= r < 32.

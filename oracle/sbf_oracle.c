@@ -22,8 +22,10 @@
  *    G  = 0x9E3779B97F4A7C15 (2^64 / golden ratio),
  *    C1 = 0xBF58476D1CE4E5B9, C2 = 0x94D049BB133111EB (SplitMix64).
  *  - Bit address: for H <= 10, slice t of width floor(64/H), its low 6 bits
- *    ([cuSBF] §IV-G bit-slicing); for H > 10, the top 6 bits of
- *    hs * ((2t+1) * G) (the golden-ratio salted fallback of §IV-G).
+ *    ([cuSBF] §IV-G bit-slicing); for H > 10, the top 6 bits of hs * salt_t
+ *    with salt_t = mix((t+1) * G), the t-th SplitMix64 output of seed 0 (the
+ *    golden-ratio-derived per-index salt of §IV-G).  A salt of the form
+ *    (2t+1) * G would make the H addresses an arithmetic progression.
  *  - Shard count: the smallest power of two >= ceil(bits/256), at least 1
  *    ([cuSBF] §IV-B).  Hash index t lives in word t mod 4 of the shard.
  *  - Invalid k-mers (any non-ACGT base) insert nothing and query false
@@ -88,7 +90,7 @@ unsigned osbf_bitaddr(uint64_t hs, unsigned t, unsigned H)
         unsigned width = 64u / H;
         return (unsigned)((hs >> (t * width)) & 63u);
     }
-    uint64_t salt = (2ull * t + 1ull) * GOLDEN;
+    uint64_t salt = osbf_mix((uint64_t)(t + 1u) * GOLDEN);
     return (unsigned)((hs * salt) >> 58);
 }
 

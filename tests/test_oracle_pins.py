@@ -80,9 +80,12 @@ def test_bitaddr_slices():
     # H = 4: the four 16-bit slices of 0x0123456789ABCDEF end in
     # 0xCDEF, 0x89AB, 0x4567, 0x0123 -> low 6 bits 0x2F, 0x2B, 0x27, 0x23
     assert [O.bitaddr(h, t, 4) for t in range(4)] == [0x2F, 0x2B, 0x27, 0x23]
+    g = _gold("splitmix64_seed1234567.json")
     for t in range(12):
-        salt = ((2 * t + 1) * GAMMA) & M64
+        salt = O.mix(((t + 1) * GAMMA) & M64)  # t-th SplitMix64 output of seed 0
         assert O.bitaddr(h, t, 12) == ((h * salt) & M64) >> 58
+    # the salts are SplitMix64 outputs: for seed 1234567 the stream is published
+    assert O.mix((g["seed"] + GAMMA) & M64) == g["outputs"][0]
 
 
 # ---- encoding and packing ---------------------------------------------------
@@ -358,3 +361,39 @@ def test_findere_suppresses_aliens():
         near += f.query_kmer(T.pack_str(km.decode()))
     alien = f.fpr_probe(trials * 20, 77)
     assert near / trials > 5 * (alien / (trials * 20) + 1e-4)
+
+
+def test_salted_bit_addresses_independent():
+    """§IV-G salted fallback (H > 10): with H = 12, one shard and s = m = k,
+    word q receives the three hash indices t = q, q+4, q+8; if their salted
+    addresses are independent a random key hits with prod_q fill_q^3."""
+    rng = np.random.default_rng(25)
+    hits, expect = 0, 0.0
+    for tr in range(40):
+        f = O.OracleFilter(31, 31, 31, 12, 256)
+        for x in rng.choice(2**62, 30, replace=False):
+            f.insert_kmer(int(x))
+        fill = [bin(int(v)).count("1") / 64 for v in f.words()]
+        n = 4000
+        hits += f.fpr_probe(n, 9000 + tr)
+        expect += n * float(np.prod([q ** 3 for q in fill]))
+    assert expect > 200
+    assert abs(hits - expect) <= 4.5 * math.sqrt(expect) + 2
+
+
+def test_bbf_fill_based_fpr():
+    """Blocked Bloom comparator (§II-A): a random key picks a uniform block and
+    hits with prod_q fill_q^(c_q), c_q the hash indices in word q."""
+    rng = np.random.default_rng(26)
+    H = 6
+    f = O.OracleFilter(31, 0, 0, H, 2**12, kind=O.KIND_BBF)
+    for x in rng.choice(2**62, 700, replace=False):
+        f.insert_kmer(int(x))
+    w = f.words().reshape(-1, 4)
+    fill = np.array([[bin(int(v)).count("1") / 64 for v in row] for row in w])
+    c = [sum(1 for t in range(H) if t % 4 == q) for q in range(4)]
+    p = float(np.mean(np.prod([fill[:, q] ** c[q] for q in range(4)], axis=0)))
+    n = 200000
+    hits = f.fpr_probe(n, 4242)
+    assert p > 1e-3
+    assert T.binom_ok(hits, n, p, z=4.5)
