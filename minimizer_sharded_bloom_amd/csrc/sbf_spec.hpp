@@ -1,24 +1,33 @@
 // sbf_spec.hpp -- compile-time specialized gfx950 kernels of the Super Bloom
 // filter ([cuSBF] §IV-C..E, §IV-G "compile-time specialization").
 //
-// Work layout (one wave64 = 64 lanes, no LDS, no barriers):
-//  - A wave owns KPW = 63 * KL consecutive k-mer starts.  Lane l < 63 owns
-//    the KL consecutive k-mers starting at p0 = wave_start + KL * l; lane 63
-//    only computes hashes for the halo of lane 62.
+// Work layout.  A 256-thread workgroup is four independent wave64s; each wave
+// owns KPW = 63 * KL consecutive k-mer starts and a private slice of LDS.
+//  - Lane l < 63 owns the KL consecutive k-mers starting at
+//    p0 = wave_start + KL * l; lane 63 only computes hashes for lane 62's halo.
 //  - Every lane loads its packed bases (KL/16 + 2 words, coalesced across the
-//    wave), then computes the m-mer hash and the s-mer hash of its own KL
-//    positions exactly once; the (w-1) m-mer hashes and (k-s) s-mer hashes past
-//    its range come from lane l+1 through a lane shift.  No hash is computed
-//    twice (apart from lane 63's 1/64 share).
-//  - The minimizer of each k-mer is a sliding-window minimum over the w m-mer
-//    hashes (van Herk / Gil-Werman block prefix and suffix minima, block = w).
-//  - Insert: consecutive valid k-mers of a lane with the same shard form a
-//    run ([cuSBF] §IV-D, Fig. 3); the run ORs its s-mer bits into four 64-bit
-//    sector masks in registers and issues one atomic OR per used sector when
-//    it ends.  Query: a lane loads a shard once per run and tests every k-mer
-//    of the run against the registers ([cuSBF] §IV-E shard sharing); the KL
-//    answer bits of a lane are one 16/32-bit store.
+//    wave) and computes the m-mer hash and the s-mer hash of its own KL
+//    positions exactly once; the w-1 m-mer hashes and k-s s-mer hashes past
+//    its range come from lane l+1 through a lane shift.
+//  - Minimizer: a sliding-window minimum over the w m-mer hashes (van Herk /
+//    Gil-Werman block prefix and suffix minima, block = w).
+//  - Runs: consecutive valid k-mers of a lane with one shard ([cuSBF] §IV-D,
+//    Fig. 3).  A wave scan numbers them; a run that continues the previous
+//    lane's last run shares that lane's slot, so a super-k-mer cut by a lane
+//    boundary still costs one record.
+//  - Findere masks: R_i, the OR of the sector masks of the k-s+1 s-mers of
+//    k-mer i, is built by binary doubling in a stream: each s-mer's masks and
+//    each doubling level are computed once, at the step they first appear.
+//  - Insert: run i's OR of R over its k-mers goes to an LDS record (shard,
+//    four 64-bit words); then four adjacent lanes OR the four words of one
+//    record into the filter in one instruction, which the memory system merges
+//    into one request.
+//  - Query: every run's shard is gathered into LDS by the whole wave at once
+//    (two lanes per 32-byte shard); then k-mer i is present iff
+//    (R_i & ~shard) == 0 over the used words ([cuSBF] Algorithm 2, Contains).
 #pragma once
+
+#include <type_traits>
 
 #include "sbf_device.hpp"
 #include "sbf_internal.hpp"
@@ -41,6 +50,17 @@ struct Cfg {
     static_assert(1 <= m && m <= k && k <= 32 && 1 <= s && s <= k && H >= 1, "bad parameters");
 };
 
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
 // Window of N bases starting at base j of a packed KK-mer x.
 template <int KK, int N>
 __device__ __forceinline__ uint64_t sub_bases(uint64_t x, int j)
@@ -57,9 +77,9 @@ __host__ __device__ inline uint64_t round64(uint64_t x) { return (x + 63) & ~63u
 
 template <class C>
 struct LaneCtx {
-    uint64_t p0;        // first k-mer of this lane
+    uint64_t p0;  // first k-mer of this lane
     uint32_t lane;
-    bool live;          // wave has work
+    bool live;    // wave has work
 };
 
 template <class C>
@@ -83,6 +103,18 @@ __device__ __forceinline__ void load_codes(const SeqArgs& a, uint64_t p0, uint32
         D[j] = ld_or0(a.codes, a.ncw, w0 + j);
 }
 
+// Value of lane l+1 in lane l (lane 63 receives its own value): one DPP
+// wave_shl:1 move per 32-bit half, no LDS traffic.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x130, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint64_t from_next_lane(uint64_t v)
+{
+    return ((uint64_t)from_next_lane((uint32_t)(v >> 32)) << 32) | from_next_lane((uint32_t)v);
+}
+
 // Shards of the lane's KL k-mers: one m-mer hash per own position, halo from
 // lane+1, then van Herk sliding minimum with block size W.
 template <class C>
@@ -95,34 +127,39 @@ __device__ __forceinline__ void lane_shards(const uint32_t (&D)[C::ND], uint32_t
         hm[i] = hash_min(top_bases(stream_window<C::ND>(D, i), C::m));
 #pragma unroll
     for (int j = 0; j < W - 1; ++j)
-        hm[KL + j] = __shfl_down(hm[j], 1);
+        hm[KL + j] = from_next_lane(hm[j]);
     if constexpr (W == 1) {
 #pragma unroll
         for (int i = 0; i < KL; ++i)
             shard[i] = (uint32_t)hm[i] & shard_mask;
     } else {
-        // suffix minima inside blocks [bW, bW+W) clipped to NM, prefix minima likewise
-        uint64_t suf[NM], pre[NM];
+        // Window [i, i+W) = tail of block i/W (suffix minimum at i) plus head of
+        // block i/W+1 (prefix minimum at i+W-1); blocks are [bW, bW+W).
+        // Pass 1 (descending) keeps the suffix minima of positions < KL in suf[]
+        // and leaves hm[] untouched; pass 2 (ascending) carries the prefix
+        // minimum in one register and closes window i = e-W+1 at each e.
+        uint64_t suf[KL];
+        uint64_t run = ~0ull;
 #pragma unroll
         for (int j = NM - 1; j >= 0; --j) {
             const bool block_end = ((j % W) == W - 1) || (j == NM - 1);
-            suf[j] = block_end ? hm[j] : (hm[j] < suf[j + 1 < NM ? j + 1 : j] ? hm[j] : suf[j + 1 < NM ? j + 1 : j]);
+            run = block_end ? hm[j] : (hm[j] < run ? hm[j] : run);
+            if (j < KL)
+                suf[j] = run;
         }
+        uint64_t pre = ~0ull;
 #pragma unroll
-        for (int j = 0; j < NM; ++j) {
-            const bool block_start = (j % W) == 0;
-            pre[j] = block_start ? hm[j] : (hm[j] < pre[j > 0 ? j - 1 : 0] ? hm[j] : pre[j > 0 ? j - 1 : 0]);
-        }
-#pragma unroll
-        for (int i = 0; i < KL; ++i) {
-            uint64_t mn;
-            if (i % W == 0) {
-                mn = suf[i];
-            } else {
-                const uint64_t a = suf[i], b = pre[i + W - 1];
-                mn = a < b ? a : b;
+        for (int e = 0; e < NM; ++e) {
+            pre = (e % W == 0) ? hm[e] : (hm[e] < pre ? hm[e] : pre);
+            const int i = e - W + 1;
+            if (i >= 0 && i < KL) {
+                uint64_t mn;
+                if (i % W == 0)
+                    mn = suf[i];
+                else
+                    mn = suf[i] < pre ? suf[i] : pre;
+                shard[i] = (uint32_t)mn & shard_mask;
             }
-            shard[i] = (uint32_t)mn & shard_mask;
         }
     }
 }
@@ -136,7 +173,7 @@ __device__ __forceinline__ void lane_smer_hashes(const uint32_t (&D)[C::ND], uin
         hs[i] = hash_s(top_bases(stream_window<C::ND>(D, i), C::s));
 #pragma unroll
     for (int j = 0; j < C::Z - 1; ++j)
-        hs[C::KL + j] = __shfl_down(hs[j], 1);
+        hs[C::KL + j] = from_next_lane(hs[j]);
 }
 
 // Valid-k-mer bits of the lane (bit i: k-mer p0+i is valid and < nk).
@@ -164,8 +201,156 @@ __device__ __forceinline__ void smer_masks(uint64_t h, uint64_t (&mk)[4])
         mk[t & 3] |= 1ull << bit_addr<C::H>(h, t);
 }
 
+// Ordering point between the unrolled steps of a pass: the packed bases pass
+// through an empty asm, so no hash of a later step can be computed before it
+// (which would keep every hash live at once).
+template <int NDW>
+__device__ __forceinline__ void step_fence(uint32_t (&D)[NDW])
+{
+#pragma unroll
+    for (int j = 0; j < NDW; ++j)
+        asm volatile("" : "+v"(D[j])::"memory");
+}
+
+// s-mer hash of the lane's own position Q (Q < KL).
+template <class C, int Q>
+__device__ __forceinline__ uint64_t smer_hash_at(const uint32_t (&D)[C::ND])
+{
+    return hash_s(top_bases(stream_window<C::ND>(D, Q), C::s));
+}
+
+// Streaming Findere masks: level l entry e = OR of the sector masks of s-mers
+// e .. e + 2^l - 1.  step<I>() hashes the s-mers that are new at k-mer I
+// (positions 0..Z-1 at I = 0, then I+Z-1), builds the doubling-level entries
+// whose last s-mer is new, and returns R_I = OR of the masks of s-mers
+// I .. I+Z-1, one level per set bit of Z.  The first Z-1 own hashes and the
+// Z-1 halo hashes of lane l+1 are computed up front (init), every other hash
+// in the step that first needs it, so few hashes are live at once.
 template <class C>
-__device__ __forceinline__ void flush_run(uint64_t* __restrict__ filter, uint32_t shard, const uint64_t (&Wm)[4])
+struct FindereMasks {
+    static constexpr int NZ = C::NZ, Z = C::Z, NL = ilog2c(Z) + 1, NH = Z > 1 ? Z - 1 : 1;
+    uint64_t L[NL][NZ][4];
+    uint64_t head[NH];  // own hashes of positions 0 .. Z-2
+    uint64_t halo[NH];  // hashes of positions KL .. KL+Z-2 (lane l+1's head)
+
+    __device__ __forceinline__ void init(const uint32_t (&D)[C::ND])
+    {
+        static_for<0, Z - 1>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            head[q] = smer_hash_at<C, q>(D);
+        });
+        static_for<0, Z - 1>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            halo[q] = from_next_lane(head[q]);
+        });
+    }
+
+    template <int Q>
+    __device__ __forceinline__ uint64_t hash_of(const uint32_t (&D)[C::ND])
+    {
+        if constexpr (Q < Z - 1)
+            return head[Q];
+        else if constexpr (Q < C::KL)
+            return smer_hash_at<C, Q>(D);
+        else
+            return halo[Q - C::KL];
+    }
+
+    template <int I>
+    __device__ __forceinline__ void step(const uint32_t (&D)[C::ND], uint64_t (&R)[4])
+    {
+        constexpr int qn = I == 0 ? 0 : I + Z - 1;
+        constexpr int qe = I + Z - 1;
+        static_for<qn, qe + 1>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            smer_masks<C>(hash_of<q>(D), L[0][q]);
+        });
+        static_for<1, NL>([&](auto lc) {
+            constexpr int l = decltype(lc)::value;
+            constexpr int span = 1 << l;
+            constexpr int e0 = (qn - span + 1) < 0 ? 0 : (qn - span + 1);
+            constexpr int e1 = qe - span + 1;
+            static_for<e0, e1 + 1>([&](auto ec) {
+                constexpr int e = decltype(ec)::value;
+#pragma unroll
+                for (int w = 0; w < C::NS; ++w)
+                    L[l][e][w] = L[l - 1][e][w] | L[l - 1][e + span / 2][w];
+            });
+        });
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            R[w] = 0;
+        static_for<0, NL>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr ((Z >> j) & 1) {
+                constexpr int off = (Z >> (j + 1)) << (j + 1);
+#pragma unroll
+                for (int w = 0; w < C::NS; ++w)
+                    R[w] |= L[j][I + off][w];
+            }
+        });
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Wave-level helpers.  Each wave owns a private slice of LDS: kSlots records
+// of (shard index, four 64-bit words).
+// ---------------------------------------------------------------------------
+constexpr int kSlots = 256;
+constexpr int kWaves = 4;  // waves per 256-thread workgroup
+
+struct WaveLds {
+    uint32_t idx[kWaves][kSlots];
+    uint64_t words[kWaves][kSlots][4];
+};
+
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t lane, uint32_t& total)
+{
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d);
+        if (lane >= (uint32_t)d)
+            x += y;
+    }
+    total = __shfl(x, 63);
+    return x - v;
+}
+
+// LDS written by some lanes of this wave becomes visible to all its lanes.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Run starts of a lane: bit i set if k-mer i is valid and does not continue
+// the previous one (invalid, or another shard).  Runs double as query segments.
+template <class C>
+__device__ __forceinline__ uint32_t run_starts(uint32_t vk, const uint32_t (&shard)[C::KL])
+{
+    uint32_t st = vk & 1u;
+#pragma unroll
+    for (int i = 1; i < C::KL; ++i) {
+        const bool cont = ((vk >> (i - 1)) & 1u) && shard[i] == shard[i - 1];
+        st |= (uint32_t)(((vk >> i) & 1u) && !cont) << i;
+    }
+    return st;
+}
+
+// Does this lane's first run continue the previous lane's last run?  Then the
+// two share one record slot (the previous lane's last).
+template <class C>
+__device__ __forceinline__ bool continues_previous(uint32_t vk, const uint32_t (&shard)[C::KL], uint32_t lane)
+{
+    const uint32_t prev_last_valid = __shfl_up((vk >> (C::KL - 1)) & 1u, 1);
+    const uint32_t prev_last_shard = __shfl_up(shard[C::KL - 1], 1);
+    return lane > 0 && (vk & 1u) && prev_last_valid && shard[0] == prev_last_shard;
+}
+
+template <class C>
+__device__ __forceinline__ void global_or_record(uint64_t* __restrict__ filter, uint32_t shard, const uint64_t (&Wm)[4])
 {
     uint64_t* base = filter + 4ull * shard;
 #pragma unroll
@@ -173,100 +358,236 @@ __device__ __forceinline__ void flush_run(uint64_t* __restrict__ filter, uint32_
         atomic_or_u64(base + q, Wm[q]);
 }
 
+// Insert ([cuSBF] Algorithm 1).  Pass A: shards, validity and run starts;
+// a wave scan gives each run a record slot.  Pass B: each run's sector masks
+// go to its slot (a run continuing the previous lane's last run ORs into that
+// slot).  Flush: four adjacent lanes OR the four words of one record into the
+// filter.  Records past kSlots go straight to the filter from their lane.
 template <class C>
 __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
 {
+    __shared__ WaveLds lds;
     const LaneCtx<C> c = lane_ctx<C>(a.nk);
     if (!c.live)
         return;  // whole wave
+    const int wv = threadIdx.x >> 6;
     uint32_t D[C::ND];
     load_codes<C>(a, c.p0, D);
     uint32_t shard[C::KL];
     lane_shards<C>(D, a.shard_mask, shard);
-    uint64_t hs[C::NZ];
-    lane_smer_hashes<C>(D, hs);
     const uint32_t vk = lane_valid<C>(a, c.p0, c.lane);
-    if (vk == 0)
-        return;
 
-    uint64_t Wm[4] = {0, 0, 0, 0};
-    bool open = false;
-    uint32_t cur = 0;
-#pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
+    // pass A: slots
+    const uint32_t st = run_starts<C>(vk, shard);
+    const uint32_t cin = continues_previous<C>(vk, shard, c.lane) ? 1u : 0u;
+    uint32_t total;
+    const uint32_t base = wave_excl_scan(__popc(st) - cin, c.lane, total);
+
+    // pass B: run masks -> records
+    FindereMasks<C> fm;
+    fm.init(D);
+    uint64_t Wr[4] = {0, 0, 0, 0};
+    uint64_t first[4] = {0, 0, 0, 0};
+    static_for<0, C::KL>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        uint64_t R[4];
+        fm.template step<i>(D, R);
         const bool vi = (vk >> i) & 1u;
-        const bool cont = open && vi && shard[i] == cur;
-        if (open && !cont)
-            flush_run<C>(a.filter, cur, Wm);
-        if (vi) {
-            if (!cont) {
+        const bool si = (st >> i) & 1u;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    Wm[q] = 0;
+        for (int w = 0; w < C::NS; ++w)
+            Wr[w] = vi ? ((si ? 0ull : Wr[w]) | R[w]) : Wr[w];
+        // the run ends here if the next k-mer does not continue it
+        bool ends;
+        if constexpr (i == C::KL - 1)
+            ends = vi;
+        else
+            ends = vi && (((st >> (i + 1)) & 1u) || !((vk >> (i + 1)) & 1u));
+        if (ends) {
+            const uint32_t ridx = __popc(st & ((2u << i) - 1u)) - 1u;
+            if (ridx == 0 && cin) {
 #pragma unroll
-                for (int j = 0; j < C::Z - 1; ++j) {
-                    uint64_t mk[4];
-                    smer_masks<C>(hs[i + j], mk);
+                for (int w = 0; w < C::NS; ++w)
+                    first[w] = Wr[w];
+            } else {
+                const uint32_t slot = base + ridx - cin;
+                if (slot < (uint32_t)kSlots) {
+                    lds.idx[wv][slot] = shard[i];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        Wm[q] |= mk[q];
+                    for (int w = 0; w < 4; ++w)
+                        lds.words[wv][slot][w] = Wr[w];
+                } else {
+                    global_or_record<C>(a.filter, shard[i], Wr);
                 }
             }
+        }
+        step_fence(D);
+    });
+    wave_lds_sync();
+    // first runs continuing the previous lane: OR into its last record
+    if (cin) {
+        const uint32_t slot = base - 1u;
+        if (slot < (uint32_t)kSlots) {
+#pragma unroll
+            for (int w = 0; w < C::NS; ++w)
+                __hip_atomic_fetch_or(&lds.words[wv][slot][w], first[w], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WAVEFRONT);
+        } else {
+            global_or_record<C>(a.filter, shard[0], first);
+        }
+    }
+    wave_lds_sync();
+
+    // flush: lane -> (record, word)
+    const uint32_t T = total < (uint32_t)kSlots ? total : (uint32_t)kSlots;
+    for (uint32_t r = c.lane; r < 4u * T; r += 64u) {
+        const uint32_t rec = r >> 2, q = r & 3u;
+        if (q < (uint32_t)C::NS) {
+            const uint64_t m = lds.words[wv][rec][q];
+            if (m)
+                atomic_or_u64(a.filter + 4ull * (lds.idx[wv][rec] & a.shard_mask) + q, m);
+        }
+    }
+}
+
+// Query of one lane's KL k-mers, each on its own: the k-mer from its base
+// window, minimizer over its w m-mers, one shard load, all s-mer masks.  The
+// path for waves whose runs exceed the LDS slots (very short runs); a runtime
+// loop keeps it small.
+template <class C>
+__device__ __forceinline__ uint32_t query_lane_direct(const SeqArgs& a, const uint32_t (&D)[C::ND], uint32_t vk)
+{
+    uint32_t bits = 0;
+    for (int i = 0; i < C::KL; ++i) {
+        if (!((vk >> i) & 1u))
+            continue;
+        const bool hi16 = i >= 16;
+        const uint32_t d0 = hi16 ? D[1] : D[0];
+        const uint32_t d1 = hi16 ? D[2] : D[1];
+        const uint32_t d2 = hi16 ? D[C::ND - 1] : D[2];
+        const uint32_t r = 2u * (uint32_t)(i & 15);
+        const uint64_t win = ((uint64_t)funnel_hi(d0, d1, r) << 32) | funnel_hi(d1, d2, r);
+        const uint64_t x = top_bases(win, C::k);
+        uint64_t mn = ~0ull;
+#pragma unroll
+        for (int j = 0; j < C::W; ++j) {
+            const uint64_t h = hash_min(sub_bases<C::k, C::m>(x, j));
+            mn = h < mn ? h : mn;
+        }
+        uint64_t w[4];
+        load_shard(a.filter, (uint32_t)mn & a.shard_mask, w);
+        uint64_t R[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < C::Z; ++j) {
             uint64_t mk[4];
-            smer_masks<C>(hs[i + C::Z - 1], mk);
+            smer_masks<C>(hash_s(sub_bases<C::k, C::s>(x, j)), mk);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                Wm[q] |= mk[q];
-            cur = shard[i];
+                R[q] |= mk[q];
         }
-        open = vi;
-    }
-    if (open)
-        flush_run<C>(a.filter, cur, Wm);
-}
-
-template <class C>
-__device__ __forceinline__ bool smer_hits(const uint64_t (&w)[4], uint64_t h)
-{
-    uint64_t acc = ~0ull;
+        uint32_t hit = 1u;
 #pragma unroll
-    for (int t = 0; t < C::H; ++t)
-        acc &= w[t & 3] >> bit_addr<C::H>(h, t);
-    return acc & 1ull;
+        for (int q = 0; q < C::NS; ++q)
+            hit &= (uint32_t)((R[q] & w[q]) == R[q]);
+        bits |= hit << i;
+    }
+    return bits;
 }
 
+// Query ([cuSBF] Algorithm 2).  Pass A: shards, validity, segment starts
+// (runs of one shard) and their slots.  Gather: the wave loads every
+// segment's 32-byte shard into LDS at once, two lanes per shard.  Pass B
+// (straight-line): k-mer i reads the words of its segment from LDS and is
+// present iff every bit of its Findere mask R_i is set: (R_i & W) == R_i.
 template <class C>
 __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
 {
+    __shared__ WaveLds lds;
     const uint64_t nk_pad = round64(a.nk);
     const LaneCtx<C> c = lane_ctx<C>(nk_pad);
     if (!c.live)
         return;
+    const int wv = threadIdx.x >> 6;
     uint32_t D[C::ND];
     load_codes<C>(a, c.p0, D);
-    uint32_t shard[C::KL];
-    lane_shards<C>(D, a.shard_mask, shard);
-    uint64_t hs[C::NZ];
-    lane_smer_hashes<C>(D, hs);
     const uint32_t vk = lane_valid<C>(a, c.p0, c.lane);
-
-    uint32_t bits = 0;
-    uint64_t w[4] = {0, 0, 0, 0};
-    bool have = false;
-    uint32_t cur = 0;
+    uint32_t st, cin, base, total;
+    {
+        uint32_t shard[C::KL];
+        lane_shards<C>(D, a.shard_mask, shard);
+        // pass A: segment slots, shard indices into LDS
+        st = run_starts<C>(vk, shard);
+        cin = continues_previous<C>(vk, shard, c.lane) ? 1u : 0u;
+        base = wave_excl_scan(__popc(st) - cin, c.lane, total);
+        if (total <= (uint32_t)kSlots) {
 #pragma unroll
-    for (int i = 0; i < C::KL; ++i) {
-        const bool vi = (vk >> i) & 1u;
-        if (vi && (!have || shard[i] != cur)) {
-            load_shard(a.filter, shard[i], w);
-            cur = shard[i];
-            have = true;
+            for (int i = 0; i < C::KL; ++i) {
+                const uint32_t ridx = __popc(st & ((1u << i) - 1u));
+                if (((st >> i) & 1u) && !(ridx == 0 && cin))
+                    lds.idx[wv][base + ridx - cin] = shard[i];
+            }
         }
-        bool pres = vi;
+    }
+    uint32_t bits;
+    if (total <= (uint32_t)kSlots) {
+        wave_lds_sync();
+        // gather: lane -> (segment, 16-byte half)
+        const uint32_t n2 = 2u * total;
+        auto half_src = [&](uint32_t r) {
+            return reinterpret_cast<const ulonglong2*>(a.filter + 4ull * (lds.idx[wv][r >> 1] & a.shard_mask)) +
+                   (r & 1u);
+        };
+        auto half_dst = [&](uint32_t r) { return reinterpret_cast<ulonglong2*>(lds.words[wv][r >> 1]) + (r & 1u); };
+        for (uint32_t r0 = c.lane; r0 < n2; r0 += 256u) {
+            // four independent 16-byte loads in flight per lane, then four LDS stores
+            const uint32_t r1 = r0 + 64u, r2 = r0 + 128u, r3 = r0 + 192u;
+            const ulonglong2 v0 = *half_src(r0);
+            ulonglong2 v1 = {0, 0}, v2 = {0, 0}, v3 = {0, 0};
+            if (r1 < n2)
+                v1 = *half_src(r1);
+            if (r2 < n2)
+                v2 = *half_src(r2);
+            if (r3 < n2)
+                v3 = *half_src(r3);
+            *half_dst(r0) = v0;
+            if (r1 < n2)
+                *half_dst(r1) = v1;
+            if (r2 < n2)
+                *half_dst(r2) = v2;
+            if (r3 < n2)
+                *half_dst(r3) = v3;
+        }
+        wave_lds_sync();
+
+        // pass B
+        FindereMasks<C> fm;
+        fm.init(D);
+        bits = 0;
+        const uint32_t seg0 = base - cin - 1u;  // slot of the segment before the lane's first start
+        static_for<0, C::KL>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            uint64_t R[4];
+            fm.template step<i>(D, R);
+            // slot of the segment holding k-mer i; clamped for invalid k-mers before any start
+            uint32_t slot = seg0 + __popc(st & ((2u << i) - 1u));
+            slot = slot < (uint32_t)kSlots ? slot : (uint32_t)kSlots - 1u;
+            const ulonglong2* ws = reinterpret_cast<const ulonglong2*>(lds.words[wv][slot]);
+            const ulonglong2 w01 = ws[0];
+            uint64_t wq[4] = {w01.x, w01.y, 0, 0};
+            if constexpr (C::NS > 2) {
+                const ulonglong2 w23 = ws[1];
+                wq[2] = w23.x;
+                wq[3] = w23.y;
+            }
+            uint32_t hit = (vk >> i) & 1u;
 #pragma unroll
-        for (int j = 0; j < C::Z; ++j)
-            pres &= smer_hits<C>(w, hs[i + j]);
-        bits |= (uint32_t)pres << i;
+            for (int q = 0; q < C::NS; ++q)
+                hit &= (uint32_t)((R[q] & wq[q]) == R[q]);
+            bits |= hit << i;
+            step_fence(D);
+        });
+    } else {
+        bits = query_lane_direct<C>(a, D, vk);
     }
     if (c.lane < (uint32_t)C::LW && c.p0 < nk_pad) {
         if constexpr (C::KL == 16)
@@ -294,12 +615,20 @@ __global__ __launch_bounds__(256) void sbf_probe_kernel(ProbeArgs a)
         }
         uint64_t w[4];
         load_shard(a.filter, (uint32_t)mn & a.shard_mask, w);
-        bool pres = true;
+        uint64_t R[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < C::Z; ++j) {
-            pres &= smer_hits<C>(w, hash_s(sub_bases<C::k, C::s>(x, j)));
+            uint64_t mk[4];
+            smer_masks<C>(hash_s(sub_bases<C::k, C::s>(x, j)), mk);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                R[q] |= mk[q];
         }
-        cnt += pres;
+        uint64_t miss = 0;
+#pragma unroll
+        for (int q = 0; q < C::NS; ++q)
+            miss |= R[q] & ~w[q];
+        cnt += miss == 0;
     }
     // wave reduction, one atomic per wave
 #pragma unroll
