@@ -71,6 +71,33 @@ __device__ __forceinline__ uint64_t sub_bases(uint64_t x, int j)
         return (x >> (2 * (KK - N - j))) & ((1ull << (2 * N)) - 1ull);
 }
 
+// 32 bits of the lane's packed base stream starting at bit OFF (OFF compile
+// time; the stream is D[0], D[1], ... with the first base in the top bits).
+template <int OFF, int NDW>
+__device__ __forceinline__ uint32_t stream_bits32(const uint32_t (&D)[NDW])
+{
+    constexpr int a = OFF >> 5, r = OFF & 31;
+    if constexpr (r == 0)
+        return D[a];
+    else
+        return __builtin_amdgcn_alignbit(D[a], D[a + 1], 32 - r);
+}
+
+// Value of the N bases starting at the lane's base P, first base most
+// significant (N <= 32): one or two funnel shifts and a shift.
+template <int P, int N, int NDW>
+__device__ __forceinline__ uint64_t bases_at(const uint32_t (&D)[NDW])
+{
+    if constexpr (2 * N <= 32) {
+        const uint32_t w = stream_bits32<2 * P>(D);
+        return 2 * N == 32 ? (uint64_t)w : (uint64_t)(w >> (32 - 2 * N));
+    } else {
+        const uint32_t lo = stream_bits32<2 * P + 2 * N - 32>(D);
+        const uint32_t hi = stream_bits32<2 * P>(D) >> (64 - 2 * N);
+        return ((uint64_t)hi << 32) | lo;
+    }
+}
+
 // Answer words are written in KL-bit pieces; the grid covers nk rounded up
 // to 64 so every piece of every output word is written.
 __host__ __device__ inline uint64_t round64(uint64_t x) { return (x + 63) & ~63ull; }
@@ -107,7 +134,8 @@ __device__ __forceinline__ void load_codes(const SeqArgs& a, uint64_t p0, uint32
 // wave_shl:1 move per 32-bit half, no LDS traffic.
 __device__ __forceinline__ uint32_t from_next_lane(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x130, 0xF, 0xF, false);
+    // bound_ctrl: lane 63 reads 0 instead of keeping an old value, so no copy
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x130, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ uint64_t from_next_lane(uint64_t v)
@@ -122,12 +150,12 @@ __device__ __forceinline__ void lane_shards(const uint32_t (&D)[C::ND], uint32_t
 {
     constexpr int W = C::W, KL = C::KL, NM = C::NM;
     uint64_t hm[NM];
-#pragma unroll
-    for (int i = 0; i < KL; ++i)
-        hm[i] = hash_min(top_bases(stream_window<C::ND>(D, i), C::m));
-#pragma unroll
-    for (int j = 0; j < W - 1; ++j)
-        hm[KL + j] = from_next_lane(hm[j]);
+    static_for<0, KL>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        hm[i] = hash_min(bases_at<i, C::m>(D));
+        if constexpr (i < W - 1)
+            hm[KL + i] = from_next_lane(hm[i]);  // lane l+1's position i is this lane's KL+i
+    });
     if constexpr (W == 1) {
 #pragma unroll
         for (int i = 0; i < KL; ++i)
@@ -216,20 +244,23 @@ __device__ __forceinline__ void step_fence(uint32_t (&D)[NDW])
 template <class C, int Q>
 __device__ __forceinline__ uint64_t smer_hash_at(const uint32_t (&D)[C::ND])
 {
-    return hash_s(top_bases(stream_window<C::ND>(D, Q), C::s));
+    return hash_s(bases_at<Q, C::s>(D));
 }
 
-// Streaming Findere masks: level l entry e = OR of the sector masks of s-mers
-// e .. e + 2^l - 1.  step<I>() hashes the s-mers that are new at k-mer I
-// (positions 0..Z-1 at I = 0, then I+Z-1), builds the doubling-level entries
-// whose last s-mer is new, and returns R_I = OR of the masks of s-mers
-// I .. I+Z-1, one level per set bit of Z.  The first Z-1 own hashes and the
-// Z-1 halo hashes of lane l+1 are computed up front (init), every other hash
-// in the step that first needs it, so few hashes are live at once.
+// Streaming Findere masks.  Level l entry e = OR of the sector masks of
+// s-mers e .. e + 2^l - 1.  R_I, the OR over the Z = k-s+1 s-mers of k-mer I,
+// is split at the top level T = floor(log2 Z) into two halves (levels T-1 at
+// I and I + 2^(T-1)) plus one stored entry per lower set bit of Z, so the top
+// level is never stored: step<I>() hashes the s-mers new at k-mer I (all of
+// 0..Z-1 at I = 0, then I+Z-1), builds the new entries of levels 0..T-1 and
+// returns R_I = T0 | T1.  The first Z-1 own hashes and the Z-1 halo hashes of
+// lane l+1 are computed by init(); every other hash in the step that first
+// needs it, so few hashes are live at once.
 template <class C>
 struct FindereMasks {
-    static constexpr int NZ = C::NZ, Z = C::Z, NL = ilog2c(Z) + 1, NH = Z > 1 ? Z - 1 : 1;
-    uint64_t L[NL][NZ][4];
+    static constexpr int NZ = C::NZ, Z = C::Z, TOP = ilog2c(Z), NLV = TOP > 0 ? TOP : 1;
+    static constexpr int NH = Z > 1 ? Z - 1 : 1;
+    uint64_t L[NLV][NZ][4];
     uint64_t head[NH];  // own hashes of positions 0 .. Z-2
     uint64_t halo[NH];  // hashes of positions KL .. KL+Z-2 (lane l+1's head)
 
@@ -257,7 +288,7 @@ struct FindereMasks {
     }
 
     template <int I>
-    __device__ __forceinline__ void step(const uint32_t (&D)[C::ND], uint64_t (&R)[4])
+    __device__ __forceinline__ void step(const uint32_t (&D)[C::ND], uint64_t (&T0)[4], uint64_t (&T1)[4])
     {
         constexpr int qn = I == 0 ? 0 : I + Z - 1;
         constexpr int qe = I + Z - 1;
@@ -265,7 +296,7 @@ struct FindereMasks {
             constexpr int q = decltype(qc)::value;
             smer_masks<C>(hash_of<q>(D), L[0][q]);
         });
-        static_for<1, NL>([&](auto lc) {
+        static_for<1, TOP>([&](auto lc) {
             constexpr int l = decltype(lc)::value;
             constexpr int span = 1 << l;
             constexpr int e0 = (qn - span + 1) < 0 ? 0 : (qn - span + 1);
@@ -279,18 +310,61 @@ struct FindereMasks {
         });
 #pragma unroll
         for (int w = 0; w < 4; ++w)
-            R[w] = 0;
-        static_for<0, NL>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            if constexpr ((Z >> j) & 1) {
-                constexpr int off = (Z >> (j + 1)) << (j + 1);
+            T0[w] = T1[w] = 0;
+        if constexpr (TOP == 0) {
 #pragma unroll
-                for (int w = 0; w < C::NS; ++w)
-                    R[w] |= L[j][I + off][w];
+            for (int w = 0; w < C::NS; ++w)
+                T0[w] = L[0][I][w];
+        } else {
+            constexpr int half = 1 << (TOP - 1);
+#pragma unroll
+            for (int w = 0; w < C::NS; ++w) {
+                T0[w] = L[TOP - 1][I][w];
+                T1[w] = L[TOP - 1][I + half][w];
             }
-        });
+            // lower set bits of Z: stored entries after the top block
+            static_for<0, TOP>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if constexpr ((Z >> j) & 1) {
+                    constexpr int off = (Z >> (j + 1)) << (j + 1);
+#pragma unroll
+                    for (int w = 0; w < C::NS; ++w)
+                        T0[w] |= L[j][I + off][w];
+                }
+            });
+        }
     }
 };
+
+// Bits of R = T0 | T1 missing from the shard words W: (T0 | T1) & ~W, one
+// 3-input bit operation per 32-bit half.
+template <class C>
+__device__ __forceinline__ uint64_t missing_bits(const uint64_t (&T0)[4], const uint64_t (&T1)[4], const uint64_t (&W)[4])
+{
+    uint64_t miss = 0;
+#pragma unroll
+    for (int q = 0; q < C::NS; ++q) {
+        const uint32_t lo = __builtin_amdgcn_bitop3_b32((uint32_t)T0[q], (uint32_t)T1[q], (uint32_t)W[q], 0x54);
+        const uint32_t hi = __builtin_amdgcn_bitop3_b32((uint32_t)(T0[q] >> 32), (uint32_t)(T1[q] >> 32),
+                                                        (uint32_t)(W[q] >> 32), 0x54);
+        miss |= ((uint64_t)hi << 32) | lo;
+    }
+    return miss;
+}
+
+// Run accumulation: Wr = (Wr & keep) | T0 | T1 with keep = 0 at a run start,
+// all ones otherwise.
+template <class C>
+__device__ __forceinline__ void accumulate_run(uint64_t (&Wr)[4], uint32_t keep, const uint64_t (&T0)[4], const uint64_t (&T1)[4])
+{
+#pragma unroll
+    for (int q = 0; q < C::NS; ++q) {
+        const uint64_t t = T0[q] | T1[q];
+        const uint32_t lo = __builtin_amdgcn_bitop3_b32((uint32_t)Wr[q], keep, (uint32_t)t, 0xEA);
+        const uint32_t hi = __builtin_amdgcn_bitop3_b32((uint32_t)(Wr[q] >> 32), keep, (uint32_t)(t >> 32), 0xEA);
+        Wr[q] = ((uint64_t)hi << 32) | lo;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Wave-level helpers.  Each wave owns a private slice of LDS: kSlots records
@@ -390,13 +464,13 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
     uint64_t first[4] = {0, 0, 0, 0};
     static_for<0, C::KL>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        uint64_t R[4];
-        fm.template step<i>(D, R);
+        uint64_t T0[4], T1[4];
+        fm.template step<i>(D, T0, T1);
         const bool vi = (vk >> i) & 1u;
-        const bool si = (st >> i) & 1u;
-#pragma unroll
-        for (int w = 0; w < C::NS; ++w)
-            Wr[w] = vi ? ((si ? 0ull : Wr[w]) | R[w]) : Wr[w];
+        // a run start clears the run masks; an invalid k-mer may add to them,
+        // as it never lies inside a run and the next start clears them again
+        const uint32_t keep = ((st >> i) & 1u) ? 0u : 0xFFFFFFFFu;
+        accumulate_run<C>(Wr, keep, T0, T1);
         // the run ends here if the next k-mer does not continue it
         bool ends;
         if constexpr (i == C::KL - 1)
@@ -566,8 +640,8 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
         const uint32_t seg0 = base - cin - 1u;  // slot of the segment before the lane's first start
         static_for<0, C::KL>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            uint64_t R[4];
-            fm.template step<i>(D, R);
+            uint64_t T0[4], T1[4];
+            fm.template step<i>(D, T0, T1);
             // slot of the segment holding k-mer i; clamped for invalid k-mers before any start
             uint32_t slot = seg0 + __popc(st & ((2u << i) - 1u));
             slot = slot < (uint32_t)kSlots ? slot : (uint32_t)kSlots - 1u;
@@ -579,11 +653,8 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
                 wq[2] = w23.x;
                 wq[3] = w23.y;
             }
-            uint32_t hit = (vk >> i) & 1u;
-#pragma unroll
-            for (int q = 0; q < C::NS; ++q)
-                hit &= (uint32_t)((R[q] & wq[q]) == R[q]);
-            bits |= hit << i;
+            const uint64_t miss = missing_bits<C>(T0, T1, wq);
+            bits |= (uint32_t)(((vk >> i) & 1u) && miss == 0) << i;
             step_fence(D);
         });
     } else {
