@@ -32,36 +32,38 @@ if ROOT not in sys.path:
 K, M_, S_, H_ = 31, 16, 28, 4
 METRIC = "insert & query Gk-mers/s (k=31,m=16,s=28,H=4) + fraction of HBM/L2 roofline"
 
-# MI355X ALU peak from unit counts and clock: 256 CUs x 4 SIMDs, each SIMD
-# retires 16 lanes of a 3-operand (VOP3-encoded) integer op per clock -- the
-# same rate as an fp64 FMA (78.6 TFLOP/s) -- and 32 lanes of a 2-operand
-# (VOP2) add/xor/shift per clock, the fp32 rate (157.3 TFLOP/s).  Work is
-# counted in VOP3-equivalent lane-ops: VOP3 = 1, VOP2 = 1/2.
+# MI355X ALU peak from unit counts and clock: 256 CUs x 4 SIMDs x 16 lanes;
+# a wave64 VALU instruction occupies a SIMD for 4 clocks, so the chip retires
+# 256 * 64 lane-instructions per clock, 3.93e13 per second at 2.4 GHz -- the
+# fp64 FMA rate (78.6 TFLOP/s).  (A few 2-operand integer ops can issue
+# faster; the kernels' own SQ counters show them issue-bound at this rate.)
 CUS, CLOCK_HZ = 256, 2.4e9
-ALU_PEAK = CUS * 64 * CLOCK_HZ  # 3.93e13 VOP3-equivalent lane-ops/s
+ALU_PEAK = CUS * 64 * CLOCK_HZ  # 3.93e13 lane-instructions/s
 HBM_PEAK = 8.0e12               # bytes/s
+
+# Algorithmic integer work per k-mer start at (k,m,s,H) = (31,16,28,4), in
+# 32-bit VALU instructions, for the sliding formulation (each position hashes
+# one m-mer and one s-mer; the minimizer is a sliding minimum; the Findere
+# mask of a k-mer is one new doubling level per s-mer).  Itemised in the design doc.
+FRONT = {
+    "m-mer window (funnel shift)": 1,
+    "h_min: 32x64 multiply with folded offset (2 mad_u64), carry move, fold": 4,
+    "sliding minimum: 3 x (64-bit compare + 2 selects)": 9,
+    "shard mask": 1,
+    "s-mer window (2 funnel shifts + shift)": 3,
+    "h_s: 64-bit add, 3 x (64-bit shift + 2 xor), 2 x (2 mul_lo + mad_u64 + add3)": 18,
+    "H=4 bit masks of the new s-mer (2 slice shifts + 4 64-bit shifts)": 6,
+    "one new doubling level of the s-mer masks (4 words x 2 halves)": 8,
+    "validity / run bookkeeping": 2,
+}
+TAIL = {
+    "query": {"(T0|T1) & ~W per half (bitop3), 3 OR reductions, compare, answer bit": 13},
+    "insert": {"T0|T1 and (Wr & keep) | t per half": 16, "record flush share (~0.12 runs/k-mer)": 1.5},
+}
 
 
 def alu_ops_per_kmer(kind: str) -> float:
-    """Algorithmic integer work per k-mer start at (k,m,s,H) = (31,16,28,4),
-    in VOP3-equivalent lane-ops, for the sliding formulation: each position
-    contributes one m-mer hash and one s-mer hash; the minimizer is a sliding
-    minimum (3 64-bit min per k-mer); a query tests (k-s+1)*H bits, an insert
-    ORs one new s-mer's H bits into the run's sector masks and re-seeds them at
-    run starts.  Itemised in DESIGN.md ("Roofline")."""
-    window = 2.0            # 64-bit base window at this position: 2 alignbit
-    h_min = 5.5             # +G (2 VOP2), 64x64 multiply (mad_u64 + 2 mul_lo + add3), fold (VOP2)
-    smer = 1.5              # s-mer = window >> (64-2s): alignbit + shift
-    h_s = 16.5              # +G (1), 3 xorshifts (2.5 each), 2 multiplies (4 each)
-    win_min = 6.0           # 3 x (64-bit compare + 2 selects)
-    misc = 1.2              # shard mask, validity, output / run bookkeeping
-    front = window + h_min + smer + h_s + win_min + misc
-    if kind == "query":
-        return front + (K - S_ + 1) * H_ * 2.5   # per bit: extract, 64-bit shift, AND
-    if kind == "insert":
-        masks = H_ * 2 + 4 + 4 + 8 + 1.2       # H addresses + 1<<b, OR new s-mer, select, re-seed ORs, flush
-        return front + masks
-    raise ValueError(kind)
+    return float(sum(FRONT.values()) + sum(TAIL[kind].values()))
 
 
 def _bytes_per_kmer(kind: str, w: int = K - M_ + 1) -> float:
@@ -215,7 +217,7 @@ def main():
         alu = rate * alu_ops_per_kmer(kind)
         mem = rate * _bytes_per_kmer(kind)
         return ({"bound": "alu", "achieved": alu / 1e12, "peak": ALU_PEAK / 1e12,
-                 "unit": "T int-ops/s", "frac": alu / ALU_PEAK, "traffic": None,
+                 "unit": "T lane-instr/s", "frac": alu / ALU_PEAK, "traffic": None,
                  "kernel": kind, "per_kmer_ops": alu_ops_per_kmer(kind)},
                 {"bound": "hbm", "achieved": mem / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                  "frac": mem / HBM_PEAK, "traffic": None, "kernel": kind, "per_kmer_bytes": _bytes_per_kmer(kind)})

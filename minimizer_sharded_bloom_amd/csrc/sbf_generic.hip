@@ -14,59 +14,77 @@ namespace sbf {
 
 // ---------------------------------------------------------------------------
 // a1: ASCII -> 2-bit codes + validity ([cuSBF] §IV-A alphabet, §IV-F
-// separators).  One lane per 16 bases: a 16-byte load, one code word and one
-// 16-bit half of a validity word.
+// separators).  One lane per 32 bases: two 16-byte loads, two code words and
+// one validity word, four bases per 32-bit SIMD-within-a-register step.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void encode4(uint32_t four, uint32_t& code4, uint32_t& valid4)
+
+// Four ASCII bytes (first base in the low byte) -> one code byte with the
+// first base in its top two bits, and four validity bits (bit j = byte j).
+__device__ __forceinline__ void encode_dword(uint32_t w, uint32_t& code_byte, uint32_t& valid4)
 {
-    code4 = 0;
-    valid4 = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const uint32_t c = (four >> (8 * b)) & 0xFFu;
-        // A=0x41 C=0x43 G=0x47 T=0x54 (and lower case): ((c>>1)^(c>>2))&3 = 0,1,2,3
-        const uint32_t code = ((c >> 1) ^ (c >> 2)) & 3u;
-        const uint32_t lc = c | 0x20u;
-        const uint32_t ok = (lc == 'a') | (lc == 'c') | (lc == 'g') | (lc == 't');
-        code4 |= code << (6 - 2 * b);
-        valid4 |= ok << b;
-    }
+    // A=0x41 C=0x43 G=0x47 T=0x54 (and lower case): ((c>>1)^(c>>2))&3 = 0,1,2,3
+    const uint32_t c = ((w >> 1) ^ (w >> 2)) & 0x03030303u;
+    // c0 + c1<<8 + c2<<16 + c3<<24 times 2^30+2^20+2^10+1 puts c0..c3 at bits
+    // 30,28,26,24 with every cross term below bit 24 and no carry into it
+    code_byte = (c * 0x40100401u) >> 24;
+    // valid iff the byte, lower-cased, is the letter its code stands for
+    const uint32_t expect = __builtin_amdgcn_perm(0x74676361u, 0x74676361u, c);  // "acgt" by code
+    const uint32_t diff = (w | 0x20202020u) ^ expect;
+    // exact zero-byte flags: high bit of byte j set iff byte j of diff is 0
+    const uint32_t t = (diff & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
+    const uint32_t z = ~(t | diff | 0x7F7F7F7Fu);
+    // flags at bits 7,15,23,31 -> bits 21..24 via one multiply
+    valid4 = ((((z >> 7) & 0x01010101u) * 0x00204081u) >> 21) & 0xFu;
+}
+
+// 16 bases (four dwords) -> one code word (first base in bits 31..30) and 16
+// validity bits.
+__device__ __forceinline__ void encode16(uint4 q, uint32_t& code, uint32_t& val)
+{
+    uint32_t b0, b1, b2, b3, v0, v1, v2, v3;
+    encode_dword(q.x, b0, v0);
+    encode_dword(q.y, b1, v1);
+    encode_dword(q.z, b2, v2);
+    encode_dword(q.w, b3, v3);
+    code = (b0 << 24) | (b1 << 16) | (b2 << 8) | b3;
+    val = v0 | (v1 << 4) | (v2 << 8) | (v3 << 12);
+}
+
+__device__ __forceinline__ uint4 load16_tail(const char* __restrict__ ascii, uint64_t base, uint64_t len)
+{
+    uint32_t q[4] = {0, 0, 0, 0};
+    for (int j = 0; j < 16 && base + j < len; ++j)
+        q[j >> 2] |= (uint32_t)(unsigned char)ascii[base + j] << (8 * (j & 3));
+    return make_uint4(q[0], q[1], q[2], q[3]);
 }
 
 __global__ __launch_bounds__(256) void pack_kernel(const char* __restrict__ ascii, uint64_t len,
-                                                   uint32_t* __restrict__ codes, uint16_t* __restrict__ valid16,
-                                                   uint64_t ncw, uint64_t nvh, int aligned16)
+                                                   uint32_t* __restrict__ codes, uint32_t* __restrict__ valid,
+                                                   uint64_t ncw, uint64_t nvw, int aligned16)
 {
-    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= nvh)
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;  // validity word index
+    if (i >= nvw)
         return;
-    const uint64_t base = 16 * i;
-    uint32_t q[4] = {0, 0, 0, 0};
-    if (base + 16 <= len && aligned16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(ascii + base);
-        q[0] = v.x;
-        q[1] = v.y;
-        q[2] = v.z;
-        q[3] = v.w;
-    } else if (base < len) {
-        for (int j = 0; j < 16 && base + j < len; ++j)
-            q[j >> 2] |= (uint32_t)(unsigned char)ascii[base + j] << (8 * (j & 3));
+    const uint64_t base = 32 * i;
+    uint4 q0, q1;
+    if (base + 32 <= len && aligned16) {
+        const uint4* p = reinterpret_cast<const uint4*>(ascii + base);
+        q0 = p[0];
+        q1 = p[1];
+    } else {
+        q0 = load16_tail(ascii, base, len);
+        q1 = load16_tail(ascii, base + 16, len);
     }
-    uint32_t code = 0, val = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t c4, v4;
-        encode4(q[j], c4, v4);
-        code |= c4 << (24 - 8 * j);
-        val |= v4 << (4 * j);
-    }
-    if (base + 16 > len) {  // bases past len are invalid
-        const uint32_t keep = base >= len ? 0u : (uint32_t)(len - base);
-        val &= (1u << keep) - 1u;
-    }
-    if (i < ncw)
-        codes[i] = code;
-    valid16[i] = (uint16_t)val;
+    uint32_t c0, c1, v0, v1;
+    encode16(q0, c0, v0);
+    encode16(q1, c1, v1);
+    uint32_t val = v0 | (v1 << 16);
+    if (base + 32 > len)  // bases past len are invalid (their zero bytes already are)
+        val &= (uint32_t)((1ull << (len - base)) - 1ull);
+    codes[2 * i] = c0;
+    if (2 * i + 1 < ncw)
+        codes[2 * i + 1] = c1;
+    valid[i] = val;
 }
 
 hipError_t launch_pack(const char* ascii, uint64_t len, uint32_t* codes, uint32_t* valid, hipStream_t st)
@@ -74,11 +92,11 @@ hipError_t launch_pack(const char* ascii, uint64_t len, uint32_t* codes, uint32_
     if (len == 0)
         return hipSuccess;
     const uint64_t ncw = (len + 15) / 16;
-    const uint64_t nvh = 2 * ((len + 31) / 32);  // 16-bit halves of validity words
+    const uint64_t nvw = (len + 31) / 32;
     const int aligned = ((uintptr_t)ascii & 15u) == 0;
-    const uint64_t blocks = (nvh + 255) / 256;
-    hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, ascii, len, codes,
-                       reinterpret_cast<uint16_t*>(valid), ncw, nvh, aligned);
+    const uint64_t blocks = (nvw + 255) / 256;
+    hipLaunchKernelGGL(pack_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, ascii, len, codes, valid, ncw, nvw,
+                       aligned);
     return hipGetLastError();
 }
 
