@@ -1,0 +1,122 @@
+"""Parameter sweep of the Super Bloom filter against a per-k-mer blocked Bloom
+filter at a fixed memory budget (the synthetic analogue of the (s, m, H)
+exploration and the false-positive comparison in "cuSBF: A Minimizer-Aware
+Bloom Filter for Genomic Sequence Data on Modern GPUs", §V-B and §V-D).
+
+For every (s, m, H) in {24,26,28,30} x {12,16,20} x {2,3,4,6} at k = 31 and
+2^30 bits: insert the 50 Mbp synthetic genome of workload 4, query its 1 M
+reads, and count positives among 10^7 random 31-mers.  The blocked Bloom
+comparator (one hash picks a 256-bit block, H bits from a second hash) runs
+at the same budget for H in {2,3,4,6}.  Prints one JSON line per point and a
+summary table.
+
+    python -m minimizer_sharded_bloom_amd.sweep [--probe-n N] [--reps R]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+import time
+
+import numpy as np
+
+from . import SuperBloomFilter, lib, check, packed_words
+from . import synthetic as S
+
+K = 31
+BITS = 2**30
+S_VALUES = (24, 26, 28, 30)
+M_VALUES = (12, 16, 20)
+H_VALUES = (2, 3, 4, 6)
+
+
+def _time_ms(torch, stream, fn, reps):
+    """Median kernel time of fn() over reps runs, events on `stream`."""
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, out=sys.stdout):
+    import torch
+
+    torch.cuda.set_device(0)
+    w = S.workload(4)
+    dev = torch.device("cuda:0")
+    genome = torch.from_numpy(w["insert"]).to(dev)
+    reads = torch.from_numpy(w["queries"][0]).to(dev)
+    L = lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    packs = {}
+    for name, t in (("genome", genome), ("reads", reads)):
+        cw, vw = packed_words(t.numel())
+        c = torch.empty(cw, dtype=torch.int32, device=dev)
+        v = torch.empty(vw, dtype=torch.int32, device=dev)
+        check(L.sbf_pack(t.data_ptr(), t.numel(), c.data_ptr(), v.data_ptr(), sp), "pack")
+        packs[name] = (c, v, t.numel())
+    gc, gv, LG = packs["genome"]
+    rc, rv, LR = packs["reads"]
+    hits_dev = torch.zeros(1, dtype=torch.int64, device=dev)
+    rows = []
+
+    def point(f, label):
+        out_bits = torch.empty(max(1, f.num_answer_words(LR)), dtype=torch.int64, device=dev)
+
+        def ins():
+            check(L.sbf_clear(f.handle, sp), "clear")
+            check(L.sbf_insert_packed(f.handle, gc.data_ptr(), gv.data_ptr(), LG, sp), "insert")
+
+        # clear + insert timed together; clear is one 128 MiB fill (~0.03 ms)
+        t_ins = _time_ms(torch, stream, ins, reps)
+        t_q = _time_ms(torch, stream, lambda: check(
+            L.sbf_query_packed(f.handle, rc.data_ptr(), rv.data_ptr(), LR, out_bits.data_ptr(), sp), "query"), reps)
+        t_p = _time_ms(torch, stream, lambda: check(
+            L.sbf_fpr_probe_device(f.handle, probe_n, seed, hits_dev.data_ptr(), sp), "probe"), reps)
+        hits = int(hits_dev.item())
+        present = int(torch.bitwise_count(out_bits).sum().item()) if hasattr(torch, "bitwise_count") else None
+        row = dict(label, insert_ms=t_ins, query_ms=t_q, probe_ms=t_p,
+                   insert_gkmers_s=(LG - K + 1) / t_ins / 1e6, query_gkmers_s=(LR - K + 1) / t_q / 1e6,
+                   probe_n=probe_n, hits=hits, fpr=hits / probe_n, specialized=f.specialized,
+                   reads_positive_words=present)
+        rows.append(row)
+        print(json.dumps(row), file=out, flush=True)
+
+    for s in S_VALUES:
+        for m in M_VALUES:
+            for H in H_VALUES:
+                with SuperBloomFilter(K, m, s, H, BITS) as f:
+                    point(f, {"kind": "sbf", "s": s, "m": m, "H": H})
+    for H in H_VALUES:
+        with SuperBloomFilter.blocked(K, H, BITS) as f:
+            point(f, {"kind": "bbf", "s": None, "m": None, "H": H})
+    return rows
+
+
+def table(rows) -> str:
+    lines = ["| kind | s | m | H | insert Gk-mers/s | query Gk-mers/s | FPR (random 31-mers) |",
+             "|---|---|---|---|---:|---:|---:|"]
+    for r in rows:
+        lines.append("| %s | %s | %s | %d | %.1f | %.1f | %.3g |" % (
+            r["kind"], r["s"] if r["s"] else "-", r["m"] if r["m"] else "-", r["H"],
+            r["insert_gkmers_s"], r["query_gkmers_s"], r["fpr"]))
+    return "\n".join(lines)
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--probe-n", type=int, default=10_000_000)
+    ap.add_argument("--reps", type=int, default=3)
+    a = ap.parse_args()
+    t0 = time.time()
+    rows = run(a.probe_n, a.reps)
+    print(table(rows))
+    print("sweep wall time %.1f s" % (time.time() - t0), file=sys.stderr)

@@ -14,11 +14,16 @@ on Modern GPUs" (§V-A, §V-D), which are not available here:
      together and joined by 'N'; filter 2^26 bits.
   3  as 2 with a 200 Mbp genome and 20 M reads; filter 2^32 bits.
   4  as 2 with a 50 Mbp genome and 1 M reads; filter 2^30 bits.
-  5  3 Gbp uniform genome with 'N' runs of 1-1000 bases covering 0.1% of it
-     (not generated here yet).
+  5  3 Gbp uniform genome with 'N' runs of 1-1000 bases at uniform positions
+     until their lengths sum to 0.1% of it; 1 M long reads in 100 batches of
+     10 k: length round(exp(N(ln 10000, 0.5^2))) clamped to 1-50 kbp, uniform
+     forward-strand start, 5% errors split equally between substitution,
+     insertion of a random base and deletion; reads joined by 'N'; filter
+     2^35 bits.  The seeded 1% read subsample is one whole batch.
 
 Seeds: genome 0, foreign sequence 1, repeats 2, read starts 3, read errors 4,
-random reads 5, shuffle 6.
+random reads 5, shuffle 6, subsample 7, 'N' runs 8, long-read layout 9,
+long-read errors 10.
 """
 from __future__ import annotations
 
@@ -29,8 +34,10 @@ N_BYTE = ord("N")
 
 CONFIG_BITS = {1: 2**20, 2: 2**26, 3: 2**32, 4: 2**30, 5: 2**35}
 CONFIG_GENOME = {1: 100_000, 2: 5_000_000, 3: 200_000_000, 4: 50_000_000, 5: 3_000_000_000}
-CONFIG_READS = {2: 2_000_000, 3: 20_000_000, 4: 1_000_000}
+CONFIG_READS = {2: 2_000_000, 3: 20_000_000, 4: 1_000_000, 5: 1_000_000}
 READ_LEN = 150
+LONG_BATCHES = 100          # configuration 5 reads come in 100 batches of 10 k
+CHUNK = 1 << 27
 
 
 def uniform_codes(n: int, seed: int) -> np.ndarray:
@@ -112,6 +119,93 @@ def short_read_set(genome: np.ndarray, R: int, L: int = READ_LEN, err: float = 0
     return join_records(reads[perm])
 
 
+# every byte value -> its four 2-bit digits as bases, most significant first
+_BYTE_TO_4BASES = ACGT[(np.arange(256)[:, None] >> np.array([6, 4, 2, 0])[None, :]) & 3].astype(np.uint8)
+_BYTE_TO_4BASES_U32 = np.ascontiguousarray(_BYTE_TO_4BASES).view("<u4").reshape(-1)
+
+
+def uniform_ascii_fast(n: int, seed: int) -> np.ndarray:
+    """n i.i.d. uniform bases as ASCII: PCG64 random bytes, four bases per
+    byte, in 2^27-byte chunks of one stream."""
+    out = np.empty(((n + 3) // 4) * 4, dtype=np.uint8)
+    view = out.view("<u4")
+    rng = np.random.default_rng(seed)
+    for lo in range(0, view.size, CHUNK):
+        hi = min(view.size, lo + CHUNK)
+        view[lo:hi] = _BYTE_TO_4BASES_U32[np.frombuffer(rng.bytes(hi - lo), dtype=np.uint8)]
+    return out[:n]
+
+
+def genome_with_n_runs(G: int, frac: float = 0.001, run=(1, 1000), seed_genome: int = 0,
+                       seed_runs: int = 8) -> np.ndarray:
+    """ASCII of a uniform genome (uniform_ascii_fast) with 'N' runs of length
+    U{run} at uniform positions until the run lengths sum to `frac` of G."""
+    out = uniform_ascii_fast(G, seed_genome)
+    rr = np.random.default_rng(seed_runs)
+    done, target = 0, int(frac * G)
+    while done < target:
+        L = int(rr.integers(run[0], run[1] + 1))
+        p = int(rr.integers(0, G - L + 1))
+        out[p:p + L] = N_BYTE
+        done += L
+    return out
+
+
+_BASE_INDEX = np.full(256, 4, dtype=np.int64)  # ASCII -> 0..3 for A,C,G,T, 4 otherwise
+_BASE_INDEX[ACGT] = np.arange(4)
+
+
+def long_read_batch(genome: np.ndarray, b: int, n: int = 10_000, median: float = 10_000.0, sigma: float = 0.5,
+                    lo: int = 1_000, hi: int = 50_000, err: float = 0.05, seed_layout: int = 9,
+                    seed_err: int = 10) -> np.ndarray:
+    """ASCII of batch b of long reads (n reads joined by 'N'): lengths
+    round(exp(N(ln median, sigma^2))) clamped to [lo, hi], uniform
+    forward-strand starts, per-base errors at rate err (positions from
+    geometric gaps) split equally between substitution (another base),
+    insertion of a random base before the base, and deletion."""
+    G = genome.size
+    rl = np.random.default_rng([seed_layout, b])
+    lens = np.clip(np.rint(np.exp(rl.normal(np.log(median), sigma, n))), lo, min(hi, G)).astype(np.int64)
+    starts = rl.integers(0, G - lens + 1)
+    tmpl = np.concatenate([genome[s0:s0 + l0] for s0, l0 in zip(starts.tolist(), lens.tolist())])
+    total = tmpl.size
+    re_ = np.random.default_rng([seed_err, b])
+    if err > 0:
+        gaps = re_.geometric(err, int(total * err * 1.2) + 1000)
+        pos = np.cumsum(gaps) - 1
+        pos = pos[pos < total]
+    else:
+        pos = np.empty(0, dtype=np.int64)
+    kind = re_.integers(0, 3, pos.size)  # 0 substitution, 1 insertion, 2 deletion
+    sub, ins, dele = pos[kind == 0], pos[kind == 1], pos[kind == 2]
+    cur = _BASE_INDEX[tmpl[sub]]
+    tmpl[sub] = ACGT[(np.minimum(cur, 3) + re_.integers(1, 4, sub.size)) & 3]
+    body = np.delete(tmpl, dele)
+    ins_at = ins - np.searchsorted(dele, ins)  # insertion points after the deletions
+    body = np.insert(body, ins_at, ACGT[re_.integers(0, 4, ins.size)])
+    # read lengths after editing, then one 'N' between reads
+    ends = np.cumsum(lens)
+    read_of = lambda q: np.searchsorted(ends, q, side="right")
+    out_lens = lens - np.bincount(read_of(dele), minlength=n) + np.bincount(read_of(ins), minlength=n)
+    return np.insert(body, np.cumsum(out_lens)[:-1], N_BYTE)
+
+
+def long_read_subsample_batch(seed: int = 7) -> int:
+    """Index of the batch that is the seeded 1% read subsample."""
+    return int(np.random.default_rng(seed).integers(0, LONG_BATCHES))
+
+
+def long_read_set(genome: np.ndarray, batches=None) -> np.ndarray:
+    """ASCII of the given batches (default: all) joined by 'N'."""
+    batches = range(LONG_BATCHES) if batches is None else batches
+    parts = []
+    for b in batches:
+        if parts:
+            parts.append(np.array([N_BYTE], dtype=np.uint8))
+        parts.append(long_read_batch(genome, b))
+    return np.concatenate(parts) if parts else np.empty(0, dtype=np.uint8)
+
+
 def workload(cfg: int) -> dict:
     """Inputs of one configuration: ASCII uint8 arrays and the filter size."""
     if cfg == 1:
@@ -122,4 +216,7 @@ def workload(cfg: int) -> dict:
         g = genome_with_repeats(CONFIG_GENOME[cfg])
         reads = short_read_set(g, CONFIG_READS[cfg])
         return {"cfg": cfg, "bits": CONFIG_BITS[cfg], "insert": to_ascii(g), "queries": [reads]}
+    if cfg == 5:
+        g = genome_with_n_runs(CONFIG_GENOME[5])
+        return {"cfg": 5, "bits": CONFIG_BITS[5], "insert": g, "queries": [long_read_set(g)]}
     raise ValueError("workload %r is not generated by this module" % cfg)

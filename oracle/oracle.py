@@ -26,7 +26,7 @@ def build(force: bool = False) -> str:
     """Compile the oracle with gcc (plain -O2, no vectorisation flags)."""
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+        subprocess.check_call(["gcc", "-O2", "-std=gnu99", "-fPIC", "-shared", "-pthread",
                                "-Wall", "-Werror", "-o", tmp, SRC])
         os.replace(tmp, LIB)
     return LIB
@@ -78,6 +78,14 @@ def lib():
         L.osbf_query_positions.restype = None
         L.osbf_fpr_probe.argtypes = [p, u64, u64]
         L.osbf_fpr_probe.restype = u64
+        L.osbf_insert_seq_mt.argtypes = [p, p, u64, u32]
+        L.osbf_insert_seq_mt.restype = None
+        L.osbf_query_seq_mt.argtypes = [p, p, u64, p, u32]
+        L.osbf_query_seq_mt.restype = None
+        L.osbf_insert_seq_sampled_mt.argtypes = [p, p, u64, u64, u64, u32]
+        L.osbf_insert_seq_sampled_mt.restype = None
+        L.osbf_query_seq_sampled_mt.argtypes = [p, p, u64, p, p, u64, u64, u32]
+        L.osbf_query_seq_sampled_mt.restype = None
         _lib = L
     return _lib
 
@@ -139,6 +147,18 @@ def minimizer_hash(x: int, k: int, m: int) -> int:
 
 # ---- filter ----------------------------------------------------------------
 
+def _threads(n: int) -> int:
+    """Thread count for the threaded drivers: n, else the cores this process
+    may use, at most 16."""
+    if n:
+        return n
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(16, avail))
+
+
 class OracleFilter:
     """A Super Bloom filter (kind=KIND_SBF) or per-k-mer blocked Bloom filter
     (kind=KIND_BBF) held in host memory by the C oracle."""
@@ -188,6 +208,35 @@ class OracleFilter:
         if nk:
             lib().osbf_query_seq(self._h, ptr, arr.size, out.ctypes.data)
         return out
+
+    def insert_seq_mt(self, seq, nthreads: int = 0):
+        """insert_seq with the k-mer starts split over threads (0 = all cores)."""
+        arr, ptr = _buf(seq)
+        lib().osbf_insert_seq_mt(self._h, ptr, arr.size, _threads(nthreads))
+
+    def query_seq_mt(self, seq, nthreads: int = 0) -> np.ndarray:
+        arr, ptr = _buf(seq)
+        nk = max(0, arr.size - self.k + 1)
+        out = np.zeros((nk + 63) // 64, dtype=np.uint64)
+        if nk:
+            lib().osbf_query_seq_mt(self._h, ptr, arr.size, out.ctypes.data, _threads(nthreads))
+        return out
+
+    def insert_seq_sampled_mt(self, seq, sample_mask: int, sample_value: int, nthreads: int = 0):
+        """Insert only k-mers whose shard s has (s & sample_mask) == sample_value."""
+        arr, ptr = _buf(seq)
+        lib().osbf_insert_seq_sampled_mt(self._h, ptr, arr.size, sample_mask, sample_value, _threads(nthreads))
+
+    def query_seq_sampled_mt(self, seq, sample_mask: int, sample_value: int, nthreads: int = 0):
+        """(answers, checked) bit words over the k-mers of sampled shards."""
+        arr, ptr = _buf(seq)
+        nk = max(0, arr.size - self.k + 1)
+        out = np.zeros((nk + 63) // 64, dtype=np.uint64)
+        checked = np.zeros_like(out)
+        if nk:
+            lib().osbf_query_seq_sampled_mt(self._h, ptr, arr.size, out.ctypes.data, checked.ctypes.data,
+                                            sample_mask, sample_value, _threads(nthreads))
+        return out, checked
 
     def query_positions(self, seq, positions) -> np.ndarray:
         arr, ptr = _buf(seq)

@@ -36,6 +36,7 @@
  */
 #include "sbf_oracle.h"
 
+#include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -276,4 +277,145 @@ uint64_t osbf_fpr_probe(const osbf* f, uint64_t n, uint64_t seed)
     for (uint64_t i = 0; i < n; ++i)
         hits += (uint64_t)osbf_query_kmer(f, osbf_probe_kmer(seed, i, f->k));
     return hits;
+}
+
+/* ---- multi-threaded drivers ------------------------------------------------
+ * The same per-k-mer definition, with the k-mer starts split into contiguous
+ * ranges over threads.  Insert ORs bits with atomic fetch-or into the one
+ * filter (OR is commutative and idempotent, so the result is the
+ * single-threaded one); query ranges are whole 64-bit answer words, so the
+ * threads write disjoint words.  Used only to check large inputs. */
+
+typedef struct {
+    osbf* f;
+    const char* seq;
+    uint64_t len, p0, p1;
+    uint64_t* out;
+    uint64_t* checked;               /* sampled query: positions that were checked */
+    uint64_t sample_mask, sample_value; /* shards with (shard & mask) == value */
+} osbf_job;
+
+static void set_bits_atomic(uint64_t* shard, uint64_t hs, unsigned H)
+{
+    for (unsigned t = 0; t < H; ++t)
+        __atomic_fetch_or(&shard[t % 4u], 1ull << osbf_bitaddr(hs, t, H), __ATOMIC_RELAXED);
+}
+
+static void* insert_worker(void* arg)
+{
+    osbf_job* j = (osbf_job*)arg;
+    osbf* f = j->f;
+    for (uint64_t p = j->p0; p < j->p1; ++p) {
+        uint64_t x;
+        if (osbf_pack_kmer(j->seq + p, f->k, &x) != 0)
+            continue;
+        uint64_t sh = osbf_shard_of(f, x);
+        if ((sh & j->sample_mask) != j->sample_value)
+            continue;
+        uint64_t* shard = f->words + 4u * sh;
+        if (f->kind == OSBF_KIND_BBF) {
+            set_bits_atomic(shard, osbf_hs(osbf_hs(x)), f->H);
+            continue;
+        }
+        for (unsigned s = 0; s + f->s <= f->k; ++s)
+            set_bits_atomic(shard, osbf_hs(osbf_subwindow(x, f->k, s, f->s)), f->H);
+    }
+    return NULL;
+}
+
+static void* query_worker(void* arg)
+{
+    osbf_job* j = (osbf_job*)arg;
+    for (uint64_t p = j->p0; p < j->p1; ++p) {
+        uint64_t x;
+        if (osbf_pack_kmer(j->seq + p, j->f->k, &x) != 0)
+            continue;
+        if (j->checked) {
+            if ((osbf_shard_of(j->f, x) & j->sample_mask) != j->sample_value)
+                continue;
+            j->checked[p / 64u] |= 1ull << (p % 64u);
+        }
+        if (osbf_query_kmer(j->f, x))
+            j->out[p / 64u] |= 1ull << (p % 64u);
+    }
+    return NULL;
+}
+
+static void run_jobs(osbf* f, const char* seq, uint64_t len, uint64_t* out, uint64_t* checked,
+                     uint64_t sample_mask, uint64_t sample_value, unsigned nthreads, void* (*fn)(void*))
+{
+    uint64_t nk = len - f->k + 1u;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    osbf_job jobs[256];
+    pthread_t th[256];
+    uint64_t chunk = (nk + nthreads - 1) / nthreads;
+    chunk = (chunk + 63u) & ~63ull; /* whole answer words per thread */
+    unsigned started = 0;
+    for (unsigned t = 0; t < nthreads; ++t) {
+        uint64_t p0 = (uint64_t)t * chunk, p1 = p0 + chunk;
+        if (p0 >= nk)
+            break;
+        if (p1 > nk)
+            p1 = nk;
+        jobs[t].f = f;
+        jobs[t].seq = seq;
+        jobs[t].len = len;
+        jobs[t].p0 = p0;
+        jobs[t].p1 = p1;
+        jobs[t].out = out;
+        jobs[t].checked = checked;
+        jobs[t].sample_mask = sample_mask;
+        jobs[t].sample_value = sample_value;
+        if (pthread_create(&th[t], NULL, fn, &jobs[t]) != 0) {
+            fn(&jobs[t]); /* run inline if a thread cannot start */
+            th[t] = 0;
+        }
+        ++started;
+    }
+    for (unsigned t = 0; t < started; ++t)
+        if (th[t])
+            pthread_join(th[t], NULL);
+}
+
+void osbf_insert_seq_mt(osbf* f, const char* seq, uint64_t len, unsigned nthreads)
+{
+    if (len < f->k)
+        return;
+    run_jobs(f, seq, len, NULL, NULL, 0, 0, nthreads, insert_worker);
+}
+
+void osbf_query_seq_mt(const osbf* f, const char* seq, uint64_t len, uint64_t* out, unsigned nthreads)
+{
+    if (len < f->k)
+        return;
+    uint64_t nk = len - f->k + 1u;
+    memset(out, 0, ((nk + 63u) / 64u) * sizeof(uint64_t));
+    run_jobs((osbf*)f, seq, len, out, NULL, 0, 0, nthreads, query_worker);
+}
+
+/* Shard-sampled insert: only k-mers whose shard satisfies
+ * (shard & sample_mask) == sample_value; the words of those shards then
+ * equal the full insert's exactly, every other shard stays empty. */
+void osbf_insert_seq_sampled_mt(osbf* f, const char* seq, uint64_t len, uint64_t sample_mask,
+                                uint64_t sample_value, unsigned nthreads)
+{
+    if (len < f->k)
+        return;
+    run_jobs(f, seq, len, NULL, NULL, sample_mask, sample_value, nthreads, insert_worker);
+}
+
+/* Query restricted to the sampled shards: checked bit p = valid k-mer p maps
+ * to a sampled shard; out bit p = its answer (0 where not checked). */
+void osbf_query_seq_sampled_mt(const osbf* f, const char* seq, uint64_t len, uint64_t* out, uint64_t* checked,
+                               uint64_t sample_mask, uint64_t sample_value, unsigned nthreads)
+{
+    if (len < f->k)
+        return;
+    uint64_t nk = len - f->k + 1u;
+    memset(out, 0, ((nk + 63u) / 64u) * sizeof(uint64_t));
+    memset(checked, 0, ((nk + 63u) / 64u) * sizeof(uint64_t));
+    run_jobs((osbf*)f, seq, len, out, checked, sample_mask, sample_value, nthreads, query_worker);
 }

@@ -82,6 +82,18 @@ void osbf_query_positions(const osbf* f, const char* seq, uint64_t len,
 /* Number of positives among n probe k-mers from the stream at `seed`. */
 uint64_t osbf_fpr_probe(const osbf* f, uint64_t n, uint64_t seed);
 
+/* The same insert and query with the k-mer starts split over threads (for
+ * checking large inputs); results equal the single-threaded calls. */
+void osbf_insert_seq_mt(osbf* f, const char* seq, uint64_t len, unsigned nthreads);
+void osbf_query_seq_mt(const osbf* f, const char* seq, uint64_t len, uint64_t* out, unsigned nthreads);
+/* Shard-sampled variants: only k-mers whose shard s has
+ * (s & sample_mask) == sample_value take part.  The sampled shards' words
+ * then equal those of the full insert; checked marks the queried k-mers. */
+void osbf_insert_seq_sampled_mt(osbf* f, const char* seq, uint64_t len, uint64_t sample_mask,
+                                uint64_t sample_value, unsigned nthreads);
+void osbf_query_seq_sampled_mt(const osbf* f, const char* seq, uint64_t len, uint64_t* out, uint64_t* checked,
+                               uint64_t sample_mask, uint64_t sample_value, unsigned nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -397,3 +397,52 @@ def test_bbf_fill_based_fpr():
     hits = f.fpr_probe(n, 4242)
     assert p > 1e-3
     assert T.binom_ok(hits, n, p, z=4.5)
+
+
+@pytest.mark.parametrize("kind,params", [(O.KIND_SBF, (31, 16, 28, 4)), (O.KIND_SBF, (21, 11, 19, 3)),
+                                         (O.KIND_BBF, (31, 0, 0, 4))])
+def test_threaded_driver_equals_single_thread(kind, params):
+    """The multi-threaded insert/query drivers split k-mer starts over
+    threads; the union and the answers must equal the plain loop's."""
+    rng = np.random.default_rng(27)
+    k, m, s, H = params
+    seq = bytearray(T.random_dna(rng, 50000))
+    for p in rng.integers(0, len(seq), 40):
+        seq[p] = ord("N")
+    seq = bytes(seq)
+    a = O.OracleFilter(k, m, s, H, 2**15, kind=kind)
+    b = O.OracleFilter(k, m, s, H, 2**15, kind=kind)
+    a.insert_seq(seq)
+    b.insert_seq_mt(seq, 7)
+    assert (a.words() == b.words()).all()
+    q = T.random_dna(rng, 30001)
+    assert (a.query_seq(q) == b.query_seq_mt(q, 5)).all()
+    assert (a.query_seq(seq) == a.query_seq_mt(seq, 3)).all()
+
+
+def test_shard_sampled_driver():
+    """The shard-sampled insert reproduces the full insert on the sampled
+    shards and nothing else; the sampled query marks exactly the valid k-mers
+    of sampled shards and answers them as the full query does."""
+    rng = np.random.default_rng(28)
+    seq = bytearray(T.random_dna(rng, 40000))
+    for p in rng.integers(0, len(seq), 30):
+        seq[p] = ord("N")
+    seq = bytes(seq)
+    full = O.OracleFilter(31, 16, 28, 4, 2**14)
+    full.insert_seq(seq)
+    samp = O.OracleFilter(31, 16, 28, 4, 2**14)
+    samp.insert_seq_sampled_mt(seq, 7, 3, 4)
+    wf, ws = full.words().reshape(-1, 4), samp.words().reshape(-1, 4)
+    sel = (np.arange(wf.shape[0]) & 7) == 3
+    assert (ws[sel] == wf[sel]).all() and not ws[~sel].any() and wf[sel].any()
+    q = T.random_dna(rng, 20000) + seq[:10000]
+    ans, checked = full.query_seq_sampled_mt(q, 7, 3, 3)
+    nk = len(q) - 31 + 1
+    cb = T.bits_of(checked, nk)
+    want = T.bits_of(full.query_seq(q), nk)
+    assert (T.bits_of(ans, nk) == (want & cb)).all()
+    for p in range(0, nk, 97):
+        km = q[p:p + 31].decode()
+        exp = T.valid_str(km) and (full.shard_of(T.pack_str(km)) & 7) == 3
+        assert cb[p] == exp
