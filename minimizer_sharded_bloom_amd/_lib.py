@@ -68,6 +68,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError("libsbf.so is not built (%s); run `python -m minimizer_sharded_bloom_amd.build`" % path)
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7 with
+    # the same soname as the system one libsbf.so is linked against.  Whichever
+    # is loaded first serves both, and torch cannot initialise its devices on
+    # the system build.  Loading torch first binds libsbf.so to torch's
+    # runtime, so device pointers and streams are shared by one runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

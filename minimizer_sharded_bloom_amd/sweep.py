@@ -82,11 +82,11 @@ def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, out=sys.st
         t_p = _time_ms(torch, stream, lambda: check(
             L.sbf_fpr_probe_device(f.handle, probe_n, seed, hits_dev.data_ptr(), sp), "probe"), reps)
         hits = int(hits_dev.item())
-        present = int(torch.bitwise_count(out_bits).sum().item()) if hasattr(torch, "bitwise_count") else None
+        present = int(np.bitwise_count(out_bits.cpu().numpy().view(np.uint64)).sum())
         row = dict(label, insert_ms=t_ins, query_ms=t_q, probe_ms=t_p,
                    insert_gkmers_s=(LG - K + 1) / t_ins / 1e6, query_gkmers_s=(LR - K + 1) / t_q / 1e6,
                    probe_n=probe_n, hits=hits, fpr=hits / probe_n, specialized=f.specialized,
-                   reads_positive_words=present)
+                   reads_positive_kmers=present)
         rows.append(row)
         print(json.dumps(row), file=out, flush=True)
 

@@ -2,6 +2,8 @@
 of the HIP library must be bit-identical to the CPU oracle on the same seeded
 inputs ("cuSBF: A Minimizer-Aware Bloom Filter for Genomic Sequence Data on
 Modern GPUs", Algorithms 1 and 2, §V-D)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -223,3 +225,26 @@ def test_config2_full():
     assert (gb[pos.astype(np.int64)] == want).all()
     assert got[-1] >> np.uint64(nk % 64) == 0 if nk % 64 else True
     torch.cuda.synchronize()
+
+
+def test_library_first_then_torch():
+    """Creating a filter before torch is imported still leaves one HIP runtime
+    in the process (the binding loads torch's before libsbf.so): torch sees the
+    device and a device-tensor insert/query works.  Runs in a fresh child
+    process, since this one has torch loaded already."""
+    import subprocess
+    import sys
+    code = (
+        "import minimizer_sharded_bloom_amd as M\n"
+        "f = M.SuperBloomFilter(31, 16, 28, 4, 2**20)\n"
+        "import torch\n"
+        "assert torch.cuda.is_available()\n"
+        "s = torch.tensor(list(b'ACGT' * 100), dtype=torch.uint8, device='cuda')\n"
+        "f.insert_seq(s)\n"
+        "r = f.query_seq(s).cpu()\n"
+        "n = 400 - 31 + 1\n"
+        "assert int(sum(bin(int(w) & (2**64 - 1)).count('1') for w in r)) == n\n"
+        "print('ok')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=100)
+    assert p.returncode == 0 and p.stdout.strip().endswith("ok"), p.stdout + p.stderr
