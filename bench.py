@@ -78,6 +78,47 @@ def _bytes_per_kmer(kind: str, w: int = K - M_ + 1) -> float:
     return seq + 64 * runs
 
 
+CSRC = os.path.join(ROOT, "minimizer_sharded_bloom_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of the HIP sources (names and bytes) the kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(name.encode() + b"\0")
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str, sha: str):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summaries under profiles/ (already scaled by the
+    copy-kernel calibration), or None when no summary was taken at the
+    current kernel sources."""
+    if not os.path.isdir(PROFILES):
+        return None
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith("_traffic.md"):
+            continue
+        kv = {}
+        with open(os.path.join(PROFILES, name)) as f:
+            for line in f:
+                key, sep, val = line.strip().partition(":")
+                if sep and line.startswith("    ") and key.replace("_", "").isalnum() and key.islower():
+                    kv[key] = val.strip()
+        if kv.get("workload") != workload or kv.get("kernel_sources_sha256") != sha:
+            continue
+        fetch, write = kv.get("%s_fetch_bytes" % kernel), kv.get("%s_write_bytes" % kernel)
+        if fetch is not None and write is not None:
+            return {"bytes": float(fetch) + float(write), "fetch": float(fetch), "write": float(write),
+                    "source": "profiles/" + name}
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,7 +128,7 @@ def parse():
                     help="synthetic configuration (default 2: 8 MiB filter, 5 Mbp genome, 2 M reads)")
     ap.add_argument("--probe-n", type=int, default=10_000_000)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="budget of the single-thread oracle baseline (0 disables it)")
+                    help="budget of the CPU oracle baseline in seconds (0 disables it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 256 MiB device copy (elementwise kernel) whose "
                          "FETCH_SIZE/WRITE_SIZE counters scale the filter kernels' counters")
@@ -96,32 +137,37 @@ def parse():
 
 def cpu_baseline(w: dict, budget_s: float) -> dict:
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    the first genome bases and read bases (about budget_s seconds of work),
-    one thread."""
-    import numpy as np
+    the first genome bases and read bases (about budget_s seconds of work)
+    through its threaded insert/query drivers on the host's cores, and the
+    probe (single-threaded in the oracle) on a proportionate count."""
     from oracle import oracle as O
 
     g, reads = w["insert"], w["queries"][0]
+    cores = O._threads(0)
     f = O.OracleFilter(K, M_, S_, H_, w["bits"])
-    # calibrate on a short piece, then size the sample to the budget
+    # calibrate insert and query on short pieces, then size the sample to the budget
+    n0 = min(g.size, 2_000_000)
     t0 = time.perf_counter()
-    f.insert_seq(g[:200_000])
-    per = (time.perf_counter() - t0) / max(1, 200_000 - K + 1)
-    f = O.OracleFilter(K, M_, S_, H_, w["bits"])
-    n_ins = int(min(g.size, max(1_000_000, budget_s * 0.3 / per)))
-    n_q = int(min(reads.size, max(1_000_000, budget_s * 0.6 / per)))
-    n_p = int(max(100_000, budget_s * 0.1 / per))
-    t0 = time.perf_counter()
-    f.insert_seq(g[:n_ins])
+    f.insert_seq_mt(g[:n0], cores)
     t1 = time.perf_counter()
-    f.query_seq(reads[:n_q])
+    f.query_seq_mt(reads[:n0], cores)
+    per_i = (t1 - t0) / max(1, n0 - K + 1)
+    per_q = (time.perf_counter() - t1) / max(1, n0 - K + 1)
+    f = O.OracleFilter(K, M_, S_, H_, w["bits"])
+    n_ins = int(min(g.size, max(1_000_000, budget_s * 0.3 / per_i)))
+    n_q = int(min(reads.size, max(1_000_000, (budget_s * 0.9 - n_ins * per_i) / per_q)))
+    n_p = int(max(100_000, budget_s * 0.1 / (per_q * cores)))
+    t0 = time.perf_counter()
+    f.insert_seq_mt(g[:n_ins], cores)
+    t1 = time.perf_counter()
+    f.query_seq_mt(reads[:n_q], cores)
     t2 = time.perf_counter()
     f.fpr_probe(n_p, 0x5EED)
     t3 = time.perf_counter()
     kmers = (n_ins - K + 1) + (n_q - K + 1) + n_p
-    return {"value": kmers / (t3 - t0) / 1e9, "unit": "Gk-mers/s", "cores": 1, "kind": "oracle",
-            "sample": "single-thread C oracle: insert of the first %d genome bases, query of the first %d read "
-                      "bases, %d probe k-mers (%.1f s)" % (n_ins, n_q, n_p, t3 - t0),
+    return {"value": kmers / (t3 - t0) / 1e9, "unit": "Gk-mers/s", "cores": cores, "kind": "oracle",
+            "sample": "C oracle, %d threads: insert of the first %d genome bases, query of the first %d read "
+                      "bases, %d probe k-mers on one thread (%.1f s)" % (cores, n_ins, n_q, n_p, t3 - t0),
             "insert_gkmers_s": (n_ins - K + 1) / (t1 - t0) / 1e9,
             "query_gkmers_s": (n_q - K + 1) / (t2 - t1) / 1e9}
 
@@ -213,14 +259,23 @@ def main():
     ins_rate = nk_g / (phase["insert"] * 1e-3)
     q_rate = nk_r / (phase["query"] * 1e-3)
 
+    sha = kernel_sources_sha256()
+    wl = "cfg%d" % a.workload
+
     def roof(kind, rate):
         alu = rate * alu_ops_per_kmer(kind)
         mem = rate * _bytes_per_kmer(kind)
-        return ({"bound": "alu", "achieved": alu / 1e12, "peak": ALU_PEAK / 1e12,
-                 "unit": "T lane-instr/s", "frac": alu / ALU_PEAK, "traffic": None,
-                 "kernel": kind, "per_kmer_ops": alu_ops_per_kmer(kind)},
-                {"bound": "hbm", "achieved": mem / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                 "frac": mem / HBM_PEAK, "traffic": None, "kernel": kind, "per_kmer_bytes": _bytes_per_kmer(kind)})
+        tr = measured_traffic(wl, kind, sha)
+        traffic = None if tr is None else tr["bytes"]
+        extra = {} if tr is None else {"traffic_fetch": tr["fetch"], "traffic_write": tr["write"],
+                                       "traffic_source": tr["source"],
+                                       "traffic_per_kmer": tr["bytes"] / (nk_r if kind == "query" else nk_g)}
+        return (dict({"bound": "alu", "achieved": alu / 1e12, "peak": ALU_PEAK / 1e12,
+                      "unit": "T lane-instr/s", "frac": alu / ALU_PEAK, "traffic": traffic,
+                      "kernel": kind, "per_kmer_ops": alu_ops_per_kmer(kind)}, **extra),
+                dict({"bound": "hbm", "achieved": mem / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                      "frac": mem / HBM_PEAK, "traffic": traffic, "kernel": kind,
+                      "per_kmer_bytes": _bytes_per_kmer(kind)}, **extra))
 
     dom = "query" if phase["query"] >= phase["insert"] else "insert"
     alu, mem = roof(dom, q_rate if dom == "query" else ins_rate)
@@ -230,7 +285,7 @@ def main():
         "metric": METRIC, "value": round(value, 3), "unit": "Gk-mers/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u64", "data": "synthetic",
-        "config": {"workload": "cfg%d" % a.workload, "k": K, "m": M_, "s": S_, "H": H_, "filter_bits": w["bits"],
+        "config": {"workload": wl, "k": K, "m": M_, "s": S_, "H": H_, "filter_bits": w["bits"],
                    "genome_bases": LG, "read_bases": LR, "probe_kmers": a.probe_n,
                    "kmers_per_step": total},
         "roofline": primary, "roofline_other": secondary,
@@ -239,6 +294,7 @@ def main():
         "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
         "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},
         "wall_s_timed": round(wall, 3), "gen_s": round(gen_s, 2),
+        "kernel_sources_sha256": sha,
     }
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
