@@ -130,12 +130,29 @@ __device__ __forceinline__ void load_codes(const SeqArgs& a, uint64_t p0, uint32
         D[j] = ld_or0(a.codes, a.ncw, w0 + j);
 }
 
-// Value of lane l+1 in lane l (lane 63 receives its own value): one DPP
-// wave_shl:1 move per 32-bit half, no LDS traffic.
+// Value of lane l+1 in lane l (lane 63 receives 0): one DPP wave_shl:1 move
+// per 32-bit half, no LDS traffic.
 __device__ __forceinline__ uint32_t from_next_lane(uint32_t v)
 {
     // bound_ctrl: lane 63 reads 0 instead of keeping an old value, so no copy
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x130, 0xF, 0xF, true);
+}
+
+// Value of lane l-1 in lane l (lane 0 receives 0): DPP wave_shr:1.
+__device__ __forceinline__ uint32_t from_prev_lane(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x138, 0xF, 0xF, true);
+}
+
+// x * 2 + (this lane's bit of the lane mask m): one v_addc with m as the
+// carry-in, so a per-k-mer compare becomes a bit of a per-lane word in one
+// instruction after the compare.
+__device__ __forceinline__ uint32_t shift_in(uint32_t x, uint64_t m)
+{
+    uint32_t r;
+    uint64_t carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(x), "s"(m));
+    return r;
 }
 
 __device__ __forceinline__ uint64_t from_next_lane(uint64_t v)
@@ -373,22 +390,25 @@ __device__ __forceinline__ void accumulate_run(uint64_t (&Wr)[4], uint32_t keep,
 constexpr int kSlots = 256;
 constexpr int kWaves = 4;  // waves per 256-thread workgroup
 
+// kSlots + 1 records per wave: the query numbers its segments from 1 and
+// parks invalid k-mers on record 0.
 struct WaveLds {
-    uint32_t idx[kWaves][kSlots];
-    uint64_t words[kWaves][kSlots][4];
+    uint32_t idx[kWaves][kSlots + 1];
+    uint64_t words[kWaves][kSlots + 1][4];
 };
 
-__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t lane, uint32_t& total)
+// Inclusive prefix sum over the wave: DPP row shifts by 1, 2, 4 and 8 sum
+// within each row of 16 lanes, then the row_bcast:15 and row_bcast:31 moves
+// carry the totals of rows 0 and 0..1 into the later rows.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
 {
-    uint32_t x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(x, d);
-        if (lane >= (uint32_t)d)
-            x += y;
-    }
-    total = __shfl(x, 63);
-    return x - v;
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);
+    return x;
 }
 
 // LDS written by some lanes of this wave becomes visible to all its lanes.
@@ -400,17 +420,18 @@ __device__ __forceinline__ void wave_lds_sync()
 }
 
 // Run starts of a lane: bit i set if k-mer i is valid and does not continue
-// the previous one (invalid, or another shard).  Runs double as query segments.
+// the previous one (invalid, or another shard).  Runs double as query
+// segments.  The shard comparisons enter a bit word through shift_in, last
+// k-mer first.
 template <class C>
 __device__ __forceinline__ uint32_t run_starts(uint32_t vk, const uint32_t (&shard)[C::KL])
 {
-    uint32_t st = vk & 1u;
+    uint32_t ne = 0;  // bit i (i >= 1): shard i differs from shard i-1
 #pragma unroll
-    for (int i = 1; i < C::KL; ++i) {
-        const bool cont = ((vk >> (i - 1)) & 1u) && shard[i] == shard[i - 1];
-        st |= (uint32_t)(((vk >> i) & 1u) && !cont) << i;
-    }
-    return st;
+    for (int i = C::KL - 1; i >= 1; --i)
+        ne = shift_in(ne, __builtin_amdgcn_ballot_w64(shard[i] != shard[i - 1]));
+    ne = (ne << 1) | 1u;
+    return vk & (ne | ~(vk << 1));
 }
 
 // Does this lane's first run continue the previous lane's last run?  Then the
@@ -418,8 +439,8 @@ __device__ __forceinline__ uint32_t run_starts(uint32_t vk, const uint32_t (&sha
 template <class C>
 __device__ __forceinline__ bool continues_previous(uint32_t vk, const uint32_t (&shard)[C::KL], uint32_t lane)
 {
-    const uint32_t prev_last_valid = __shfl_up((vk >> (C::KL - 1)) & 1u, 1);
-    const uint32_t prev_last_shard = __shfl_up(shard[C::KL - 1], 1);
+    const uint32_t prev_last_valid = from_prev_lane((vk >> (C::KL - 1)) & 1u);
+    const uint32_t prev_last_shard = from_prev_lane(shard[C::KL - 1]);
     return lane > 0 && (vk & 1u) && prev_last_valid && shard[0] == prev_last_shard;
 }
 
@@ -454,8 +475,10 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
     // pass A: slots
     const uint32_t st = run_starts<C>(vk, shard);
     const uint32_t cin = continues_previous<C>(vk, shard, c.lane) ? 1u : 0u;
-    uint32_t total;
-    const uint32_t base = wave_excl_scan(__popc(st) - cin, c.lane, total);
+    const uint32_t nrec = __popc(st) - cin;
+    const uint32_t incl = wave_incl_scan(nrec);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    const uint32_t base = incl - nrec;
 
     // pass B: run masks -> records
     FindereMasks<C> fm;
@@ -569,10 +592,13 @@ __device__ __forceinline__ uint32_t query_lane_direct(const SeqArgs& a, const ui
 }
 
 // Query ([cuSBF] Algorithm 2).  Pass A: shards, validity, segment starts
-// (runs of one shard) and their slots.  Gather: the wave loads every
-// segment's 32-byte shard into LDS at once, two lanes per shard.  Pass B
-// (straight-line): k-mer i reads the words of its segment from LDS and is
-// present iff every bit of its Findere mask R_i is set: (R_i & W) == R_i.
+// (runs of one shard) and, per k-mer, the LDS record of its segment (segments
+// are numbered from 1 across the wave; invalid k-mers get record 0).  Every
+// k-mer writes its shard index to its record: all valid k-mers of a segment
+// carry the same shard, so no write needs a branch.  Gather: the wave loads
+// every segment's 32-byte shard into LDS at once, two lanes per shard.  Pass B
+// (straight-line): k-mer i reads the words of its record and is present iff
+// every bit of its Findere mask R_i is set: (R_i & W) == R_i.
 template <class C>
 __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
 {
@@ -585,51 +611,56 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
     uint32_t D[C::ND];
     load_codes<C>(a, c.p0, D);
     const uint32_t vk = lane_valid<C>(a, c.p0, c.lane);
-    uint32_t st, cin, base, total;
+    uint32_t st, total;
+    uint32_t rec[C::KL];
     {
         uint32_t shard[C::KL];
         lane_shards<C>(D, a.shard_mask, shard);
-        // pass A: segment slots, shard indices into LDS
+        // pass A: segment records, shard indices into LDS
         st = run_starts<C>(vk, shard);
-        cin = continues_previous<C>(vk, shard, c.lane) ? 1u : 0u;
-        base = wave_excl_scan(__popc(st) - cin, c.lane, total);
+        const uint32_t cin = continues_previous<C>(vk, shard, c.lane) ? 1u : 0u;
+        const uint32_t nseg = __popc(st) - cin;
+        const uint32_t incl = wave_incl_scan(nseg);
+        total = __builtin_amdgcn_readlane(incl, 63);
+        const uint32_t first = incl - nseg - cin;  // record of the segment before the lane's first start
+#pragma unroll
+        for (int i = 0; i < C::KL; ++i)
+            rec[i] = (__popc(st & ((2u << i) - 1u)) + first) * ((vk >> i) & 1u);
         if (total <= (uint32_t)kSlots) {
 #pragma unroll
-            for (int i = 0; i < C::KL; ++i) {
-                const uint32_t ridx = __popc(st & ((1u << i) - 1u));
-                if (((st >> i) & 1u) && !(ridx == 0 && cin))
-                    lds.idx[wv][base + ridx - cin] = shard[i];
-            }
+            for (int i = 0; i < C::KL; ++i)
+                lds.idx[wv][rec[i]] = shard[i];
         }
     }
     uint32_t bits;
     if (total <= (uint32_t)kSlots) {
         wave_lds_sync();
-        // gather: lane -> (segment, 16-byte half)
-        const uint32_t n2 = 2u * total;
-        auto half_src = [&](uint32_t r) {
-            return reinterpret_cast<const ulonglong2*>(a.filter + 4ull * (lds.idx[wv][r >> 1] & a.shard_mask)) +
-                   (r & 1u);
+        // gather: lane -> (record 1 + lane/2 + 32 j, 16-byte half lane & 1), four
+        // loads in flight before their LDS stores.  Records past `total` hold
+        // stale indices, masked into the filter, and are never read.
+        const uint32_t half = c.lane & 1u;
+        const uint32_t r0 = 1u + (c.lane >> 1);
+        auto src = [&](uint32_t r) {
+            const uint32_t sh = lds.idx[wv][r] & a.shard_mask;
+            return reinterpret_cast<const ulonglong2*>(a.filter + 4ull * sh) + half;
         };
-        auto half_dst = [&](uint32_t r) { return reinterpret_cast<ulonglong2*>(lds.words[wv][r >> 1]) + (r & 1u); };
-        for (uint32_t r0 = c.lane; r0 < n2; r0 += 256u) {
-            // four independent 16-byte loads in flight per lane, then four LDS stores
-            const uint32_t r1 = r0 + 64u, r2 = r0 + 128u, r3 = r0 + 192u;
-            const ulonglong2 v0 = *half_src(r0);
-            ulonglong2 v1 = {0, 0}, v2 = {0, 0}, v3 = {0, 0};
-            if (r1 < n2)
-                v1 = *half_src(r1);
-            if (r2 < n2)
-                v2 = *half_src(r2);
-            if (r3 < n2)
-                v3 = *half_src(r3);
-            *half_dst(r0) = v0;
-            if (r1 < n2)
-                *half_dst(r1) = v1;
-            if (r2 < n2)
-                *half_dst(r2) = v2;
-            if (r3 < n2)
-                *half_dst(r3) = v3;
+        auto dst = [&](uint32_t r) { return reinterpret_cast<ulonglong2*>(lds.words[wv][r]) + half; };
+#pragma unroll
+        for (uint32_t jb = 0; jb < (uint32_t)kSlots / 32u; jb += 4u) {
+            if (32u * jb >= total)
+                break;
+            const uint32_t ra = r0 + 32u * jb, rb = ra + 32u, rc = ra + 64u, rd = ra + 96u;
+            const ulonglong2 va = *src(ra);
+            const ulonglong2 vb = 32u * (jb + 1u) < total ? *src(rb) : ulonglong2{0, 0};
+            const ulonglong2 vc = 32u * (jb + 2u) < total ? *src(rc) : ulonglong2{0, 0};
+            const ulonglong2 vd = 32u * (jb + 3u) < total ? *src(rd) : ulonglong2{0, 0};
+            *dst(ra) = va;
+            if (32u * (jb + 1u) < total)
+                *dst(rb) = vb;
+            if (32u * (jb + 2u) < total)
+                *dst(rc) = vc;
+            if (32u * (jb + 3u) < total)
+                *dst(rd) = vd;
         }
         wave_lds_sync();
 
@@ -637,15 +668,11 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
         FindereMasks<C> fm;
         fm.init(D);
         bits = 0;
-        const uint32_t seg0 = base - cin - 1u;  // slot of the segment before the lane's first start
         static_for<0, C::KL>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             uint64_t T0[4], T1[4];
             fm.template step<i>(D, T0, T1);
-            // slot of the segment holding k-mer i; clamped for invalid k-mers before any start
-            uint32_t slot = seg0 + __popc(st & ((2u << i) - 1u));
-            slot = slot < (uint32_t)kSlots ? slot : (uint32_t)kSlots - 1u;
-            const ulonglong2* ws = reinterpret_cast<const ulonglong2*>(lds.words[wv][slot]);
+            const ulonglong2* ws = reinterpret_cast<const ulonglong2*>(lds.words[wv][rec[i]]);
             const ulonglong2 w01 = ws[0];
             uint64_t wq[4] = {w01.x, w01.y, 0, 0};
             if constexpr (C::NS > 2) {
@@ -654,9 +681,10 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
                 wq[3] = w23.y;
             }
             const uint64_t miss = missing_bits<C>(T0, T1, wq);
-            bits |= (uint32_t)(((vk >> i) & 1u) && miss == 0) << i;
+            bits |= (uint32_t)(miss == 0) << i;
             step_fence(D);
         });
+        bits &= vk;
     } else {
         bits = query_lane_direct<C>(a, D, vk);
     }
