@@ -104,9 +104,10 @@ __host__ __device__ inline uint64_t round64(uint64_t x) { return (x + 63) & ~63u
 
 template <class C>
 struct LaneCtx {
-    uint64_t p0;  // first k-mer of this lane
+    uint64_t wstart;  // first k-mer of this wave (wave-uniform)
+    uint64_t p0;      // first k-mer of this lane
     uint32_t lane;
-    bool live;    // wave has work
+    bool live;        // wave has work
 };
 
 template <class C>
@@ -114,20 +115,37 @@ __device__ __forceinline__ LaneCtx<C> lane_ctx(uint64_t nk_pad)
 {
     LaneCtx<C> c;
     c.lane = threadIdx.x & 63u;
-    const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const uint64_t wstart = wave * (uint64_t)C::KPW;
-    c.live = wstart < nk_pad;
-    c.p0 = wstart + (uint64_t)C::KL * c.lane;
+    const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x >> 6) + wib;
+    c.wstart = wave * (uint64_t)C::KPW;
+    c.live = c.wstart < nk_pad;
+    c.p0 = c.wstart + (uint64_t)C::KL * c.lane;
     return c;
 }
 
-template <class C>
-__device__ __forceinline__ void load_codes(const SeqArgs& a, uint64_t p0, uint32_t (&D)[C::ND])
+// Raw buffer over the 32-bit words [w0, n) of an array, w0 wave-uniform: a
+// read past the end returns 0 through the buffer range check, so lane loads
+// need no bounds branches.  Descriptor word 3: 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t word_buffer(const uint32_t* a, uint64_t n, uint64_t w0)
 {
-    const uint64_t w0 = p0 >> 4;
+    const uint64_t b = w0 < n ? w0 : n;
+    const uint64_t bytes = (n - b) * 4ull;
+    const uint32_t nrec = bytes < 0xFFFFFFFFull ? (uint32_t)bytes : 0xFFFFFFFFu;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a + b), (short)0, (int)nrec, 0x00020000);
+}
+
+// Packed code words of the lane: KL/16 own words and two more for the halo
+// (0 past the end of the sequence).  KPW is a multiple of 16, so the wave's
+// first k-mer starts a code word.
+template <class C>
+__device__ __forceinline__ void load_codes(const SeqArgs& a, const LaneCtx<C>& c, uint32_t (&D)[C::ND])
+{
+    static_assert(C::KPW % 16 == 0, "wave start must align to a code word");
+    const auto rs = word_buffer(a.codes, a.ncw, c.wstart >> 4);
+    const uint32_t o = c.lane * (uint32_t)(C::KL / 16) * 4u;
 #pragma unroll
     for (int j = 0; j < C::ND; ++j)
-        D[j] = ld_or0(a.codes, a.ncw, w0 + j);
+        D[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(o + 4u * j), 0, 0);
 }
 
 // Value of lane l+1 in lane l (lane 63 receives 0): one DPP wave_shl:1 move
@@ -160,10 +178,13 @@ __device__ __forceinline__ uint64_t from_next_lane(uint64_t v)
     return ((uint64_t)from_next_lane((uint32_t)(v >> 32)) << 32) | from_next_lane((uint32_t)v);
 }
 
-// Shards of the lane's KL k-mers: one m-mer hash per own position, halo from
-// lane+1, then van Herk sliding minimum with block size W.
+// Shard keys of the lane's KL k-mers: the low 32 bits of the minimizer hash
+// (one m-mer hash per own position, halo from lane+1, van Herk sliding
+// minimum with block size W).  The shard is key & shard_mask, applied where a
+// shard is addressed; runs compare keys, which can only split a run where two
+// minimizers share a shard -- the union and the answers are the same.
 template <class C>
-__device__ __forceinline__ void lane_shards(const uint32_t (&D)[C::ND], uint32_t shard_mask, uint32_t (&shard)[C::KL])
+__device__ __forceinline__ void lane_shards(const uint32_t (&D)[C::ND], uint32_t (&shard)[C::KL])
 {
     constexpr int W = C::W, KL = C::KL, NM = C::NM;
     uint64_t hm[NM];
@@ -176,7 +197,7 @@ __device__ __forceinline__ void lane_shards(const uint32_t (&D)[C::ND], uint32_t
     if constexpr (W == 1) {
 #pragma unroll
         for (int i = 0; i < KL; ++i)
-            shard[i] = (uint32_t)hm[i] & shard_mask;
+            shard[i] = (uint32_t)hm[i];
     } else {
         // Window [i, i+W) = tail of block i/W (suffix minimum at i) plus head of
         // block i/W+1 (prefix minimum at i+W-1); blocks are [bW, bW+W).
@@ -203,7 +224,7 @@ __device__ __forceinline__ void lane_shards(const uint32_t (&D)[C::ND], uint32_t
                     mn = suf[i];
                 else
                     mn = suf[i] < pre ? suf[i] : pre;
-                shard[i] = (uint32_t)mn & shard_mask;
+                shard[i] = (uint32_t)mn;
             }
         }
     }
@@ -221,17 +242,43 @@ __device__ __forceinline__ void lane_smer_hashes(const uint32_t (&D)[C::ND], uin
         hs[C::KL + j] = from_next_lane(hs[j]);
 }
 
-// Valid-k-mer bits of the lane (bit i: k-mer p0+i is valid and < nk).
-template <class C>
-__device__ __forceinline__ uint32_t lane_valid(const SeqArgs& a, uint64_t p0, uint32_t lane)
+// Bit i set iff bits i .. i+KK-1 of v are all set: the zero bits of v are
+// smeared down by KK-1 places (binary doubling), then complemented.  Bits
+// within KK-1 of the top are not meaningful.
+template <int KK>
+__device__ __forceinline__ uint64_t valid_starts(uint64_t v)
 {
-    if (lane >= (uint32_t)C::LW || p0 >= a.nk)
-        return 0u;
-    uint64_t v = run_and<C::k>(valid_window64(a.valid, a.nvw, p0));
-    const uint64_t rem = a.nk - p0;
-    if (rem < (uint64_t)C::KL)
-        v &= (1ull << rem) - 1ull;
-    return (uint32_t)v & (uint32_t)((C::KL == 32) ? 0xFFFFFFFFu : ((1u << C::KL) - 1u));
+    uint64_t z = ~v;
+    static_for<0, 6>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int covered = 1 << j;  // z bit i covers offsets [0, covered) before this step
+        if constexpr (covered < KK) {
+            constexpr int sh = covered < KK - covered ? covered : KK - covered;
+            z |= z >> sh;
+        }
+    });
+    return ~z;
+}
+
+// Valid-k-mer bits of the lane (bit i: k-mer p0+i is valid and < nk), from
+// the 64 validity bits starting at base p0 (three words, funnel shifts).
+template <class C>
+__device__ __forceinline__ uint32_t lane_valid(const SeqArgs& a, const LaneCtx<C>& c)
+{
+    static_assert(C::KL + C::k - 1 <= 64, "validity window");
+    const auto rv = word_buffer(a.valid, a.nvw, c.wstart >> 5);
+    const uint32_t bit = (uint32_t)(c.wstart & 31u) + (uint32_t)C::KL * c.lane;
+    const uint32_t o = (bit >> 5) * 4u, off = bit & 31u;
+    const uint32_t v0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, (int)o, 0, 0);
+    const uint32_t v1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, (int)(o + 4u), 0, 0);
+    const uint32_t v2 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, (int)(o + 8u), 0, 0);
+    const uint64_t win = ((uint64_t)__builtin_amdgcn_alignbit(v2, v1, off) << 32) | __builtin_amdgcn_alignbit(v1, v0, off);
+    const uint32_t v = (uint32_t)valid_starts<C::k>(win);
+    const uint64_t rem = a.nk > c.p0 ? a.nk - c.p0 : 0;
+    uint32_t keep = rem >= (uint64_t)C::KL ? (C::KL == 32 ? 0xFFFFFFFFu : (1u << C::KL) - 1u) : (1u << rem) - 1u;
+    if (c.lane >= (uint32_t)C::LW)
+        keep = 0;
+    return v & keep;
 }
 
 // Sector masks of one s-mer hash: hash index t sets one bit in word t mod 4.
@@ -465,12 +512,12 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
     const LaneCtx<C> c = lane_ctx<C>(a.nk);
     if (!c.live)
         return;  // whole wave
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar LDS bases
     uint32_t D[C::ND];
-    load_codes<C>(a, c.p0, D);
+    load_codes<C>(a, c, D);
     uint32_t shard[C::KL];
-    lane_shards<C>(D, a.shard_mask, shard);
-    const uint32_t vk = lane_valid<C>(a, c.p0, c.lane);
+    lane_shards<C>(D, shard);
+    const uint32_t vk = lane_valid<C>(a, c);
 
     // pass A: slots
     const uint32_t st = run_starts<C>(vk, shard);
@@ -514,7 +561,7 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
                     for (int w = 0; w < 4; ++w)
                         lds.words[wv][slot][w] = Wr[w];
                 } else {
-                    global_or_record<C>(a.filter, shard[i], Wr);
+                    global_or_record<C>(a.filter, shard[i] & a.shard_mask, Wr);
                 }
             }
         }
@@ -530,7 +577,7 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
                 __hip_atomic_fetch_or(&lds.words[wv][slot][w], first[w], __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_WAVEFRONT);
         } else {
-            global_or_record<C>(a.filter, shard[0], first);
+            global_or_record<C>(a.filter, shard[0] & a.shard_mask, first);
         }
     }
     wave_lds_sync();
@@ -607,15 +654,15 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
     const LaneCtx<C> c = lane_ctx<C>(nk_pad);
     if (!c.live)
         return;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar LDS bases
     uint32_t D[C::ND];
-    load_codes<C>(a, c.p0, D);
-    const uint32_t vk = lane_valid<C>(a, c.p0, c.lane);
+    load_codes<C>(a, c, D);
+    const uint32_t vk = lane_valid<C>(a, c);
     uint32_t st, total;
     uint32_t rec[C::KL];
     {
         uint32_t shard[C::KL];
-        lane_shards<C>(D, a.shard_mask, shard);
+        lane_shards<C>(D, shard);
         // pass A: segment records, shard indices into LDS
         st = run_starts<C>(vk, shard);
         const uint32_t cin = continues_previous<C>(vk, shard, c.lane) ? 1u : 0u;
@@ -681,10 +728,10 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
                 wq[3] = w23.y;
             }
             const uint64_t miss = missing_bits<C>(T0, T1, wq);
-            bits |= (uint32_t)(miss == 0) << i;
+            bits = shift_in(bits, __builtin_amdgcn_ballot_w64(miss == 0));  // k-mer i lands at bit KL-1-i
             step_fence(D);
         });
-        bits &= vk;
+        bits = (__builtin_bitreverse32(bits) >> (32 - C::KL)) & vk;
     } else {
         bits = query_lane_direct<C>(a, D, vk);
     }
