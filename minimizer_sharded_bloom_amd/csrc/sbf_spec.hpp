@@ -683,8 +683,8 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
     if (total <= (uint32_t)kSlots) {
         wave_lds_sync();
         // gather: lane -> (record 1 + lane/2 + 32 j, 16-byte half lane & 1), four
-        // loads in flight before their LDS stores.  Records past `total` hold
-        // stale indices, masked into the filter, and are never read.
+        // loads in flight before their LDS stores; a lane past the last record
+        // loads nothing.
         const uint32_t half = c.lane & 1u;
         const uint32_t r0 = 1u + (c.lane >> 1);
         auto src = [&](uint32_t r) {
@@ -697,16 +697,17 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
             if (32u * jb >= total)
                 break;
             const uint32_t ra = r0 + 32u * jb, rb = ra + 32u, rc = ra + 64u, rd = ra + 96u;
-            const ulonglong2 va = *src(ra);
-            const ulonglong2 vb = 32u * (jb + 1u) < total ? *src(rb) : ulonglong2{0, 0};
-            const ulonglong2 vc = 32u * (jb + 2u) < total ? *src(rc) : ulonglong2{0, 0};
-            const ulonglong2 vd = 32u * (jb + 3u) < total ? *src(rd) : ulonglong2{0, 0};
-            *dst(ra) = va;
-            if (32u * (jb + 1u) < total)
+            const ulonglong2 va = ra <= total ? *src(ra) : ulonglong2{0, 0};
+            const ulonglong2 vb = rb <= total ? *src(rb) : ulonglong2{0, 0};
+            const ulonglong2 vc = rc <= total ? *src(rc) : ulonglong2{0, 0};
+            const ulonglong2 vd = rd <= total ? *src(rd) : ulonglong2{0, 0};
+            if (ra <= total)
+                *dst(ra) = va;
+            if (rb <= total)
                 *dst(rb) = vb;
-            if (32u * (jb + 2u) < total)
+            if (rc <= total)
                 *dst(rc) = vc;
-            if (32u * (jb + 3u) < total)
+            if (rd <= total)
                 *dst(rd) = vd;
         }
         wave_lds_sync();
