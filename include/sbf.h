@@ -59,6 +59,7 @@ extern "C" {
 #define SBF_EUNSUPPORTED (-2) /* reserved: parameter combination not available */
 #define SBF_ENOMEM (-3)       /* device or host allocation failed */
 #define SBF_EDEVICE (-4)      /* a HIP runtime call or kernel launch failed */
+#define SBF_EIO (-5)          /* a file could not be opened or read, or is not valid FASTA/FASTQ */
 
 /* filter kinds */
 #define SBF_KIND_SBF 0 /* Super Bloom filter */
@@ -145,11 +146,16 @@ int sbf_query_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid,
 
 /*
  * Sequence-native insert ([cuSBF] §IV-A input forms, §IV-F records joined by
- * an invalid separator).  flags = SBF_HOST: `seq` is host memory; it is staged
- * to the device, packed and inserted, and the call synchronizes.
- * SBF_DEVICE: `seq` is device memory; packing goes to the handle's staging
- * buffer and the call is asynchronous on `stream`.  The staging buffer grows
- * on demand; growing synchronizes `stream` first.
+ * an invalid separator).  flags = SBF_HOST: `seq` is host memory; it goes
+ * through the handle's host pipeline ([cuSBF] §IV-G host staging): chunks of
+ * up to sbf_set_staging() k-mer starts (consecutive chunks overlap by k-1
+ * bases) are copied into pinned buffers, sent to the device and packed and
+ * inserted on two alternating streams, so the copy of one chunk overlaps the
+ * kernels of the other; the work is ordered after earlier work on `stream`
+ * and the call synchronizes.  SBF_DEVICE: `seq` is device memory; packing
+ * goes to the handle's staging buffer and the call is asynchronous on
+ * `stream`.  Staging buffers grow on demand (growing synchronizes `stream`)
+ * and stay allocated until sbf_destroy.
  */
 int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void* stream);
 
@@ -160,6 +166,74 @@ int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void
  */
 int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits,
                   uint32_t flags, void* stream);
+
+/*
+ * Chunk size of the host pipeline, in k-mer starts (rounded up to a multiple
+ * of 64; 64 <= chunk_bases <= 2^34; default 2^27).  Each of the two slots
+ * holds chunk_bases + 64 bytes of pinned input, the same on the device, its
+ * packed form and chunk_bases/64 + 1 answer words (pinned and device).
+ * Buffers of another size are freed; the next host call allocates anew.
+ */
+int sbf_set_staging(sbf_t* h, uint64_t chunk_bases);
+
+/* ---- FASTA / FASTQ input ([cuSBF] §IV-A input forms, §IV-F, §IV-G) -------
+ * A FASTA or FASTQ file, plain or gzip-compressed (detected from the data),
+ * becomes the "normalized stream": the sequence of each record with line
+ * breaks and other bytes <= 0x20 removed, records joined by one 'N', so every
+ * k-mer that spans two records is invalid ([cuSBF] §IV-F).  FASTA: '>' starts
+ * a record, ';' lines are comments.  FASTQ: '@' header, sequence lines up to a
+ * '+' line, then quality lines until they hold as many bytes as the sequence.
+ * Record r spans [start_r, end_r) of the stream, start_0 = 0 and
+ * start_r = end_{r-1} + 1.
+ */
+typedef struct sbf_fastx sbf_fastx_t;
+
+/* Open a reader (host only, no device use).  SBF_EIO if the file cannot be
+ * opened. */
+int sbf_fastx_open(sbf_fastx_t** out, const char* path);
+
+/*
+ * Next piece of the normalized stream: up to cap bytes into buf, *len bytes
+ * written.  If ends is not NULL, the stream offsets end_r of the records that
+ * end within this piece go to ends[0 .. *n_ends) (the call stops early rather
+ * than drop one when ends_cap are reported).  *len == 0 and *n_ends == 0
+ * together mean the end of the stream.  SBF_EIO on a read error or malformed
+ * input (text in sbf_last_error); the reader is then unusable.
+ */
+int sbf_fastx_read(sbf_fastx_t* r, char* buf, uint64_t cap, uint64_t* len,
+                   uint64_t* ends, uint64_t ends_cap, uint64_t* n_ends);
+
+/* Records started so far (0 for NULL). */
+uint64_t sbf_fastx_records(const sbf_fastx_t* r);
+
+/* Close a reader; NULL is a no-op. */
+int sbf_fastx_close(sbf_fastx_t* r);
+
+typedef struct sbf_fastx_stats {
+    uint64_t records;     /* records in the file */
+    uint64_t bases;       /* length of the normalized stream, separators included */
+    uint64_t chunks;      /* pipeline chunks processed */
+    double parse_seconds; /* host time spent reading, decompressing and normalizing */
+    double total_seconds; /* wall time of the call */
+} sbf_fastx_stats_t;
+
+/*
+ * Insert every valid k-mer of a FASTA/FASTQ file through the host pipeline:
+ * the reader writes the normalized stream straight into the pinned chunk
+ * buffers while the device works on the previous chunk.  Synchronizes.
+ * stats may be NULL.  SBF_EIO for file errors; no partial insert is undone.
+ */
+int sbf_insert_fastx(sbf_t* h, const char* path, sbf_fastx_stats_t* stats);
+
+/*
+ * Query a FASTA/FASTQ file: for record r < cap, hits[r] = number of its
+ * k-mers reported present and kmers[r] = number of its k-mer starts
+ * (max(0, length - k + 1)); either array may be NULL.  Records beyond cap are
+ * processed but not reported; stats->records gives their number.
+ * Synchronizes.
+ */
+int sbf_query_fastx(sbf_t* h, const char* path, uint64_t* hits, uint64_t* kmers, uint64_t cap,
+                    sbf_fastx_stats_t* stats);
 
 /*
  * False-positive probe ([cuSBF] §V-D): query n k-mers drawn on the device

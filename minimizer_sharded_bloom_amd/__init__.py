@@ -9,13 +9,14 @@ to the C ABI of include/sbf.h; PyTorch provides device memory and streams.
 from __future__ import annotations
 
 import ctypes
+import os
 
 import numpy as np
 
 from . import _lib
 from ._lib import SBF_DEVICE, SBF_HOST, SbfError, check
 
-__all__ = ["SuperBloomFilter", "pack", "packed_words", "SbfError", "lib"]
+__all__ = ["SuperBloomFilter", "pack", "packed_words", "SbfError", "lib", "fastx_stream", "count_fastx_records"]
 
 
 def lib():
@@ -188,6 +189,33 @@ class SuperBloomFilter:
                                          _stream_ptr(stream)), "sbf_query_packed")
         return out[:nw]
 
+    # ---- host pipeline and FASTA/FASTQ files -----------------------------------
+    def set_staging(self, chunk_bases: int):
+        """Chunk size (k-mer starts) of the host pipeline behind host-resident
+        insert/query and the FASTX calls."""
+        check(lib().sbf_set_staging(self._h, chunk_bases), "sbf_set_staging")
+
+    def insert_fastx(self, path) -> dict:
+        """Insert every valid k-mer of a FASTA/FASTQ file (plain or gzip);
+        returns the reader/pipeline statistics."""
+        st = _lib.SbfFastxStats()
+        check(lib().sbf_insert_fastx(self._h, os.fsencode(path), ctypes.byref(st)), "sbf_insert_fastx")
+        return _stats(st)
+
+    def query_fastx(self, path, max_records: int | None = None):
+        """Per-record (hits, kmers) uint64 arrays for a FASTA/FASTQ file, and
+        the statistics.  Without max_records the file's records are counted
+        first with the reader."""
+        if max_records is None:
+            max_records = count_fastx_records(path)
+        hits = np.zeros(max(1, max_records), dtype=np.uint64)
+        kmers = np.zeros_like(hits)
+        st = _lib.SbfFastxStats()
+        check(lib().sbf_query_fastx(self._h, os.fsencode(path), hits.ctypes.data, kmers.ctypes.data, max_records,
+                                    ctypes.byref(st)), "sbf_query_fastx")
+        n = min(max_records, st.records)
+        return hits[:n], kmers[:n], _stats(st)
+
     # ---- false-positive probe ---------------------------------------------------
     def fpr_probe(self, n: int, seed: int) -> int:
         hits = ctypes.c_uint64()
@@ -198,3 +226,34 @@ class SuperBloomFilter:
         check(lib().sbf_fpr_probe_device(self._h, n, seed & (2**64 - 1), out.data_ptr(), _stream_ptr(stream)),
               "sbf_fpr_probe_device")
         return out
+
+
+def _stats(st) -> dict:
+    return {"records": st.records, "bases": st.bases, "chunks": st.chunks,
+            "parse_seconds": st.parse_seconds, "total_seconds": st.total_seconds}
+
+
+def fastx_stream(path, piece: int = 1 << 24):
+    """Iterate over (bytes of the normalized stream, record end offsets) pieces
+    of a FASTA/FASTQ file as the library's reader produces them (host only):
+    records joined by one 'N', line breaks and whitespace removed."""
+    L = lib()
+    r = ctypes.c_void_p()
+    check(L.sbf_fastx_open(ctypes.byref(r), os.fsencode(path)), "sbf_fastx_open")
+    try:
+        buf = np.empty(piece, dtype=np.uint8)
+        ends = np.empty(1 << 16, dtype=np.uint64)
+        n, ne = ctypes.c_uint64(), ctypes.c_uint64()
+        while True:
+            check(L.sbf_fastx_read(r, buf.ctypes.data, buf.size, ctypes.byref(n), ends.ctypes.data, ends.size,
+                                   ctypes.byref(ne)), "sbf_fastx_read")
+            if n.value == 0 and ne.value == 0:
+                return
+            yield buf[:n.value].tobytes(), ends[:ne.value].copy()
+    finally:
+        L.sbf_fastx_close(r)
+
+
+def count_fastx_records(path) -> int:
+    """Number of records of a FASTA/FASTQ file (one pass of the reader)."""
+    return int(sum(e.size for _, e in fastx_stream(path)))

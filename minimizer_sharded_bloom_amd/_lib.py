@@ -15,6 +15,7 @@ SBF_EINVAL = -1
 SBF_EUNSUPPORTED = -2
 SBF_ENOMEM = -3
 SBF_EDEVICE = -4
+SBF_EIO = -5
 SBF_KIND_SBF = 0
 SBF_KIND_BBF = 1
 SBF_HOST = 1
@@ -25,6 +26,11 @@ class SbfInfo(ctypes.Structure):
     _fields_ = [("k", ctypes.c_uint32), ("m", ctypes.c_uint32), ("s", ctypes.c_uint32),
                 ("H", ctypes.c_uint32), ("kind", ctypes.c_uint32), ("specialized", ctypes.c_uint32),
                 ("num_shards", ctypes.c_uint64), ("filter_bytes", ctypes.c_uint64)]
+
+
+class SbfFastxStats(ctypes.Structure):
+    _fields_ = [("records", ctypes.c_uint64), ("bases", ctypes.c_uint64), ("chunks", ctypes.c_uint64),
+                ("parse_seconds", ctypes.c_double), ("total_seconds", ctypes.c_double)]
 
 
 _u32, _u64, _p, _int = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int
@@ -45,6 +51,13 @@ SIGNATURES = {
     "sbf_query_seq": (_int, [_p, _p, _u64, _p, _u32, _p]),
     "sbf_fpr_probe": (_int, [_p, _u64, _u64, ctypes.POINTER(_u64)]),
     "sbf_fpr_probe_device": (_int, [_p, _u64, _u64, _p, _p]),
+    "sbf_set_staging": (_int, [_p, _u64]),
+    "sbf_fastx_open": (_int, [ctypes.POINTER(_p), ctypes.c_char_p]),
+    "sbf_fastx_read": (_int, [_p, _p, _u64, ctypes.POINTER(_u64), _p, _u64, ctypes.POINTER(_u64)]),
+    "sbf_fastx_records": (_u64, [_p]),
+    "sbf_fastx_close": (_int, [_p]),
+    "sbf_insert_fastx": (_int, [_p, ctypes.c_char_p, ctypes.POINTER(SbfFastxStats)]),
+    "sbf_query_fastx": (_int, [_p, ctypes.c_char_p, _p, _p, _u64, ctypes.POINTER(SbfFastxStats)]),
     "sbf_strerror": (ctypes.c_char_p, [_int]),
     "sbf_last_error": (ctypes.c_char_p, []),
 }

@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libsbf.so")
 OBJDIR = os.path.join(PKG, "_build")
 ARCH = os.environ.get("SBF_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["sbf_api.cpp", "sbf_generic.hip", "inst_m16.hip", "inst_m12.hip", "inst_m20.hip", "inst_extra.hip"]
+SOURCES = ["sbf_api.cpp", "sbf_host.cpp", "sbf_fastx.cpp", "sbf_generic.hip", "inst_m16.hip", "inst_m12.hip",
+           "inst_m20.hip", "inst_extra.hip"]
 HEADERS = ["sbf_device.hpp", "sbf_internal.hpp", "sbf_spec.hpp", "sbf_spec_list.hpp"]
 
 
@@ -53,7 +54,7 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-lz", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))

@@ -9,7 +9,7 @@
 #include <string>
 
 #include "../../include/sbf.h"
-#include "sbf_internal.hpp"
+#include "sbf_handle.hpp"
 
 namespace sbf {
 const SpecEntry* spec_table_m12(size_t* n);
@@ -35,26 +35,11 @@ bool find_specialized(const Params& p, KernelSet* out)
 }
 }  // namespace sbf
 
-struct sbf_handle {
-    sbf::Params P;
-    uint64_t num_shards;
-    uint64_t* d_filter;
-    sbf::KernelSet ks;
-    int device;
-    // staging: ASCII bytes, packed codes, validity, probe counter
-    char* d_ascii;
-    uint64_t ascii_cap;
-    uint32_t* d_codes;
-    uint32_t* d_valid;
-    uint64_t packed_cap;  // bases
-    uint64_t* d_out;      // query bits for host-facing queries
-    uint64_t out_cap;     // words
-    unsigned long long* d_hits;
-};
-
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
+
+namespace sbf {
 
 int fail(int code, const char* what)
 {
@@ -70,15 +55,35 @@ int fail_hip(hipError_t e, const char* what)
 
 void ok() { g_last_error.clear(); }
 
-uint64_t code_words(uint64_t len) { return (len + 15) / 16; }
-uint64_t valid_words(uint64_t len) { return (len + 31) / 32; }
-uint64_t out_words(uint64_t len, uint32_t k) { return len < k ? 0 : (len - k + 1 + 63) / 64; }
-
 int set_device(const sbf_t* h)
 {
     hipError_t e = hipSetDevice(h->device);
     return e == hipSuccess ? SBF_OK : fail_hip(e, "hipSetDevice");
 }
+
+uint64_t code_words(uint64_t len) { return (len + 15) / 16; }
+uint64_t valid_words(uint64_t len) { return (len + 31) / 32; }
+
+SeqArgs seq_args(sbf_t* h, const uint32_t* codes, const uint32_t* valid, uint64_t len, uint64_t* out,
+                 hipStream_t st)
+{
+    SeqArgs a;
+    a.codes = codes;
+    a.valid = valid;
+    a.ncw = code_words(len);
+    a.nvw = valid_words(len);
+    a.nk = len - h->P.k + 1;
+    a.filter = h->d_filter;
+    a.shard_mask = (uint32_t)(h->num_shards - 1);
+    a.out = out;
+    a.stream = st;
+    return a;
+}
+
+}  // namespace sbf
+
+namespace {
+using namespace sbf;
 
 int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
 {
@@ -136,29 +141,6 @@ int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
     return SBF_OK;
 }
 
-// Grow a device buffer; synchronizes `st` first so no queued work still uses it.
-template <class T>
-int grow(T** buf, uint64_t* cap, uint64_t need, uint64_t elem, hipStream_t st, const char* what)
-{
-    if (*cap >= need)
-        return SBF_OK;
-    hipError_t e = hipStreamSynchronize(st);
-    if (e != hipSuccess)
-        return fail_hip(e, what);
-    if (*buf)
-        (void)hipFree(*buf);
-    *buf = nullptr;
-    *cap = 0;
-    const uint64_t n = need + need / 4 + 1024;
-    e = hipMalloc(reinterpret_cast<void**>(buf), n * elem);
-    if (e != hipSuccess) {
-        *buf = nullptr;
-        return fail_hip(e, what);
-    }
-    *cap = n;
-    return SBF_OK;
-}
-
 int grow_packed(sbf_t* h, uint64_t len, hipStream_t st)
 {
     if (h->packed_cap >= len)
@@ -188,38 +170,12 @@ int grow_packed(sbf_t* h, uint64_t len, hipStream_t st)
     return SBF_OK;
 }
 
-sbf::SeqArgs seq_args(sbf_t* h, const uint32_t* codes, const uint32_t* valid, uint64_t len, uint64_t* out,
-                      hipStream_t st)
-{
-    sbf::SeqArgs a;
-    a.codes = codes;
-    a.valid = valid;
-    a.ncw = code_words(len);
-    a.nvw = valid_words(len);
-    a.nk = len - h->P.k + 1;
-    a.filter = h->d_filter;
-    a.shard_mask = (uint32_t)(h->num_shards - 1);
-    a.out = out;
-    a.stream = st;
-    return a;
-}
-
-// Stage a sequence (host or device) as packed codes in the handle's buffers.
-int stage_packed(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, hipStream_t st)
+// Pack a device-resident sequence into the handle's staging buffers.
+int stage_packed(sbf_t* h, const char* d_seq, uint64_t len, hipStream_t st)
 {
     int rc = grow_packed(h, len, st);
     if (rc)
         return rc;
-    const char* d_seq = seq;
-    if (flags == SBF_HOST) {
-        rc = grow(&h->d_ascii, &h->ascii_cap, len, 1, st, "hipMalloc(ascii staging)");
-        if (rc)
-            return rc;
-        hipError_t e = hipMemcpyAsync(h->d_ascii, seq, len, hipMemcpyHostToDevice, st);
-        if (e != hipSuccess)
-            return fail_hip(e, "hipMemcpyAsync(sequence)");
-        d_seq = h->d_ascii;
-    }
     hipError_t e = sbf::launch_pack(d_seq, len, h->d_codes, h->d_valid, st);
     return e == hipSuccess ? SBF_OK : fail_hip(e, "pack launch");
 }
@@ -253,14 +209,11 @@ int sbf_destroy(sbf_t* h)
     hipError_t e = hipDeviceSynchronize();
     (void)hipFree(h->d_filter);
     (void)hipFree(h->d_hits);
-    if (h->d_ascii)
-        (void)hipFree(h->d_ascii);
     if (h->d_codes)
         (void)hipFree(h->d_codes);
     if (h->d_valid)
         (void)hipFree(h->d_valid);
-    if (h->d_out)
-        (void)hipFree(h->d_out);
+    sbf::free_host_staging(h->host);
     delete h;
     if (e != hipSuccess)
         return fail_hip(e, "sbf_destroy");
@@ -408,13 +361,13 @@ int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void
     if (rc)
         return rc;
     hipStream_t st = (hipStream_t)stream;
-    rc = stage_packed(h, seq, len, flags, st);
+    if (flags == SBF_HOST)
+        return sbf::host_insert(h, seq, len, st);
+    rc = stage_packed(h, seq, len, st);
     if (rc)
         return rc;
     const sbf::SeqArgs a = seq_args(h, h->d_codes, h->d_valid, len, nullptr, st);
     hipError_t e = h->ks.insert(a, h->P);
-    if (e == hipSuccess && flags == SBF_HOST)
-        e = hipStreamSynchronize(st);
     if (e != hipSuccess)
         return fail_hip(e, "insert");
     ok();
@@ -437,24 +390,13 @@ int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits, u
     if (rc)
         return rc;
     hipStream_t st = (hipStream_t)stream;
-    rc = stage_packed(h, seq, len, flags, st);
+    if (flags == SBF_HOST)
+        return sbf::host_query(h, seq, len, out_bits, st);
+    rc = stage_packed(h, seq, len, st);
     if (rc)
         return rc;
-    const uint64_t nw = out_words(len, h->P.k);
-    uint64_t* d_out = out_bits;
-    if (flags == SBF_HOST) {
-        rc = grow(&h->d_out, &h->out_cap, nw, 8, st, "hipMalloc(query staging)");
-        if (rc)
-            return rc;
-        d_out = h->d_out;
-    }
-    const sbf::SeqArgs a = seq_args(h, h->d_codes, h->d_valid, len, d_out, st);
+    const sbf::SeqArgs a = seq_args(h, h->d_codes, h->d_valid, len, out_bits, st);
     hipError_t e = h->ks.query(a, h->P);
-    if (e == hipSuccess && flags == SBF_HOST) {
-        e = hipMemcpyAsync(out_bits, d_out, 8 * nw, hipMemcpyDeviceToHost, st);
-        if (e == hipSuccess)
-            e = hipStreamSynchronize(st);
-    }
     if (e != hipSuccess)
         return fail_hip(e, "query");
     ok();

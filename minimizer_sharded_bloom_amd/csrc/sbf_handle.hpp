@@ -1,0 +1,60 @@
+// sbf_handle.hpp -- the filter handle behind sbf_t, shared by the C-ABI
+// translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sbf.h"
+#include "sbf_internal.hpp"
+
+namespace sbf {
+
+// Double-buffered staging of host-resident sequences ([cuSBF] §IV-G host
+// staging): slot b holds a pinned input chunk, its device copy, packed codes
+// and validity, and the chunk's answer words (device and pinned), and runs
+// on its own stream, so the copy of one chunk overlaps the kernels of the
+// other.  Created on first use and kept until the handle is destroyed.
+struct HostStaging {
+    uint64_t chunk = 1ull << 27;  // k-mer starts per chunk, a multiple of 64
+    uint64_t built_for = 0;       // chunk size the buffers below were sized for
+    hipStream_t s[2] = {nullptr, nullptr};
+    hipEvent_t done[2] = {nullptr, nullptr};  // slot's copy, kernels and answer copy finished
+    char* h_in[2] = {nullptr, nullptr};       // pinned
+    uint64_t* h_out[2] = {nullptr, nullptr};  // pinned
+    char* d_in[2] = {nullptr, nullptr};
+    uint32_t* d_codes[2] = {nullptr, nullptr};
+    uint32_t* d_valid[2] = {nullptr, nullptr};
+    uint64_t* d_out[2] = {nullptr, nullptr};
+};
+
+}  // namespace sbf
+
+struct sbf_handle {
+    sbf::Params P;
+    uint64_t num_shards;
+    uint64_t* d_filter;
+    sbf::KernelSet ks;
+    int device;
+    // packing of device-resident sequences (SBF_DEVICE calls)
+    uint32_t* d_codes;
+    uint32_t* d_valid;
+    uint64_t packed_cap;  // bases
+    unsigned long long* d_hits;
+    sbf::HostStaging host;
+};
+
+namespace sbf {
+// Error reporting shared by the C-ABI translation units (sbf_api.cpp).
+int fail(int code, const char* what);
+int fail_hip(hipError_t e, const char* what);
+void ok();
+int set_device(const sbf_t* h);
+SeqArgs seq_args(sbf_t* h, const uint32_t* codes, const uint32_t* valid, uint64_t len, uint64_t* out,
+                 hipStream_t st);
+void free_host_staging(HostStaging& hs);
+// Host-resident insert / query through the chunked pipeline (sbf_host.cpp);
+// both synchronize before returning.
+int host_insert(sbf_t* h, const char* seq, uint64_t len, hipStream_t st);
+int host_query(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits, hipStream_t st);
+}  // namespace sbf

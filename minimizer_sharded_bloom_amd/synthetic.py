@@ -220,3 +220,38 @@ def workload(cfg: int) -> dict:
         g = genome_with_n_runs(CONFIG_GENOME[5])
         return {"cfg": 5, "bits": CONFIG_BITS[5], "insert": g, "queries": [long_read_set(g)]}
     raise ValueError("workload %r is not generated by this module" % cfg)
+
+
+def split_records(stream: np.ndarray) -> list:
+    """Records of an 'N'-joined stream as uint8 arrays (every 'N' is a record
+    separator, so only streams whose records hold no 'N' round-trip)."""
+    cuts = np.flatnonzero(stream == N_BYTE)
+    return np.split(stream, cuts + 1) if cuts.size else [stream]
+
+
+def write_fasta(path: str, records, width: int = 60, gz: bool = False, crlf: bool = False,
+                names: str = "read") -> None:
+    """FASTA file of the given records (uint8 arrays or bytes, trailing 'N'
+    separators stripped) with `width`-base lines; gzip if gz."""
+    import gzip
+    eol = b"\r\n" if crlf else b"\n"
+    opener = gzip.open if gz else open
+    with opener(path, "wb") as f:
+        for i, r in enumerate(records):
+            s = bytes(r).rstrip(b"N")
+            f.write(b">%s_%d length=%d" % (names.encode(), i, len(s)) + eol)
+            for a in range(0, len(s), width):
+                f.write(s[a:a + width] + eol)
+
+
+def write_fastq(path: str, records, gz: bool = False, seed_qual: int = 12) -> None:
+    """FASTQ file (4-line records) of the given records with random quality
+    strings (Phred+33 '!'..'J', seeded)."""
+    import gzip
+    rng = np.random.default_rng(seed_qual)
+    opener = gzip.open if gz else open
+    with opener(path, "wb") as f:
+        for i, r in enumerate(records):
+            s = bytes(r).rstrip(b"N")
+            q = (rng.integers(33, 75, len(s), dtype=np.uint8)).tobytes()
+            f.write(b"@read_%d\n%s\n+\n%s\n" % (i, s, q))

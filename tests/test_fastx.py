@@ -1,0 +1,160 @@
+"""The library's FASTA/FASTQ reader (host code, no GPU) against the reference
+normalization in tests/fastx_ref.py: records joined by one 'N', line breaks
+and whitespace removed ([cuSBF] §IV-A input forms, §IV-F separators), for
+plain and gzip files, multi-line records, CRLF, comments, empty records and
+FASTQ quality lines that start with '@'."""
+import ctypes
+import gzip
+import os
+
+import numpy as np
+import pytest
+
+import minimizer_sharded_bloom_amd as M
+from minimizer_sharded_bloom_amd import _lib
+from minimizer_sharded_bloom_amd import synthetic as S
+from tests import fastx_ref as R
+
+
+def read_all(path, piece=1 << 20, ends_cap=1 << 16):
+    """Whole normalized stream and record ends through sbf_fastx_read with the
+    given piece size and end-offset capacity."""
+    L = M.lib()
+    r = ctypes.c_void_p()
+    assert L.sbf_fastx_open(ctypes.byref(r), os.fsencode(path)) == 0
+    out, ends = bytearray(), []
+    buf = np.empty(piece, dtype=np.uint8)
+    eb = np.empty(ends_cap, dtype=np.uint64)
+    n, ne = ctypes.c_uint64(), ctypes.c_uint64()
+    try:
+        while True:
+            rc = L.sbf_fastx_read(r, buf.ctypes.data, piece, ctypes.byref(n), eb.ctypes.data, ends_cap,
+                                  ctypes.byref(ne))
+            if rc:
+                raise M.SbfError(rc, "sbf_fastx_read")
+            if n.value == 0 and ne.value == 0:
+                break
+            out += buf[:n.value].tobytes()
+            ends += [int(x) for x in eb[:ne.value]]
+        nrec = L.sbf_fastx_records(r)
+    finally:
+        L.sbf_fastx_close(r)
+    return bytes(out), ends, nrec
+
+
+def random_records(rng, n, max_len=400, alphabet=b"ACGTacgtN"):
+    a = np.frombuffer(alphabet, dtype=np.uint8)
+    lens = rng.integers(0, max_len, n)
+    lens[rng.random(n) < 0.1] = 0  # some empty records
+    return [a[rng.integers(0, a.size, l)].tobytes() for l in lens]
+
+
+def fasta_text(rng, recs, crlf=False, comments=False):
+    eol = b"\r\n" if crlf else b"\n"
+    parts = []
+    for i, s in enumerate(recs):
+        parts.append(b">rec %d some description" % i + eol)
+        if comments and rng.random() < 0.3:
+            parts.append(b"; a comment line" + eol)
+        w = int(rng.integers(1, 100))
+        for a in range(0, len(s), w):
+            parts.append(s[a:a + w] + eol)
+        if rng.random() < 0.2:
+            parts.append(eol)  # blank line
+    return b"".join(parts)
+
+
+def fastq_text(rng, recs, multiline=False):
+    parts = []
+    for i, s in enumerate(recs):
+        q = bytes(rng.integers(33, 75, len(s), dtype=np.uint8))
+        q = b"@" + q[1:] if len(q) > 1 and rng.random() < 0.3 else q  # quality starting with '@'
+        parts.append(b"@read%d\n" % i)
+        if multiline and len(s) > 10:
+            w = int(rng.integers(5, 40))
+            parts += [s[a:a + w] + b"\n" for a in range(0, len(s), w)]
+            parts.append(b"+\n")
+            parts += [q[a:a + w] + b"\n" for a in range(0, len(q), w)]
+        else:
+            parts.append(s + b"\n+read%d\n" % i + q + b"\n")
+    return b"".join(parts)
+
+
+def write(tmp_path, name, data, gz=False):
+    p = tmp_path / name
+    if gz:
+        with gzip.open(p, "wb") as f:
+            f.write(data)
+    else:
+        p.write_bytes(data)
+    return str(p)
+
+
+@pytest.mark.parametrize("gz", [False, True])
+@pytest.mark.parametrize("kind", ["fasta", "fasta_crlf", "fastq", "fastq_multiline"])
+def test_reader_matches_reference(tmp_path, kind, gz):
+    rng = np.random.default_rng(["fasta", "fasta_crlf", "fastq", "fastq_multiline"].index(kind) * 2 + int(gz))
+    recs = random_records(rng, 300)
+    if kind.startswith("fasta"):
+        text = fasta_text(rng, recs, crlf=kind.endswith("crlf"), comments=True)
+    else:
+        text = fastq_text(rng, recs, multiline=kind.endswith("multiline"))
+    path = write(tmp_path, "in", text, gz)
+    want, want_ends = R.normalize(text)
+    assert want == b"N".join(recs)  # the reference agrees with how the file was built
+    for piece, ecap in [(1 << 20, 1 << 16), (7, 1), (64, 3), (1000, 1)]:
+        got, ends, nrec = read_all(path, piece, ecap)
+        assert got == want, (piece, ecap)
+        assert ends == want_ends, (piece, ecap)
+        assert nrec == len(recs)
+
+
+def test_reader_multimember_gzip(tmp_path):
+    rng = np.random.default_rng(5)
+    a = fasta_text(rng, random_records(rng, 50))
+    b = fasta_text(rng, random_records(rng, 50))
+    p = tmp_path / "mm.fa.gz"
+    p.write_bytes(gzip.compress(a) + gzip.compress(b))
+    got, ends, _ = read_all(str(p))
+    want, want_ends = R.normalize(a + b)
+    assert got == want and ends == want_ends
+
+
+def test_reader_synthetic_writers(tmp_path):
+    """write_fasta / write_fastq of generated reads read back as the reads
+    joined by 'N'."""
+    g = S.genome_with_repeats(20_000)
+    reads = S.short_read_set(g, 200)
+    recs = S.split_records(reads)
+    assert len(recs) == 200
+    for name, fn in [("r.fa", lambda p: S.write_fasta(p, recs, width=70)),
+                     ("r.fa.gz", lambda p: S.write_fasta(p, recs, gz=True, crlf=True)),
+                     ("r.fq", lambda p: S.write_fastq(p, recs))]:
+        p = str(tmp_path / name)
+        fn(p)
+        got, ends, nrec = read_all(p)
+        assert got == reads.tobytes() and nrec == 200
+        assert ends == [int(x) for x in np.flatnonzero(np.append(reads, ord("N")) == ord("N"))]
+
+
+def test_reader_empty_and_errors(tmp_path):
+    L = M.lib()
+    got, ends, nrec = read_all(write(tmp_path, "empty", b""))
+    assert got == b"" and ends == [] and nrec == 0
+    got, ends, _ = read_all(write(tmp_path, "hdr", b">only\n>two\n"))
+    assert got == b"N" and ends == [0, 1]
+    r = ctypes.c_void_p()
+    assert L.sbf_fastx_open(ctypes.byref(r), b"/nonexistent/file.fa") == _lib.SBF_EIO
+    for name, data in [("raw", b"ACGTACGT\n"), ("badfq", b"@r\nACGT\n+\nII\n"), ("badhdr", b"@r\nAC\n+\nII\nXX\n")]:
+        with pytest.raises(M.SbfError) as e:
+            read_all(write(tmp_path, name, data))
+        assert e.value.code == _lib.SBF_EIO
+
+
+def test_fastx_stream_helper(tmp_path):
+    rng = np.random.default_rng(9)
+    recs = random_records(rng, 100, alphabet=b"ACGT")
+    path = write(tmp_path, "x.fa", fasta_text(rng, recs))
+    pieces = list(M.fastx_stream(path, piece=1000))
+    assert b"".join(p for p, _ in pieces) == b"N".join(recs)
+    assert M.count_fastx_records(path) == 100
