@@ -82,12 +82,17 @@ CSRC = os.path.join(ROOT, "minimizer_sharded_bloom_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+KERNEL_HEADERS = ("sbf_device.hpp", "sbf_internal.hpp", "sbf_spec.hpp", "sbf_spec_list.hpp")
+
+
 def kernel_sources_sha256() -> str:
-    """Hash of the HIP sources (names and bytes) the kernels are built from."""
+    """Hash of the sources (names and bytes) the device kernels are built
+    from: the .hip files and the headers they include (not the host-only
+    C-ABI, pipeline and reader sources)."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+        if name.endswith(".hip") or name in KERNEL_HEADERS:
             h.update(name.encode() + b"\0")
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(f.read())

@@ -150,8 +150,9 @@ int sbf_query_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid,
  * through the handle's host pipeline ([cuSBF] §IV-G host staging): chunks of
  * up to sbf_set_staging() k-mer starts (consecutive chunks overlap by k-1
  * bases) are copied into pinned buffers, sent to the device and packed and
- * inserted on two alternating streams, so the copy of one chunk overlaps the
- * kernels of the other; the work is ordered after earlier work on `stream`
+ * inserted on three rotating streams, so the host fills one chunk while the
+ * copies and kernels of the others run; the work is ordered after earlier
+ * work on `stream`
  * and the call synchronizes.  SBF_DEVICE: `seq` is device memory; packing
  * goes to the handle's staging buffer and the call is asynchronous on
  * `stream`.  Staging buffers grow on demand (growing synchronizes `stream`)
@@ -169,7 +170,7 @@ int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits,
 
 /*
  * Chunk size of the host pipeline, in k-mer starts (rounded up to a multiple
- * of 64; 64 <= chunk_bases <= 2^34; default 2^27).  Each of the two slots
+ * of 64; 64 <= chunk_bases <= 2^34; default 2^26).  Each of the three slots
  * holds chunk_bases + 64 bytes of pinned input, the same on the device, its
  * packed form and chunk_bases/64 + 1 answer words (pinned and device).
  * Buffers of another size are freed; the next host call allocates anew.

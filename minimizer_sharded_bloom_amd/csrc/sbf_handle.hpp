@@ -10,22 +10,25 @@
 
 namespace sbf {
 
-// Double-buffered staging of host-resident sequences ([cuSBF] §IV-G host
-// staging): slot b holds a pinned input chunk, its device copy, packed codes
-// and validity, and the chunk's answer words (device and pinned), and runs
-// on its own stream, so the copy of one chunk overlaps the kernels of the
-// other.  Created on first use and kept until the handle is destroyed.
+// Staging of host-resident sequences ([cuSBF] §IV-G host staging): a ring
+// of kHostSlots slots; slot b holds a pinned input chunk, its device copy,
+// packed codes and validity, and the chunk's answer words (device and
+// pinned), and runs on its own stream, so the host fills one slot while the
+// copies and kernels of the others run.  Created on first use and kept until
+// the handle is destroyed.
+constexpr int kHostSlots = 3;
+
 struct HostStaging {
-    uint64_t chunk = 1ull << 27;  // k-mer starts per chunk, a multiple of 64
+    uint64_t chunk = 1ull << 26;  // k-mer starts per chunk, a multiple of 64
     uint64_t built_for = 0;       // chunk size the buffers below were sized for
-    hipStream_t s[2] = {nullptr, nullptr};
-    hipEvent_t done[2] = {nullptr, nullptr};  // slot's copy, kernels and answer copy finished
-    char* h_in[2] = {nullptr, nullptr};       // pinned
-    uint64_t* h_out[2] = {nullptr, nullptr};  // pinned
-    char* d_in[2] = {nullptr, nullptr};
-    uint32_t* d_codes[2] = {nullptr, nullptr};
-    uint32_t* d_valid[2] = {nullptr, nullptr};
-    uint64_t* d_out[2] = {nullptr, nullptr};
+    hipStream_t s[kHostSlots] = {};
+    hipEvent_t done[kHostSlots] = {};  // slot's copy, kernels and answer copy finished
+    char* h_in[kHostSlots] = {};       // pinned
+    uint64_t* h_out[kHostSlots] = {};  // pinned
+    char* d_in[kHostSlots] = {};
+    uint32_t* d_codes[kHostSlots] = {};
+    uint32_t* d_valid[kHostSlots] = {};
+    uint64_t* d_out[kHostSlots] = {};
 };
 
 }  // namespace sbf

@@ -6,14 +6,17 @@
 // alternating streams.  Here a chunk is up to `chunk` k-mer starts plus the
 // k-1 bases that the last of them reaches; consecutive chunks overlap by k-1
 // bases, so every k-mer start belongs to exactly one chunk.  Slot b (b = chunk
-// index mod 2) owns a pinned buffer, device buffers and a stream.  While slot
-// b's copy, pack, insert or query and answer copy run, the host fills slot
-// 1-b (a copy from the caller's memory, or the FASTX reader writing the
-// normalized stream straight into pinned memory).
+// index mod kHostSlots) owns a pinned buffer, device buffers and a stream.
+// While the copies, pack, insert or query and answer copy of the other slots
+// run, the host fills the next slot (a copy from the caller's memory, or the
+// FASTX reader writing the normalized stream straight into pinned memory).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
+#include <condition_variable>
+#include <mutex>
 #include <cstring>
 #include <new>
 #include <string>
@@ -35,27 +38,105 @@ double now_s()
     return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch()).count();
 }
 
-// memcpy split over threads for large copies (pageable source -> pinned).
-void par_memcpy(char* dst, const char* src, uint64_t n)
-{
-    const uint64_t kMin = 8ull << 20;
-    unsigned hw = std::thread::hardware_concurrency();
-    unsigned t = (unsigned)std::min<uint64_t>(std::min(8u, hw ? hw : 1u), n / kMin);
-    if (t <= 1) {
-        std::memcpy(dst, src, n);
-        return;
+// Persistent copy threads: a large pageable -> pinned copy is split into
+// parts taken by the caller and the workers (at most 16 threads in all).
+class CopyPool {
+public:
+    static CopyPool& get()
+    {
+        static CopyPool pool;
+        return pool;
     }
-    std::vector<std::thread> th;
-    const uint64_t part = (n + t - 1) / t;
-    for (unsigned i = 1; i < t; ++i) {
-        const uint64_t a = i * part, b = std::min(n, a + part);
-        if (a < b)
-            th.emplace_back([=] { std::memcpy(dst + a, src + a, b - a); });
+    void copy(char* dst, const char* src, uint64_t n)
+    {
+        const uint64_t kPart = 4ull << 20;
+        if (workers_.empty() || n < 2 * kPart) {
+            std::memcpy(dst, src, n);
+            return;
+        }
+        std::unique_lock<std::mutex> lk(mu_);
+        dst_ = dst;
+        src_ = src;
+        n_ = n;
+        part_ = std::max<uint64_t>(kPart, (n + 4 * nthreads() - 1) / (4 * nthreads()));
+        nparts_ = (n + part_ - 1) / part_;
+        next_.store(0);
+        left_ = nparts_;
+        ++gen_;
+        lk.unlock();
+        cv_.notify_all();
+        work();
+        lk.lock();
+        // every part copied and no worker still inside work(), so the next
+        // job may rewrite the job fields
+        done_.wait(lk, [&] { return left_ == 0 && active_ == 0; });
     }
-    std::memcpy(dst, src, std::min(n, part));
-    for (auto& x : th)
-        x.join();
-}
+
+private:
+    CopyPool()
+    {
+        unsigned hw = std::thread::hardware_concurrency();
+        const unsigned t = std::min(16u, hw ? hw : 1u);
+        for (unsigned i = 1; i < t; ++i)
+            workers_.emplace_back([this] { loop(); });
+    }
+    ~CopyPool()
+    {
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            stop_ = true;
+        }
+        cv_.notify_all();
+        for (auto& t : workers_)
+            t.join();
+    }
+    unsigned nthreads() const { return (unsigned)workers_.size() + 1; }
+    void work()
+    {
+        uint64_t done = 0;
+        for (;;) {
+            const uint64_t i = next_.fetch_add(1);
+            if (i >= nparts_)
+                break;
+            const uint64_t a = i * part_, b = std::min(n_, a + part_);
+            std::memcpy(dst_ + a, src_ + a, b - a);
+            ++done;
+        }
+        if (done) {
+            std::lock_guard<std::mutex> lk(mu_);
+            left_ -= done;
+            if (left_ == 0)
+                done_.notify_all();
+        }
+    }
+    void loop()
+    {
+        uint64_t seen = 0;
+        for (;;) {
+            {
+                std::unique_lock<std::mutex> lk(mu_);
+                cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+                if (stop_)
+                    return;
+                seen = gen_;
+                ++active_;
+            }
+            work();
+            std::lock_guard<std::mutex> lk(mu_);
+            if (--active_ == 0)
+                done_.notify_all();
+        }
+    }
+    std::vector<std::thread> workers_;
+    std::mutex mu_;
+    std::condition_variable cv_, done_;
+    char* dst_ = nullptr;
+    const char* src_ = nullptr;
+    uint64_t n_ = 0, part_ = 0, nparts_ = 0, left_ = 0, gen_ = 0;
+    unsigned active_ = 0;  // workers inside work()
+    std::atomic<uint64_t> next_{0};
+    bool stop_ = false;
+};
 
 int ensure_staging(sbf_t* h)
 {
@@ -66,7 +147,7 @@ int ensure_staging(sbf_t* h)
     const uint64_t in_bytes = hs.chunk + 64;  // + k-1 <= 31 bases of overlap, padded
     const uint64_t out_words = hs.chunk / 64 + 1;
     hipError_t e = hipSuccess;
-    for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+    for (int b = 0; b < kHostSlots && e == hipSuccess; ++b) {
         e = hipStreamCreateWithFlags(&hs.s[b], hipStreamNonBlocking);
         if (e == hipSuccess)
             e = hipEventCreateWithFlags(&hs.done[b], hipEventDisableTiming);
@@ -125,13 +206,13 @@ int run_pipeline(sbf_t* h, Source& src, Sink* sink, hipStream_t user, uint64_t* 
     hipError_t e = hipEventCreateWithFlags(&start, hipEventDisableTiming);
     if (e == hipSuccess)
         e = hipEventRecord(start, user);
-    for (int b = 0; b < 2 && e == hipSuccess; ++b)
+    for (int b = 0; b < kHostSlots && e == hipSuccess; ++b)
         e = hipStreamWaitEvent(hs.s[b], start, 0);
     if (e != hipSuccess) {
         (void)hipEventDestroy(start);
         return fail_hip(e, "pipeline start");
     }
-    Slot slot[2];
+    Slot slot[kHostSlots];
     uint64_t first = 0;    // stream offset of the next chunk's first byte
     uint64_t carry = 0;    // bytes at the front of the next chunk copied from the previous one
     const char* carry_src = nullptr;
@@ -149,7 +230,7 @@ int run_pipeline(sbf_t* h, Source& src, Sink* sink, hipStream_t user, uint64_t* 
         return r;
     };
     for (uint64_t i = 0; !ended; ++i) {
-        const int b = (int)(i & 1);
+        const int b = (int)(i % kHostSlots);
         e = drain(b);
         if (e != hipSuccess)
             break;
@@ -202,14 +283,14 @@ int run_pipeline(sbf_t* h, Source& src, Sink* sink, hipStream_t user, uint64_t* 
     }
     // drain both slots (oldest first) even after an error, so no copy still
     // targets the pinned buffers
-    const int b0 = (int)(nchunks & 1);
-    hipError_t e2 = drain(b0);
-    hipError_t e3 = drain(1 - b0);
+    for (uint64_t j = nchunks >= kHostSlots ? nchunks - kHostSlots : 0; j < nchunks; ++j) {
+        const hipError_t e2 = drain((int)(j % kHostSlots));
+        if (e == hipSuccess)
+            e = e2;
+    }
     (void)hipEventDestroy(start);
     if (rc)
         return rc;
-    if (e == hipSuccess)
-        e = e2 != hipSuccess ? e2 : e3;
     if (e != hipSuccess)
         return fail_hip(e, "host pipeline");
     if (chunks_out)
@@ -228,7 +309,7 @@ struct MemSource : Source {
     int next(char* dst, uint64_t cap, uint64_t* got) override
     {
         const uint64_t n = std::min(cap, left);
-        par_memcpy(dst, p, n);
+        CopyPool::get().copy(dst, p, n);
         p += n;
         left -= n;
         *got = n;
@@ -343,7 +424,7 @@ struct RecordSink : Sink {
 
 void free_host_staging(HostStaging& hs)
 {
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kHostSlots; ++b) {
         if (hs.s[b])
             (void)hipStreamSynchronize(hs.s[b]);
         if (hs.h_in[b])

@@ -255,3 +255,31 @@ def write_fastq(path: str, records, gz: bool = False, seed_qual: int = 12) -> No
             s = bytes(r).rstrip(b"N")
             q = (rng.integers(33, 75, len(s), dtype=np.uint8)).tobytes()
             f.write(b"@read_%d\n%s\n+\n%s\n" % (i, s, q))
+
+
+def fasta_bytes(seq: np.ndarray, width: int = 80, name: bytes = b"chr1") -> np.ndarray:
+    """One-record FASTA file contents (uint8) of a long sequence, `width`
+    bases per line; vectorized for genome-sized inputs."""
+    n = seq.size
+    full = n // width
+    body = np.empty((full, width + 1), dtype=np.uint8)
+    body[:, :width] = seq[:full * width].reshape(full, width)
+    body[:, width] = ord("\n")
+    tail = seq[full * width:]
+    parts = [np.frombuffer(b">" + name + b"\n", dtype=np.uint8), body.reshape(-1)]
+    if tail.size:
+        parts += [tail, np.frombuffer(b"\n", dtype=np.uint8)]
+    return np.concatenate(parts)
+
+
+def fastq_bytes(reads: np.ndarray, seed_qual: int = 12) -> np.ndarray:
+    """FASTQ file contents (uint8) of equal-length reads given as an (n, L)
+    ASCII array: '@r\\n', the read, '\\n+\\n', a seeded quality string, '\\n'."""
+    n, L = reads.shape
+    rec = np.empty((n, 3 + L + 3 + L + 1), dtype=np.uint8)
+    rec[:, 0:3] = np.frombuffer(b"@r\n", dtype=np.uint8)
+    rec[:, 3:3 + L] = reads
+    rec[:, 3 + L:6 + L] = np.frombuffer(b"\n+\n", dtype=np.uint8)
+    rec[:, 6 + L:6 + 2 * L] = np.random.default_rng(seed_qual).integers(33, 75, (n, L), dtype=np.uint8)
+    rec[:, -1] = ord("\n")
+    return rec.reshape(-1)

@@ -93,3 +93,18 @@ def test_fastx_insert_and_query(tmp_path, fmt, gz, chunk):
     # capped output: the first records only, the count of all
     h2, k2, st2 = f.query_fastx(q_path, max_records=10)
     assert h2.size == 10 and (h2 == want_hits[:10]).all() and st2["records"] == len(reads)
+
+
+def test_host_pipeline_large_matches_device_path():
+    """64 MB host inputs (copied into pinned memory by the copy threads) give
+    the filter and answers of the device-resident path."""
+    seq = S.to_ascii(S.uniform_codes(64_000_000, 77))
+    dev = G.to_dev(seq)
+    a = G.gpu_filter(MAIN, 2**26)
+    b = G.gpu_filter(MAIN, 2**26)
+    a.insert_seq(seq)  # host memory, default chunk
+    b.insert_seq(dev)
+    G.assert_words_equal(a.words(), b.words(), "host vs device insert")
+    q = S.to_ascii(S.uniform_codes(48_000_000, 78))
+    q[::997] = ord("N")
+    G.assert_words_equal(a.query_seq(q), G.dev_bits_to_np(b.query_seq(G.to_dev(q))), "host vs device query")
