@@ -17,3 +17,14 @@
 // Fig. 2 (k=9, m=5, s=6), s = m = k (one m-mer, one s-mer), k = 32 (a full
 // 64-bit k-mer), a wide halo (w - 1 = 20), and the salted bit address (H > 10).
 #define SBF_EXTRA(X) X(9, 5, 6, 3) X(31, 31, 31, 4) X(32, 16, 28, 4) X(21, 1, 19, 5) X(31, 16, 28, 12)
+
+// Slices of the wider grid of [cuSBF] §V-B / Fig. 4 through the operating
+// point (31,16,28,4): s = 16..31 at (m, H) = (16, 4), m = 8..31 at
+// (s, H) = (28, 4), and H in {1, 5, 8, 16} at (m, s) = (16, 28) (H = 12 is in
+// SBF_EXTRA; the sweep above holds the rest).  Split for parallel builds.
+#define SBF_SLICE_S_A(X) X(31, 16, 16, 4) X(31, 16, 17, 4) X(31, 16, 18, 4) X(31, 16, 19, 4) X(31, 16, 20, 4) X(31, 16, 21, 4)
+#define SBF_SLICE_S_B(X) X(31, 16, 22, 4) X(31, 16, 23, 4) X(31, 16, 25, 4) X(31, 16, 27, 4) X(31, 16, 29, 4) X(31, 16, 31, 4)
+#define SBF_SLICE_M_A(X) X(31, 8, 28, 4) X(31, 9, 28, 4) X(31, 10, 28, 4) X(31, 11, 28, 4) X(31, 13, 28, 4) X(31, 14, 28, 4) X(31, 15, 28, 4)
+#define SBF_SLICE_M_B(X) X(31, 17, 28, 4) X(31, 18, 28, 4) X(31, 19, 28, 4) X(31, 21, 28, 4) X(31, 22, 28, 4) X(31, 23, 28, 4) X(31, 24, 28, 4)
+#define SBF_SLICE_M_C(X) X(31, 25, 28, 4) X(31, 26, 28, 4) X(31, 27, 28, 4) X(31, 28, 28, 4) X(31, 29, 28, 4) X(31, 30, 28, 4) X(31, 31, 28, 4)
+#define SBF_SLICE_H(X) X(31, 16, 28, 1) X(31, 16, 28, 5) X(31, 16, 28, 8) X(31, 16, 28, 16)

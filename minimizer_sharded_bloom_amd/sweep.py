@@ -8,9 +8,11 @@ For every (s, m, H) in {24,26,28,30} x {12,16,20} x {2,3,4,6} at k = 31 and
 reads, and count positives among 10^7 random 31-mers.  The blocked Bloom
 comparator (one hash picks a 256-bit block, H bits from a second hash) runs
 at the same budget for H in {2,3,4,6}.  Prints one JSON line per point and a
-summary table.
+summary table.  With --grid: the slices of the wider grid (Fig. 4) through
+the operating point -- s = 16..31 at (m, H) = (16, 4), m = 8..31 at
+(s, H) = (28, 4), H in {1,2,3,4,5,6,8,12,16} at (m, s) = (16, 28).
 
-    python -m minimizer_sharded_bloom_amd.sweep [--probe-n N] [--reps R]
+    python -m minimizer_sharded_bloom_amd.sweep [--probe-n N] [--reps R] [--grid]
 """
 from __future__ import annotations
 
@@ -45,7 +47,7 @@ def _time_ms(torch, stream, fn, reps):
     return float(np.median(ts))
 
 
-def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, out=sys.stdout):
+def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, grid: bool = False, out=sys.stdout):
     import torch
 
     torch.cuda.set_device(0)
@@ -90,6 +92,14 @@ def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, out=sys.st
         rows.append(row)
         print(json.dumps(row), file=out, flush=True)
 
+    if grid:
+        for kind, pts in (("slice_s", [(16, s, 4) for s in range(16, 32)]),
+                          ("slice_m", [(m, 28, 4) for m in range(8, 32)]),
+                          ("slice_h", [(16, 28, H) for H in (1, 2, 3, 4, 5, 6, 8, 12, 16)])):
+            for m, s, H in pts:
+                with SuperBloomFilter(K, m, s, H, BITS) as f:
+                    point(f, {"kind": kind, "s": s, "m": m, "H": H})
+        return rows
     for s in S_VALUES:
         for m in M_VALUES:
             for H in H_VALUES:
@@ -102,12 +112,12 @@ def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, out=sys.st
 
 
 def table(rows) -> str:
-    lines = ["| kind | s | m | H | insert Gk-mers/s | query Gk-mers/s | FPR (random 31-mers) |",
-             "|---|---|---|---|---:|---:|---:|"]
+    lines = ["| kind | s | m | H | insert Gk-mers/s | query Gk-mers/s | FPR (random 31-mers) | specialized |",
+             "|---|---|---|---|---:|---:|---:|---|"]
     for r in rows:
-        lines.append("| %s | %s | %s | %d | %.1f | %.1f | %.3g |" % (
+        lines.append("| %s | %s | %s | %d | %.1f | %.1f | %.3g | %s |" % (
             r["kind"], r["s"] if r["s"] else "-", r["m"] if r["m"] else "-", r["H"],
-            r["insert_gkmers_s"], r["query_gkmers_s"], r["fpr"]))
+            r["insert_gkmers_s"], r["query_gkmers_s"], r["fpr"], "yes" if r["specialized"] else "no"))
     return "\n".join(lines)
 
 
@@ -115,8 +125,10 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--probe-n", type=int, default=10_000_000)
     ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--grid", action="store_true",
+                    help="instead: the s-, m- and H-slices through (s, m, H) = (28, 16, 4)")
     a = ap.parse_args()
     t0 = time.time()
-    rows = run(a.probe_n, a.reps)
+    rows = run(a.probe_n, a.reps, grid=a.grid)
     print(table(rows))
     print("sweep wall time %.1f s" % (time.time() - t0), file=sys.stderr)

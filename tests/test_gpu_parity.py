@@ -184,6 +184,35 @@ def test_sweep_instantiations(m):
             assert g.fpr_probe(20000, s * H) == o.fpr_probe(20000, s * H)
 
 
+GRID_SLICES = ([(31, 16, s, 4) for s in (16, 17, 18, 19, 20, 21, 22, 23, 25, 27, 29, 31)]
+               + [(31, m, 28, 4) for m in (8, 9, 10, 11, 13, 14, 15, 17, 18, 19, 21, 22, 23, 24, 25, 26, 27, 28,
+                                          29, 30, 31)]
+               + [(31, 16, 28, H) for H in (1, 5, 8, 16)])
+
+
+def test_grid_slices():
+    """Every set of the s-, m- and H-slices through the operating point is
+    specialized and bit-exact on a short genome, reads and probes."""
+    genome = S.genome_with_repeats(30000, seed_genome=90)
+    reads = S.short_read_set(genome, 200)
+    gs = S.to_ascii(genome)
+    for params in GRID_SLICES:
+        g, o = _run_pair(params, 2**16, [gs], [reads])
+        assert g.specialized, params
+        assert g.fpr_probe(20000, sum(params)) == o.fpr_probe(20000, sum(params))
+
+
+@pytest.mark.parametrize("params", [(31, 16, 16, 4), (31, 8, 28, 4), (31, 14, 28, 4), (31, 16, 28, 16)])
+def test_grid_slice_edges(params):
+    """Edge lengths (lane, wave and word boundaries) on the widest Findere
+    window (s = 16), the widest minimizer window (m = 8, 32 k-mers per lane),
+    the first m with 32 k-mers per lane, and the most hashes (H = 16)."""
+    rng = np.random.default_rng(43 + sum(params))
+    ins = [T.random_dna(rng, L) for L in EDGE_LENGTHS]
+    qs = [T.random_dna(rng, L) for L in EDGE_LENGTHS] + ins[-6:]
+    _run_pair(params, 2**14, ins, qs)
+
+
 def test_repeated_launches_same_result():
     """OR is idempotent: inserting the same data with the filter not cleared,
     and again after clear, gives the same words (no lost atomic updates)."""
