@@ -162,4 +162,12 @@ __device__ __forceinline__ void load_shard(const uint64_t* __restrict__ filter, 
     w[3] = b.y;
 }
 
+// LDS written by some lanes of this wave becomes visible to all its lanes.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace sbf

@@ -122,6 +122,7 @@ hipError_t launch_fill_zero(uint64_t* p, uint64_t nwords, hipStream_t st)
 // Generic per-k-mer kernels (runtime k, m, s, H; SBF and BBF).
 // ---------------------------------------------------------------------------
 
+
 // Packed value of the k-mer starting at base p (first base most significant).
 __device__ __forceinline__ uint64_t kmer_at(const uint32_t* __restrict__ codes, uint64_t ncw, uint64_t p, uint32_t k)
 {
@@ -179,20 +180,37 @@ __device__ __forceinline__ void kmer_masks(uint64_t x, const Params& P, uint64_t
     }
 }
 
+// One k-mer per lane, 64 k-mers per wave step.  Each lane stages its shard
+// and four masks in LDS; then four adjacent lanes OR the four words of one
+// record into the filter in one instruction, which the memory system merges
+// into one request per k-mer instead of four.
 __global__ __launch_bounds__(256) void generic_insert_kernel(SeqArgs a, Params P)
 {
+    __shared__ uint32_t rec_idx[4][64];
+    __shared__ uint64_t rec_words[4][64][4];
+    const uint32_t lane = threadIdx.x & 63u, wv = threadIdx.x >> 6;
+    const uint64_t nk_pad = (a.nk + 63) & ~63ull;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t p = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; p < a.nk; p += stride) {
-        if (!kmer_valid_at(a.valid, a.nvw, p, P.k))
-            continue;
-        const uint64_t x = kmer_at(a.codes, a.ncw, p, P.k);
-        const uint32_t sh = kmer_shard(x, P, a.shard_mask);
-        uint64_t mk[4];
-        kmer_masks(x, P, mk);
-        uint64_t* base = a.filter + 4ull * sh;
+    for (uint64_t p0 = (uint64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63u); p0 < nk_pad; p0 += stride) {
+        const uint64_t p = p0 + lane;
+        uint64_t mk[4] = {0, 0, 0, 0};
+        uint32_t sh = 0;
+        if (p < a.nk && kmer_valid_at(a.valid, a.nvw, p, P.k)) {
+            const uint64_t x = kmer_at(a.codes, a.ncw, p, P.k);
+            sh = kmer_shard(x, P, a.shard_mask);
+            kmer_masks(x, P, mk);
+        }
+        rec_idx[wv][lane] = sh;
         for (int q = 0; q < 4; ++q)
-            if (mk[q])
-                atomic_or_u64(base + q, mk[q]);
+            rec_words[wv][lane][q] = mk[q];
+        wave_lds_sync();
+        for (uint32_t j = 0; j < 4; ++j) {
+            const uint32_t r = (lane >> 2) + 16u * j, q = lane & 3u;
+            const uint64_t m = rec_words[wv][r][q];
+            if (m)
+                atomic_or_u64(a.filter + 4ull * rec_idx[wv][r] + q, m);
+        }
+        wave_lds_sync();  // the next step overwrites the records
     }
 }
 

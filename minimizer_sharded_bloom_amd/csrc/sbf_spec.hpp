@@ -458,13 +458,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
     return x;
 }
 
-// LDS written by some lanes of this wave becomes visible to all its lanes.
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Run starts of a lane: bit i set if k-mer i is valid and does not continue
 // the previous one (invalid, or another shard).  Runs double as query
