@@ -20,6 +20,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 KIND_SBF = 0
 KIND_BBF = 1
+KIND_WIDE = 2  # 512-bit blocks, each hash addressing the whole block
 
 
 def build(force: bool = False) -> str:
@@ -48,6 +49,10 @@ def lib():
             getattr(L, name).restype = u64
         L.osbf_bitaddr.argtypes = [u64, u32, u32]
         L.osbf_bitaddr.restype = u32
+        L.osbf_bitaddr_wide.argtypes = [u64, u32, u32]
+        L.osbf_bitaddr_wide.restype = u32
+        L.osbf_words_per_shard.argtypes = [p]
+        L.osbf_words_per_shard.restype = u32
         L.osbf_probe_kmer.argtypes = [u64, u64, u32]
         L.osbf_probe_kmer.restype = u64
         L.osbf_pack_kmer.argtypes = [ctypes.c_char_p, u32, ctypes.POINTER(u64)]
@@ -125,6 +130,10 @@ def bitaddr(h: int, t: int, H: int) -> int:
     return lib().osbf_bitaddr(h, t, H)
 
 
+def bitaddr_wide(h: int, t: int, H: int) -> int:
+    return lib().osbf_bitaddr_wide(h, t, H)
+
+
 def probe_kmer(seed: int, i: int, k: int) -> int:
     return lib().osbf_probe_kmer(seed & (2**64 - 1), i, k)
 
@@ -160,8 +169,9 @@ def _threads(n: int) -> int:
 
 
 class OracleFilter:
-    """A Super Bloom filter (kind=KIND_SBF) or per-k-mer blocked Bloom filter
-    (kind=KIND_BBF) held in host memory by the C oracle."""
+    """A Super Bloom filter (kind=KIND_SBF), its wide-block variant
+    (KIND_WIDE) or a per-k-mer blocked Bloom filter (KIND_BBF) held in host
+    memory by the C oracle."""
 
     def __init__(self, k, m, s, H, bits, kind=KIND_SBF):
         self.k, self.m, self.s, self.H, self.kind = k, m, s, H, kind
@@ -181,9 +191,13 @@ class OracleFilter:
     def num_shards(self) -> int:
         return lib().osbf_num_shards(self._h)
 
+    @property
+    def words_per_shard(self) -> int:
+        return lib().osbf_words_per_shard(self._h)
+
     def words(self) -> np.ndarray:
-        """Copy of the filter: uint64[4 * num_shards]."""
-        n = 4 * self.num_shards
+        """Copy of the filter: uint64[words_per_shard * num_shards]."""
+        n = self.words_per_shard * self.num_shards
         ptr = lib().osbf_words(self._h)
         return np.ctypeslib.as_array(ptr, shape=(n,)).copy()
 

@@ -28,6 +28,12 @@
  *    (2t+1) * G would make the H addresses an arithmetic progression.
  *  - Shard count: the smallest power of two >= ceil(bits/256), at least 1
  *    ([cuSBF] §IV-B).  Hash index t lives in word t mod 4 of the shard.
+ *  - Wide variant (OSBF_KIND_WIDE), the layout [cuSBF] §V-D attributes to the
+ *    CPU Super Bloom reference: 512-bit blocks, each hash index addressing any
+ *    bit of the block.  Block count: the smallest power of two >=
+ *    ceil(bits/512).  Address of hash t: for H <= 7, slice t of width
+ *    floor(64/H), its low 9 bits; for H > 7, the top 9 bits of hs * salt_t
+ *    (salt_t as above).  Address a sets bit a mod 64 of word a / 64.
  *  - Invalid k-mers (any non-ACGT base) insert nothing and query false
  *    ([cuSBF] Algorithms 1 and 2, §IV-F).
  *  - Probe k-mers: the i-th output of the SplitMix64 stream seeded with
@@ -95,6 +101,18 @@ unsigned osbf_bitaddr(uint64_t hs, unsigned t, unsigned H)
     return (unsigned)((hs * salt) >> 58);
 }
 
+/* Wide variant: a 9-bit address into a 512-bit block (the CPU reference's
+ * whole-block addressing, [cuSBF] §V-D), sliced or salted as above. */
+unsigned osbf_bitaddr_wide(uint64_t hs, unsigned t, unsigned H)
+{
+    if (H <= 7) {
+        unsigned width = 64u / H;
+        return (unsigned)((hs >> (t * width)) & 511u);
+    }
+    uint64_t salt = osbf_mix((uint64_t)(t + 1u) * GOLDEN);
+    return (unsigned)((hs * salt) >> 55);
+}
+
 /* [cuSBF] §V-D: uniformly random k-mers, drawn from SplitMix64. */
 uint64_t osbf_probe_kmer(uint64_t seed, uint64_t i, unsigned k)
 {
@@ -142,21 +160,22 @@ uint64_t osbf_minimizer_hash(uint64_t x, unsigned k, unsigned m)
 
 osbf* osbf_create(int kind, unsigned k, unsigned m, unsigned s, unsigned H, uint64_t bits)
 {
-    if (kind != OSBF_KIND_SBF && kind != OSBF_KIND_BBF)
+    if (kind != OSBF_KIND_SBF && kind != OSBF_KIND_BBF && kind != OSBF_KIND_WIDE)
         return NULL;
     if (k < 1 || k > 32 || H < 1 || H > 64 || bits < 1)
         return NULL;
-    if (kind == OSBF_KIND_SBF && (m < 1 || m > k || s < 1 || s > k))
+    if (kind != OSBF_KIND_BBF && (m < 1 || m > k || s < 1 || s > k))
         return NULL;
     /* [cuSBF] §IV-B: shard count rounded up to a power of two. */
-    uint64_t need = bits / 256u + (bits % 256u != 0);
+    const uint64_t block = kind == OSBF_KIND_WIDE ? 512u : 256u;
+    uint64_t need = bits / block + (bits % block != 0);
     uint64_t n = 1;
     while (n < need)
         n <<= 1;
     osbf* f = (osbf*)calloc(1, sizeof(osbf));
     if (!f)
         return NULL;
-    f->words = (uint64_t*)calloc(4u * n, sizeof(uint64_t));
+    f->words = (uint64_t*)calloc((block / 64u) * n, sizeof(uint64_t));
     if (!f->words) {
         free(f);
         return NULL;
@@ -179,6 +198,7 @@ void osbf_destroy(osbf* f)
 }
 
 uint64_t osbf_num_shards(const osbf* f) { return f->num_shards; }
+unsigned osbf_words_per_shard(const osbf* f) { return f->kind == OSBF_KIND_WIDE ? 8u : 4u; }
 uint64_t* osbf_words(osbf* f) { return f->words; }
 
 /* SBF: [cuSBF] Algorithm 1, shard = minimizer hash & (N-1).
@@ -190,18 +210,31 @@ uint64_t osbf_shard_of(const osbf* f, uint64_t x)
     return osbf_minimizer_hash(x, f->k, f->m) & (f->num_shards - 1u);
 }
 
-/* [cuSBF] §IV-B: hash index t sets one bit in word t mod 4 of the shard. */
-static void set_bits(uint64_t* shard, uint64_t hs, unsigned H)
+/* [cuSBF] §IV-B: hash index t sets one bit in word t mod 4 of the shard;
+ * wide variant: bit a mod 64 of word a / 64 for its 9-bit address a. */
+static void set_bits(const osbf* f, uint64_t* shard, uint64_t hs)
 {
-    for (unsigned t = 0; t < H; ++t)
-        shard[t % 4u] |= 1ull << osbf_bitaddr(hs, t, H);
+    for (unsigned t = 0; t < f->H; ++t) {
+        if (f->kind == OSBF_KIND_WIDE) {
+            unsigned a = osbf_bitaddr_wide(hs, t, f->H);
+            shard[a / 64u] |= 1ull << (a % 64u);
+        } else {
+            shard[t % 4u] |= 1ull << osbf_bitaddr(hs, t, f->H);
+        }
+    }
 }
 
-static int test_bits(const uint64_t* shard, uint64_t hs, unsigned H)
+static int test_bits(const osbf* f, const uint64_t* shard, uint64_t hs)
 {
-    for (unsigned t = 0; t < H; ++t)
-        if (!((shard[t % 4u] >> osbf_bitaddr(hs, t, H)) & 1u))
+    for (unsigned t = 0; t < f->H; ++t) {
+        if (f->kind == OSBF_KIND_WIDE) {
+            unsigned a = osbf_bitaddr_wide(hs, t, f->H);
+            if (!((shard[a / 64u] >> (a % 64u)) & 1u))
+                return 0;
+        } else if (!((shard[t % 4u] >> osbf_bitaddr(hs, t, f->H)) & 1u)) {
             return 0;
+        }
+    }
     return 1;
 }
 
@@ -210,24 +243,24 @@ static int test_bits(const uint64_t* shard, uint64_t hs, unsigned H)
  * hash of the k-mer's block hash. */
 void osbf_insert_kmer(osbf* f, uint64_t x)
 {
-    uint64_t* shard = f->words + 4u * osbf_shard_of(f, x);
+    uint64_t* shard = f->words + osbf_words_per_shard(f) * osbf_shard_of(f, x);
     if (f->kind == OSBF_KIND_BBF) {
-        set_bits(shard, osbf_hs(osbf_hs(x)), f->H);
+        set_bits(f, shard, osbf_hs(osbf_hs(x)));
         return;
     }
     for (unsigned j = 0; j + f->s <= f->k; ++j)
-        set_bits(shard, osbf_hs(osbf_subwindow(x, f->k, j, f->s)), f->H);
+        set_bits(f, shard, osbf_hs(osbf_subwindow(x, f->k, j, f->s)));
 }
 
 /* [cuSBF] §II-B-2 and Algorithm 2 (Contains): present only if every s-mer
  * finds all of its H bits. */
 int osbf_query_kmer(const osbf* f, uint64_t x)
 {
-    const uint64_t* shard = f->words + 4u * osbf_shard_of(f, x);
+    const uint64_t* shard = f->words + osbf_words_per_shard(f) * osbf_shard_of(f, x);
     if (f->kind == OSBF_KIND_BBF)
-        return test_bits(shard, osbf_hs(osbf_hs(x)), f->H);
+        return test_bits(f, shard, osbf_hs(osbf_hs(x)));
     for (unsigned j = 0; j + f->s <= f->k; ++j)
-        if (!test_bits(shard, osbf_hs(osbf_subwindow(x, f->k, j, f->s)), f->H))
+        if (!test_bits(f, shard, osbf_hs(osbf_subwindow(x, f->k, j, f->s))))
             return 0;
     return 1;
 }
@@ -295,10 +328,16 @@ typedef struct {
     uint64_t sample_mask, sample_value; /* shards with (shard & mask) == value */
 } osbf_job;
 
-static void set_bits_atomic(uint64_t* shard, uint64_t hs, unsigned H)
+static void set_bits_atomic(const osbf* f, uint64_t* shard, uint64_t hs)
 {
-    for (unsigned t = 0; t < H; ++t)
-        __atomic_fetch_or(&shard[t % 4u], 1ull << osbf_bitaddr(hs, t, H), __ATOMIC_RELAXED);
+    for (unsigned t = 0; t < f->H; ++t) {
+        if (f->kind == OSBF_KIND_WIDE) {
+            unsigned a = osbf_bitaddr_wide(hs, t, f->H);
+            __atomic_fetch_or(&shard[a / 64u], 1ull << (a % 64u), __ATOMIC_RELAXED);
+        } else {
+            __atomic_fetch_or(&shard[t % 4u], 1ull << osbf_bitaddr(hs, t, f->H), __ATOMIC_RELAXED);
+        }
+    }
 }
 
 static void* insert_worker(void* arg)
@@ -312,13 +351,13 @@ static void* insert_worker(void* arg)
         uint64_t sh = osbf_shard_of(f, x);
         if ((sh & j->sample_mask) != j->sample_value)
             continue;
-        uint64_t* shard = f->words + 4u * sh;
+        uint64_t* shard = f->words + osbf_words_per_shard(f) * sh;
         if (f->kind == OSBF_KIND_BBF) {
-            set_bits_atomic(shard, osbf_hs(osbf_hs(x)), f->H);
+            set_bits_atomic(f, shard, osbf_hs(osbf_hs(x)));
             continue;
         }
         for (unsigned s = 0; s + f->s <= f->k; ++s)
-            set_bits_atomic(shard, osbf_hs(osbf_subwindow(x, f->k, s, f->s)), f->H);
+            set_bits_atomic(f, shard, osbf_hs(osbf_subwindow(x, f->k, s, f->s)));
     }
     return NULL;
 }

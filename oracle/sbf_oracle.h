@@ -30,6 +30,7 @@ extern "C" {
 /* kind of filter */
 #define OSBF_KIND_SBF 0 /* Super Bloom filter (minimizer shard + Findere s-mers) */
 #define OSBF_KIND_BBF 1 /* per-k-mer blocked Bloom filter with the same shard layout */
+#define OSBF_KIND_WIDE 2 /* SBF with 512-bit blocks, each hash addressing the whole block */
 
 typedef struct osbf osbf;
 
@@ -43,6 +44,8 @@ uint64_t osbf_mix(uint64_t z);
 uint64_t osbf_hs(uint64_t v);
 /* bit position (0..63) of hash index t of an s-mer hash, for H hashes */
 unsigned osbf_bitaddr(uint64_t hs, unsigned t, unsigned H);
+/* wide variant: bit position (0..511) in the 512-bit block */
+unsigned osbf_bitaddr_wide(uint64_t hs, unsigned t, unsigned H);
 /* i-th probe k-mer (0-based) of the stream started at `seed` */
 uint64_t osbf_probe_kmer(uint64_t seed, uint64_t i, unsigned k);
 
@@ -60,7 +63,10 @@ uint64_t osbf_minimizer_hash(uint64_t x, unsigned k, unsigned m);
 osbf* osbf_create(int kind, unsigned k, unsigned m, unsigned s, unsigned H, uint64_t bits);
 void osbf_destroy(osbf* f);
 uint64_t osbf_num_shards(const osbf* f);
-/* the filter: 4 * num_shards words, shard j is words 4j..4j+3 */
+/* 4, or 8 for the wide variant */
+unsigned osbf_words_per_shard(const osbf* f);
+/* the filter: W * num_shards words (W = words per shard), shard j is words
+ * Wj .. Wj+W-1 */
 uint64_t* osbf_words(osbf* f);
 
 /* shard a packed k-mer maps to */

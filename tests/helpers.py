@@ -66,3 +66,15 @@ def binom_ok(hits: int, n: int, p: float, z: float = 3.5) -> bool:
     mu = n * p
     sd = math.sqrt(max(n * p * (1 - p), 1e-12))
     return abs(hits - mu) <= z * sd + 1.0
+
+
+def kmer_bits_wide_str(kmer: str, s: int, H: int):
+    """{(word, bit)} that the k-mer's s-mers set in a 512-bit block of the
+    wide variant, from the text: address a -> (a // 64, a % 64)."""
+    out = set()
+    for j in range(len(kmer) - s + 1):
+        h = O.hs(pack_str(kmer[j:j + s]))
+        for t in range(H):
+            a = O.bitaddr_wide(h, t, H)
+            out.add((a // 64, a % 64))
+    return out

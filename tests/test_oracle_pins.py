@@ -400,7 +400,7 @@ def test_bbf_fill_based_fpr():
 
 
 @pytest.mark.parametrize("kind,params", [(O.KIND_SBF, (31, 16, 28, 4)), (O.KIND_SBF, (21, 11, 19, 3)),
-                                         (O.KIND_BBF, (31, 0, 0, 4))])
+                                         (O.KIND_BBF, (31, 0, 0, 4)), (O.KIND_WIDE, (31, 16, 28, 4))])
 def test_threaded_driver_equals_single_thread(kind, params):
     """The multi-threaded insert/query drivers split k-mer starts over
     threads; the union and the answers must equal the plain loop's."""
@@ -446,3 +446,95 @@ def test_shard_sampled_driver():
         km = q[p:p + 31].decode()
         exp = T.valid_str(km) and (full.shard_of(T.pack_str(km)) & 7) == 3
         assert cb[p] == exp
+
+
+# ---- wide variant: 512-bit blocks, whole-block addressing ([cuSBF] §V-D) ----
+
+def test_wide_bitaddr_slices_and_salt():
+    """Hand-sliced 9-bit addresses for H = 4 (slices of 16 bits, low 9 bits)
+    and the salted form for H > 7 (top 9 bits of hs * mix((t+1) G))."""
+    h = 0x0123456789ABCDEF
+    assert [O.bitaddr_wide(h, t, 4) for t in range(4)] == [0x1EF, 0x1AB, 0x167, 0x123]
+    assert [O.bitaddr_wide(h, t, 7) for t in range(7)] == [(h >> (9 * t)) & 511 for t in range(7)]
+    G = 0x9E3779B97F4A7C15
+    for H in (8, 12):
+        for t in range(H):
+            salt = O.mix(((t + 1) * G) & (2**64 - 1))
+            assert O.bitaddr_wide(h, t, H) == ((h * salt) & (2**64 - 1)) >> 55
+
+
+@pytest.mark.parametrize("k,m,s,H", [(31, 16, 28, 4), (21, 8, 15, 3), (31, 16, 28, 8)])
+def test_wide_single_kmer_bits(k, m, s, H):
+    """One k-mer touches one 512-bit block; the set bits are exactly the
+    addresses of its s-mers cut from the text, anywhere in the block."""
+    rng = np.random.default_rng(31 + k + m + s + H)
+    for _ in range(20):
+        f = O.OracleFilter(k, m, s, H, 2**15, kind=O.KIND_WIDE)
+        assert f.words_per_shard == 8 and f.num_shards == 2**15 // 512
+        km = T.random_dna(rng, k).decode()
+        x = O.pack_kmer(km)
+        f.insert_kmer(x)
+        w = f.words().reshape(-1, 8)
+        nz = np.nonzero(w.any(axis=1))[0]
+        assert list(nz) == [f.shard_of(x)]
+        assert f.shard_of(x) == T.minimizer_hash_str(km, m) % f.num_shards
+        got = {(q, b) for q in range(8) for b in range(64) if (int(w[nz[0], q]) >> b) & 1}
+        assert got == T.kmer_bits_wide_str(km, s, H)
+        assert f.query_kmer(x)
+
+
+def test_wide_classic_bloom_eq1():
+    """Textbook reduction: one 512-bit block (bits = 512) and s = m = k make a
+    classic Bloom filter of 512 bits with H = 4 hash functions.  Given the
+    filter, a random key hits with probability fill^H (independent uniform
+    addresses); the mean fill after n keys is 1 - (1 - 1/512)^(Hn), whose
+    large-m form gives Eq. (1)."""
+    rng = np.random.default_rng(32)
+    k, H, n, trials, probes = 31, 4, 60, 50, 4000
+    hits, expect, fills = 0, 0.0, []
+    for tr in range(trials):
+        f = O.OracleFilter(k, k, k, H, 512, kind=O.KIND_WIDE)
+        for x in rng.choice(2**62, n, replace=False):
+            f.insert_kmer(int(x))
+        fill = sum(bin(int(v)).count("1") for v in f.words()) / 512
+        fills.append(fill)
+        hits += f.fpr_probe(probes, 7000 + tr)
+        expect += probes * fill ** H
+    assert abs(hits - expect) <= 4.5 * math.sqrt(expect) + 2
+    mean_fill = 1 - (1 - 1 / 512) ** (H * n)
+    assert abs(np.mean(fills) - mean_fill) < 4.5 * np.std(fills) / math.sqrt(trials) + 1e-3
+    eq1 = (1 - math.exp(-H * n / 512)) ** H
+    assert abs(mean_fill ** H - eq1) / eq1 < 0.05
+
+
+@pytest.mark.parametrize("k,m,s,H", [(31, 16, 28, 4), (31, 16, 24, 2)])
+def test_wide_fpr_fill_based(k, m, s, H):
+    """A random alien k-mer lands in a uniform block and each of its
+    (k-s+1) H addresses is uniform over the block's 512 bits:
+    P(hit) = mean over blocks of fill^((k-s+1) H)."""
+    rng = np.random.default_rng(33 + s)
+    f = O.OracleFilter(k, m, s, H, 2**14, kind=O.KIND_WIDE)
+    f.insert_seq(T.random_dna(rng, 6000))
+    w = f.words().reshape(-1, 8)
+    fill = np.array([sum(bin(int(v)).count("1") for v in row) / 512 for row in w])
+    p = float(np.mean(fill ** ((k - s + 1) * H)))
+    n = 200000
+    hits = f.fpr_probe(n, 0x5EED)
+    assert p > 1e-4
+    assert T.binom_ok(hits, n, p, z=4.5)
+
+
+def test_wide_blocks_lower_fpr_than_sectors():
+    """At one memory budget and input, whole-block addressing in 512-bit
+    blocks gives a lower false-positive rate than 64-bit sectors in 256-bit
+    shards ([cuSBF] §V-D: the CPU reference's layout; cuSBF trades dispersion
+    for branch-free masks)."""
+    rng = np.random.default_rng(34)
+    seq = T.random_dna(rng, 60000)
+    rates = {}
+    for kind in (O.KIND_SBF, O.KIND_WIDE):
+        f = O.OracleFilter(31, 16, 28, 4, 2**19, kind=kind)
+        f.insert_seq(seq)
+        rates[kind] = f.fpr_probe(400000, 77) / 400000
+    assert rates[O.KIND_SBF] > 5e-4  # ~640 hits: the comparison is not noise
+    assert rates[O.KIND_WIDE] < 0.5 * rates[O.KIND_SBF]
