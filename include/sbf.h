@@ -64,6 +64,7 @@ extern "C" {
 /* filter kinds */
 #define SBF_KIND_SBF 0 /* Super Bloom filter */
 #define SBF_KIND_BBF 1 /* per-k-mer blocked Bloom filter, same shard layout */
+#define SBF_KIND_WIDE 2 /* Super Bloom filter with 512-bit blocks, whole-block addressing */
 
 /* where the pointers of a *_seq / copy call live */
 #define SBF_HOST 1u
@@ -76,7 +77,8 @@ typedef struct sbf_info {
     uint32_t kind;       /* SBF_KIND_* */
     uint32_t specialized; /* 1 if a compile-time specialized kernel set serves it */
     uint64_t num_shards;  /* N, a power of two */
-    uint64_t filter_bytes; /* 32 * N */
+    uint64_t filter_bytes; /* 8 * words_per_shard * N */
+    uint32_t words_per_shard; /* 4, or 8 for SBF_KIND_WIDE */
 } sbf_info_t;
 
 /*
@@ -96,6 +98,18 @@ int sbf_create(sbf_t** out, uint32_t k, uint32_t m, uint32_t s, uint32_t H, uint
  */
 int sbf_create_bbf(sbf_t** out, uint32_t k, uint32_t H, uint64_t bits);
 
+/*
+ * Create an empty wide-block Super Bloom filter: the layout [cuSBF] §V-D
+ * attributes to the CPU Super Bloom reference.  Shards are 512-bit blocks
+ * (uint64_t[8N], N = smallest power of two >= ceil(bits / 512)), chosen by
+ * the minimizer as above; hash index t of an s-mer hash h_s addresses any of
+ * the block's 512 bits: a = bits [t*floor(64/H), +9) of h_s for H <= 7, the
+ * top 9 bits of h_s * S_t for H > 7; it sets bit a mod 64 of word a / 64.
+ * Same calls and parameter ranges as sbf_create; shard j of the copied filter
+ * is words 8j .. 8j+7.
+ */
+int sbf_create_wide(sbf_t** out, uint32_t k, uint32_t m, uint32_t s, uint32_t H, uint64_t bits);
+
 /* Free a filter and its buffers (synchronizes the device). NULL is a no-op. */
 int sbf_destroy(sbf_t* h);
 
@@ -106,9 +120,10 @@ int sbf_clear(sbf_t* h, void* stream);
 int sbf_info(const sbf_t* h, sbf_info_t* out);
 
 /*
- * Copy the raw filter words (uint64_t[4N], shard j = words 4j..4j+3) to dst.
- * flags = SBF_HOST: dst is host memory, synchronizes; SBF_DEVICE: device
- * memory, asynchronous on `stream`.  SBF_EINVAL if bytes < 32 * N.
+ * Copy the raw filter words (uint64_t[W*N], shard j = words Wj..Wj+W-1, W =
+ * words_per_shard) to dst.  flags = SBF_HOST: dst is host memory,
+ * synchronizes; SBF_DEVICE: device memory, asynchronous on `stream`.
+ * SBF_EINVAL if bytes < 8 * W * N.
  */
 int sbf_copy_filter(const sbf_t* h, void* dst, uint64_t bytes, uint32_t flags, void* stream);
 

@@ -78,12 +78,15 @@ def pack(ascii_dev, stream=None):
 
 class SuperBloomFilter:
     """A Super Bloom filter (or, with `blocked()`, the per-k-mer blocked Bloom
-    comparator) living in device memory."""
+    comparator; with `wide()`, the 512-bit whole-block variant) living in
+    device memory."""
 
     def __init__(self, k: int, m: int, s: int, H: int, bits: int, *, _kind: int = _lib.SBF_KIND_SBF):
         h = ctypes.c_void_p()
         if _kind == _lib.SBF_KIND_BBF:
             check(lib().sbf_create_bbf(ctypes.byref(h), k, H, bits), "sbf_create_bbf")
+        elif _kind == _lib.SBF_KIND_WIDE:
+            check(lib().sbf_create_wide(ctypes.byref(h), k, m, s, H, bits), "sbf_create_wide")
         else:
             check(lib().sbf_create(ctypes.byref(h), k, m, s, H, bits), "sbf_create")
         self._h = h
@@ -94,10 +97,16 @@ class SuperBloomFilter:
         self.specialized = bool(inf.specialized)
         self.num_shards = inf.num_shards
         self.filter_bytes = inf.filter_bytes
+        self.words_per_shard = inf.words_per_shard
 
     @classmethod
     def blocked(cls, k: int, H: int, bits: int) -> "SuperBloomFilter":
         return cls(k, 0, 0, H, bits, _kind=_lib.SBF_KIND_BBF)
+
+    @classmethod
+    def wide(cls, k: int, m: int, s: int, H: int, bits: int) -> "SuperBloomFilter":
+        """Wide-block variant: 512-bit blocks, each hash addressing the whole block."""
+        return cls(k, m, s, H, bits, _kind=_lib.SBF_KIND_WIDE)
 
     def close(self):
         if getattr(self, "_h", None) and self._h.value:
@@ -128,15 +137,15 @@ class SuperBloomFilter:
         check(lib().sbf_clear(self._h, _stream_ptr(stream)), "sbf_clear")
 
     def words(self) -> np.ndarray:
-        """Host copy of the filter words (uint64[4N]); synchronizes."""
-        out = np.empty(4 * self.num_shards, dtype=np.uint64)
+        """Host copy of the filter words (uint64[W*N], W = words_per_shard); synchronizes."""
+        out = np.empty(self.words_per_shard * self.num_shards, dtype=np.uint64)
         check(lib().sbf_copy_filter(self._h, out.ctypes.data, out.nbytes, SBF_HOST, None), "sbf_copy_filter")
         return out
 
     def words_device(self, stream=None):
         """Device copy of the filter words as an int64 tensor (asynchronous)."""
         torch = _torch()
-        out = torch.empty(4 * self.num_shards, dtype=torch.int64, device="cuda")
+        out = torch.empty(self.words_per_shard * self.num_shards, dtype=torch.int64, device="cuda")
         check(lib().sbf_copy_filter(self._h, out.data_ptr(), out.numel() * 8, SBF_DEVICE, _stream_ptr(stream)),
               "sbf_copy_filter")
         return out

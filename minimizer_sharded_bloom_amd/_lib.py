@@ -18,6 +18,7 @@ SBF_EDEVICE = -4
 SBF_EIO = -5
 SBF_KIND_SBF = 0
 SBF_KIND_BBF = 1
+SBF_KIND_WIDE = 2
 SBF_HOST = 1
 SBF_DEVICE = 2
 
@@ -25,7 +26,8 @@ SBF_DEVICE = 2
 class SbfInfo(ctypes.Structure):
     _fields_ = [("k", ctypes.c_uint32), ("m", ctypes.c_uint32), ("s", ctypes.c_uint32),
                 ("H", ctypes.c_uint32), ("kind", ctypes.c_uint32), ("specialized", ctypes.c_uint32),
-                ("num_shards", ctypes.c_uint64), ("filter_bytes", ctypes.c_uint64)]
+                ("num_shards", ctypes.c_uint64), ("filter_bytes", ctypes.c_uint64),
+                ("words_per_shard", ctypes.c_uint32)]
 
 
 class SbfFastxStats(ctypes.Structure):
@@ -38,6 +40,7 @@ _u32, _u64, _p, _int = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p, ctypes
 SIGNATURES = {
     "sbf_create": (_int, [ctypes.POINTER(_p), _u32, _u32, _u32, _u32, _u64]),
     "sbf_create_bbf": (_int, [ctypes.POINTER(_p), _u32, _u32, _u64]),
+    "sbf_create_wide": (_int, [ctypes.POINTER(_p), _u32, _u32, _u32, _u32, _u64]),
     "sbf_destroy": (_int, [_p]),
     "sbf_clear": (_int, [_p, _p]),
     "sbf_info": (_int, [_p, ctypes.POINTER(SbfInfo)]),

@@ -100,15 +100,17 @@ int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
         return fail(SBF_EINVAL, "out is NULL");
     if (P.k < 1 || P.k > 32)
         return fail(SBF_EINVAL, "k must be in 1..32");
-    if (P.kind == SBF_KIND_SBF && (P.m < 1 || P.m > P.k))
+    if (P.kind != SBF_KIND_BBF && (P.m < 1 || P.m > P.k))
         return fail(SBF_EINVAL, "m must be in 1..k");
-    if (P.kind == SBF_KIND_SBF && (P.s < 1 || P.s > P.k))
+    if (P.kind != SBF_KIND_BBF && (P.s < 1 || P.s > P.k))
         return fail(SBF_EINVAL, "s must be in 1..k");
     if (P.H < 1 || P.H > 64)
         return fail(SBF_EINVAL, "H must be in 1..64");
     if (bits < 1 || bits > (1ull << 40))
         return fail(SBF_EINVAL, "bits must be in 1..2^40");
-    const uint64_t need = (bits + 255) / 256;
+    const uint32_t wps = P.kind == SBF_KIND_WIDE ? 8u : 4u;
+    const uint64_t block = 64ull * wps;
+    const uint64_t need = (bits + block - 1) / block;
     uint64_t n = 1;
     while (n < need)
         n <<= 1;
@@ -118,6 +120,7 @@ int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
         return fail(SBF_ENOMEM, "host allocation failed");
     h->P = P;
     h->num_shards = n;
+    h->wps = wps;
     if (!sbf::find_specialized(P, &h->ks))
         h->ks = sbf::generic_kernels();
     hipError_t e = hipGetDevice(&h->device);
@@ -125,7 +128,7 @@ int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
         delete h;
         return fail_hip(e, "hipGetDevice");
     }
-    e = hipMalloc(reinterpret_cast<void**>(&h->d_filter), 32 * n);
+    e = hipMalloc(reinterpret_cast<void**>(&h->d_filter), 8ull * wps * n);
     if (e != hipSuccess) {
         delete h;
         return fail_hip(e, "hipMalloc(filter)");
@@ -136,7 +139,7 @@ int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
         delete h;
         return fail_hip(e, "hipMalloc(counter)");
     }
-    e = sbf::launch_fill_zero(h->d_filter, 4 * n, nullptr);
+    e = sbf::launch_fill_zero(h->d_filter, (uint64_t)wps * n, nullptr);
     if (e == hipSuccess)
         e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -210,6 +213,12 @@ int sbf_create_bbf(sbf_t** out, uint32_t k, uint32_t H, uint64_t bits)
     return create_impl(out, P, bits);
 }
 
+int sbf_create_wide(sbf_t** out, uint32_t k, uint32_t m, uint32_t s, uint32_t H, uint64_t bits)
+{
+    sbf::Params P{SBF_KIND_WIDE, k, m, s, H};
+    return create_impl(out, P, bits);
+}
+
 int sbf_destroy(sbf_t* h)
 {
     if (!h)
@@ -237,7 +246,7 @@ int sbf_clear(sbf_t* h, void* stream)
     int rc = set_device(h);
     if (rc)
         return rc;
-    hipError_t e = sbf::launch_fill_zero(h->d_filter, 4 * h->num_shards, (hipStream_t)stream);
+    hipError_t e = sbf::launch_fill_zero(h->d_filter, (uint64_t)h->wps * h->num_shards, (hipStream_t)stream);
     if (e != hipSuccess)
         return fail_hip(e, "clear launch");
     ok();
@@ -255,7 +264,8 @@ int sbf_info(const sbf_t* h, sbf_info_t* o)
     o->kind = h->P.kind;
     o->specialized = (uint32_t)h->ks.specialized;
     o->num_shards = h->num_shards;
-    o->filter_bytes = 32 * h->num_shards;
+    o->filter_bytes = 8ull * h->wps * h->num_shards;
+    o->words_per_shard = h->wps;
     ok();
     return SBF_OK;
 }
@@ -266,7 +276,8 @@ int sbf_copy_filter(const sbf_t* h, void* dst, uint64_t bytes, uint32_t flags, v
         return fail(SBF_EINVAL, "NULL argument");
     if (check_flags(flags))
         return SBF_EINVAL;
-    if (bytes < 32 * h->num_shards)
+    const uint64_t fbytes = 8ull * h->wps * h->num_shards;
+    if (bytes < fbytes)
         return fail(SBF_EINVAL, "destination smaller than the filter");
     int rc = set_device(h);
     if (rc)
@@ -274,11 +285,11 @@ int sbf_copy_filter(const sbf_t* h, void* dst, uint64_t bytes, uint32_t flags, v
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
     if (flags == SBF_HOST) {
-        e = hipMemcpyAsync(dst, h->d_filter, 32 * h->num_shards, hipMemcpyDeviceToHost, st);
+        e = hipMemcpyAsync(dst, h->d_filter, fbytes, hipMemcpyDeviceToHost, st);
         if (e == hipSuccess)
             e = hipStreamSynchronize(st);
     } else {
-        e = hipMemcpyAsync(dst, h->d_filter, 32 * h->num_shards, hipMemcpyDeviceToDevice, st);
+        e = hipMemcpyAsync(dst, h->d_filter, fbytes, hipMemcpyDeviceToDevice, st);
     }
     if (e != hipSuccess)
         return fail_hip(e, "copy filter");

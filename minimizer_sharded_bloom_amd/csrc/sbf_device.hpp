@@ -61,6 +61,26 @@ __device__ __forceinline__ uint32_t bit_addr_rt(uint64_t h, uint32_t t, uint32_t
     return (uint32_t)((h * salt_of(t)) >> 58);
 }
 
+// Wide-block variant: 9-bit address into a 512-bit block, slices of width
+// floor(64/H) for H <= 7, else the top 9 bits of h * salt_t.
+template <int H>
+__device__ __forceinline__ uint32_t bit_addr_wide(uint64_t h, int t)
+{
+    if constexpr (H <= 7) {
+        constexpr int width = 64 / H;
+        return (uint32_t)(h >> (t * width)) & 511u;
+    } else {
+        return (uint32_t)((h * salt_of((uint32_t)t)) >> 55);
+    }
+}
+
+__device__ __forceinline__ uint32_t bit_addr_wide_rt(uint64_t h, uint32_t t, uint32_t H)
+{
+    if (H <= 7)
+        return (uint32_t)(h >> (t * (64u / H))) & 511u;
+    return (uint32_t)((h * salt_of(t)) >> 55);
+}
+
 // Top 32 bits of the 64-bit value (a:b) shifted left by r, 0 <= r < 32.
 __device__ __forceinline__ uint32_t funnel_hi(uint32_t a, uint32_t b, uint32_t r)
 {

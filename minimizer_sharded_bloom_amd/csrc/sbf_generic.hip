@@ -164,36 +164,58 @@ __device__ __forceinline__ uint32_t kmer_shard(uint64_t x, const Params& P, uint
     return (uint32_t)mn & shard_mask;
 }
 
-__device__ __forceinline__ void kmer_masks(uint64_t x, const Params& P, uint64_t (&mk)[4])
+// Words per shard: 8 for the wide-block variant (kind 2), else 4.
+__device__ __forceinline__ uint32_t shard_words(const Params& P) { return P.kind == 2 ? 8u : 4u; }
+
+// Bits of one hash value: word t mod 4 (sectorized kinds) or, for the wide
+// variant, bit a mod 64 of word a / 64 for the 9-bit address a
+// ([cuSBF] §V-D, the CPU reference's whole-block addressing).
+__device__ __forceinline__ void hash_bits(uint64_t h, const Params& P, uint64_t (&mk)[8])
 {
-    mk[0] = mk[1] = mk[2] = mk[3] = 0;
-    if (P.kind == 1) {
-        const uint64_t hb = hash_s(hash_s(x));
-        for (uint32_t t = 0; t < P.H; ++t)
-            mk[t & 3] |= 1ull << bit_addr_rt(hb, t, P.H);
-        return;
-    }
-    for (uint32_t j = 0; j + P.s <= P.k; ++j) {
-        const uint64_t h = hash_s(sub_rt(x, P.k, j, P.s));
-        for (uint32_t t = 0; t < P.H; ++t)
-            mk[t & 3] |= 1ull << bit_addr_rt(h, t, P.H);
+    for (uint32_t t = 0; t < P.H; ++t) {
+        if (P.kind == 2) {
+            const uint32_t a = bit_addr_wide_rt(h, t, P.H);
+            const uint64_t bit = 1ull << (a & 63u);
+#pragma unroll
+            for (uint32_t w = 0; w < 8; ++w)
+                mk[w] |= (a >> 6) == w ? bit : 0ull;
+        } else {
+            const uint64_t bit = 1ull << bit_addr_rt(h, t, P.H);
+#pragma unroll
+            for (uint32_t w = 0; w < 4; ++w)
+                mk[w] |= (t & 3u) == w ? bit : 0ull;
+        }
     }
 }
 
+__device__ __forceinline__ void kmer_masks(uint64_t x, const Params& P, uint64_t (&mk)[8])
+{
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+        mk[w] = 0;
+    if (P.kind == 1) {
+        hash_bits(hash_s(hash_s(x)), P, mk);
+        return;
+    }
+    for (uint32_t j = 0; j + P.s <= P.k; ++j)
+        hash_bits(hash_s(sub_rt(x, P.k, j, P.s)), P, mk);
+}
+
 // One k-mer per lane, 64 k-mers per wave step.  Each lane stages its shard
-// and four masks in LDS; then four adjacent lanes OR the four words of one
-// record into the filter in one instruction, which the memory system merges
-// into one request per k-mer instead of four.
+// and masks in LDS; then W adjacent lanes (W = words per shard) OR the W
+// words of one record into the filter in one instruction, which the memory
+// system merges into one request per k-mer instead of W.
 __global__ __launch_bounds__(256) void generic_insert_kernel(SeqArgs a, Params P)
 {
     __shared__ uint32_t rec_idx[4][64];
-    __shared__ uint64_t rec_words[4][64][4];
+    __shared__ uint64_t rec_words[4][64][8];
     const uint32_t lane = threadIdx.x & 63u, wv = threadIdx.x >> 6;
+    const uint32_t W = shard_words(P), lw = W == 8 ? 3u : 2u;
     const uint64_t nk_pad = (a.nk + 63) & ~63ull;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t p0 = (uint64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63u); p0 < nk_pad; p0 += stride) {
         const uint64_t p = p0 + lane;
-        uint64_t mk[4] = {0, 0, 0, 0};
+        uint64_t mk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         uint32_t sh = 0;
         if (p < a.nk && kmer_valid_at(a.valid, a.nvw, p, P.k)) {
             const uint64_t x = kmer_at(a.codes, a.ncw, p, P.k);
@@ -201,26 +223,30 @@ __global__ __launch_bounds__(256) void generic_insert_kernel(SeqArgs a, Params P
             kmer_masks(x, P, mk);
         }
         rec_idx[wv][lane] = sh;
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 8; ++q)
             rec_words[wv][lane][q] = mk[q];
         wave_lds_sync();
-        for (uint32_t j = 0; j < 4; ++j) {
-            const uint32_t r = (lane >> 2) + 16u * j, q = lane & 3u;
+        for (uint32_t j = 0; j < W; ++j) {
+            const uint32_t r = (lane >> lw) + (64u >> lw) * j, q = lane & (W - 1u);
             const uint64_t m = rec_words[wv][r][q];
             if (m)
-                atomic_or_u64(a.filter + 4ull * rec_idx[wv][r] + q, m);
+                atomic_or_u64(a.filter + (uint64_t)W * rec_idx[wv][r] + q, m);
         }
         wave_lds_sync();  // the next step overwrites the records
     }
 }
 
-// Every query mask bit must be set in the shard.
-__device__ __forceinline__ bool shard_has(const uint64_t* __restrict__ filter, uint32_t sh, const uint64_t (&mk)[4])
+// Every query mask bit must be set in the shard (W words).
+__device__ __forceinline__ bool shard_has(const uint64_t* __restrict__ filter, uint32_t sh, const uint64_t (&mk)[8],
+                                          uint32_t W)
 {
-    uint64_t w[4];
-    load_shard(filter, sh, w);
-    return ((w[0] & mk[0]) == mk[0]) & ((w[1] & mk[1]) == mk[1]) & ((w[2] & mk[2]) == mk[2]) &
-           ((w[3] & mk[3]) == mk[3]);
+    const ulonglong2* p = reinterpret_cast<const ulonglong2*>(filter + (uint64_t)W * sh);
+    bool ok = true;
+    for (uint32_t i = 0; i < W / 2; ++i) {
+        const ulonglong2 v = p[i];
+        ok &= ((v.x & mk[2 * i]) == mk[2 * i]) & ((v.y & mk[2 * i + 1]) == mk[2 * i + 1]);
+    }
+    return ok;
 }
 
 // One k-mer per lane; grid-stride over 64-aligned groups so each wave's
@@ -234,9 +260,9 @@ __global__ __launch_bounds__(256) void generic_query_kernel(SeqArgs a, Params P)
         bool pres = false;
         if (p < a.nk && kmer_valid_at(a.valid, a.nvw, p, P.k)) {
             const uint64_t x = kmer_at(a.codes, a.ncw, p, P.k);
-            uint64_t mk[4];
+            uint64_t mk[8];
             kmer_masks(x, P, mk);
-            pres = shard_has(a.filter, kmer_shard(x, P, a.shard_mask), mk);
+            pres = shard_has(a.filter, kmer_shard(x, P, a.shard_mask), mk, shard_words(P));
         }
         const uint64_t word = __ballot(pres);
         if ((threadIdx.x & 63u) == 0)
@@ -250,9 +276,9 @@ __global__ __launch_bounds__(256) void generic_probe_kernel(ProbeArgs a, Params 
     uint32_t cnt = 0;
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += stride) {
         const uint64_t x = splitmix_fin(a.seed + (i + 1) * kGolden) >> (64 - 2 * P.k);
-        uint64_t mk[4];
+        uint64_t mk[8];
         kmer_masks(x, P, mk);
-        cnt += shard_has(a.filter, kmer_shard(x, P, a.shard_mask), mk);
+        cnt += shard_has(a.filter, kmer_shard(x, P, a.shard_mask), mk, shard_words(P));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)

@@ -36,6 +36,7 @@ struct HostStaging {
 struct sbf_handle {
     sbf::Params P;
     uint64_t num_shards;
+    uint32_t wps;  // 64-bit words per shard: 4, or 8 for the wide-block variant
     uint64_t* d_filter;
     sbf::KernelSet ks;
     int device;

@@ -23,12 +23,15 @@ def gpu_filter(params, bits, kind="sbf"):
     k, m, s, H = params
     if kind == "bbf":
         return M.SuperBloomFilter.blocked(k, H, bits)
+    if kind == "wide":
+        return M.SuperBloomFilter.wide(k, m, s, H, bits)
     return M.SuperBloomFilter(k, m, s, H, bits)
 
 
 def oracle_filter(params, bits, kind="sbf"):
     k, m, s, H = params
-    return O.OracleFilter(k, m, s, H, bits, kind=O.KIND_BBF if kind == "bbf" else O.KIND_SBF)
+    kinds = {"sbf": O.KIND_SBF, "bbf": O.KIND_BBF, "wide": O.KIND_WIDE}
+    return O.OracleFilter(k, m, s, H, bits, kind=kinds[kind])
 
 
 def dev_bits_to_np(t) -> np.ndarray:

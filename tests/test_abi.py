@@ -80,3 +80,12 @@ def test_packed_words(lib):
     for n, c, v in [(0, 0, 0), (1, 1, 1), (16, 1, 1), (17, 2, 1), (32, 2, 1), (33, 3, 2), (10**10, 625000000, 312500000)]:
         lib.sbf_packed_words(n, ctypes.byref(cw), ctypes.byref(vw))
         assert (cw.value, vw.value) == (c, v)
+
+
+def test_wide_rejects_bad_parameters(lib):
+    h = ctypes.c_void_p(0)
+    assert lib.sbf_create_wide(ctypes.byref(h), 31, 32, 28, 4, 512) == _lib.SBF_EINVAL
+    assert lib.sbf_create_wide(ctypes.byref(h), 31, 16, 0, 4, 512) == _lib.SBF_EINVAL
+    assert lib.sbf_create_wide(ctypes.byref(h), 31, 16, 28, 65, 512) == _lib.SBF_EINVAL
+    assert lib.sbf_create_wide(ctypes.byref(h), 31, 16, 28, 4, 0) == _lib.SBF_EINVAL
+    assert h.value is None
