@@ -82,7 +82,7 @@ CSRC = os.path.join(ROOT, "minimizer_sharded_bloom_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-KERNEL_HEADERS = ("sbf_device.hpp", "sbf_internal.hpp", "sbf_spec.hpp", "sbf_spec_list.hpp")
+KERNEL_HEADERS = ("sbf_device.hpp", "sbf_internal.hpp", "sbf_spec.hpp", "sbf_spec_list.hpp", "sbf_wide.hpp")
 
 
 def kernel_sources_sha256() -> str:

@@ -28,3 +28,10 @@
 #define SBF_SLICE_M_B(X) X(31, 17, 28, 4) X(31, 18, 28, 4) X(31, 19, 28, 4) X(31, 21, 28, 4) X(31, 22, 28, 4) X(31, 23, 28, 4) X(31, 24, 28, 4)
 #define SBF_SLICE_M_C(X) X(31, 25, 28, 4) X(31, 26, 28, 4) X(31, 27, 28, 4) X(31, 28, 28, 4) X(31, 29, 28, 4) X(31, 30, 28, 4) X(31, 31, 28, 4)
 #define SBF_SLICE_H(X) X(31, 16, 28, 1) X(31, 16, 28, 5) X(31, 16, 28, 8) X(31, 16, 28, 16)
+
+// Wide-block variant (512-bit blocks, whole-block addressing): the operating
+// point and its neighbours in s, H and m.
+#define SBF_WIDE(X)                                                                                               \
+    X(31, 16, 28, 4) X(31, 16, 24, 4) X(31, 16, 26, 4) X(31, 16, 30, 4) X(31, 16, 28, 2) X(31, 16, 28, 3)          \
+    X(31, 16, 28, 6) X(31, 16, 28, 8) X(31, 12, 28, 4) X(31, 20, 28, 4) X(31, 16, 24, 2) X(31, 12, 30, 6)          \
+    X(21, 11, 19, 3) X(32, 16, 28, 4) X(9, 5, 6, 12) X(31, 8, 28, 4) X(31, 31, 28, 4)

@@ -7,7 +7,8 @@ For every (s, m, H) in {24,26,28,30} x {12,16,20} x {2,3,4,6} at k = 31 and
 2^30 bits: insert the 50 Mbp synthetic genome of workload 4, query its 1 M
 reads, and count positives among 10^7 random 31-mers.  The blocked Bloom
 comparator (one hash picks a 256-bit block, H bits from a second hash) runs
-at the same budget for H in {2,3,4,6}.  Prints one JSON line per point and a
+at the same budget for H in {2,3,4,6}, and the wide-block variant (512-bit
+blocks, whole-block addressing; §V-D) at ten points around (28, 16, 4).  Prints one JSON line per point and a
 summary table.  With --grid: the slices of the wider grid (Fig. 4) through
 the operating point -- s = 16..31 at (m, H) = (16, 4), m = 8..31 at
 (s, H) = (28, 4), H in {1,2,3,4,5,6,8,12,16} at (m, s) = (16, 28).
@@ -108,6 +109,10 @@ def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, grid: bool
     for H in H_VALUES:
         with SuperBloomFilter.blocked(K, H, BITS) as f:
             point(f, {"kind": "bbf", "s": None, "m": None, "H": H})
+    for m, s, H in [(16, 24, 4), (16, 26, 4), (16, 28, 4), (16, 30, 4), (16, 28, 2), (16, 28, 3), (16, 28, 6),
+                    (16, 28, 8), (12, 28, 4), (20, 28, 4)]:
+        with SuperBloomFilter.wide(K, m, s, H, BITS) as f:
+            point(f, {"kind": "wide", "s": s, "m": m, "H": H})
     return rows
 
 

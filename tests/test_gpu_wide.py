@@ -63,3 +63,13 @@ def test_wide_config4_full():
     s = G.gpu_filter((31, 16, 28, 4), w["bits"])
     s.insert_seq(G.to_dev(w["insert"]))
     assert hw < s.fpr_probe(n, 0x5EED)
+
+
+def test_wide_overflow_paths():
+    """m = k: every k-mer is its own segment, so every wave has more segments
+    than LDS records and takes the per-k-mer paths of insert and query."""
+    rng = np.random.default_rng(71)
+    ins = [T.random_dna(rng, L) for L in (5000, 20011)]
+    qs = [T.random_dna(rng, 9000)] + ins
+    g, _ = _pair((31, 31, 28, 4), 2**16, ins, qs)
+    assert g.specialized
