@@ -170,7 +170,14 @@ def cpu_baseline(w: dict, budget_s: float) -> dict:
     f.fpr_probe(n_p, 0x5EED)
     t3 = time.perf_counter()
     kmers = (n_ins - K + 1) + (n_q - K + 1) + n_p
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": kmers / (t3 - t0) / 1e9, "unit": "Gk-mers/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
             "sample": "C oracle, %d threads: insert of the first %d genome bases, query of the first %d read "
                       "bases, %d probe k-mers on one thread (%.1f s)" % (cores, n_ins, n_q, n_p, t3 - t0),
             "insert_gkmers_s": (n_ins - K + 1) / (t1 - t0) / 1e9,
