@@ -22,6 +22,10 @@ KIND_SBF = 0
 KIND_BBF = 1
 KIND_WIDE = 2  # 512-bit blocks, each hash addressing the whole block
 
+ALPHA_DNA = 0      # A C G T, 2 bits per symbol
+ALPHA_PROTEIN = 1  # letters A-Z, 5 bits per symbol
+ALPHA_TRIPLET = 2  # non-overlapping DNA codons, 6 bits per symbol
+
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (plain -O2, no vectorisation flags)."""
@@ -63,6 +67,18 @@ def lib():
         L.osbf_minimizer_hash.restype = u64
         L.osbf_create.argtypes = [ctypes.c_int, u32, u32, u32, u32, u64]
         L.osbf_create.restype = p
+        L.osbf_create_alpha.argtypes = [ctypes.c_int, u32, u32, u32, u32, u32, u64]
+        L.osbf_create_alpha.restype = p
+        L.osbf_code_protein.argtypes = [ctypes.c_ubyte]
+        L.osbf_code_protein.restype = ctypes.c_int
+        L.osbf_code_triplet.argtypes = [ctypes.c_char_p]
+        L.osbf_code_triplet.restype = ctypes.c_int
+        L.osbf_symbol_bits.argtypes = [u32]
+        L.osbf_symbol_bits.restype = u32
+        L.osbf_pack_kmer_alpha.argtypes = [u32, p, u64, u32, ctypes.POINTER(u64)]
+        L.osbf_pack_kmer_alpha.restype = ctypes.c_int
+        L.osbf_probe_kmer_alpha.argtypes = [u32, u64, u64, u32]
+        L.osbf_probe_kmer_alpha.restype = u64
         L.osbf_destroy.argtypes = [p]
         L.osbf_destroy.restype = None
         L.osbf_num_shards.argtypes = [p]
@@ -146,6 +162,39 @@ def pack_kmer(s) -> int | None:
     return None if rc != 0 else x.value
 
 
+def code_protein(c) -> int:
+    if isinstance(c, str):
+        c = ord(c)
+    return lib().osbf_code_protein(c)
+
+
+def code_triplet(codon) -> int:
+    if isinstance(codon, str):
+        codon = codon.encode("ascii")
+    assert len(codon) == 3
+    return lib().osbf_code_triplet(codon)
+
+
+def symbol_bits(alpha: int) -> int:
+    return lib().osbf_symbol_bits(alpha)
+
+
+def pack_kmer_alpha(alpha: int, seq, p: int, k: int) -> int | None:
+    """k symbols from symbol p of seq, packed first-most-significant."""
+    arr, ptr = _buf(seq)
+    x = ctypes.c_uint64(0)
+    rc = lib().osbf_pack_kmer_alpha(alpha, ptr, p, k, ctypes.byref(x))
+    return None if rc != 0 else x.value
+
+
+def probe_kmer_alpha(alpha: int, seed: int, i: int, k: int) -> int:
+    return lib().osbf_probe_kmer_alpha(alpha, seed & (2**64 - 1), i, k)
+
+
+def n_symbols(alpha: int, nbytes: int) -> int:
+    return nbytes // 3 if alpha == ALPHA_TRIPLET else nbytes
+
+
 def subwindow(x: int, k: int, i: int, w: int) -> int:
     return lib().osbf_subwindow(x, k, i, w)
 
@@ -173,12 +222,16 @@ class OracleFilter:
     (KIND_WIDE) or a per-k-mer blocked Bloom filter (KIND_BBF) held in host
     memory by the C oracle."""
 
-    def __init__(self, k, m, s, H, bits, kind=KIND_SBF):
-        self.k, self.m, self.s, self.H, self.kind = k, m, s, H, kind
-        self._h = lib().osbf_create(kind, k, m, s, H, bits)
+    def __init__(self, k, m, s, H, bits, kind=KIND_SBF, alpha=ALPHA_DNA):
+        self.k, self.m, self.s, self.H, self.kind, self.alpha = k, m, s, H, kind, alpha
+        self._h = lib().osbf_create_alpha(kind, alpha, k, m, s, H, bits)
         if not self._h:
-            raise ValueError("oracle: invalid parameters (k=%d m=%d s=%d H=%d bits=%d)"
-                             % (k, m, s, H, bits))
+            raise ValueError("oracle: invalid parameters (alphabet=%d k=%d m=%d s=%d H=%d bits=%d)"
+                             % (alpha, k, m, s, H, bits))
+
+    def _nk(self, nbytes: int) -> int:
+        """k-mer starts in a sequence of nbytes bytes."""
+        return max(0, n_symbols(self.alpha, nbytes) - self.k + 1)
 
     def close(self):
         if self._h:
@@ -215,9 +268,9 @@ class OracleFilter:
         lib().osbf_insert_seq(self._h, ptr, arr.size)
 
     def query_seq(self, seq) -> np.ndarray:
-        """uint64 bit words, bit p = answer for the k-mer starting at p."""
+        """uint64 bit words, bit p = answer for the k-mer starting at symbol p."""
         arr, ptr = _buf(seq)
-        nk = max(0, arr.size - self.k + 1)
+        nk = self._nk(arr.size)
         out = np.zeros((nk + 63) // 64, dtype=np.uint64)
         if nk:
             lib().osbf_query_seq(self._h, ptr, arr.size, out.ctypes.data)
@@ -230,7 +283,7 @@ class OracleFilter:
 
     def query_seq_mt(self, seq, nthreads: int = 0) -> np.ndarray:
         arr, ptr = _buf(seq)
-        nk = max(0, arr.size - self.k + 1)
+        nk = self._nk(arr.size)
         out = np.zeros((nk + 63) // 64, dtype=np.uint64)
         if nk:
             lib().osbf_query_seq_mt(self._h, ptr, arr.size, out.ctypes.data, _threads(nthreads))
@@ -244,7 +297,7 @@ class OracleFilter:
     def query_seq_sampled_mt(self, seq, sample_mask: int, sample_value: int, nthreads: int = 0):
         """(answers, checked) bit words over the k-mers of sampled shards."""
         arr, ptr = _buf(seq)
-        nk = max(0, arr.size - self.k + 1)
+        nk = self._nk(arr.size)
         out = np.zeros((nk + 63) // 64, dtype=np.uint64)
         checked = np.zeros_like(out)
         if nk:

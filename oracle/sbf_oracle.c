@@ -39,6 +39,16 @@
  *  - Probe k-mers: the i-th output of the SplitMix64 stream seeded with
  *    `seed`, mix(seed + (i+1) * G), shifted right by 64-2k
  *    ([cuSBF] §V-D measures the FPR on uniformly random k-mers).
+ *  - Other alphabets ([cuSBF] §IV-A: proteins, 26 symbols of 5 bits; DNA
+ *    triplets, 64 symbols of 6 bits spanning 3 bytes): a protein symbol is a
+ *    letter A-Z or a-z, code = its place in the alphabet (0..25); a triplet
+ *    symbol is the codon at bytes 3j .. 3j+2 (non-overlapping, from the first
+ *    byte), code = 16 c0 + 4 c1 + c2 with the DNA codes above, invalid if any
+ *    of its bases is.  k-mers, m-mers and s-mers count symbols; a k-mer packs
+ *    its symbols first-most-significant at b bits each (b = 2, 5, 6), so
+ *    k * b <= 64.  Probe k-mers: triplets take the top 6k bits of the
+ *    SplitMix64 output as for DNA; a protein k-mer's symbol j is
+ *    floor(26 u / 2^64), u = mix(seed + (i k + j + 1) * G).
  */
 #include "sbf_oracle.h"
 
@@ -52,6 +62,7 @@
 
 struct osbf {
     int kind;
+    unsigned alpha, b; /* alphabet, bits per symbol */
     unsigned k, m, s, H;
     uint64_t num_shards;
     uint64_t* words;
@@ -90,6 +101,56 @@ uint64_t osbf_hs(uint64_t v)
     return osbf_mix(v + GOLDEN);
 }
 
+/* [cuSBF] §IV-A: proteins, 26 letters, 5 bits each. */
+int osbf_code_protein(unsigned char c)
+{
+    if (c >= 'A' && c <= 'Z')
+        return c - 'A';
+    if (c >= 'a' && c <= 'z')
+        return c - 'a';
+    return -1;
+}
+
+/* [cuSBF] §IV-A: DNA triplets, 64 symbols of 6 bits, one codon of 3 bytes. */
+int osbf_code_triplet(const char* p)
+{
+    int c0 = osbf_code((unsigned char)p[0]), c1 = osbf_code((unsigned char)p[1]), c2 = osbf_code((unsigned char)p[2]);
+    if (c0 < 0 || c1 < 0 || c2 < 0)
+        return -1;
+    return 16 * c0 + 4 * c1 + c2;
+}
+
+unsigned osbf_symbol_bits(unsigned alpha) { return alpha == OSBF_ALPHA_PROTEIN ? 5u : alpha == OSBF_ALPHA_TRIPLET ? 6u : 2u; }
+
+/* Symbols in a sequence of len bytes. */
+static uint64_t n_symbols(unsigned alpha, uint64_t len) { return alpha == OSBF_ALPHA_TRIPLET ? len / 3u : len; }
+
+/* Code of symbol j, or -1 if invalid. */
+static int symbol_at(unsigned alpha, const char* seq, uint64_t j)
+{
+    if (alpha == OSBF_ALPHA_PROTEIN)
+        return osbf_code_protein((unsigned char)seq[j]);
+    if (alpha == OSBF_ALPHA_TRIPLET)
+        return osbf_code_triplet(seq + 3u * j);
+    return osbf_code((unsigned char)seq[j]);
+}
+
+/* Pack the k symbols starting at symbol p (first most significant, b bits
+ * each).  0 and *x on success, -1 if a symbol is invalid. */
+int osbf_pack_kmer_alpha(unsigned alpha, const char* seq, uint64_t p, unsigned k, uint64_t* x)
+{
+    const unsigned b = osbf_symbol_bits(alpha);
+    uint64_t v = 0;
+    for (unsigned j = 0; j < k; ++j) {
+        int c = symbol_at(alpha, seq, p + j);
+        if (c < 0)
+            return -1;
+        v = (v << b) | (uint64_t)c;
+    }
+    *x = v;
+    return 0;
+}
+
 /* [cuSBF] §IV-G, bit-slicing and the salted fallback. */
 unsigned osbf_bitaddr(uint64_t hs, unsigned t, unsigned H)
 {
@@ -120,9 +181,32 @@ uint64_t osbf_probe_kmer(uint64_t seed, uint64_t i, unsigned k)
     return r >> (64u - 2u * k);
 }
 
+/* Probe k-mer i for any alphabet (see the readings above). */
+uint64_t osbf_probe_kmer_alpha(unsigned alpha, uint64_t seed, uint64_t i, unsigned k)
+{
+    if (alpha == OSBF_ALPHA_PROTEIN) {
+        uint64_t x = 0;
+        for (unsigned j = 0; j < k; ++j) {
+            uint64_t u = osbf_mix(seed + ((uint64_t)i * k + j + 1ull) * GOLDEN);
+            x = (x << 5) | (uint64_t)(((unsigned __int128)u * 26u) >> 64);
+        }
+        return x;
+    }
+    const unsigned bits = osbf_symbol_bits(alpha) * k;
+    uint64_t r = osbf_mix(seed + (i + 1ull) * GOLDEN);
+    return bits >= 64 ? r : r >> (64u - bits);
+}
+
 static uint64_t low_mask(unsigned nbases)
 {
     return nbases >= 32 ? ~0ull : ((1ull << (2u * nbases)) - 1ull);
+}
+
+/* Window of w symbols starting at symbol i of a packed k-mer, b bits each. */
+static uint64_t sub_b(uint64_t x, unsigned k, unsigned i, unsigned w, unsigned b)
+{
+    const unsigned bits = b * w;
+    return (x >> (b * (k - w - i))) & (bits >= 64 ? ~0ull : ((1ull << bits) - 1ull));
 }
 
 /* [cuSBF] §IV-C: pack k symbols into one 64-bit word by shift-and-OR. */
@@ -160,9 +244,16 @@ uint64_t osbf_minimizer_hash(uint64_t x, unsigned k, unsigned m)
 
 osbf* osbf_create(int kind, unsigned k, unsigned m, unsigned s, unsigned H, uint64_t bits)
 {
+    return osbf_create_alpha(kind, OSBF_ALPHA_DNA, k, m, s, H, bits);
+}
+
+osbf* osbf_create_alpha(int kind, unsigned alpha, unsigned k, unsigned m, unsigned s, unsigned H, uint64_t bits)
+{
     if (kind != OSBF_KIND_SBF && kind != OSBF_KIND_BBF && kind != OSBF_KIND_WIDE)
         return NULL;
-    if (k < 1 || k > 32 || H < 1 || H > 64 || bits < 1)
+    if (alpha > OSBF_ALPHA_TRIPLET)
+        return NULL;
+    if (k < 1 || k * osbf_symbol_bits(alpha) > 64 || H < 1 || H > 64 || bits < 1)
         return NULL;
     if (kind != OSBF_KIND_BBF && (m < 1 || m > k || s < 1 || s > k))
         return NULL;
@@ -181,6 +272,8 @@ osbf* osbf_create(int kind, unsigned k, unsigned m, unsigned s, unsigned H, uint
         return NULL;
     }
     f->kind = kind;
+    f->alpha = alpha;
+    f->b = osbf_symbol_bits(alpha);
     f->k = k;
     f->m = m;
     f->s = s;
@@ -207,7 +300,13 @@ uint64_t osbf_shard_of(const osbf* f, uint64_t x)
 {
     if (f->kind == OSBF_KIND_BBF)
         return osbf_hs(x) & (f->num_shards - 1u);
-    return osbf_minimizer_hash(x, f->k, f->m) & (f->num_shards - 1u);
+    uint64_t best = ~0ull;
+    for (unsigned i = 0; i + f->m <= f->k; ++i) {
+        uint64_t h = osbf_hmin(sub_b(x, f->k, i, f->m, f->b));
+        if (h < best)
+            best = h;
+    }
+    return best & (f->num_shards - 1u);
 }
 
 /* [cuSBF] §IV-B: hash index t sets one bit in word t mod 4 of the shard;
@@ -249,7 +348,7 @@ void osbf_insert_kmer(osbf* f, uint64_t x)
         return;
     }
     for (unsigned j = 0; j + f->s <= f->k; ++j)
-        set_bits(f, shard, osbf_hs(osbf_subwindow(x, f->k, j, f->s)));
+        set_bits(f, shard, osbf_hs(sub_b(x, f->k, j, f->s, f->b)));
 }
 
 /* [cuSBF] §II-B-2 and Algorithm 2 (Contains): present only if every s-mer
@@ -260,7 +359,7 @@ int osbf_query_kmer(const osbf* f, uint64_t x)
     if (f->kind == OSBF_KIND_BBF)
         return test_bits(f, shard, osbf_hs(osbf_hs(x)));
     for (unsigned j = 0; j + f->s <= f->k; ++j)
-        if (!test_bits(f, shard, osbf_hs(osbf_subwindow(x, f->k, j, f->s))))
+        if (!test_bits(f, shard, osbf_hs(sub_b(x, f->k, j, f->s, f->b))))
             return 0;
     return 1;
 }
@@ -268,11 +367,12 @@ int osbf_query_kmer(const osbf* f, uint64_t x)
 /* [cuSBF] §IV-D / §IV-F: every k-mer start; invalid k-mers are skipped. */
 void osbf_insert_seq(osbf* f, const char* seq, uint64_t len)
 {
-    if (len < f->k)
+    const uint64_t ns = n_symbols(f->alpha, len);
+    if (ns < f->k)
         return;
-    for (uint64_t p = 0; p + f->k <= len; ++p) {
+    for (uint64_t p = 0; p + f->k <= ns; ++p) {
         uint64_t x;
-        if (osbf_pack_kmer(seq + p, f->k, &x) == 0)
+        if (osbf_pack_kmer_alpha(f->alpha, seq, p, f->k, &x) == 0)
             osbf_insert_kmer(f, x);
     }
 }
@@ -280,13 +380,14 @@ void osbf_insert_seq(osbf* f, const char* seq, uint64_t len)
 /* [cuSBF] §IV-E: one answer per k-mer start, invalid k-mers answer false. */
 void osbf_query_seq(const osbf* f, const char* seq, uint64_t len, uint64_t* out)
 {
-    if (len < f->k)
+    const uint64_t ns = n_symbols(f->alpha, len);
+    if (ns < f->k)
         return;
-    uint64_t nk = len - f->k + 1u;
+    uint64_t nk = ns - f->k + 1u;
     memset(out, 0, ((nk + 63u) / 64u) * sizeof(uint64_t));
     for (uint64_t p = 0; p < nk; ++p) {
         uint64_t x;
-        if (osbf_pack_kmer(seq + p, f->k, &x) == 0 && osbf_query_kmer(f, x))
+        if (osbf_pack_kmer_alpha(f->alpha, seq, p, f->k, &x) == 0 && osbf_query_kmer(f, x))
             out[p / 64u] |= 1ull << (p % 64u);
     }
 }
@@ -298,7 +399,7 @@ void osbf_query_positions(const osbf* f, const char* seq, uint64_t len,
         uint64_t x;
         uint64_t p = pos[i];
         out[i] = 0;
-        if (p + f->k <= len && osbf_pack_kmer(seq + p, f->k, &x) == 0)
+        if (p + f->k <= n_symbols(f->alpha, len) && osbf_pack_kmer_alpha(f->alpha, seq, p, f->k, &x) == 0)
             out[i] = (uint8_t)osbf_query_kmer(f, x);
     }
 }
@@ -308,7 +409,7 @@ uint64_t osbf_fpr_probe(const osbf* f, uint64_t n, uint64_t seed)
 {
     uint64_t hits = 0;
     for (uint64_t i = 0; i < n; ++i)
-        hits += (uint64_t)osbf_query_kmer(f, osbf_probe_kmer(seed, i, f->k));
+        hits += (uint64_t)osbf_query_kmer(f, osbf_probe_kmer_alpha(f->alpha, seed, i, f->k));
     return hits;
 }
 
@@ -346,7 +447,7 @@ static void* insert_worker(void* arg)
     osbf* f = j->f;
     for (uint64_t p = j->p0; p < j->p1; ++p) {
         uint64_t x;
-        if (osbf_pack_kmer(j->seq + p, f->k, &x) != 0)
+        if (osbf_pack_kmer_alpha(f->alpha, j->seq, p, f->k, &x) != 0)
             continue;
         uint64_t sh = osbf_shard_of(f, x);
         if ((sh & j->sample_mask) != j->sample_value)
@@ -357,7 +458,7 @@ static void* insert_worker(void* arg)
             continue;
         }
         for (unsigned s = 0; s + f->s <= f->k; ++s)
-            set_bits_atomic(f, shard, osbf_hs(osbf_subwindow(x, f->k, s, f->s)));
+            set_bits_atomic(f, shard, osbf_hs(sub_b(x, f->k, s, f->s, f->b)));
     }
     return NULL;
 }
@@ -367,7 +468,7 @@ static void* query_worker(void* arg)
     osbf_job* j = (osbf_job*)arg;
     for (uint64_t p = j->p0; p < j->p1; ++p) {
         uint64_t x;
-        if (osbf_pack_kmer(j->seq + p, j->f->k, &x) != 0)
+        if (osbf_pack_kmer_alpha(j->f->alpha, j->seq, p, j->f->k, &x) != 0)
             continue;
         if (j->checked) {
             if ((osbf_shard_of(j->f, x) & j->sample_mask) != j->sample_value)
@@ -383,7 +484,7 @@ static void* query_worker(void* arg)
 static void run_jobs(osbf* f, const char* seq, uint64_t len, uint64_t* out, uint64_t* checked,
                      uint64_t sample_mask, uint64_t sample_value, unsigned nthreads, void* (*fn)(void*))
 {
-    uint64_t nk = len - f->k + 1u;
+    uint64_t nk = n_symbols(f->alpha, len) - f->k + 1u;
     if (nthreads < 1)
         nthreads = 1;
     if (nthreads > 256)
@@ -421,16 +522,16 @@ static void run_jobs(osbf* f, const char* seq, uint64_t len, uint64_t* out, uint
 
 void osbf_insert_seq_mt(osbf* f, const char* seq, uint64_t len, unsigned nthreads)
 {
-    if (len < f->k)
+    if (n_symbols(f->alpha, len) < f->k)
         return;
     run_jobs(f, seq, len, NULL, NULL, 0, 0, nthreads, insert_worker);
 }
 
 void osbf_query_seq_mt(const osbf* f, const char* seq, uint64_t len, uint64_t* out, unsigned nthreads)
 {
-    if (len < f->k)
+    if (n_symbols(f->alpha, len) < f->k)
         return;
-    uint64_t nk = len - f->k + 1u;
+    uint64_t nk = n_symbols(f->alpha, len) - f->k + 1u;
     memset(out, 0, ((nk + 63u) / 64u) * sizeof(uint64_t));
     run_jobs((osbf*)f, seq, len, out, NULL, 0, 0, nthreads, query_worker);
 }
@@ -441,7 +542,7 @@ void osbf_query_seq_mt(const osbf* f, const char* seq, uint64_t len, uint64_t* o
 void osbf_insert_seq_sampled_mt(osbf* f, const char* seq, uint64_t len, uint64_t sample_mask,
                                 uint64_t sample_value, unsigned nthreads)
 {
-    if (len < f->k)
+    if (n_symbols(f->alpha, len) < f->k)
         return;
     run_jobs(f, seq, len, NULL, NULL, sample_mask, sample_value, nthreads, insert_worker);
 }
@@ -451,9 +552,9 @@ void osbf_insert_seq_sampled_mt(osbf* f, const char* seq, uint64_t len, uint64_t
 void osbf_query_seq_sampled_mt(const osbf* f, const char* seq, uint64_t len, uint64_t* out, uint64_t* checked,
                                uint64_t sample_mask, uint64_t sample_value, unsigned nthreads)
 {
-    if (len < f->k)
+    if (n_symbols(f->alpha, len) < f->k)
         return;
-    uint64_t nk = len - f->k + 1u;
+    uint64_t nk = n_symbols(f->alpha, len) - f->k + 1u;
     memset(out, 0, ((nk + 63u) / 64u) * sizeof(uint64_t));
     memset(checked, 0, ((nk + 63u) / 64u) * sizeof(uint64_t));
     run_jobs((osbf*)f, seq, len, out, checked, sample_mask, sample_value, nthreads, query_worker);

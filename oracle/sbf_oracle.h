@@ -32,6 +32,11 @@ extern "C" {
 #define OSBF_KIND_BBF 1 /* per-k-mer blocked Bloom filter with the same shard layout */
 #define OSBF_KIND_WIDE 2 /* SBF with 512-bit blocks, each hash addressing the whole block */
 
+/* alphabet of the sequences ([cuSBF] §IV-A) */
+#define OSBF_ALPHA_DNA 0     /* A C G T, 2 bits per symbol */
+#define OSBF_ALPHA_PROTEIN 1 /* letters A-Z, 5 bits per symbol */
+#define OSBF_ALPHA_TRIPLET 2 /* non-overlapping DNA codons, 6 bits per symbol */
+
 typedef struct osbf osbf;
 
 /* ---- primitives (exposed for the pins) ---------------------------------- */
@@ -49,6 +54,19 @@ unsigned osbf_bitaddr_wide(uint64_t hs, unsigned t, unsigned H);
 /* i-th probe k-mer (0-based) of the stream started at `seed` */
 uint64_t osbf_probe_kmer(uint64_t seed, uint64_t i, unsigned k);
 
+/* protein code 0..25 of a letter (either case), or -1 */
+int osbf_code_protein(unsigned char c);
+/* triplet code 16 c0 + 4 c1 + c2 of the codon at p[0..2], or -1 */
+int osbf_code_triplet(const char* p);
+/* bits per symbol: 2, 5 or 6 */
+unsigned osbf_symbol_bits(unsigned alpha);
+/* Pack the k symbols starting at symbol p of seq (for triplets symbol j is
+ * bytes 3j..3j+2), first most significant, b bits each.  0 and *x, or -1 if
+ * a symbol is invalid. */
+int osbf_pack_kmer_alpha(unsigned alpha, const char* seq, uint64_t p, unsigned k, uint64_t* x);
+/* i-th probe k-mer for an alphabet (DNA: osbf_probe_kmer) */
+uint64_t osbf_probe_kmer_alpha(unsigned alpha, uint64_t seed, uint64_t i, unsigned k);
+
 /* Pack k bases starting at seq into a k-mer value, first base most
  * significant.  Returns 0 and sets *x if every base is valid, else -1. */
 int osbf_pack_kmer(const char* seq, unsigned k, uint64_t* x);
@@ -61,6 +79,10 @@ uint64_t osbf_minimizer_hash(uint64_t x, unsigned k, unsigned m);
 
 /* Returns NULL on invalid parameters or allocation failure. */
 osbf* osbf_create(int kind, unsigned k, unsigned m, unsigned s, unsigned H, uint64_t bits);
+/* The same for an alphabet; k, m and s count symbols, k * b <= 64.  The
+ * sequence calls below then take symbol positions: for triplets a sequence of
+ * len bytes holds floor(len / 3) symbols. */
+osbf* osbf_create_alpha(int kind, unsigned alpha, unsigned k, unsigned m, unsigned s, unsigned H, uint64_t bits);
 void osbf_destroy(osbf* f);
 uint64_t osbf_num_shards(const osbf* f);
 /* 4, or 8 for the wide variant */

@@ -78,3 +78,55 @@ def kmer_bits_wide_str(kmer: str, s: int, H: int):
             a = O.bitaddr_wide(h, t, H)
             out.add((a // 64, a % 64))
     return out
+
+
+# ---- other alphabets (§IV-A: proteins 5 bits, DNA triplets 6 bits) ----------
+
+BITS = {O.ALPHA_DNA: 2, O.ALPHA_PROTEIN: 5, O.ALPHA_TRIPLET: 6}
+
+
+def symbols_of(alpha: int, text: bytes) -> list:
+    """Symbol codes of a byte string, None for an invalid symbol.  Protein: a
+    letter's place in A..Z (either case); triplet: the codons at bytes 3j..3j+2
+    read as base-4 numbers of their bases; DNA: the base codes."""
+    if alpha == O.ALPHA_PROTEIN:
+        out = []
+        for c in text:
+            ch = chr(c)
+            out.append(ord(ch.upper()) - ord("A") if ch.isascii() and ch.isalpha() else None)
+        return out
+    if alpha == O.ALPHA_TRIPLET:
+        out = []
+        for j in range(len(text) // 3):
+            cod = text[3 * j:3 * j + 3].decode("latin-1")
+            out.append(pack_str(cod) if valid_str(cod) else None)
+        return out
+    return [CODE.get(chr(c)) for c in text]
+
+
+def pack_symbols(codes, b: int) -> int:
+    v = 0
+    for c in codes:
+        v = (v << b) | c
+    return v
+
+
+def kmer_bits_alpha(codes, alpha: int, s: int, H: int):
+    """{(sector, bit)} a k-mer of symbol codes sets, from its s-mers cut out
+    of the code list and packed on their own."""
+    b = BITS[alpha]
+    out = set()
+    for j in range(len(codes) - s + 1):
+        h = O.hs(pack_symbols(codes[j:j + s], b))
+        for t in range(H):
+            out.add((t % 4, O.bitaddr(h, t, H)))
+    return out
+
+
+def minimizer_hash_alpha(codes, alpha: int, m: int) -> int:
+    b = BITS[alpha]
+    return min(O.hmin(pack_symbols(codes[i:i + m], b)) for i in range(len(codes) - m + 1))
+
+
+def random_protein(rng: np.random.Generator, n: int, alphabet=b"ACDEFGHIKLMNPQRSTVWY") -> bytes:
+    return np.frombuffer(alphabet, dtype=np.uint8)[rng.integers(0, len(alphabet), n)].tobytes()

@@ -538,3 +538,181 @@ def test_wide_blocks_lower_fpr_than_sectors():
         rates[kind] = f.fpr_probe(400000, 77) / 400000
     assert rates[O.KIND_SBF] > 5e-4  # ~640 hits: the comparison is not noise
     assert rates[O.KIND_WIDE] < 0.5 * rates[O.KIND_SBF]
+
+
+# ---- other alphabets (§IV-A, §IV-C) -------------------------------------------
+
+def test_protein_code_table_exhaustive():
+    """§IV-A: 26 protein symbols of 5 bits; letters of either case map to
+    their place in the alphabet, every other byte is invalid."""
+    for c in range(256):
+        ch = chr(c)
+        want = ord(ch.upper()) - 65 if ch.isascii() and ch.isalpha() else -1
+        assert O.code_protein(c) == want, c
+    assert O.symbol_bits(O.ALPHA_PROTEIN) == 5 and max(O.code_protein(c) for c in range(256)) == 25
+
+
+def test_triplet_code_table_exhaustive():
+    """§IV-A: 64 triplet symbols of 6 bits spanning three bytes.  Every codon
+    over ACGTN (both cases) against 16 c0 + 4 c1 + c2; the valid ones form a
+    bijection onto 0..63."""
+    bases = "ACGTNacgtn"
+    seen = set()
+    for a in bases:
+        for b in bases:
+            for c in bases:
+                cod = a + b + c
+                got = O.code_triplet(cod)
+                if "N" in cod.upper():
+                    assert got == -1, cod
+                else:
+                    want = 16 * T.CODE[a] + 4 * T.CODE[b] + T.CODE[c]
+                    assert got == want, cod
+                    seen.add(got)
+    assert seen == set(range(64)) and O.symbol_bits(O.ALPHA_TRIPLET) == 6
+
+
+def test_alphabet_pack_known_answers():
+    """§IV-C: shift-and-OR packing at the symbol width.  Hand-computed values:
+    protein ACD = 0b00000_00010_00011 = 0x43; triplets AAA|CCC = 0*64 + 21.
+    A triplet k-mer packs to the same integer as the 3k bases it spans packed
+    as DNA (six bits = three 2-bit codes), at every codon start."""
+    assert O.pack_kmer_alpha(O.ALPHA_PROTEIN, b"ACD", 0, 3) == 0x43
+    assert O.pack_kmer_alpha(O.ALPHA_PROTEIN, b"acd", 0, 3) == 0x43
+    assert O.pack_kmer_alpha(O.ALPHA_PROTEIN, b"ZZZZZZZZZZZZ", 0, 12) == int("11001" * 12, 2)
+    assert O.pack_kmer_alpha(O.ALPHA_TRIPLET, b"AAACCC", 0, 2) == 21
+    assert O.pack_kmer_alpha(O.ALPHA_TRIPLET, b"TTTTTTTTTTTTTTTTTTTTTTTTTTTTTT", 0, 10) == 2**60 - 1
+    assert O.pack_kmer_alpha(O.ALPHA_PROTEIN, b"AC*D", 0, 4) is None
+    assert O.pack_kmer_alpha(O.ALPHA_TRIPLET, b"AAACNC", 0, 2) is None
+    rng = np.random.default_rng(40)
+    seq = T.random_dna(rng, 300)
+    for k in (1, 4, 10):
+        for p in range(0, 100 - k):
+            x = O.pack_kmer_alpha(O.ALPHA_TRIPLET, seq, p, k)
+            assert x == O.pack_kmer(seq[3 * p:3 * p + 3 * k]), (k, p)
+            assert x == O.pack_kmer_alpha(O.ALPHA_DNA, seq, 3 * p, 3 * k)
+
+
+@pytest.mark.parametrize("alpha,k,m,s,H", [(O.ALPHA_PROTEIN, 12, 6, 10, 4), (O.ALPHA_PROTEIN, 9, 4, 7, 3),
+                                           (O.ALPHA_PROTEIN, 5, 5, 5, 12), (O.ALPHA_TRIPLET, 10, 5, 8, 4),
+                                           (O.ALPHA_TRIPLET, 7, 3, 7, 2)])
+def test_alphabet_single_kmer_bits(alpha, k, m, s, H):
+    """§II-B / §IV-B for other alphabets: the shard is the minimizer over the
+    k-m+1 m-mers of symbols and the set bits are those of the k-s+1 s-mers,
+    each cut out of the symbol list and packed on its own."""
+    rng = np.random.default_rng(41 + alpha * 7 + k)
+    b = T.BITS[alpha]
+    for _ in range(20):
+        f = O.OracleFilter(k, m, s, H, 2**14, alpha=alpha)
+        text = T.random_protein(rng, k) if alpha == O.ALPHA_PROTEIN else T.random_dna(rng, 3 * k)
+        codes = T.symbols_of(alpha, text)
+        x = T.pack_symbols(codes, b)
+        assert O.pack_kmer_alpha(alpha, text, 0, k) == x
+        f.insert_seq(text)
+        w = f.words().reshape(-1, 4)
+        nz = np.nonzero(w.any(axis=1))[0]
+        assert list(nz) == [T.minimizer_hash_alpha(codes, alpha, m) % f.num_shards]
+        got = {(q, bit) for q in range(4) for bit in range(64) if (int(w[nz[0], q]) >> bit) & 1}
+        assert got == T.kmer_bits_alpha(codes, alpha, s, H)
+        assert f.query_kmer(x)
+
+
+@pytest.mark.parametrize("alpha", [O.ALPHA_PROTEIN, O.ALPHA_TRIPLET])
+def test_alphabet_query_seq_matches_per_kmer(alpha):
+    """§II-A no false negatives, §IV-F invalid symbols: query_seq equals the
+    per-k-mer answer from the text at every symbol start; a k-mer holding an
+    invalid symbol answers 0; for triplets, trailing bytes short of a codon
+    are ignored."""
+    rng = np.random.default_rng(42 + alpha)
+    k, m, s, H = (10, 5, 8, 4) if alpha == O.ALPHA_PROTEIN else (8, 4, 6, 3)
+    f = O.OracleFilter(k, m, s, H, 2**12, alpha=alpha)
+    if alpha == O.ALPHA_PROTEIN:
+        ins = bytearray(T.random_protein(rng, 3000, b"ACDEFGHIKLMNPQRSTVWYacdefxbz"))
+        bad = b"*-1 "
+    else:
+        ins = bytearray(T.random_dna(rng, 3 * 1000 + 2))
+        bad = b"N"
+    for p in rng.integers(0, len(ins), 10):
+        ins[p] = bad[int(rng.integers(0, len(bad)))]
+    ins = bytes(ins)
+    f.insert_seq(ins)
+    codes = T.symbols_of(alpha, ins)
+    nk = len(codes) - k + 1
+    got = T.bits_of(f.query_seq(ins), nk)
+    want = np.array([all(c is not None for c in codes[p:p + k]) for p in range(nk)], dtype=np.uint8)
+    assert (got == want).all()
+    # a second, uninserted sequence: per-k-mer answers from the text
+    q = bytes(T.random_protein(rng, 800) if alpha == O.ALPHA_PROTEIN else T.random_dna(rng, 3 * 300 + 1))
+    qc = T.symbols_of(alpha, q)
+    nq = len(qc) - k + 1
+    got = T.bits_of(f.query_seq(q), nq)
+    for p in range(nq):
+        want = f.query_kmer(T.pack_symbols(qc[p:p + k], T.BITS[alpha]))
+        assert got[p] == want
+    pos = rng.integers(0, len(qc), 200)
+    qp = f.query_positions(q, pos)
+    for i, p in enumerate(pos):
+        assert qp[i] == (got[p] if p + k <= len(qc) else 0)
+
+
+@pytest.mark.parametrize("alpha", [O.ALPHA_PROTEIN, O.ALPHA_TRIPLET])
+def test_alphabet_insert_union_and_edges(alpha):
+    """Insert is a set union (order-free, idempotent) for any alphabet;
+    sequences shorter than k symbols insert nothing; k = 12 proteins and
+    k = 10 triplets (60 bits) are the largest k, one more is refused."""
+    rng = np.random.default_rng(43 + alpha)
+    gen = (lambda n: T.random_protein(rng, n)) if alpha == O.ALPHA_PROTEIN else (lambda n: T.random_dna(rng, 3 * n))
+    a, b = gen(400), gen(300)
+    kmax = 12 if alpha == O.ALPHA_PROTEIN else 10
+    args = (kmax, kmax // 2, kmax - 2, 4, 2**13)
+    f1, f2, f3 = (O.OracleFilter(*args, alpha=alpha) for _ in range(3))
+    f1.insert_seq(a); f1.insert_seq(b)
+    f2.insert_seq(b); f2.insert_seq(a); f2.insert_seq(a)
+    f3.insert_seq(gen(kmax - 1))
+    f3.insert_seq(b"")
+    assert (f1.words() == f2.words()).all() and f1.words().any()
+    assert not f3.words().any()
+    with pytest.raises(ValueError):
+        O.OracleFilter(kmax + 1, 4, 4, 4, 2**13, alpha=alpha)
+    with pytest.raises(ValueError):
+        O.OracleFilter(5, 4, 4, 4, 2**13, alpha=3)
+
+
+def test_alphabet_probe_symbols_uniform():
+    """§V-D random probes for other alphabets: protein probe symbols are
+    uniform over the 26 letters at every position, triplet probe symbols
+    uniform over the 64 codons (chi-square, 5 sigma)."""
+    for alpha, k, q in [(O.ALPHA_PROTEIN, 12, 26), (O.ALPHA_TRIPLET, 10, 64)]:
+        b = T.BITS[alpha]
+        n = 20000
+        counts = np.zeros((k, q), dtype=np.int64)
+        for i in range(n):
+            x = O.probe_kmer_alpha(alpha, 1234, i, k)
+            assert x < 1 << (b * k)
+            for j in range(k):
+                counts[j, (x >> (b * (k - 1 - j))) & ((1 << b) - 1)] += 1
+        assert counts.sum(axis=1).tolist() == [n] * k
+        e = n / q
+        chi = ((counts - e) ** 2 / e).sum(axis=1)
+        dof = q - 1
+        assert (chi < dof + 5 * math.sqrt(2 * dof)).all(), chi
+    # DNA's alphabet-generic probe is the DNA probe
+    assert all(O.probe_kmer_alpha(O.ALPHA_DNA, 9, i, 31) == O.probe_kmer(9, i, 31) for i in range(100))
+
+
+@pytest.mark.parametrize("alpha,k,m,s,H", [(O.ALPHA_PROTEIN, 12, 6, 10, 4), (O.ALPHA_TRIPLET, 10, 5, 8, 4)])
+def test_alphabet_fpr_fill_based(alpha, k, m, s, H):
+    """Eq. (2) with the shard loads, as for DNA: a random alien k-mer of the
+    alphabet lands in a uniform shard and each of its k-s+1 s-mers must hit."""
+    rng = np.random.default_rng(44 + alpha)
+    f = O.OracleFilter(k, m, s, H, 2**14, alpha=alpha)
+    f.insert_seq(T.random_protein(rng, 5000) if alpha == O.ALPHA_PROTEIN else T.random_dna(rng, 3 * 5000))
+    w = f.words().reshape(-1, 4)
+    fill = np.array([[bin(int(v)).count("1") / 64 for v in row] for row in w])
+    c = [sum(1 for t in range(H) if t % 4 == q) for q in range(4)]
+    z1 = k - s + 1
+    p = float(np.mean(np.prod([fill[:, q] ** (c[q] * z1) for q in range(4)], axis=0)))
+    n = 200000
+    hits = f.fpr_probe(n, 0xA1FA)
+    assert p > 1e-4
+    assert T.binom_ok(hits, n, p, z=4.5)
