@@ -56,7 +56,7 @@ extern "C" {
 /* return codes */
 #define SBF_OK 0
 #define SBF_EINVAL (-1)       /* bad argument (parameter range, NULL pointer, size) */
-#define SBF_EUNSUPPORTED (-2) /* reserved: parameter combination not available */
+#define SBF_EUNSUPPORTED (-2) /* call not available for this filter (see sbf_create_alphabet) */
 #define SBF_ENOMEM (-3)       /* device or host allocation failed */
 #define SBF_EDEVICE (-4)      /* a HIP runtime call or kernel launch failed */
 #define SBF_EIO (-5)          /* a file could not be opened or read, or is not valid FASTA/FASTQ */
@@ -65,6 +65,11 @@ extern "C" {
 #define SBF_KIND_SBF 0 /* Super Bloom filter */
 #define SBF_KIND_BBF 1 /* per-k-mer blocked Bloom filter, same shard layout */
 #define SBF_KIND_WIDE 2 /* Super Bloom filter with 512-bit blocks, whole-block addressing */
+
+/* sequence alphabets ([cuSBF] §IV-A) */
+#define SBF_ALPHABET_DNA 0u     /* A C G T, 2 bits per symbol */
+#define SBF_ALPHABET_PROTEIN 1u /* letters A-Z, 5 bits per symbol */
+#define SBF_ALPHABET_TRIPLET 2u /* DNA codons of 3 bytes, 6 bits per symbol */
 
 /* where the pointers of a *_seq / copy call live */
 #define SBF_HOST 1u
@@ -79,6 +84,7 @@ typedef struct sbf_info {
     uint64_t num_shards;  /* N, a power of two */
     uint64_t filter_bytes; /* 8 * words_per_shard * N */
     uint32_t words_per_shard; /* 4, or 8 for SBF_KIND_WIDE */
+    uint32_t alphabet;        /* SBF_ALPHABET_* */
 } sbf_info_t;
 
 /*
@@ -109,6 +115,34 @@ int sbf_create_bbf(sbf_t** out, uint32_t k, uint32_t H, uint64_t bits);
  * is words 8j .. 8j+7.
  */
 int sbf_create_wide(sbf_t** out, uint32_t k, uint32_t m, uint32_t s, uint32_t H, uint64_t bits);
+
+/*
+ * Create an empty Super Bloom filter over another alphabet ([cuSBF] §IV-A:
+ * proteins, 26 symbols of 5 bits; DNA triplets, 64 symbols of 6 bits that
+ * span three bytes).  k, m and s count symbols and a k-mer packs its symbols
+ * first-most-significant at b bits each, so k * b <= 64: k <= 12 for
+ * proteins, k <= 10 for triplets (DNA: k <= 32, the same as sbf_create).
+ * Symbol codes:
+ *   protein  a letter of either case -> its place in A..Z (0..25); every other
+ *            byte is invalid
+ *   triplet  symbol j is bytes 3j .. 3j+2 (non-overlapping, from the first
+ *            byte; a last 1 or 2 bytes are ignored), code 16 c0 + 4 c1 + c2
+ *            with the DNA codes; invalid if any of its bases is
+ * Shard, s-mer bits and layout are those of sbf_create with symbols in place
+ * of bases.  On a protein or triplet filter, positions in the sequence calls
+ * are symbol positions: a sequence of len bytes has n = len (protein) or
+ * floor(len / 3) (triplet) symbols, n - k + 1 k-mer starts, and query output
+ * has ceil((n - k + 1) / 64) words.  sbf_insert_seq, sbf_query_seq (host or
+ * device), sbf_fpr_probe* (protein probe symbol j of k-mer i is
+ * floor(26 u / 2^64), u the SplitMix64 output number i*k + j + 1 of the seed;
+ * triplet probes take the top 6k bits of output i + 1), sbf_clear, sbf_info
+ * and sbf_copy_filter work as for DNA; the packed and FASTA/FASTQ calls
+ * return SBF_EUNSUPPORTED.  alphabet = SBF_ALPHABET_DNA is sbf_create.
+ * Errors: SBF_EINVAL (unknown alphabet, parameter ranges), SBF_ENOMEM,
+ * SBF_EDEVICE.
+ */
+int sbf_create_alphabet(sbf_t** out, uint32_t alphabet, uint32_t k, uint32_t m, uint32_t s, uint32_t H,
+                        uint64_t bits);
 
 /* Free a filter and its buffers (synchronizes the device). NULL is a no-op. */
 int sbf_destroy(sbf_t* h);
@@ -146,7 +180,8 @@ int sbf_pack(const char* d_ascii, uint64_t len, uint32_t* d_codes, uint32_t* d_v
 
 /*
  * Insert every valid k-mer of a packed device sequence ([cuSBF] §IV-D,
- * Algorithm 1).  Asynchronous on `stream`; len < k is a no-op.
+ * Algorithm 1).  Asynchronous on `stream`; len < k is a no-op.  DNA filters
+ * only (SBF_EUNSUPPORTED otherwise), as is sbf_query_packed.
  */
 int sbf_insert_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid,
                       uint64_t len, void* stream);
@@ -171,7 +206,8 @@ int sbf_query_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid,
  * and the call synchronizes.  SBF_DEVICE: `seq` is device memory; packing
  * goes to the handle's staging buffer and the call is asynchronous on
  * `stream`.  Staging buffers grow on demand (growing synchronizes `stream`)
- * and stay allocated until sbf_destroy.
+ * and stay allocated until sbf_destroy.  Protein and triplet filters read the
+ * text itself (no packing; chunks overlap by k-1 symbols).
  */
 int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void* stream);
 
@@ -234,7 +270,9 @@ typedef struct sbf_fastx_stats {
 } sbf_fastx_stats_t;
 
 /*
- * Insert every valid k-mer of a FASTA/FASTQ file through the host pipeline:
+ * Insert every valid k-mer of a FASTA/FASTQ file through the host pipeline
+ * (DNA filters; SBF_EUNSUPPORTED for protein and triplet filters, whose
+ * alphabets the 'N' record separator does not fit):
  * the reader writes the normalized stream straight into the pinned chunk
  * buffers while the device works on the previous chunk.  Synchronizes.
  * stats may be NULL.  SBF_EIO for file errors; no partial insert is undone.

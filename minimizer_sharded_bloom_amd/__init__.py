@@ -14,7 +14,8 @@ import os
 import numpy as np
 
 from . import _lib
-from ._lib import SBF_DEVICE, SBF_HOST, SbfError, check
+from ._lib import (SBF_ALPHABET_DNA, SBF_ALPHABET_PROTEIN, SBF_ALPHABET_TRIPLET, SBF_DEVICE, SBF_HOST, SbfError,
+                   check)
 
 __all__ = ["SuperBloomFilter", "pack", "packed_words", "SbfError", "lib", "fastx_stream", "count_fastx_records"]
 
@@ -81,9 +82,12 @@ class SuperBloomFilter:
     comparator; with `wide()`, the 512-bit whole-block variant) living in
     device memory."""
 
-    def __init__(self, k: int, m: int, s: int, H: int, bits: int, *, _kind: int = _lib.SBF_KIND_SBF):
+    def __init__(self, k: int, m: int, s: int, H: int, bits: int, *, _kind: int = _lib.SBF_KIND_SBF,
+                 _alphabet: int = _lib.SBF_ALPHABET_DNA):
         h = ctypes.c_void_p()
-        if _kind == _lib.SBF_KIND_BBF:
+        if _alphabet != _lib.SBF_ALPHABET_DNA:
+            check(lib().sbf_create_alphabet(ctypes.byref(h), _alphabet, k, m, s, H, bits), "sbf_create_alphabet")
+        elif _kind == _lib.SBF_KIND_BBF:
             check(lib().sbf_create_bbf(ctypes.byref(h), k, H, bits), "sbf_create_bbf")
         elif _kind == _lib.SBF_KIND_WIDE:
             check(lib().sbf_create_wide(ctypes.byref(h), k, m, s, H, bits), "sbf_create_wide")
@@ -98,6 +102,7 @@ class SuperBloomFilter:
         self.num_shards = inf.num_shards
         self.filter_bytes = inf.filter_bytes
         self.words_per_shard = inf.words_per_shard
+        self.alphabet = inf.alphabet
 
     @classmethod
     def blocked(cls, k: int, H: int, bits: int) -> "SuperBloomFilter":
@@ -107,6 +112,16 @@ class SuperBloomFilter:
     def wide(cls, k: int, m: int, s: int, H: int, bits: int) -> "SuperBloomFilter":
         """Wide-block variant: 512-bit blocks, each hash addressing the whole block."""
         return cls(k, m, s, H, bits, _kind=_lib.SBF_KIND_WIDE)
+
+    @classmethod
+    def protein(cls, k: int, m: int, s: int, H: int, bits: int) -> "SuperBloomFilter":
+        """Protein alphabet: letters A-Z, 5 bits per symbol, k <= 12."""
+        return cls(k, m, s, H, bits, _alphabet=_lib.SBF_ALPHABET_PROTEIN)
+
+    @classmethod
+    def triplet(cls, k: int, m: int, s: int, H: int, bits: int) -> "SuperBloomFilter":
+        """DNA-triplet alphabet: codons of 3 bytes, 6 bits per symbol, k <= 10."""
+        return cls(k, m, s, H, bits, _alphabet=_lib.SBF_ALPHABET_TRIPLET)
 
     def close(self):
         if getattr(self, "_h", None) and self._h.value:
@@ -129,8 +144,13 @@ class SuperBloomFilter:
     def handle(self) -> int:
         return self._h.value
 
+    def num_symbols(self, length: int) -> int:
+        """Symbols in `length` bytes (a triplet symbol is 3 bytes)."""
+        return length // 3 if self.alphabet == _lib.SBF_ALPHABET_TRIPLET else length
+
     def num_answer_words(self, length: int) -> int:
-        return 0 if length < self.k else (length - self.k + 1 + 63) // 64
+        n = self.num_symbols(length)
+        return 0 if n < self.k else (n - self.k + 1 + 63) // 64
 
     # ---- filter state ------------------------------------------------------
     def clear(self, stream=None):

@@ -19,6 +19,9 @@ SBF_EIO = -5
 SBF_KIND_SBF = 0
 SBF_KIND_BBF = 1
 SBF_KIND_WIDE = 2
+SBF_ALPHABET_DNA = 0
+SBF_ALPHABET_PROTEIN = 1
+SBF_ALPHABET_TRIPLET = 2
 SBF_HOST = 1
 SBF_DEVICE = 2
 
@@ -27,7 +30,7 @@ class SbfInfo(ctypes.Structure):
     _fields_ = [("k", ctypes.c_uint32), ("m", ctypes.c_uint32), ("s", ctypes.c_uint32),
                 ("H", ctypes.c_uint32), ("kind", ctypes.c_uint32), ("specialized", ctypes.c_uint32),
                 ("num_shards", ctypes.c_uint64), ("filter_bytes", ctypes.c_uint64),
-                ("words_per_shard", ctypes.c_uint32)]
+                ("words_per_shard", ctypes.c_uint32), ("alphabet", ctypes.c_uint32)]
 
 
 class SbfFastxStats(ctypes.Structure):
@@ -41,6 +44,7 @@ SIGNATURES = {
     "sbf_create": (_int, [ctypes.POINTER(_p), _u32, _u32, _u32, _u32, _u64]),
     "sbf_create_bbf": (_int, [ctypes.POINTER(_p), _u32, _u32, _u64]),
     "sbf_create_wide": (_int, [ctypes.POINTER(_p), _u32, _u32, _u32, _u32, _u64]),
+    "sbf_create_alphabet": (_int, [ctypes.POINTER(_p), _u32, _u32, _u32, _u32, _u32, _u64]),
     "sbf_destroy": (_int, [_p]),
     "sbf_clear": (_int, [_p, _p]),
     "sbf_info": (_int, [_p, ctypes.POINTER(SbfInfo)]),

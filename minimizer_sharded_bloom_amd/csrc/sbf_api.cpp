@@ -26,6 +26,8 @@ const SpecEntry* spec_table_wide(size_t* n);
 
 bool find_specialized(const Params& p, KernelSet* out)
 {
+    if (p.alpha != SBF_ALPHABET_DNA)
+        return false;
     typedef const SpecEntry* (*TableFn)(size_t*);
     static const TableFn tables[] = {spec_table_m12,       spec_table_m16,       spec_table_m20,
                                      spec_table_extra,     spec_table_slice_s_a, spec_table_slice_s_b,
@@ -77,12 +79,29 @@ uint64_t valid_words(uint64_t len) { return (len + 31) / 32; }
 SeqArgs seq_args(sbf_t* h, const uint32_t* codes, const uint32_t* valid, uint64_t len, uint64_t* out,
                  hipStream_t st)
 {
-    SeqArgs a;
+    SeqArgs a{};
     a.codes = codes;
     a.valid = valid;
     a.ncw = code_words(len);
     a.nvw = valid_words(len);
     a.nk = len - h->P.k + 1;
+    a.filter = h->d_filter;
+    a.shard_mask = (uint32_t)(h->num_shards - 1);
+    a.out = out;
+    a.stream = st;
+    return a;
+}
+
+uint32_t symbol_bytes(const sbf_t* h) { return h->P.alpha == SBF_ALPHABET_TRIPLET ? 3u : 1u; }
+
+uint64_t symbols_of(const sbf_t* h, uint64_t len) { return len / symbol_bytes(h); }
+
+SeqArgs text_args(sbf_t* h, const char* text, uint64_t len, uint64_t* out, hipStream_t st)
+{
+    SeqArgs a{};
+    a.text = text;
+    a.nsym = symbols_of(h, len);
+    a.nk = a.nsym - h->P.k + 1;
     a.filter = h->d_filter;
     a.shard_mask = (uint32_t)(h->num_shards - 1);
     a.out = out;
@@ -99,6 +118,12 @@ int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
 {
     if (!out)
         return fail(SBF_EINVAL, "out is NULL");
+    if (P.alpha > SBF_ALPHABET_TRIPLET)
+        return fail(SBF_EINVAL, "unknown alphabet");
+    if (P.alpha == SBF_ALPHABET_PROTEIN && (P.k < 1 || P.k > 12))
+        return fail(SBF_EINVAL, "k must be in 1..12 for proteins (5 bits per symbol)");
+    if (P.alpha == SBF_ALPHABET_TRIPLET && (P.k < 1 || P.k > 10))
+        return fail(SBF_EINVAL, "k must be in 1..10 for triplets (6 bits per symbol)");
     if (P.k < 1 || P.k > 32)
         return fail(SBF_EINVAL, "k must be in 1..32");
     if (P.kind != SBF_KIND_BBF && (P.m < 1 || P.m > P.k))
@@ -122,7 +147,9 @@ int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
     h->P = P;
     h->num_shards = n;
     h->wps = wps;
-    if (!sbf::find_specialized(P, &h->ks))
+    if (P.alpha != SBF_ALPHABET_DNA)
+        h->ks = sbf::alpha_kernels(P.alpha);
+    else if (!sbf::find_specialized(P, &h->ks))
         h->ks = sbf::generic_kernels();
     hipError_t e = hipGetDevice(&h->device);
     if (e != hipSuccess) {
@@ -220,6 +247,13 @@ int sbf_create_wide(sbf_t** out, uint32_t k, uint32_t m, uint32_t s, uint32_t H,
     return create_impl(out, P, bits);
 }
 
+int sbf_create_alphabet(sbf_t** out, uint32_t alphabet, uint32_t k, uint32_t m, uint32_t s, uint32_t H,
+                        uint64_t bits)
+{
+    sbf::Params P{SBF_KIND_SBF, k, m, s, H, alphabet};
+    return create_impl(out, P, bits);
+}
+
 int sbf_destroy(sbf_t* h)
 {
     if (!h)
@@ -267,6 +301,7 @@ int sbf_info(const sbf_t* h, sbf_info_t* o)
     o->num_shards = h->num_shards;
     o->filter_bytes = 8ull * h->wps * h->num_shards;
     o->words_per_shard = h->wps;
+    o->alphabet = h->P.alpha;
     ok();
     return SBF_OK;
 }
@@ -327,6 +362,8 @@ int sbf_insert_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid
 {
     if (!h)
         return fail(SBF_EINVAL, "handle is NULL");
+    if (h->P.alpha != SBF_ALPHABET_DNA)
+        return fail(SBF_EUNSUPPORTED, "packed input is DNA only");
     if (len < h->P.k) {
         ok();
         return SBF_OK;
@@ -349,6 +386,8 @@ int sbf_query_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid,
 {
     if (!h)
         return fail(SBF_EINVAL, "handle is NULL");
+    if (h->P.alpha != SBF_ALPHABET_DNA)
+        return fail(SBF_EUNSUPPORTED, "packed input is DNA only");
     if (len < h->P.k) {
         ok();
         return SBF_OK;
@@ -372,7 +411,7 @@ int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void
         return fail(SBF_EINVAL, "handle is NULL");
     if (check_flags(flags))
         return SBF_EINVAL;
-    if (len < h->P.k) {
+    if (symbols_of(h, len) < h->P.k) {
         ok();
         return SBF_OK;
     }
@@ -384,6 +423,13 @@ int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void
     hipStream_t st = (hipStream_t)stream;
     if (flags == SBF_HOST)
         return sbf::host_insert(h, seq, len, st);
+    if (h->P.alpha != SBF_ALPHABET_DNA) {
+        hipError_t e = h->ks.insert(text_args(h, seq, len, nullptr, st), h->P);
+        if (e != hipSuccess)
+            return fail_hip(e, "insert");
+        ok();
+        return SBF_OK;
+    }
     rc = stage_packed(h, seq, len, st);
     if (rc)
         return rc;
@@ -401,7 +447,7 @@ int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits, u
         return fail(SBF_EINVAL, "handle is NULL");
     if (check_flags(flags))
         return SBF_EINVAL;
-    if (len < h->P.k) {
+    if (symbols_of(h, len) < h->P.k) {
         ok();
         return SBF_OK;
     }
@@ -413,6 +459,13 @@ int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits, u
     hipStream_t st = (hipStream_t)stream;
     if (flags == SBF_HOST)
         return sbf::host_query(h, seq, len, out_bits, st);
+    if (h->P.alpha != SBF_ALPHABET_DNA) {
+        hipError_t e = h->ks.query(text_args(h, seq, len, out_bits, st), h->P);
+        if (e != hipSuccess)
+            return fail_hip(e, "query");
+        ok();
+        return SBF_OK;
+    }
     rc = stage_packed(h, seq, len, st);
     if (rc)
         return rc;
@@ -468,9 +521,10 @@ const char* sbf_strerror(int code)
     switch (code) {
     case SBF_OK: return "ok";
     case SBF_EINVAL: return "invalid argument";
-    case SBF_EUNSUPPORTED: return "unsupported parameter combination";
+    case SBF_EUNSUPPORTED: return "not available for this filter";
     case SBF_ENOMEM: return "out of memory";
     case SBF_EDEVICE: return "device error";
+    case SBF_EIO: return "file error";
     default: return "unknown error";
     }
 }

@@ -182,6 +182,25 @@ __device__ __forceinline__ void load_shard(const uint64_t* __restrict__ filter, 
     w[3] = b.y;
 }
 
+// Value of lane l+1 in lane l (lane 63 receives 0): one DPP wave_shl:1 move
+// per 32-bit half, no LDS traffic.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v)
+{
+    // bound_ctrl: lane 63 reads 0 instead of keeping an old value, so no copy
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x130, 0xF, 0xF, true);
+}
+
+// Value of lane l-1 in lane l (lane 0 receives 0): DPP wave_shr:1.
+__device__ __forceinline__ uint32_t from_prev_lane(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x138, 0xF, 0xF, true);
+}
+
+__device__ __forceinline__ uint64_t from_next_lane(uint64_t v)
+{
+    return ((uint64_t)from_next_lane((uint32_t)(v >> 32)) << 32) | from_next_lane((uint32_t)v);
+}
+
 // LDS written by some lanes of this wave becomes visible to all its lanes.
 __device__ __forceinline__ void wave_lds_sync()
 {

@@ -56,6 +56,11 @@ void ok();
 int set_device(const sbf_t* h);
 SeqArgs seq_args(sbf_t* h, const uint32_t* codes, const uint32_t* valid, uint64_t len, uint64_t* out,
                  hipStream_t st);
+// Protein and triplet filters: bytes per symbol (1 or 3), symbols in len
+// bytes, and launch arguments over the text itself.
+uint32_t symbol_bytes(const sbf_t* h);
+uint64_t symbols_of(const sbf_t* h, uint64_t len);
+SeqArgs text_args(sbf_t* h, const char* text, uint64_t len, uint64_t* out, hipStream_t st);
 void free_host_staging(HostStaging& hs);
 // Host-resident insert / query through the chunked pipeline (sbf_host.cpp);
 // both synchronize before returning.

@@ -144,7 +144,8 @@ int ensure_staging(sbf_t* h)
     if (hs.built_for == hs.chunk && hs.s[0])
         return SBF_OK;
     free_host_staging(hs);
-    const uint64_t in_bytes = hs.chunk + 64;  // + k-1 <= 31 bases of overlap, padded
+    // + k-1 <= 31 symbols of overlap, padded; a triplet symbol is 3 bytes
+    const uint64_t in_bytes = (hs.chunk + 64) * symbol_bytes(h);
     const uint64_t out_words = hs.chunk / 64 + 1;
     hipError_t e = hipSuccess;
     for (int b = 0; b < kHostSlots && e == hipSuccess; ++b) {
@@ -200,7 +201,8 @@ int run_pipeline(sbf_t* h, Source& src, Sink* sink, hipStream_t user, uint64_t* 
         return rc;
     HostStaging& hs = h->host;
     const uint64_t k = h->P.k;
-    const uint64_t want = hs.chunk + k - 1;
+    const uint64_t sb = symbol_bytes(h);  // bytes per symbol
+    const uint64_t want = (hs.chunk + k - 1) * sb;
     // order after the caller's earlier work on `user`
     hipEvent_t start;
     hipError_t e = hipEventCreateWithFlags(&start, hipEventDisableTiming);
@@ -255,16 +257,21 @@ int run_pipeline(sbf_t* h, Source& src, Sink* sink, hipStream_t user, uint64_t* 
         t_src += now_s() - t0;
         if (rc)
             break;
-        if (have < k)
+        const uint64_t nsym = have / sb;
+        if (nsym < k)
             break;  // no k-mer starts left
-        const uint64_t nk = have - k + 1;
+        const uint64_t nk = nsym - k + 1;
         const hipStream_t s = hs.s[b];
         e = hipMemcpyAsync(hs.d_in[b], dst, have, hipMemcpyHostToDevice, s);
-        if (e == hipSuccess)
-            e = launch_pack(hs.d_in[b], have, hs.d_codes[b], hs.d_valid[b], s);
-        if (e == hipSuccess) {
-            const SeqArgs a = seq_args(h, hs.d_codes[b], hs.d_valid[b], have, sink ? hs.d_out[b] : nullptr, s);
+        if (e == hipSuccess && h->P.alpha != SBF_ALPHABET_DNA) {
+            const SeqArgs a = text_args(h, hs.d_in[b], have, sink ? hs.d_out[b] : nullptr, s);
             e = sink ? h->ks.query(a, h->P) : h->ks.insert(a, h->P);
+        } else if (e == hipSuccess) {
+            e = launch_pack(hs.d_in[b], have, hs.d_codes[b], hs.d_valid[b], s);
+            if (e == hipSuccess) {
+                const SeqArgs a = seq_args(h, hs.d_codes[b], hs.d_valid[b], have, sink ? hs.d_out[b] : nullptr, s);
+                e = sink ? h->ks.query(a, h->P) : h->ks.insert(a, h->P);
+            }
         }
         if (e == hipSuccess && sink)
             e = hipMemcpyAsync(hs.h_out[b], hs.d_out[b], 8 * words_for(nk), hipMemcpyDeviceToHost, s);
@@ -277,8 +284,9 @@ int run_pipeline(sbf_t* h, Source& src, Sink* sink, hipStream_t user, uint64_t* 
         slot[b].nk = nk;
         ++nchunks;
         // the next chunk starts at the k-mer after this chunk's last one
-        carry = k - 1;
-        carry_src = dst + have - carry;
+        // (have = want, a whole number of symbols, unless the input ended)
+        carry = (k - 1) * sb;
+        carry_src = dst + nsym * sb - carry;
         first += nk;
     }
     // drain both slots (oldest first) even after an error, so no copy still
@@ -538,6 +546,8 @@ int sbf_insert_fastx(sbf_t* h, const char* path, sbf_fastx_stats_t* stats)
 {
     if (!h || !path)
         return sbf::fail(SBF_EINVAL, "NULL argument");
+    if (h->P.alpha != SBF_ALPHABET_DNA)
+        return sbf::fail(SBF_EUNSUPPORTED, "FASTA/FASTQ input is DNA only");
     int rc = sbf::set_device(h);
     if (rc)
         return rc;
@@ -566,6 +576,8 @@ int sbf_query_fastx(sbf_t* h, const char* path, uint64_t* hits, uint64_t* kmers,
 {
     if (!h || !path || (cap && !hits && !kmers))
         return sbf::fail(SBF_EINVAL, "bad argument");
+    if (h->P.alpha != SBF_ALPHABET_DNA)
+        return sbf::fail(SBF_EUNSUPPORTED, "FASTA/FASTQ input is DNA only");
     int rc = sbf::set_device(h);
     if (rc)
         return rc;

@@ -18,6 +18,10 @@ struct SeqArgs {
     uint32_t shard_mask;    // N - 1
     uint64_t* out;          // query bits (query only)
     hipStream_t stream;
+    // Protein and triplet alphabets read the ASCII text itself: symbol j is
+    // byte j (protein) or bytes 3j..3j+2 (triplet); nk counts symbol starts.
+    const char* text;
+    uint64_t nsym;
 };
 
 // Arguments of one false-positive probe launch.
@@ -33,6 +37,7 @@ struct ProbeArgs {
 // Runtime parameters, used by the generic (non-specialized) kernels.
 struct Params {
     uint32_t kind, k, m, s, H;
+    uint32_t alpha;  // SBF_ALPHABET_*: 0 DNA, 1 protein, 2 DNA triplets
 };
 
 typedef hipError_t (*SeqLaunch)(const SeqArgs&, const Params&);
@@ -55,6 +60,8 @@ struct SpecEntry {
 bool find_specialized(const Params& p, KernelSet* out);
 // Kernel set for any valid parameters (one k-mer per lane, runtime loops).
 KernelSet generic_kernels();
+// Kernel set of the protein (alpha 1) or triplet (alpha 2) Super Bloom filter.
+KernelSet alpha_kernels(uint32_t alpha);
 
 // Small utility launches.
 hipError_t launch_pack(const char* ascii, uint64_t len, uint32_t* codes, uint32_t* valid, hipStream_t st);

@@ -148,20 +148,6 @@ __device__ __forceinline__ void load_codes(const SeqArgs& a, const LaneCtx<C>& c
         D[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(o + 4u * j), 0, 0);
 }
 
-// Value of lane l+1 in lane l (lane 63 receives 0): one DPP wave_shl:1 move
-// per 32-bit half, no LDS traffic.
-__device__ __forceinline__ uint32_t from_next_lane(uint32_t v)
-{
-    // bound_ctrl: lane 63 reads 0 instead of keeping an old value, so no copy
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x130, 0xF, 0xF, true);
-}
-
-// Value of lane l-1 in lane l (lane 0 receives 0): DPP wave_shr:1.
-__device__ __forceinline__ uint32_t from_prev_lane(uint32_t v)
-{
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x138, 0xF, 0xF, true);
-}
-
 // x * 2 + (this lane's bit of the lane mask m): one v_addc with m as the
 // carry-in, so a per-k-mer compare becomes a bit of a per-lane word in one
 // instruction after the compare.
@@ -171,11 +157,6 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t x, uint64_t m)
     uint64_t carry_out;
     asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(x), "s"(m));
     return r;
-}
-
-__device__ __forceinline__ uint64_t from_next_lane(uint64_t v)
-{
-    return ((uint64_t)from_next_lane((uint32_t)(v >> 32)) << 32) | from_next_lane((uint32_t)v);
 }
 
 // Shard keys of the lane's KL k-mers: the low 32 bits of the minimizer hash

@@ -21,9 +21,24 @@ on Modern GPUs" (§V-A, §V-D), which are not available here:
      insertion of a random base and deletion; reads joined by 'N'; filter
      2^35 bits.  The seeded 1% read subsample is one whole batch.
 
+Other alphabets (§IV-A; the evaluation measures DNA only, so these follow
+the DNA workloads' shapes):
+
+  protein  a 16 M-residue proteome: residues i.i.d. uniform over the 20
+           standard amino acids, copied 50-300-residue segments (5%
+           substitutions) overwriting 5% of it, proteins of length
+           round(exp(N(ln 350, 0.6^2))) clamped to 30-5000 joined by '*';
+           queries: 2 M peptides of 50 residues, half sampled from the
+           proteome at uniform starts with 1% substitutions, half uniform,
+           shuffled and joined by '*'; filter 2^28 bits (16 per k-mer).
+  triplet  a 48 Mbp genome as in 2 (16 M codons); queries: 2 M reads of 150
+           bp, half sampled at codon-aligned starts with 1% substitutions,
+           half uniform, joined by "NNN" so each read starts on a codon
+           boundary; filter 2^28 bits.
+
 Seeds: genome 0, foreign sequence 1, repeats 2, read starts 3, read errors 4,
 random reads 5, shuffle 6, subsample 7, 'N' runs 8, long-read layout 9,
-long-read errors 10.
+long-read errors 10, proteome 20, protein lengths 21, peptides 22.
 """
 from __future__ import annotations
 
@@ -220,6 +235,89 @@ def workload(cfg: int) -> dict:
         g = genome_with_n_runs(CONFIG_GENOME[5])
         return {"cfg": 5, "bits": CONFIG_BITS[5], "insert": g, "queries": [long_read_set(g)]}
     raise ValueError("workload %r is not generated by this module" % cfg)
+
+
+AMINO = np.frombuffer(b"ACDEFGHIKLMNPQRSTVWY", dtype=np.uint8)
+STOP_BYTE = ord("*")
+PROTEIN_RESIDUES = 16_000_000
+TRIPLET_GENOME = 48_000_000
+ALPHA_READS = 2_000_000
+ALPHA_BITS = 2**28
+
+
+def proteome(n: int, frac: float = 0.05, seg=(50, 300), sub: float = 0.05, seed: int = 20,
+             seed_len: int = 21) -> np.ndarray:
+    """ASCII of about n residues of proteins joined by '*' (see the module
+    docstring)."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, AMINO.size, n, dtype=np.uint8)
+    done, target = 0, int(frac * n)
+    while n > 2 * seg[1] and done < target:
+        L = int(rng.integers(seg[0], seg[1] + 1))
+        src, dst = (int(x) for x in rng.integers(0, n - L + 1, 2))
+        if abs(src - dst) < L:
+            continue
+        piece = idx[src:src + L].copy()
+        hit = rng.random(L) < sub
+        piece[hit] = (piece[hit] + rng.integers(1, AMINO.size, int(hit.sum()), dtype=np.uint8)) % AMINO.size
+        idx[dst:dst + L] = piece
+        done += L
+    out = AMINO[idx]
+    # protein boundaries: overwrite one residue with '*' after each protein
+    lr = np.random.default_rng(seed_len)
+    lens = np.clip(np.round(np.exp(lr.normal(np.log(350.0), 0.6, n // 30 + 1))), 30, 5000).astype(np.int64)
+    cuts = np.cumsum(lens + 1) - 1
+    out[cuts[cuts < n]] = STOP_BYTE
+    return out
+
+
+def peptide_set(prot: np.ndarray, R: int, L: int = 50, err: float = 0.01, seed: int = 22) -> np.ndarray:
+    """ASCII of R peptides of L residues (R/2 sampled from prot with
+    substitutions, R/2 uniform), shuffled and joined by '*'."""
+    rng = np.random.default_rng(seed)
+    half = R // 2
+    starts = rng.integers(0, prot.size - L + 1, half)
+    samp = prot[starts[:, None] + np.arange(L)[None, :]]
+    hit = rng.random(samp.shape) < err
+    samp[hit] = AMINO[rng.integers(0, AMINO.size, int(hit.sum()))]
+    rand = AMINO[rng.integers(0, AMINO.size, (R - half, L))]
+    pep = np.concatenate([samp, rand])[rng.permutation(R)]
+    out = np.empty((R, L + 1), dtype=np.uint8)
+    out[:, :L] = pep
+    out[:, L] = STOP_BYTE
+    return out.reshape(-1)[:-1] if R else np.empty(0, dtype=np.uint8)
+
+
+def codon_read_set(genome: np.ndarray, R: int, L: int = READ_LEN, err: float = 0.01, seed: int = 22) -> np.ndarray:
+    """ASCII of R reads of L bases (L a multiple of 3; R/2 sampled at
+    codon-aligned starts with substitutions, R/2 uniform), shuffled and
+    joined by "NNN"."""
+    assert L % 3 == 0
+    rng = np.random.default_rng(seed)
+    half = R // 2
+    starts = 3 * rng.integers(0, (genome.size - L) // 3 + 1, half)
+    samp = genome[starts[:, None] + np.arange(L)[None, :]]
+    substitute(samp, err, rng)
+    reads = np.concatenate([samp, rng.integers(0, 4, (R - half, L), dtype=np.uint8)])[rng.permutation(R)]
+    out = np.empty((R, L + 3), dtype=np.uint8)
+    out[:, :L] = ACGT[reads]
+    out[:, L:] = N_BYTE
+    return out.reshape(-1)[:-3] if R else np.empty(0, dtype=np.uint8)
+
+
+def alpha_workload(name: str, scale: float = 1.0) -> dict:
+    """Protein or triplet workload (module docstring); scale < 1 shrinks
+    every size for tests."""
+    R = max(2, int(ALPHA_READS * scale))
+    if name == "protein":
+        prot = proteome(max(1000, int(PROTEIN_RESIDUES * scale)))
+        return {"name": name, "bits": max(256, int(ALPHA_BITS * scale)), "insert": prot,
+                "queries": [peptide_set(prot, R)]}
+    if name == "triplet":
+        g = genome_with_repeats(max(3000, int(TRIPLET_GENOME * scale)) // 3 * 3)
+        return {"name": name, "bits": max(256, int(ALPHA_BITS * scale)), "insert": to_ascii(g),
+                "queries": [codon_read_set(g, R)]}
+    raise ValueError("unknown alphabet workload %r" % name)
 
 
 def split_records(stream: np.ndarray) -> list:

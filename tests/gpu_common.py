@@ -21,6 +21,10 @@ def to_dev(arr):
 def gpu_filter(params, bits, kind="sbf"):
     import minimizer_sharded_bloom_amd as M
     k, m, s, H = params
+    if kind == "protein":
+        return M.SuperBloomFilter.protein(k, m, s, H, bits)
+    if kind == "triplet":
+        return M.SuperBloomFilter.triplet(k, m, s, H, bits)
     if kind == "bbf":
         return M.SuperBloomFilter.blocked(k, H, bits)
     if kind == "wide":
@@ -30,6 +34,9 @@ def gpu_filter(params, bits, kind="sbf"):
 
 def oracle_filter(params, bits, kind="sbf"):
     k, m, s, H = params
+    if kind in ("protein", "triplet"):
+        alpha = O.ALPHA_PROTEIN if kind == "protein" else O.ALPHA_TRIPLET
+        return O.OracleFilter(k, m, s, H, bits, alpha=alpha)
     kinds = {"sbf": O.KIND_SBF, "bbf": O.KIND_BBF, "wide": O.KIND_WIDE}
     return O.OracleFilter(k, m, s, H, bits, kind=kinds[kind])
 

@@ -89,3 +89,15 @@ def test_wide_rejects_bad_parameters(lib):
     assert lib.sbf_create_wide(ctypes.byref(h), 31, 16, 28, 65, 512) == _lib.SBF_EINVAL
     assert lib.sbf_create_wide(ctypes.byref(h), 31, 16, 28, 4, 0) == _lib.SBF_EINVAL
     assert h.value is None
+
+
+def test_alphabet_rejects_bad_parameters(lib):
+    """Protein k <= 12 and triplet k <= 10 (k symbols of 5 or 6 bits in 64);
+    unknown alphabets; the usual m, s, H, bits ranges.  Checked before any
+    device use."""
+    h = ctypes.c_void_p(0)
+    P, TR = _lib.SBF_ALPHABET_PROTEIN, _lib.SBF_ALPHABET_TRIPLET
+    for args in [(P, 13, 6, 10, 4, 4096), (P, 0, 1, 1, 4, 4096), (TR, 11, 5, 8, 4, 4096), (3, 5, 3, 4, 4, 4096),
+                 (P, 12, 13, 10, 4, 4096), (P, 12, 6, 0, 4, 4096), (TR, 10, 5, 8, 65, 4096), (TR, 10, 5, 8, 4, 0)]:
+        assert lib.sbf_create_alphabet(ctypes.byref(h), *args) == _lib.SBF_EINVAL, args
+    assert h.value is None
