@@ -16,6 +16,11 @@ runs on.
 
 Prints one JSON line.  `value` = k-mers processed per second over the step
 (genome k-mer starts + read k-mer starts + probe k-mers) / step time.
+
+`--alphabet protein|triplet` times the same step over the protein (k=12,
+m=6, s=10, H=4) or DNA-triplet (k=10, m=5, s=8, H=4) filter on its synthetic
+workload (16 M symbols inserted into 2^28 bits, 2 M queries); those kernels
+read the ASCII text directly, so the step has no pack launches.
 """
 from __future__ import annotations
 
@@ -64,6 +69,36 @@ TAIL = {
 
 def alu_ops_per_kmer(kind: str) -> float:
     return float(sum(FRONT.values()) + sum(TAIL[kind].values()))
+
+
+# Other alphabets (one symbol per lane, sliding windows across lanes): the
+# same per-position work as the DNA front end, except that each position
+# decodes its symbol from ASCII and extends its m-mer and s-mer values by one
+# symbol (64-bit shift, OR, mask each) instead of cutting them from packed
+# words.  Itemised in the design doc.
+ALPHAS = {
+    "protein": {"params": (12, 6, 10, 4), "bytes_per_symbol": 1,
+                "decode": {"decode a letter: or, subtract, compare": 3}},
+    "triplet": {"params": (10, 5, 8, 4), "bytes_per_symbol": 3,
+                "decode": {"decode a codon: 3 x (2 shifts, xor, and, compare against acgt) + 2 shift-ors": 17}},
+}
+ALPHA_WINDOWS = {"m-mer and s-mer extended by one symbol (2 x 64-bit shift, or, and)": 8}
+
+
+def alpha_alu_ops_per_kmer(alpha: str, kind: str) -> float:
+    drop = ("m-mer window (funnel shift)", "s-mer window (2 funnel shifts + shift)")
+    front = sum(v for k2, v in FRONT.items() if k2 not in drop)
+    return float(front + sum(ALPHA_WINDOWS.values()) + sum(ALPHAS[alpha]["decode"].values())
+                 + sum(TAIL[kind].values()))
+
+
+def alpha_bytes_per_kmer(alpha: str, kind: str) -> float:
+    """Text bytes of one symbol streamed once, one 32-byte shard read per run
+    (a write-back too for an insert), a query's answer bit."""
+    k, m = ALPHAS[alpha]["params"][:2]
+    runs = 2.0 / (k - m + 2)
+    b = ALPHAS[alpha]["bytes_per_symbol"]
+    return b + 0.125 + 32 * runs if kind == "query" else b + 64 * runs
 
 
 def _bytes_per_kmer(kind: str, w: int = K - M_ + 1) -> float:
@@ -131,6 +166,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4],
                     help="synthetic configuration (default 2: 8 MiB filter, 5 Mbp genome, 2 M reads)")
+    ap.add_argument("--alphabet", default="dna", choices=["dna", "protein", "triplet"],
+                    help="dna (default, --workload applies) or the protein / DNA-triplet workload")
     ap.add_argument("--probe-n", type=int, default=10_000_000)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline in seconds (0 disables it)")
@@ -140,7 +177,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w: dict, budget_s: float) -> dict:
+def cpu_baseline(w: dict, budget_s: float, params=(K, M_, S_, H_), alpha: str = "dna") -> dict:
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     the first genome bases and read bases (about budget_s seconds of work)
     through its threaded insert/query drivers on the host's cores, and the
@@ -149,16 +186,23 @@ def cpu_baseline(w: dict, budget_s: float) -> dict:
 
     g, reads = w["insert"], w["queries"][0]
     cores = O._threads(0)
-    f = O.OracleFilter(K, M_, S_, H_, w["bits"])
+    al = {"dna": O.ALPHA_DNA, "protein": O.ALPHA_PROTEIN, "triplet": O.ALPHA_TRIPLET}[alpha]
+    sb = 3 if alpha == "triplet" else 1
+    k = params[0]
+
+    def nkm(nbytes):
+        return max(0, nbytes // sb - k + 1)
+
+    f = O.OracleFilter(*params, w["bits"], alpha=al)
     # calibrate insert and query on short pieces, then size the sample to the budget
     n0 = min(g.size, 2_000_000)
     t0 = time.perf_counter()
     f.insert_seq_mt(g[:n0], cores)
     t1 = time.perf_counter()
     f.query_seq_mt(reads[:n0], cores)
-    per_i = (t1 - t0) / max(1, n0 - K + 1)
-    per_q = (time.perf_counter() - t1) / max(1, n0 - K + 1)
-    f = O.OracleFilter(K, M_, S_, H_, w["bits"])
+    per_i = (t1 - t0) / max(1, nkm(n0))
+    per_q = (time.perf_counter() - t1) / max(1, nkm(n0))
+    f = O.OracleFilter(*params, w["bits"], alpha=al)
     n_ins = int(min(g.size, max(1_000_000, budget_s * 0.3 / per_i)))
     n_q = int(min(reads.size, max(1_000_000, (budget_s * 0.9 - n_ins * per_i) / per_q)))
     n_p = int(max(100_000, budget_s * 0.1 / (per_q * cores)))
@@ -169,7 +213,7 @@ def cpu_baseline(w: dict, budget_s: float) -> dict:
     t2 = time.perf_counter()
     f.fpr_probe(n_p, 0x5EED)
     t3 = time.perf_counter()
-    kmers = (n_ins - K + 1) + (n_q - K + 1) + n_p
+    kmers = nkm(n_ins) + nkm(n_q) + n_p
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as fh:
@@ -178,10 +222,10 @@ def cpu_baseline(w: dict, budget_s: float) -> dict:
         pass
     return {"value": kmers / (t3 - t0) / 1e9, "unit": "Gk-mers/s", "cores": cores, "kind": "oracle",
             "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
-            "sample": "C oracle, %d threads: insert of the first %d genome bases, query of the first %d read "
-                      "bases, %d probe k-mers on one thread (%.1f s)" % (cores, n_ins, n_q, n_p, t3 - t0),
-            "insert_gkmers_s": (n_ins - K + 1) / (t1 - t0) / 1e9,
-            "query_gkmers_s": (n_q - K + 1) / (t2 - t1) / 1e9}
+            "sample": "C oracle, %d threads: insert of the first %d bytes of the inserted text, query of the first %d bytes of the "
+                      "query text, %d probe k-mers on one thread (%.1f s)" % (cores, n_ins, n_q, n_p, t3 - t0),
+            "insert_gkmers_s": nkm(n_ins) / (t1 - t0) / 1e9,
+            "query_gkmers_s": nkm(n_q) / (t2 - t1) / 1e9}
 
 
 def main():
@@ -199,6 +243,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     lib = M.lib()
+    if a.alphabet != "dna":
+        return main_alpha(a, torch, M, S, lib)
 
     t_gen = time.perf_counter()
     w = S.workload(a.workload)
@@ -310,6 +356,107 @@ def main():
     }
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def main_alpha(a, torch, M, S, lib):
+    """The step over a protein or DNA-triplet filter: clear, insert the
+    reference text, query the reads, probe (no pack launches: these kernels
+    decode the ASCII themselves)."""
+    alpha = a.alphabet
+    k, m, s, H = ALPHAS[alpha]["params"]
+    t_gen = time.perf_counter()
+    w = S.alpha_workload(alpha)
+    gen_s = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    ref = torch.from_numpy(w["insert"]).to(dev)
+    reads = torch.from_numpy(w["queries"][0]).to(dev)
+    LG, LR = ref.numel(), reads.numel()
+    f = (M.SuperBloomFilter.protein if alpha == "protein" else M.SuperBloomFilter.triplet)(k, m, s, H, w["bits"])
+    out = torch.empty(f.num_answer_words(LR), dtype=torch.int64, device=dev)
+    hits = torch.zeros(1, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    names = ["clear", "insert", "query", "probe"]
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record(stream)
+        mark(0)
+        M.check(lib.sbf_clear(f.handle, sp), "clear")
+        mark(1)
+        M.check(lib.sbf_insert_seq(f.handle, ref.data_ptr(), LG, M.SBF_DEVICE, sp), "insert")
+        mark(2)
+        M.check(lib.sbf_query_seq(f.handle, reads.data_ptr(), LR, out.data_ptr(), M.SBF_DEVICE, sp), "query")
+        mark(3)
+        M.check(lib.sbf_fpr_probe_device(f.handle, a.probe_n, 0x5EED, hits.data_ptr(), sp), "probe")
+        mark(4)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(a.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / a.steps
+    phase = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / a.steps for i, n in enumerate(names)}
+
+    if a.calibrate_copy:
+        src = torch.ones(1 << 25, dtype=torch.int64, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        torch.add(src, 0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    nk_g, nk_r = f.num_symbols(LG) - k + 1, f.num_symbols(LR) - k + 1
+    total = nk_g + nk_r + a.probe_n
+    value = total / (ms_step * 1e-3) / 1e9
+    ins_rate = nk_g / (phase["insert"] * 1e-3)
+    q_rate = nk_r / (phase["query"] * 1e-3)
+    sha = kernel_sources_sha256()
+
+    def roof(kind, rate):
+        ops = alpha_alu_ops_per_kmer(alpha, kind)
+        alu, mem = rate * ops, rate * alpha_bytes_per_kmer(alpha, kind)
+        tr = measured_traffic(alpha, kind, sha)
+        traffic = None if tr is None else tr["bytes"]
+        extra = {} if tr is None else {"traffic_fetch": tr["fetch"], "traffic_write": tr["write"],
+                                       "traffic_source": tr["source"],
+                                       "traffic_per_kmer": tr["bytes"] / (nk_r if kind == "query" else nk_g)}
+        return (dict({"bound": "alu", "achieved": alu / 1e12, "peak": ALU_PEAK / 1e12, "unit": "T lane-instr/s",
+                      "frac": alu / ALU_PEAK, "traffic": traffic, "kernel": kind, "per_kmer_ops": ops}, **extra),
+                dict({"bound": "hbm", "achieved": mem / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                      "frac": mem / HBM_PEAK, "traffic": traffic, "kernel": kind,
+                      "per_kmer_bytes": alpha_bytes_per_kmer(alpha, kind)}, **extra))
+
+    dom = "query" if phase["query"] >= phase["insert"] else "insert"
+    alu, mem = roof(dom, q_rate if dom == "query" else ins_rate)
+    primary, secondary = (alu, mem) if alu["frac"] >= mem["frac"] else (mem, alu)
+    res = {
+        "metric": "insert & query Gk-mers/s, %s alphabet (k=%d,m=%d,s=%d,H=%d) + fraction of ALU/HBM roofline"
+                  % (alpha, k, m, s, H),
+        "value": round(value, 3), "unit": "Gk-mers/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u64", "data": "synthetic",
+        "config": {"workload": alpha, "k": k, "m": m, "s": s, "H": H, "filter_bits": w["bits"],
+                   "insert_bytes": LG, "query_bytes": LR, "probe_kmers": a.probe_n, "kmers_per_step": total},
+        "roofline": primary, "roofline_other": secondary,
+        "insert_gkmers_s": round(ins_rate / 1e9, 3), "query_gkmers_s": round(q_rate / 1e9, 3),
+        "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
+        "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},
+        "wall_s_timed": round(wall, 3), "gen_s": round(gen_s, 2), "kernel_sources_sha256": sha,
+    }
+    if a.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, (k, m, s, H), alpha)
     print(json.dumps(res), flush=True)
 
 

@@ -94,6 +94,35 @@ struct Alphabet<SBF_ALPHABET_TRIPLET> {
     }
 };
 
+// Parameters of one kernel instance: compile-time (K, M, S, H nonzero, every
+// loop unrolled and every mask index static) or, with zeros, taken from the
+// run-time Params (the same code with run-time loops).
+template <int A, int K, int M, int S, int H>
+struct ACfg {
+    static constexpr int kAlpha = A;
+    static constexpr bool kStatic = K != 0;
+    static constexpr uint32_t kK = K, kM = M, kS = S, kH = H;
+    __device__ static __forceinline__ uint32_t k(const Params& P) { return K ? (uint32_t)K : P.k; }
+    __device__ static __forceinline__ uint32_t m(const Params& P) { return M ? (uint32_t)M : P.m; }
+    __device__ static __forceinline__ uint32_t s(const Params& P) { return S ? (uint32_t)S : P.s; }
+    __device__ static __forceinline__ uint32_t h(const Params& P) { return H ? (uint32_t)H : P.H; }
+};
+
+// h_min of a value below 2^32: (v + G) * C1 = v * C1 + G * C1 (mod 2^64), a
+// 32 x 64-bit product.
+__device__ __forceinline__ uint64_t hash_min32(uint32_t v)
+{
+    constexpr uint64_t kGC1 = kGolden * kMulA;
+    const uint64_t u = (uint64_t)v * kMulA + kGC1;
+    return u ^ (u >> 32);
+}
+
+// Every bit of the four masks is set in the shard words w.
+__device__ __forceinline__ bool covers(const uint64_t (&w)[4], const uint64_t (&mk)[4])
+{
+    return ((~w[0] & mk[0]) | (~w[1] & mk[1]) | (~w[2] & mk[2]) | (~w[3] & mk[3])) == 0;
+}
+
 // Value of lane l+d in lane l for a wave-uniform d >= 1 (lanes past 63 read
 // garbage; only halo lanes look there).
 __device__ __forceinline__ uint32_t lane_down(uint32_t v, uint32_t d, uint32_t lane)
@@ -112,6 +141,7 @@ __device__ __forceinline__ uint64_t lane_down(uint64_t v, uint32_t d, uint32_t l
 __device__ __forceinline__ uint64_t window_min(uint64_t v, uint32_t w, uint32_t lane)
 {
     uint32_t span = 1;
+#pragma unroll
     while (2u * span <= w) {
         const uint64_t o = lane_down(v, span, lane);
         v = o < v ? o : v;
@@ -129,12 +159,15 @@ __device__ __forceinline__ void window_or(uint64_t (&mk)[4], uint32_t z, uint32_
 {
     const uint32_t nq = H < 4u ? H : 4u;
     uint32_t span = 1;
+#pragma unroll
     while (2u * span <= z) {
+#pragma unroll
         for (uint32_t q = 0; q < nq; ++q)
             mk[q] |= lane_down(mk[q], span, lane);
         span *= 2u;
     }
     if (span < z)
+#pragma unroll
         for (uint32_t q = 0; q < nq; ++q)
             mk[q] |= lane_down(mk[q], z - span, lane);
 }
@@ -143,11 +176,12 @@ __device__ __forceinline__ void window_or(uint64_t (&mk)[4], uint32_t z, uint32_
 // starts at this lane, its shard, its four sector masks and whether it is
 // to be processed (complete within the wave, every symbol valid, start
 // before `end`).
-template <int A>
+template <class C>
 __device__ __forceinline__ bool wave_step(const SeqArgs& a, const Params& P, uint64_t base, uint64_t end,
                                           uint32_t lane, uint32_t& shard, uint64_t (&mk)[4])
 {
-    using Al = Alphabet<A>;
+    using Al = Alphabet<C::kAlpha>;
+    const uint32_t k = C::k(P), m = C::m(P), s = C::s(P), H = C::h(P);
     const uint64_t p = base + lane;
     bool ok = false;
     uint32_t sym = 0;
@@ -156,42 +190,78 @@ __device__ __forceinline__ bool wave_step(const SeqArgs& a, const Params& P, uin
     const uint64_t V = __ballot(ok);
 
     // m-mer and s-mer starting here: symbols of lanes l .. l+max(m,s)-1
-    const uint32_t nr = P.m > P.s ? P.m : P.s;
-    uint64_t acc = sym, vm = sym, vs = sym;
-    uint32_t t = sym;
-    for (uint32_t i = 1; i < nr; ++i) {
-        t = from_next_lane(t);
-        acc = (acc << Al::B) | t;
-        if (i + 1u == P.m)
-            vm = acc;
-        if (i + 1u == P.s)
-            vs = acc;
+    uint64_t hm, vs;
+    if constexpr (C::kStatic) {
+        // 32-bit rolling values of up to P symbols (P * B <= 32); an s-mer of
+        // more than P symbols is its first P and the (s-P)-symbol value that
+        // lane l+P holds
+        constexpr uint32_t P = 32u / Al::B;
+        static_assert(C::kS <= 2 * P && C::kM <= P, "window longer than two 32-bit pieces");
+        constexpr uint32_t S1 = C::kS <= P ? C::kS : P, S2 = C::kS - S1;
+        constexpr uint32_t NR = C::kM > S1 ? C::kM : S1;
+        uint32_t acc = sym, t = sym, am = sym, as1 = sym, as2 = sym;
+#pragma unroll
+        for (uint32_t i = 1; i < NR; ++i) {
+            t = from_next_lane(t);
+            acc = (acc << Al::B) | t;
+            if (i + 1u == C::kM)
+                am = acc;
+            if (i + 1u == S1)
+                as1 = acc;
+            if (i + 1u == S2)
+                as2 = acc;
+        }
+        hm = hash_min32(am);
+        if constexpr (S2 > 0)
+            vs = ((uint64_t)as1 << (Al::B * S2)) | lane_down(as2, P, lane);
+        else
+            vs = as1;
+    } else {
+        const uint32_t nr = m > s ? m : s;
+        uint64_t acc = sym, vm = sym;
+        uint32_t t = sym;
+        vs = sym;
+        for (uint32_t i = 1; i < nr; ++i) {
+            t = from_next_lane(t);
+            acc = (acc << Al::B) | t;
+            if (i + 1u == m)
+                vm = acc;
+            if (i + 1u == s)
+                vs = acc;
+        }
+        hm = hash_min(vm);
     }
-    shard = (uint32_t)window_min(hash_min(vm), P.k - P.m + 1u, lane) & a.shard_mask;
+    shard = (uint32_t)window_min(hm, k - m + 1u, lane) & a.shard_mask;
 
     const uint64_t h = hash_s(vs);
     mk[0] = mk[1] = mk[2] = mk[3] = 0;
-    for (uint32_t j = 0; j < P.H; ++j) {
-        const uint64_t bit = 1ull << bit_addr_rt(h, j, P.H);
+    if constexpr (C::kStatic) {
 #pragma unroll
-        for (uint32_t q = 0; q < 4; ++q)
-            mk[q] |= (j & 3u) == q ? bit : 0ull;
+        for (uint32_t j = 0; j < H; ++j)
+            mk[j & 3u] |= 1ull << bit_addr_rt(h, j, H);
+    } else {
+        for (uint32_t j = 0; j < H; ++j) {
+            const uint64_t bit = 1ull << bit_addr_rt(h, j, H);
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q)
+                mk[q] |= (j & 3u) == q ? bit : 0ull;
+        }
     }
-    window_or(mk, P.k - P.s + 1u, P.H, lane);
+    window_or(mk, k - s + 1u, H, lane);
 
     // k-mer l is valid iff symbols l .. l+k-1 are (bits past lane 63 are 0)
-    const uint64_t kv = run_and_rt(V, P.k);
-    return ((kv >> lane) & 1ull) && lane + P.k <= 64u && p < end;
+    const uint64_t kv = run_and_rt(V, k);
+    return ((kv >> lane) & 1ull) && lane + k <= 64u && p < end;
 }
 
-template <int A>
+template <class C>
 __global__ __launch_bounds__(256) void alpha_insert_kernel(SeqArgs a, Params P)
 {
     __shared__ uint64_t rec_mk[4][64][4];
     __shared__ uint32_t rec_sh[4][64];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t S = 65u - P.k;  // k-mers per wave step
+    const uint32_t S = 65u - C::k(P);  // k-mers per wave step
     const uint64_t ntasks = (a.nk + kTask - 1) / kTask;
     const uint64_t wstride = (uint64_t)gridDim.x * 4u;
     const uint64_t le = (2ull << lane) - 1ull;  // lanes 0 .. lane
@@ -201,7 +271,7 @@ __global__ __launch_bounds__(256) void alpha_insert_kernel(SeqArgs a, Params P)
         for (uint64_t base = t0; base < t1; base += S) {
             uint32_t shard;
             uint64_t mk[4];
-            const bool kv = wave_step<A>(a, P, base, t1, lane, shard, mk);
+            const bool kv = wave_step<C>(a, P, base, t1, lane, shard, mk);
             // runs: consecutive valid k-mers of one shard
             const uint32_t psh = from_prev_lane(shard);
             const uint32_t pkv = from_prev_lane(kv ? 1u : 0u);
@@ -236,12 +306,12 @@ __global__ __launch_bounds__(256) void alpha_insert_kernel(SeqArgs a, Params P)
     }
 }
 
-template <int A>
+template <class C>
 __global__ __launch_bounds__(256) void alpha_query_kernel(SeqArgs a, Params P)
 {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t S = 65u - P.k;
+    const uint32_t S = 65u - C::k(P);
     const uint64_t ntasks = (a.nk + kTask - 1) / kTask;
     const uint64_t wstride = (uint64_t)gridDim.x * 4u;
     for (uint64_t task = (uint64_t)blockIdx.x * 4u + wv; task < ntasks; task += wstride) {
@@ -253,12 +323,11 @@ __global__ __launch_bounds__(256) void alpha_query_kernel(SeqArgs a, Params P)
         for (uint64_t base = t0; base < t1; base += S) {
             uint32_t shard;
             uint64_t mk[4];
-            bool pres = wave_step<A>(a, P, base, t1, lane, shard, mk);
+            bool pres = wave_step<C>(a, P, base, t1, lane, shard, mk);
             if (pres) {
                 uint64_t w[4];
                 load_shard(a.filter, shard, w);
-                pres = ((w[0] & mk[0]) == mk[0]) & ((w[1] & mk[1]) == mk[1]) & ((w[2] & mk[2]) == mk[2]) &
-                       ((w[3] & mk[3]) == mk[3]);
+                pres = covers(w, mk);
             }
             const uint64_t bits = __ballot(pres);  // bits 0 .. S-1
             acc |= bits << nb;
@@ -279,36 +348,44 @@ __global__ __launch_bounds__(256) void alpha_query_kernel(SeqArgs a, Params P)
 }
 
 // One random k-mer per lane ([cuSBF] §V-D), every step from its definition.
-template <int A>
+template <class C>
 __global__ __launch_bounds__(256) void alpha_probe_kernel(ProbeArgs a, Params P)
 {
-    using Al = Alphabet<A>;
+    using Al = Alphabet<C::kAlpha>;
     const uint32_t B = Al::B;
-    const uint64_t mmask = (1ull << (B * P.m)) - 1ull;  // B * m <= 60
-    const uint64_t smask = (1ull << (B * P.s)) - 1ull;
+    const uint32_t k = C::k(P), m = C::m(P), s = C::s(P), H = C::h(P);
+    const uint64_t mmask = (1ull << (B * m)) - 1ull;  // B * m <= 60
+    const uint64_t smask = (1ull << (B * s)) - 1ull;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     uint32_t cnt = 0;
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += stride) {
-        const uint64_t x = Al::probe(a.seed, i, P.k);
+        const uint64_t x = Al::probe(a.seed, i, k);
         uint64_t mn = ~0ull;
-        for (uint32_t j = 0; j + P.m <= P.k; ++j) {
-            const uint64_t hm = hash_min((x >> (B * (P.k - P.m - j))) & mmask);
+#pragma unroll
+        for (uint32_t j = 0; j + m <= k; ++j) {
+            const uint64_t hm = hash_min((x >> (B * (k - m - j))) & mmask);
             mn = hm < mn ? hm : mn;
         }
         uint64_t mk[4] = {0, 0, 0, 0};
-        for (uint32_t j = 0; j + P.s <= P.k; ++j) {
-            const uint64_t h = hash_s((x >> (B * (P.k - P.s - j))) & smask);
-            for (uint32_t t = 0; t < P.H; ++t) {
-                const uint64_t bit = 1ull << bit_addr_rt(h, t, P.H);
 #pragma unroll
-                for (uint32_t q = 0; q < 4; ++q)
-                    mk[q] |= (t & 3u) == q ? bit : 0ull;
+        for (uint32_t j = 0; j + s <= k; ++j) {
+            const uint64_t h = hash_s((x >> (B * (k - s - j))) & smask);
+            if constexpr (C::kStatic) {
+#pragma unroll
+                for (uint32_t t = 0; t < H; ++t)
+                    mk[t & 3u] |= 1ull << bit_addr_rt(h, t, H);
+            } else {
+                for (uint32_t t = 0; t < H; ++t) {
+                    const uint64_t bit = 1ull << bit_addr_rt(h, t, H);
+#pragma unroll
+                    for (uint32_t q = 0; q < 4; ++q)
+                        mk[q] |= (t & 3u) == q ? bit : 0ull;
+                }
             }
         }
         uint64_t w[4];
         load_shard(a.filter, (uint32_t)mn & a.shard_mask, w);
-        cnt += ((w[0] & mk[0]) == mk[0]) & ((w[1] & mk[1]) == mk[1]) & ((w[2] & mk[2]) == mk[2]) &
-               ((w[3] & mk[3]) == mk[3]);
+        cnt += covers(w, mk) ? 1u : 0u;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
@@ -326,25 +403,25 @@ uint32_t task_blocks(uint64_t nk)
     return (uint32_t)(b ? b : 1);
 }
 
-template <int A>
+template <class C>
 hipError_t alpha_insert(const SeqArgs& a, const Params& P)
 {
     if (a.nk == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(alpha_insert_kernel<A>, dim3(task_blocks(a.nk)), dim3(256), 0, a.stream, a, P);
+    hipLaunchKernelGGL(alpha_insert_kernel<C>, dim3(task_blocks(a.nk)), dim3(256), 0, a.stream, a, P);
     return hipGetLastError();
 }
 
-template <int A>
+template <class C>
 hipError_t alpha_query(const SeqArgs& a, const Params& P)
 {
     if (a.nk == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(alpha_query_kernel<A>, dim3(task_blocks(a.nk)), dim3(256), 0, a.stream, a, P);
+    hipLaunchKernelGGL(alpha_query_kernel<C>, dim3(task_blocks(a.nk)), dim3(256), 0, a.stream, a, P);
     return hipGetLastError();
 }
 
-template <int A>
+template <class C>
 hipError_t alpha_probe(const ProbeArgs& a, const Params& P)
 {
     if (a.n == 0)
@@ -352,26 +429,43 @@ hipError_t alpha_probe(const ProbeArgs& a, const Params& P)
     uint64_t b = (a.n + 255) / 256;
     if (b > 8192)
         b = 8192;
-    hipLaunchKernelGGL(alpha_probe_kernel<A>, dim3((uint32_t)b), dim3(256), 0, a.stream, a, P);
+    hipLaunchKernelGGL(alpha_probe_kernel<C>, dim3((uint32_t)b), dim3(256), 0, a.stream, a, P);
     return hipGetLastError();
 }
 
-template <int A>
+template <class C>
 KernelSet make_alpha()
 {
     KernelSet ks;
-    ks.insert = &alpha_insert<A>;
-    ks.query = &alpha_query<A>;
-    ks.probe = &alpha_probe<A>;
-    ks.specialized = 0;
+    ks.insert = &alpha_insert<C>;
+    ks.query = &alpha_query<C>;
+    ks.probe = &alpha_probe<C>;
+    ks.specialized = C::kStatic ? 1 : 0;
     return ks;
 }
 
+// Compile-time instances: the default protein (k=12, m=6, s=10, H=4) and
+// triplet (k=10, m=5, s=8, H=4) parameters and one neighbour of each.
+struct AlphaEntry {
+    uint32_t alpha, k, m, s, H;
+    KernelSet (*make)();
+};
+constexpr uint32_t kP = SBF_ALPHABET_PROTEIN, kT = SBF_ALPHABET_TRIPLET;
+const AlphaEntry kAlphaTable[] = {
+    {kP, 12, 6, 10, 4, &make_alpha<ACfg<kP, 12, 6, 10, 4>>},
+    {kP, 9, 4, 7, 3, &make_alpha<ACfg<kP, 9, 4, 7, 3>>},
+    {kT, 10, 5, 8, 4, &make_alpha<ACfg<kT, 10, 5, 8, 4>>},
+    {kT, 7, 3, 7, 2, &make_alpha<ACfg<kT, 7, 3, 7, 2>>},
+};
+
 }  // namespace
 
-KernelSet alpha_kernels(uint32_t alpha)
+KernelSet alpha_kernels(const Params& P)
 {
-    return alpha == SBF_ALPHABET_TRIPLET ? make_alpha<SBF_ALPHABET_TRIPLET>() : make_alpha<SBF_ALPHABET_PROTEIN>();
+    for (const AlphaEntry& e : kAlphaTable)
+        if (e.alpha == P.alpha && e.k == P.k && e.m == P.m && e.s == P.s && e.H == P.H)
+            return e.make();
+    return P.alpha == SBF_ALPHABET_TRIPLET ? make_alpha<ACfg<kT, 0, 0, 0, 0>>() : make_alpha<ACfg<kP, 0, 0, 0, 0>>();
 }
 
 }  // namespace sbf

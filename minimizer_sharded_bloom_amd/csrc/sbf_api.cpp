@@ -148,7 +148,7 @@ int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
     h->num_shards = n;
     h->wps = wps;
     if (P.alpha != SBF_ALPHABET_DNA)
-        h->ks = sbf::alpha_kernels(P.alpha);
+        h->ks = sbf::alpha_kernels(P);
     else if (!sbf::find_specialized(P, &h->ks))
         h->ks = sbf::generic_kernels();
     hipError_t e = hipGetDevice(&h->device);

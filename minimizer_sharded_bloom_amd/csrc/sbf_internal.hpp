@@ -60,8 +60,9 @@ struct SpecEntry {
 bool find_specialized(const Params& p, KernelSet* out);
 // Kernel set for any valid parameters (one k-mer per lane, runtime loops).
 KernelSet generic_kernels();
-// Kernel set of the protein (alpha 1) or triplet (alpha 2) Super Bloom filter.
-KernelSet alpha_kernels(uint32_t alpha);
+// Kernel set of the protein (alpha 1) or triplet (alpha 2) Super Bloom
+// filter: compile-time specialized for a few parameter sets, else run-time.
+KernelSet alpha_kernels(const Params& P);
 
 // Small utility launches.
 hipError_t launch_pack(const char* ascii, uint64_t len, uint32_t* codes, uint32_t* valid, hipStream_t st);

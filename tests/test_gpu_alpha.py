@@ -23,6 +23,9 @@ PARAMS = {
     "triplet": [(10, 5, 8, 4), (7, 3, 7, 2), (10, 10, 6, 11), (1, 1, 1, 4), (4, 2, 3, 4), (10, 2, 10, 8)],
 }
 CASES = [(a, p) for a in PARAMS for p in PARAMS[a]]
+# parameter sets with compile-time kernels; every other set takes the
+# run-time kernels of its alphabet
+SPECIALIZED = {"protein": [(12, 6, 10, 4), (9, 4, 7, 3)], "triplet": [(10, 5, 8, 4), (7, 3, 7, 2)]}
 
 
 def text(alpha, rng, nsym, bad=0.002):
@@ -61,6 +64,7 @@ def test_alpha_parity(alpha, params):
     ins = text(alpha, rng, 20011)
     qs = [ins[:9000], text(alpha, rng, 7777)]
     g, o = pair(alpha, params, 2**15, [ins], qs)
+    assert g.specialized == (params in SPECIALIZED[alpha])
     assert g.fpr_probe(100_000, 0xA1) == o.fpr_probe(100_000, 0xA1)
 
 
