@@ -118,3 +118,60 @@ def test_long_read_batch_error_rate():
         diff = np.flatnonzero(a[:m] != c[:m])
         first.append(diff[0] if diff.size else m)
     assert 15 < np.mean(first) < 30
+
+
+def test_proteome_layout():
+    """Residues from the 20 standard amino acids, near-uniform; one '*' per
+    protein with the stated mean length; copied segments make some 20-mers
+    repeat; seeded."""
+    p = S.proteome(400_000)
+    assert p.size == 400_000 and (p == S.proteome(400_000)).all()
+    stops = int((p == S.STOP_BYTE).sum())
+    res = p[p != S.STOP_BYTE]
+    assert set(np.unique(res).tolist()) <= set(S.AMINO.tolist())
+    freq = np.bincount(res, minlength=256)[S.AMINO] / res.size
+    assert abs(freq - 0.05).max() < 0.005
+    mean_len = p.size / stops
+    assert 380 < mean_len < 460  # exp(ln 350 + 0.6^2 / 2) ~ 419, plus the stop byte
+    win = np.lib.stride_tricks.sliding_window_view(p[:200_000], 20)
+    _, counts = np.unique(win, axis=0, return_counts=True)
+    assert (counts > 1).sum() > 100  # copied segments
+
+
+def test_peptide_set_layout():
+    """50-residue peptides joined by '*'; with no substitutions the sampled
+    half are proteome substrings and the uniform half (almost) never are."""
+    p = S.proteome(50_000)
+    q = S.peptide_set(p, 400, err=0.0)
+    assert q.size == 400 * 51 - 1
+    peps = np.append(q, np.uint8(S.STOP_BYTE)).reshape(400, 51)
+    assert (peps[:, 50] == S.STOP_BYTE).all()
+    text = p.tobytes()
+    found = sum(peps[i, :50].tobytes() in text for i in range(400))
+    assert 190 <= found <= 210
+
+
+def test_codon_read_set_layout():
+    """150-bp reads joined by "NNN" (every read starts on a codon of the
+    stream); with no substitutions the sampled half are genome substrings at
+    codon-aligned offsets."""
+    g = S.genome_with_repeats(60_000)
+    q = S.codon_read_set(g, 300, err=0.0)
+    assert q.size == 300 * 153 - 3
+    reads = np.append(q, np.full(3, S.N_BYTE, dtype=np.uint8)).reshape(300, 153)
+    assert (reads[:, 150:] == S.N_BYTE).all()
+    gt = S.to_ascii(g).tobytes()
+    hits = 0
+    for r in reads[:, :150]:
+        at = gt.find(r.tobytes())
+        if at >= 0:
+            hits += 1
+            assert at % 3 == 0
+    assert 140 <= hits <= 160
+
+
+def test_alpha_workload_sizes():
+    w = S.alpha_workload("protein", scale=0.01)
+    assert w["insert"].size == 160_000 and w["bits"] == int(S.ALPHA_BITS * 0.01)
+    w = S.alpha_workload("triplet", scale=0.01)
+    assert w["insert"].size % 3 == 0 and w["queries"][0].size == 20_000 * 153 - 3
