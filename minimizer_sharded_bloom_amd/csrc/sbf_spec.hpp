@@ -34,13 +34,17 @@
 
 namespace sbf {
 
-template <int K_, int M_, int S_, int H_>
+// KL_ = 0: 16 k-mers per lane, or 32 when the halo exceeds 16; a nonzero
+// KL_ (16 or 32) fixes it.
+template <int K_, int M_, int S_, int H_, int KL_ = 0>
 struct Cfg {
     static constexpr int k = K_, m = M_, s = S_, H = H_;
     static constexpr int W = k - m + 1;    // m-mers per k-mer
     static constexpr int Z = k - s + 1;    // s-mers per k-mer (Findere z+1)
     static constexpr int HALO = (W - 1 > Z - 1) ? W - 1 : Z - 1;
-    static constexpr int KL = HALO <= 16 ? 16 : 32;  // k-mers per lane
+    static constexpr int KL = KL_ ? KL_ : (HALO <= 16 ? 16 : 32);  // k-mers per lane
+    static_assert(KL == 16 || KL == 32, "16 or 32 k-mers per lane");
+    static_assert(HALO <= KL, "halo must come from the next lane alone");
     static constexpr int LW = 63;                    // working lanes per wave
     static constexpr int KPW = KL * LW;              // k-mers per wave
     static constexpr int ND = KL / 16 + 2;           // code words per lane
@@ -789,13 +793,18 @@ hipError_t launch_probe(const ProbeArgs& a, const Params&)
     return hipGetLastError();
 }
 
+// The query takes 32 k-mers per lane while k-s+1 <= 8: its per-lane work
+// (code loads, halo moves, scan, gather) is then spread over twice the
+// k-mers.  More s-mers per k-mer make the doubling levels too large for 32
+// (over 160 VGPRs), and the insert measures faster at 16.
 template <int K, int M, int S, int H>
 KernelSet spec_set()
 {
     using C = Cfg<K, M, S, H>;
+    using CQ = Cfg<K, M, S, H, (K - S + 1 <= 8 ? 32 : 0)>;
     KernelSet ks;
     ks.insert = &launch_insert<C>;
-    ks.query = &launch_query<C>;
+    ks.query = &launch_query<CQ>;
     ks.probe = &launch_probe<C>;
     ks.specialized = 1;
     return ks;
