@@ -159,6 +159,58 @@ def measured_traffic(workload: str, kernel: str, sha: str):
     return None
 
 
+def valid_kmer_count(text, k: int, alpha: str = "dna") -> int:
+    """k-mer starts whose k symbols are all valid (positions with an invalid
+    symbol, e.g. a record separator, are not): the throughput count of valid
+    k-mers, next to the count of k-mer starts."""
+    import numpy as np
+
+    if alpha == "protein":
+        v = ((text | 0x20) >= ord("a")) & ((text | 0x20) <= ord("z"))
+    else:
+        ok = np.zeros(256, dtype=bool)
+        ok[list(b"ACGTacgt")] = True
+        v = ok[text]
+        if alpha == "triplet":
+            n = v.size // 3
+            v = v[:3 * n].reshape(n, 3).all(axis=1)
+    edges = np.concatenate([[-1], np.flatnonzero(~v), [v.size]])
+    runs = np.diff(edges) - 1
+    return int(np.maximum(runs - k + 1, 0).sum())
+
+
+def matched_ceilings(lib, torch, filt, stream, n_ops: int = 1 << 25) -> dict:
+    """Random 32-byte shard reads over the filter itself and random 32-byte
+    shard OR-updates (four lanes, one 64-bit atomic each) over a scratch table
+    of the same size, in G operations/s (median of 3 after one warm-up):
+    the memory ceilings the query / probe and the insert flush can reach."""
+    n_sh = filt.num_shards
+    table = lib.sbf_filter_device_ptr(filt.handle)
+    scratch = torch.zeros(4 * n_sh, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int64, device="cuda")
+    sp = stream.cuda_stream
+    out = {"table_bytes": 32 * n_sh, "ops": n_ops}
+    for name, call in (("shard_reads_g_per_s",
+                        lambda seed: lib.sbf_membench_shard_reads(table, n_sh, n_ops, seed, sink.data_ptr(), sp)),
+                       ("shard_ors_g_per_s",
+                        lambda seed: lib.sbf_membench_shard_ors(scratch.data_ptr(), n_sh, n_ops, seed, sp))):
+        ts = []
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = call(0xC0FFEE + rep)
+            e1.record(stream)
+            if rc != 0:
+                raise RuntimeError("%s failed (%d)" % (name, rc))
+            torch.cuda.synchronize()
+            if rep:
+                ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        out[name] = round(n_ops / (ts[1] * 1e-3) / 1e9, 3)
+    del scratch
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +223,8 @@ def parse():
     ap.add_argument("--probe-n", type=int, default=10_000_000)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline in seconds (0 disables it)")
+    ap.add_argument("--no-membench", dest="membench", action="store_false",
+                    help="skip the matched-ceiling microbenchmarks (random shard reads / OR-updates) run after timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 256 MiB device copy (elementwise kernel) whose "
                          "FETCH_SIZE/WRITE_SIZE counters scale the filter kernels' counters")
@@ -214,6 +268,13 @@ def cpu_baseline(w: dict, budget_s: float, params=(K, M_, S_, H_), alpha: str = 
     f.fpr_probe(n_p, 0x5EED)
     t3 = time.perf_counter()
     kmers = nkm(n_ins) + nkm(n_q) + n_p
+    # the plain single-threaded oracle on a short sample of both inputs
+    n1 = int(min(g.size, reads.size, 1_000_000))
+    f1 = O.OracleFilter(*params, w["bits"], alpha=al)
+    s0 = time.perf_counter()
+    f1.insert_seq(g[:n1])
+    f1.query_seq(reads[:n1])
+    single = 2 * nkm(n1) / (time.perf_counter() - s0) / 1e9
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as fh:
@@ -225,7 +286,9 @@ def cpu_baseline(w: dict, budget_s: float, params=(K, M_, S_, H_), alpha: str = 
             "sample": "C oracle, %d threads: insert of the first %d bytes of the inserted text, query of the first %d bytes of the "
                       "query text, %d probe k-mers on one thread (%.1f s)" % (cores, n_ins, n_q, n_p, t3 - t0),
             "insert_gkmers_s": nkm(n_ins) / (t1 - t0) / 1e9,
-            "query_gkmers_s": nkm(n_q) / (t2 - t1) / 1e9}
+            "query_gkmers_s": nkm(n_q) / (t2 - t1) / 1e9,
+            "single_thread_gkmers_s": single,
+            "single_thread_sample": "insert then query of the first %d bytes of each text on one thread" % n1}
 
 
 def main():
@@ -302,6 +365,8 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / a.steps
     phase = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / a.steps for i, n in enumerate(names)}
+    phase_med = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    ceilings = matched_ceilings(lib, torch, f, stream) if a.membench else None
 
     if a.calibrate_copy:
         src = torch.ones(1 << 25, dtype=torch.int64, device=dev)   # 256 MiB
@@ -314,6 +379,7 @@ def main():
     nk_g, nk_r = LG - K + 1, LR - K + 1
     total = nk_g + nk_r + a.probe_n
     value = total / (ms_step * 1e-3) / 1e9
+    vk_g, vk_r = valid_kmer_count(genome_h, K), valid_kmer_count(reads_h, K)
     ins_rate = nk_g / (phase["insert"] * 1e-3)
     q_rate = nk_r / (phase["query"] * 1e-3)
 
@@ -351,9 +417,21 @@ def main():
         "pack_gbases_s": round((LG + LR) / ((phase["pack_genome"] + phase["pack_reads"]) * 1e-3) / 1e9, 3),
         "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
         "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},
+        "phase_ms_median": {k2: round(v, 4) for k2, v in phase_med.items()},
+        "valid_kmers": {"insert": vk_g, "query": vk_r},
+        "value_valid_gkmers_s": round((vk_g + vk_r + a.probe_n) / (ms_step * 1e-3) / 1e9, 3),
+        "insert_valid_gkmers_s": round(vk_g / (phase["insert"] * 1e-3) / 1e9, 3),
+        "query_valid_gkmers_s": round(vk_r / (phase["query"] * 1e-3) / 1e9, 3),
         "wall_s_timed": round(wall, 3), "gen_s": round(gen_s, 2),
         "kernel_sources_sha256": sha,
     }
+    if ceilings is not None:
+        # runs per k-mer for random minimizers, 2/(w+1): the insert's record
+        # flushes and the query's shard reads, set against the matched ceilings
+        runs = 2.0 / (K - M_ + 2)
+        ceilings["insert_records_est_g_per_s"] = round(ins_rate * runs / 1e9, 3)
+        ceilings["insert_frac_of_or_ceiling"] = round(ins_rate * runs / 1e9 / ceilings["shard_ors_g_per_s"], 3)
+        res["matched_ceilings"] = ceilings
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
     print(json.dumps(res), flush=True)
@@ -409,6 +487,9 @@ def main_alpha(a, torch, M, S, lib):
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / a.steps
     phase = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / a.steps for i, n in enumerate(names)}
+    import numpy as np
+    phase_med = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    ceilings = matched_ceilings(lib, torch, f, stream) if a.membench else None
 
     if a.calibrate_copy:
         src = torch.ones(1 << 25, dtype=torch.int64, device=dev)   # 256 MiB
@@ -418,6 +499,7 @@ def main_alpha(a, torch, M, S, lib):
         del src, dst
 
     nk_g, nk_r = f.num_symbols(LG) - k + 1, f.num_symbols(LR) - k + 1
+    vk_g, vk_r = valid_kmer_count(w["insert"], k, alpha), valid_kmer_count(w["queries"][0], k, alpha)
     total = nk_g + nk_r + a.probe_n
     value = total / (ms_step * 1e-3) / 1e9
     ins_rate = nk_g / (phase["insert"] * 1e-3)
@@ -453,8 +535,16 @@ def main_alpha(a, torch, M, S, lib):
         "insert_gkmers_s": round(ins_rate / 1e9, 3), "query_gkmers_s": round(q_rate / 1e9, 3),
         "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
         "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},
+        "phase_ms_median": {k2: round(v, 4) for k2, v in phase_med.items()},
+        "valid_kmers": {"insert": vk_g, "query": vk_r},
+        "value_valid_gkmers_s": round((vk_g + vk_r + a.probe_n) / (ms_step * 1e-3) / 1e9, 3),
         "wall_s_timed": round(wall, 3), "gen_s": round(gen_s, 2), "kernel_sources_sha256": sha,
     }
+    if ceilings is not None:
+        runs = 2.0 / (k - m + 2)
+        ceilings["insert_records_est_g_per_s"] = round(ins_rate * runs / 1e9, 3)
+        ceilings["insert_frac_of_or_ceiling"] = round(ins_rate * runs / 1e9 / ceilings["shard_ors_g_per_s"], 3)
+        res["matched_ceilings"] = ceilings
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, (k, m, s, H), alpha)
     print(json.dumps(res), flush=True)

@@ -300,6 +300,26 @@ int sbf_fpr_probe(sbf_t* h, uint64_t n, uint64_t seed, uint64_t* hits);
 /* As sbf_fpr_probe, asynchronous: the count lands in *d_hits (device). */
 int sbf_fpr_probe_device(sbf_t* h, uint64_t n, uint64_t seed, uint64_t* d_hits, void* stream);
 
+/* ---- measurement support (not the method) ------------------------------
+ * Matched memory ceilings for the filter kernels' access patterns ([cuSBF]
+ * §V-E speed of light): n operations on uniformly random shards of a device
+ * table of nshard 32-byte shards (uint64_t[4 * nshard], nshard a power of
+ * two; shard of operation j = SplitMix64 output j + 1 of the seed, masked).
+ * Asynchronous on `stream`; the caller times them.  SBF_EINVAL for NULL
+ * pointers or an nshard that is not a power of two; n must be below 2^60.
+ */
+
+/* Read the 32 bytes of each operation's shard (two 16-byte loads per lane),
+ * as the query and probe kernels read theirs.  d_sink (one device word) is
+ * written only if the XOR of everything read hits a fixed 64-bit value. */
+int sbf_membench_shard_reads(const uint64_t* d_table, uint64_t nshard, uint64_t n, uint64_t seed,
+                             uint64_t* d_sink, void* stream);
+
+/* OR one bit into each of the four words of each operation's shard, four
+ * adjacent lanes with one 64-bit atomic each, as the insert flushes a run's
+ * record.  Modifies the table. */
+int sbf_membench_shard_ors(uint64_t* d_table, uint64_t nshard, uint64_t n, uint64_t seed, void* stream);
+
 /* Static text for a return code. */
 const char* sbf_strerror(int code);
 

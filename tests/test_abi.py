@@ -101,3 +101,12 @@ def test_alphabet_rejects_bad_parameters(lib):
                  (P, 12, 13, 10, 4, 4096), (P, 12, 6, 0, 4, 4096), (TR, 10, 5, 8, 65, 4096), (TR, 10, 5, 8, 4, 0)]:
         assert lib.sbf_create_alphabet(ctypes.byref(h), *args) == _lib.SBF_EINVAL, args
     assert h.value is None
+
+
+def test_membench_rejects_bad_sizes(lib):
+    """Refused before any device use: NULL tables, shard counts that are not
+    powers of two."""
+    assert lib.sbf_membench_shard_ors(None, 1024, 10, 1, None) == _lib.SBF_EINVAL
+    assert lib.sbf_membench_shard_ors(8, 1000, 10, 1, None) == _lib.SBF_EINVAL
+    assert lib.sbf_membench_shard_reads(8, 0, 10, 1, 8, None) == _lib.SBF_EINVAL
+    assert lib.sbf_membench_shard_reads(8, 1024, 10, 1, None, None) == _lib.SBF_EINVAL

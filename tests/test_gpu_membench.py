@@ -1,0 +1,33 @@
+"""The matched-ceiling microbenchmarks stay inside the table they are given
+and do what they say: every OR lands in the table (guard words around it stay
+zero), the four words of an updated shard change together, and bad sizes are
+refused before any launch."""
+import numpy as np
+import pytest
+
+import minimizer_sharded_bloom_amd as M
+from minimizer_sharded_bloom_amd import _lib
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+
+def test_membench_stays_in_bounds():
+    torch = G.torch_cuda()
+    L = M.lib()
+    nsh, guard = 1 << 10, 4096
+    buf = torch.zeros(4 * nsh + 2 * guard, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int64, device="cuda")
+    table = buf.data_ptr() + 8 * guard
+    assert L.sbf_membench_shard_ors(table, nsh, 5000, 7, None) == _lib.SBF_OK
+    assert L.sbf_membench_shard_reads(table, nsh, 5000, 7, sink.data_ptr(), None) == _lib.SBF_OK
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy().view(np.uint64)
+    assert not h[:guard].any() and not h[guard + 4 * nsh:].any()
+    sh = h[guard:guard + 4 * nsh].reshape(nsh, 4)
+    touched = sh.any(axis=1)
+    assert (sh[touched] != 0).all()          # all four words of an updated shard
+    assert 0.9 < touched.mean() <= 1.0       # 5000 random shards cover ~99% of 1024
+    assert L.sbf_membench_shard_ors(table, 1000, 10, 7, None) == _lib.SBF_EINVAL
+    assert L.sbf_membench_shard_reads(table, 0, 10, 7, sink.data_ptr(), None) == _lib.SBF_EINVAL
+    assert L.sbf_membench_shard_reads(table, nsh, 10, 7, None, None) == _lib.SBF_EINVAL
