@@ -30,6 +30,8 @@ import os
 import sys
 import time
 
+T0 = time.perf_counter()
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -159,24 +161,34 @@ def measured_traffic(workload: str, kernel: str, sha: str):
     return None
 
 
-def valid_kmer_count(text, k: int, alpha: str = "dna") -> int:
+def valid_kmer_count(text, k: int, alpha: str = "dna", chunk: int = 3 << 26) -> int:
     """k-mer starts whose k symbols are all valid (positions with an invalid
     symbol, e.g. a record separator, are not): the throughput count of valid
-    k-mers, next to the count of k-mer starts."""
+    k-mers, next to the count of k-mer starts.  Counted chunk by chunk, with
+    the valid run that crosses a chunk boundary carried over."""
     import numpy as np
 
+    ok = np.zeros(256, dtype=bool)
     if alpha == "protein":
-        v = ((text | 0x20) >= ord("a")) & ((text | 0x20) <= ord("z"))
+        ok[[c for c in range(256) if ord("a") <= (c | 0x20) <= ord("z")]] = True
     else:
-        ok = np.zeros(256, dtype=bool)
         ok[list(b"ACGTacgt")] = True
-        v = ok[text]
-        if alpha == "triplet":
-            n = v.size // 3
-            v = v[:3 * n].reshape(n, 3).all(axis=1)
-    edges = np.concatenate([[-1], np.flatnonzero(~v), [v.size]])
-    runs = np.diff(edges) - 1
-    return int(np.maximum(runs - k + 1, 0).sum())
+    sb = 3 if alpha == "triplet" else 1
+    n_sym = text.size // sb
+    total, cur = 0, 0
+    for lo in range(0, n_sym, chunk):
+        hi = min(n_sym, lo + chunk)
+        v = ok[text[lo * sb:hi * sb]]
+        if sb > 1:
+            v = v.reshape(hi - lo, sb).all(axis=1)
+        bad = np.flatnonzero(~v)
+        if bad.size == 0:
+            cur += hi - lo
+            continue
+        total += max(0, cur + int(bad[0]) - k + 1)
+        total += int(np.maximum(np.diff(bad) - k, 0).sum())
+        cur = hi - lo - 1 - int(bad[-1])
+    return total + max(0, cur - k + 1)
 
 
 def matched_ceilings(lib, torch, filt, stream, n_ops: int = 1 << 25) -> dict:
@@ -216,8 +228,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4],
-                    help="synthetic configuration (default 2: 8 MiB filter, 5 Mbp genome, 2 M reads)")
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="synthetic configuration (default 2: 8 MiB filter, 5 Mbp genome, 2 M reads; "
+                         "5: 4 GiB filter, 3 Gbp genome, 1 M long reads)")
     ap.add_argument("--alphabet", default="dna", choices=["dna", "protein", "triplet"],
                     help="dna (default, --workload applies) or the protein / DNA-triplet workload")
     ap.add_argument("--probe-n", type=int, default=10_000_000)
@@ -225,6 +238,9 @@ def parse():
                     help="budget of the CPU oracle baseline in seconds (0 disables it)")
     ap.add_argument("--no-membench", dest="membench", action="store_false",
                     help="skip the matched-ceiling microbenchmarks (random shard reads / OR-updates) run after timing")
+    ap.add_argument("--data-cache", default="",
+                    help="directory for the generated inputs: saved there (.npy) after generating, memory-mapped "
+                         "from there when present (profiled runs then skip the forking long-read generator)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 256 MiB device copy (elementwise kernel) whose "
                          "FETCH_SIZE/WRITE_SIZE counters scale the filter kernels' counters")
@@ -291,6 +307,31 @@ def cpu_baseline(w: dict, budget_s: float, params=(K, M_, S_, H_), alpha: str = 
             "single_thread_sample": "insert then query of the first %d bytes of each text on one thread" % n1}
 
 
+def progress(msg: str) -> None:
+    """One progress line on stderr (the JSON result alone goes to stdout)."""
+    print("[bench %.1fs] %s" % (time.perf_counter() - T0, msg), file=sys.stderr, flush=True)
+
+
+def cached_workload(S, cfg: int, cache: str) -> dict:
+    """S.workload(cfg), or its inserted and last query text memory-mapped
+    from `cache` when saved there before (and saved there after generating)."""
+    import numpy as np
+
+    if not cache:
+        return S.workload(cfg)
+    names = [os.path.join(cache, "cfg%d_%s.npy" % (cfg, part)) for part in ("insert", "query")]
+    if all(os.path.exists(n) for n in names):
+        ins, qry = (np.load(n, mmap_mode="r") for n in names)
+        return {"cfg": cfg, "bits": S.CONFIG_BITS[cfg], "insert": ins, "queries": [qry]}
+    w = S.workload(cfg)
+    progress("generated; saving to %s" % cache)
+    os.makedirs(cache, exist_ok=True)
+    for n, arr in zip(names, (w["insert"], w["queries"][-1])):
+        np.save(n + ".tmp.npy", arr)
+        os.replace(n + ".tmp.npy", n)
+    return w
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -303,16 +344,20 @@ def main():
     import minimizer_sharded_bloom_amd as M
     from minimizer_sharded_bloom_amd import synthetic as S
 
+    if a.alphabet == "dna":
+        # inputs first: the long-read generator forks workers, which must
+        # happen before this process initializes the GPU
+        t_gen = time.perf_counter()
+        w = cached_workload(S, a.workload, a.data_cache)
+        genome_h, reads_h = w["insert"], w["queries"][-1]
+        gen_s = time.perf_counter() - t_gen
+        progress("inputs ready (%.1f s): %d + %d bases" % (gen_s, genome_h.size, reads_h.size))
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     lib = M.lib()
     if a.alphabet != "dna":
         return main_alpha(a, torch, M, S, lib)
 
-    t_gen = time.perf_counter()
-    w = S.workload(a.workload)
-    genome_h, reads_h = w["insert"], w["queries"][-1]
-    gen_s = time.perf_counter() - t_gen
     dev = torch.device("cuda:0")
     genome = torch.from_numpy(genome_h).to(dev)
     reads = torch.from_numpy(reads_h).to(dev)
@@ -366,7 +411,9 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / a.steps
     phase = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / a.steps for i, n in enumerate(names)}
     phase_med = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    progress("timed steps done")
     ceilings = matched_ceilings(lib, torch, f, stream) if a.membench else None
+    progress("matched ceilings done")
 
     if a.calibrate_copy:
         src = torch.ones(1 << 25, dtype=torch.int64, device=dev)   # 256 MiB
@@ -434,6 +481,7 @@ def main():
         res["matched_ceilings"] = ceilings
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+        progress("cpu baseline done")
     print(json.dumps(res), flush=True)
 
 
@@ -446,6 +494,7 @@ def main_alpha(a, torch, M, S, lib):
     t_gen = time.perf_counter()
     w = S.alpha_workload(alpha)
     gen_s = time.perf_counter() - t_gen
+    progress("inputs ready (%.1f s)" % gen_s)
     dev = torch.device("cuda:0")
     ref = torch.from_numpy(w["insert"]).to(dev)
     reads = torch.from_numpy(w["queries"][0]).to(dev)
@@ -489,7 +538,9 @@ def main_alpha(a, torch, M, S, lib):
     phase = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / a.steps for i, n in enumerate(names)}
     import numpy as np
     phase_med = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    progress("timed steps done")
     ceilings = matched_ceilings(lib, torch, f, stream) if a.membench else None
+    progress("matched ceilings done")
 
     if a.calibrate_copy:
         src = torch.ones(1 << 25, dtype=torch.int64, device=dev)   # 256 MiB
@@ -547,6 +598,7 @@ def main_alpha(a, torch, M, S, lib):
         res["matched_ceilings"] = ceilings
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, (k, m, s, H), alpha)
+        progress("cpu baseline done")
     print(json.dumps(res), flush=True)
 
 

@@ -42,6 +42,9 @@ long-read errors 10, proteome 20, protein lengths 21, peptides 22.
 """
 from __future__ import annotations
 
+import multiprocessing as mp
+import os
+
 import numpy as np
 
 ACGT = np.frombuffer(b"ACGT", dtype=np.uint8)
@@ -210,15 +213,46 @@ def long_read_subsample_batch(seed: int = 7) -> int:
     return int(np.random.default_rng(seed).integers(0, LONG_BATCHES))
 
 
-def long_read_set(genome: np.ndarray, batches=None) -> np.ndarray:
-    """ASCII of the given batches (default: all) joined by 'N'."""
-    batches = range(LONG_BATCHES) if batches is None else batches
-    parts = []
-    for b in batches:
-        if parts:
-            parts.append(np.array([N_BYTE], dtype=np.uint8))
-        parts.append(long_read_batch(genome, b))
-    return np.concatenate(parts) if parts else np.empty(0, dtype=np.uint8)
+_FORK_GENOME = None  # the genome that forked batch workers read (set only while a pool runs)
+
+
+def _long_read_batch_forked(bn) -> np.ndarray:
+    return long_read_batch(_FORK_GENOME, bn[0], n=bn[1])
+
+
+def long_read_set(genome: np.ndarray, batches=None, workers: int = 0, n: int = 10_000) -> np.ndarray:
+    """ASCII of the given batches (default: all) joined by 'N'.  Batches are
+    seeded by their index alone, so `workers` > 1 (forked processes that
+    share the genome copy-on-write; 0 = min(16, CPUs)) gives the same bytes
+    as one process.  `n` reads per batch.  Call it before the process
+    initializes a GPU."""
+    global _FORK_GENOME
+    batches = list(range(LONG_BATCHES) if batches is None else batches)
+    if workers <= 0:
+        workers = min(16, os.cpu_count() or 1)
+    workers = min(workers, len(batches))
+    if workers > 1 and "fork" in mp.get_all_start_methods():
+        _FORK_GENOME = genome
+        try:
+            with mp.get_context("fork").Pool(workers) as pool:
+                parts = pool.map(_long_read_batch_forked, [(b, n) for b in batches], chunksize=1)
+        finally:
+            _FORK_GENOME = None
+    else:
+        parts = [long_read_batch(genome, b, n=n) for b in batches]
+    if not parts:
+        return np.empty(0, dtype=np.uint8)
+    out = np.empty(sum(p.size for p in parts) + len(parts) - 1, dtype=np.uint8)
+    at = 0
+    for i in range(len(parts)):
+        part = parts[i]
+        parts[i] = None  # release each batch once copied
+        if i:
+            out[at] = N_BYTE
+            at += 1
+        out[at:at + part.size] = part
+        at += part.size
+    return out
 
 
 def workload(cfg: int) -> dict:

@@ -82,6 +82,19 @@ def test_long_read_batch_layout_and_lengths():
     assert lens.min() >= 900 and lens.max() <= 51_000
 
 
+def test_long_read_set_parallel_equals_sequential():
+    """Forked batch workers give the bytes of one process: batches joined by
+    one 'N' in the order asked for."""
+    genome = S.uniform_ascii_fast(300_000, 0)
+    order = [5, 2, 7]
+    par = S.long_read_set(genome, order, workers=3, n=300)
+    seq = S.long_read_set(genome, order, workers=1, n=300)
+    parts = [S.long_read_batch(genome, b, n=300) for b in order]
+    want = np.concatenate([parts[0], [ord("N")], parts[1], [ord("N")], parts[2]]).astype(np.uint8)
+    assert np.array_equal(par, want) and np.array_equal(seq, want)
+    assert S.long_read_set(genome, [], workers=3).size == 0
+
+
 def test_long_read_batch_error_free_reads_are_genome_substrings():
     genome = S.uniform_ascii_fast(500_000, 0)
     b = S.long_read_batch(genome, 0, n=200, err=0.0)
