@@ -426,7 +426,7 @@ constexpr int kWaves = 4;  // waves per 256-thread workgroup
 // parks invalid k-mers on record 0.
 struct WaveLds {
     uint32_t idx[kWaves][kSlots + 1];
-    uint64_t words[kWaves][kSlots + 1][4];
+    alignas(16) uint64_t words[kWaves][kSlots + 1][4];  // 32-byte records, 16-byte halves
 };
 
 // Inclusive prefix sum over the wave: DPP row shifts by 1, 2, 4 and 8 sum
@@ -660,34 +660,30 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
     uint32_t bits;
     if (total <= (uint32_t)kSlots) {
         wave_lds_sync();
-        // gather: lane -> (record 1 + lane/2 + 32 j, 16-byte half lane & 1), four
-        // loads in flight before their LDS stores; a lane past the last record
-        // loads nothing.
+        // gather: lane -> (record 1 + lane/2 + 32 j, 16-byte half lane & 1).
+        // Each load goes straight from the filter into LDS (one 1 KiB group
+        // of 32 records per instruction, lane l at byte 16 l), so every
+        // group's loads are in flight at once and no VGPR stages them; a lane
+        // past the last record loads nothing.
         const uint32_t half = c.lane & 1u;
         const uint32_t r0 = 1u + (c.lane >> 1);
-        auto src = [&](uint32_t r) {
-            const uint32_t sh = lds.idx[wv][r] & a.shard_mask;
-            return reinterpret_cast<const ulonglong2*>(a.filter + 4ull * sh) + half;
-        };
-        auto dst = [&](uint32_t r) { return reinterpret_cast<ulonglong2*>(lds.words[wv][r]) + half; };
+        uint32_t gsh[kSlots / 32];
 #pragma unroll
-        for (uint32_t jb = 0; jb < (uint32_t)kSlots / 32u; jb += 4u) {
-            if (32u * jb >= total)
+        for (int j = 0; j < kSlots / 32; ++j) {
+            if (32u * j >= total)
                 break;
-            const uint32_t ra = r0 + 32u * jb, rb = ra + 32u, rc = ra + 64u, rd = ra + 96u;
-            const ulonglong2 va = ra <= total ? *src(ra) : ulonglong2{0, 0};
-            const ulonglong2 vb = rb <= total ? *src(rb) : ulonglong2{0, 0};
-            const ulonglong2 vc = rc <= total ? *src(rc) : ulonglong2{0, 0};
-            const ulonglong2 vd = rd <= total ? *src(rd) : ulonglong2{0, 0};
-            if (ra <= total)
-                *dst(ra) = va;
-            if (rb <= total)
-                *dst(rb) = vb;
-            if (rc <= total)
-                *dst(rc) = vc;
-            if (rd <= total)
-                *dst(rd) = vd;
+            const uint32_t r = r0 + 32u * j;
+            gsh[j] = lds.idx[wv][r <= total ? r : 0u] & a.shard_mask;
         }
+#pragma unroll
+        for (int j = 0; j < kSlots / 32; ++j) {
+            if (32u * j >= total)
+                break;
+            if (r0 + 32u * j <= total)
+                __builtin_amdgcn_global_load_lds(a.filter + 4ull * gsh[j] + 2u * half, &lds.words[wv][1 + 32 * j][0],
+                                                 16, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         wave_lds_sync();
 
         // pass B
