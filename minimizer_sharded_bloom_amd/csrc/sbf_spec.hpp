@@ -429,6 +429,48 @@ struct WaveLds {
     alignas(16) uint64_t words[kWaves][kSlots + 1][4];  // 32-byte records, 16-byte halves
 };
 
+// Gather of a wave's records 1 .. total into LDS: record r is the RB-byte
+// shard (idx[r] & shard_mask) of the filter, copied to words + RB * r.  Each
+// load goes straight from the filter into LDS: one instruction fills a group
+// of 64 * 16 / RB consecutive records (1 KiB, lane l at byte 16 l), so all
+// groups' loads are in flight at once and no VGPR stages them.  A lane past
+// the last record loads nothing.  idx holds NSLOT + 1 entries; the loads are
+// complete when this returns.
+template <int RB, int NSLOT>
+__device__ __forceinline__ void gather_records(const uint64_t* __restrict__ filter, uint32_t shard_mask,
+                                               const uint32_t* idx, char* words, uint32_t total, uint32_t lane)
+{
+    constexpr int LPR = RB / 16;       // lanes per record
+    constexpr int RPG = 64 / LPR;      // records per group
+    constexpr int NG = NSLOT / RPG;    // groups
+    constexpr int CH = 8;              // groups whose indices are read before their loads
+    static_assert(NSLOT % RPG == 0, "whole groups");
+    const uint32_t part = lane % LPR;
+    const uint32_t r0 = 1u + lane / LPR;
+#pragma unroll
+    for (int g0 = 0; g0 < NG; g0 += CH) {
+        if ((uint32_t)(RPG * g0) >= total)
+            break;
+        uint32_t sh[CH];
+#pragma unroll
+        for (int j = 0; j < CH && g0 + j < NG; ++j) {
+            if ((uint32_t)(RPG * (g0 + j)) >= total)
+                break;
+            const uint32_t r = r0 + (uint32_t)(RPG * (g0 + j));
+            sh[j] = idx[r <= total ? r : 0u] & shard_mask;
+        }
+#pragma unroll
+        for (int j = 0; j < CH && g0 + j < NG; ++j) {
+            if ((uint32_t)(RPG * (g0 + j)) >= total)
+                break;
+            if (r0 + (uint32_t)(RPG * (g0 + j)) <= total)
+                __builtin_amdgcn_global_load_lds(filter + (uint64_t)(RB / 8) * sh[j] + 2u * part,
+                                                 words + RB * (1 + RPG * (g0 + j)), 16, 0, 0);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Inclusive prefix sum over the wave: DPP row shifts by 1, 2, 4 and 8 sum
 // within each row of 16 lanes, then the row_bcast:15 and row_bcast:31 moves
 // carry the totals of rows 0 and 0..1 into the later rows.
@@ -660,30 +702,8 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
     uint32_t bits;
     if (total <= (uint32_t)kSlots) {
         wave_lds_sync();
-        // gather: lane -> (record 1 + lane/2 + 32 j, 16-byte half lane & 1).
-        // Each load goes straight from the filter into LDS (one 1 KiB group
-        // of 32 records per instruction, lane l at byte 16 l), so every
-        // group's loads are in flight at once and no VGPR stages them; a lane
-        // past the last record loads nothing.
-        const uint32_t half = c.lane & 1u;
-        const uint32_t r0 = 1u + (c.lane >> 1);
-        uint32_t gsh[kSlots / 32];
-#pragma unroll
-        for (int j = 0; j < kSlots / 32; ++j) {
-            if (32u * j >= total)
-                break;
-            const uint32_t r = r0 + 32u * j;
-            gsh[j] = lds.idx[wv][r <= total ? r : 0u] & a.shard_mask;
-        }
-#pragma unroll
-        for (int j = 0; j < kSlots / 32; ++j) {
-            if (32u * j >= total)
-                break;
-            if (r0 + 32u * j <= total)
-                __builtin_amdgcn_global_load_lds(a.filter + 4ull * gsh[j] + 2u * half, &lds.words[wv][1 + 32 * j][0],
-                                                 16, 0, 0);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        gather_records<32, kSlots>(a.filter, a.shard_mask, lds.idx[wv], reinterpret_cast<char*>(&lds.words[wv][0][0]),
+                                   total, c.lane);
         wave_lds_sync();
 
         // pass B

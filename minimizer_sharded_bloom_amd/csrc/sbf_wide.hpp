@@ -39,7 +39,7 @@ template <class C>
 struct WideLds {
     static constexpr int NW = WideShape<C>::kWavesPerBlock, NS = WideShape<C>::kSlots;
     uint32_t idx[NW][NS + 1];
-    uint32_t words[NW][NS + 1][16];  // 512-bit blocks as 16 32-bit words
+    alignas(16) uint32_t words[NW][NS + 1][16];  // 512-bit blocks as 16 32-bit words
 };
 
 // Streaming s-mer bit addresses: positions 0 .. KL+Z-2 of the lane (own KL,
@@ -188,32 +188,8 @@ __global__ __launch_bounds__(256) void wide_query_kernel(SeqArgs a)
     uint32_t bits;
     if (total <= (uint32_t)kSlotsW) {
         wave_lds_sync();
-        // gather: lane -> (record 1 + lane/4 + 16 j, 16-byte quarter lane & 3)
-        const uint32_t qtr = c.lane & 3u;
-        const uint32_t r0 = 1u + (c.lane >> 2);
-        auto src = [&](uint32_t r) {
-            const uint32_t sh = lds.idx[wv][r] & a.shard_mask;
-            return reinterpret_cast<const ulonglong2*>(a.filter + 8ull * sh) + qtr;
-        };
-        auto dst = [&](uint32_t r) { return reinterpret_cast<ulonglong2*>(lds.words[wv][r]) + qtr; };
-#pragma unroll
-        for (uint32_t jb = 0; jb < kSlotsW / 16u; jb += 4u) {
-            if (16u * jb >= total)
-                break;
-            const uint32_t ra = r0 + 16u * jb, rb = ra + 16u, rc = ra + 32u, rd = ra + 48u;
-            const ulonglong2 va = ra <= total ? *src(ra) : ulonglong2{0, 0};
-            const ulonglong2 vb = rb <= total ? *src(rb) : ulonglong2{0, 0};
-            const ulonglong2 vc = rc <= total ? *src(rc) : ulonglong2{0, 0};
-            const ulonglong2 vd = rd <= total ? *src(rd) : ulonglong2{0, 0};
-            if (ra <= total)
-                *dst(ra) = va;
-            if (rb <= total)
-                *dst(rb) = vb;
-            if (rc <= total)
-                *dst(rc) = vc;
-            if (rd <= total)
-                *dst(rd) = vd;
-        }
+        gather_records<64, kSlotsW>(a.filter, a.shard_mask, lds.idx[wv],
+                                    reinterpret_cast<char*>(&lds.words[wv][0][0]), total, c.lane);
         wave_lds_sync();
 
         WideAddr<C> wa;
