@@ -416,35 +416,47 @@ __device__ __forceinline__ void accumulate_run(uint64_t (&Wr)[4], uint32_t keep,
 }
 
 // ---------------------------------------------------------------------------
-// Wave-level helpers.  Each wave owns a private slice of LDS: kSlots records
+// Wave-level helpers.  Each wave owns a private slice of LDS: NSLOT records
 // of (shard index, four 64-bit words).
 // ---------------------------------------------------------------------------
-constexpr int kSlots = 256;
-constexpr int kWaves = 4;  // waves per 256-thread workgroup
+constexpr int kSlots = 256;  // insert: records per wave (more go straight to the filter)
+constexpr int kWaves = 4;    // waves per 256-thread workgroup
 
-// kSlots + 1 records per wave: the query numbers its segments from 1 and
-// parks invalid k-mers on record 0.
-struct WaveLds {
-    uint32_t idx[kWaves][kSlots + 1];
-    alignas(16) uint64_t words[kWaves][kSlots + 1][4];  // 32-byte records, 16-byte halves
+// Query segments per wave before the direct path.  A wave of 2016 k-mers
+// (32 per lane) of random sequence holds 2/(w+1) segments per k-mer: about
+// 239 at w = 16 (standard deviation about 8), 269 at w = 14.  280 slots keep
+// a workgroup at 40.5 KB, so four fit in a CU's 160 KB; w <= 14 takes 352
+// slots and three workgroups.  A wave of 1008 k-mers keeps 256.
+template <class C>
+constexpr int query_slots() { return C::KL == 32 ? (C::W <= 14 ? 352 : 280) : 256; }
+
+// NSLOT + 1 records per wave of (shard index, four 64-bit words).  The query
+// numbers its segments from 1 and parks invalid k-mers on record 0.  The
+// indices sit in their own array: pass A writes one per k-mer, and at a
+// 4-byte stride neighbouring records fall in different LDS banks.
+template <int NSLOT>
+struct WaveLdsN {
+    uint32_t idx[kWaves][NSLOT + 1];
+    alignas(16) uint64_t words[kWaves][NSLOT + 1][4];  // 32-byte records, 16-byte halves
 };
+using WaveLds = WaveLdsN<kSlots>;
 
 // Gather of a wave's records 1 .. total into LDS: record r is the RB-byte
 // shard (idx[r] & shard_mask) of the filter, copied to words + RB * r.  Each
 // load goes straight from the filter into LDS: one instruction fills a group
 // of 64 * 16 / RB consecutive records (1 KiB, lane l at byte 16 l), so all
 // groups' loads are in flight at once and no VGPR stages them.  A lane past
-// the last record loads nothing.  idx holds NSLOT + 1 entries; the loads are
-// complete when this returns.
+// the last record loads nothing.  idx holds NSLOT + 1 entries and words
+// NSLOT + 1 records; total <= NSLOT.  The loads are complete when this
+// returns.
 template <int RB, int NSLOT>
 __device__ __forceinline__ void gather_records(const uint64_t* __restrict__ filter, uint32_t shard_mask,
                                                const uint32_t* idx, char* words, uint32_t total, uint32_t lane)
 {
     constexpr int LPR = RB / 16;       // lanes per record
     constexpr int RPG = 64 / LPR;      // records per group
-    constexpr int NG = NSLOT / RPG;    // groups
-    constexpr int CH = 8;              // groups whose indices are read before their loads
-    static_assert(NSLOT % RPG == 0, "whole groups");
+    constexpr int NG = (NSLOT + RPG - 1) / RPG;  // groups (the last may be partial)
+    constexpr int CH = 8;                        // groups whose indices are read before their loads
     const uint32_t part = lane % LPR;
     const uint32_t r0 = 1u + lane / LPR;
 #pragma unroll
@@ -669,7 +681,8 @@ __device__ __forceinline__ uint32_t query_lane_direct(const SeqArgs& a, const ui
 template <class C>
 __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
 {
-    __shared__ WaveLds lds;
+    constexpr int kQuerySlots = query_slots<C>();
+    __shared__ WaveLdsN<kQuerySlots> lds;
     const uint64_t nk_pad = round64(a.nk);
     const LaneCtx<C> c = lane_ctx<C>(nk_pad);
     if (!c.live)
@@ -693,17 +706,17 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
 #pragma unroll
         for (int i = 0; i < C::KL; ++i)
             rec[i] = (__popc(st & ((2u << i) - 1u)) + first) * ((vk >> i) & 1u);
-        if (total <= (uint32_t)kSlots) {
+        if (total <= (uint32_t)kQuerySlots) {
 #pragma unroll
             for (int i = 0; i < C::KL; ++i)
                 lds.idx[wv][rec[i]] = shard[i];
         }
     }
     uint32_t bits;
-    if (total <= (uint32_t)kSlots) {
+    if (total <= (uint32_t)kQuerySlots) {
         wave_lds_sync();
-        gather_records<32, kSlots>(a.filter, a.shard_mask, lds.idx[wv], reinterpret_cast<char*>(&lds.words[wv][0][0]),
-                                   total, c.lane);
+        gather_records<32, kQuerySlots>(a.filter, a.shard_mask, lds.idx[wv], reinterpret_cast<char*>(&lds.words[wv][0][0]),
+                                        total, c.lane);
         wave_lds_sync();
 
         // pass B
