@@ -385,20 +385,31 @@ struct FindereMasks {
     }
 };
 
-// Bits of R = T0 | T1 missing from the shard words W: (T0 | T1) & ~W, one
-// 3-input bit operation per 32-bit half.
-template <class C>
-__device__ __forceinline__ uint64_t missing_bits(const uint64_t (&T0)[4], const uint64_t (&T1)[4], const uint64_t (&W)[4])
+// Lane mask of v == 0 from one 64-bit compare (left to itself the compiler
+// ORs the halves and compares 32 bits, one more vector instruction).
+__device__ __forceinline__ uint64_t lanes_zero64(uint64_t v)
 {
-    uint64_t miss = 0;
+    uint64_t m;
+    asm("v_cmp_eq_u64_e64 %0, 0, %1" : "=s"(m) : "v"(v));
+    return m;
+}
+
+// Lanes whose k-mer has every bit of R = T0 | T1 set in the shard words W:
+// per word, (T0 | T1) & ~W is one 3-input bit operation per 32-bit half and
+// one 64-bit compare with zero; the words' lane masks are ANDed on the scalar
+// unit.
+template <class C>
+__device__ __forceinline__ uint64_t lanes_present(const uint64_t (&T0)[4], const uint64_t (&T1)[4], const uint64_t (&W)[4])
+{
+    uint64_t present = ~0ull;
 #pragma unroll
     for (int q = 0; q < C::NS; ++q) {
         const uint32_t lo = __builtin_amdgcn_bitop3_b32((uint32_t)T0[q], (uint32_t)T1[q], (uint32_t)W[q], 0x54);
         const uint32_t hi = __builtin_amdgcn_bitop3_b32((uint32_t)(T0[q] >> 32), (uint32_t)(T1[q] >> 32),
                                                         (uint32_t)(W[q] >> 32), 0x54);
-        miss |= ((uint64_t)hi << 32) | lo;
+        present &= lanes_zero64(((uint64_t)hi << 32) | lo);
     }
-    return miss;
+    return present;
 }
 
 // Run accumulation: Wr = (Wr & keep) | T0 | T1 with keep = 0 at a run start,
@@ -422,16 +433,18 @@ __device__ __forceinline__ void accumulate_run(uint64_t (&Wr)[4], uint32_t keep,
 constexpr int kSlots = 256;  // insert: records per wave (more go straight to the filter)
 constexpr int kWaves = 4;    // waves per 256-thread workgroup
 
-// Query segments per wave before the direct path.  A wave of 2016 k-mers
+// Query records per wave before the direct path.  A wave of 2016 k-mers
 // (32 per lane) of random sequence holds 2/(w+1) segments per k-mer: about
-// 239 at w = 16 (standard deviation about 8), 269 at w = 14.  280 slots keep
+// 239 at w = 16 (standard deviation about 8), 269 at w = 14; short reads add
+// one gap record per read but cut the segments there (about 213 per wave for
+// 150-base reads).  280 slots keep
 // a workgroup at 40.5 KB, so four fit in a CU's 160 KB; w <= 14 takes 352
 // slots and three workgroups.  A wave of 1008 k-mers keeps 256.
 template <class C>
 constexpr int query_slots() { return C::KL == 32 ? (C::W <= 14 ? 352 : 280) : 256; }
 
 // NSLOT + 1 records per wave of (shard index, four 64-bit words).  The query
-// numbers its segments from 1 and parks invalid k-mers on record 0.  The
+// numbers its records from 1 (record 0 is unused).  The
 // indices sit in their own array: pass A writes one per k-mer, and at a
 // 4-byte stride neighbouring records fall in different LDS banks.
 template <int NSLOT>
@@ -521,6 +534,33 @@ __device__ __forceinline__ bool continues_previous(uint32_t vk, const uint32_t (
     const uint32_t prev_last_valid = from_prev_lane((vk >> (C::KL - 1)) & 1u);
     const uint32_t prev_last_shard = from_prev_lane(shard[C::KL - 1]);
     return lane > 0 && (vk & 1u) && prev_last_valid && shard[0] == prev_last_shard;
+}
+
+// Record numbers of a query lane's k-mers; returns the wave's record count.
+// Records number, from 1 across the wave, the segments (runs of valid k-mers
+// with one shard) and the gaps (runs of invalid k-mers); one that continues
+// the previous lane's last keeps its number.  Every k-mer can then write its
+// shard index into its own record with no branch and no validity test: a
+// segment's k-mers all carry its shard, and a gap's record holds some index
+// whose answers the validity bits clear.
+template <class C>
+__device__ __forceinline__ uint32_t query_records(uint32_t vk, const uint32_t (&shard)[C::KL], uint32_t lane,
+                                                  uint32_t (&rec)[C::KL])
+{
+    constexpr uint32_t all = C::KL == 32 ? 0xFFFFFFFFu : (1u << C::KL) - 1u;
+    const uint32_t st = run_starts<C>(vk, shard);
+    const uint32_t gs = (st | (~vk & ((vk << 1) | 1u))) & all;  // plus gap starts
+    const uint32_t prev_valid = from_prev_lane((vk >> (C::KL - 1)) & 1u);
+    const uint32_t prev_shard = from_prev_lane(shard[C::KL - 1]);
+    const bool cont = lane > 0 && ((vk & 1u) ? (prev_valid && shard[0] == prev_shard) : !prev_valid);
+    const uint32_t cin = cont ? 1u : 0u;
+    const uint32_t n = __popc(gs) - cin;
+    const uint32_t incl = wave_incl_scan(n);
+    const uint32_t first = incl - n - cin;  // record of the lane's k-mers before its first start
+#pragma unroll
+    for (int i = 0; i < C::KL; ++i)
+        rec[i] = __popc(gs & ((2u << i) - 1u)) + first;
+    return __builtin_amdgcn_readlane(incl, 63);
 }
 
 template <class C>
@@ -670,14 +710,14 @@ __device__ __forceinline__ uint32_t query_lane_direct(const SeqArgs& a, const ui
     return bits;
 }
 
-// Query ([cuSBF] Algorithm 2).  Pass A: shards, validity, segment starts
-// (runs of one shard) and, per k-mer, the LDS record of its segment (segments
-// are numbered from 1 across the wave; invalid k-mers get record 0).  Every
-// k-mer writes its shard index to its record: all valid k-mers of a segment
-// carry the same shard, so no write needs a branch.  Gather: the wave loads
-// every segment's 32-byte shard into LDS at once, two lanes per shard.  Pass B
-// (straight-line): k-mer i reads the words of its record and is present iff
-// every bit of its Findere mask R_i is set: (R_i & W) == R_i.
+// Query ([cuSBF] Algorithm 2).  Pass A: shards, validity, and per k-mer the
+// LDS record of its segment (a run of one shard) or gap (a run of invalid
+// k-mers), numbered from 1 across the wave.  Every k-mer writes its shard
+// index to its record: all k-mers of a segment carry the same shard, so no
+// write needs a branch.  Gather: the wave loads every record's 32-byte shard
+// into LDS at once, two lanes per shard.  Pass B (straight-line): k-mer i
+// reads the words of its record and is present iff every bit of its Findere
+// mask R_i is set: (R_i & W) == R_i; invalid k-mers answer 0.
 template <class C>
 __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
 {
@@ -691,21 +731,13 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
     uint32_t D[C::ND];
     load_codes<C>(a, c, D);
     const uint32_t vk = lane_valid<C>(a, c);
-    uint32_t st, total;
+    uint32_t total;
     uint32_t rec[C::KL];
     {
         uint32_t shard[C::KL];
         lane_shards<C>(D, shard);
-        // pass A: segment records, shard indices into LDS
-        st = run_starts<C>(vk, shard);
-        const uint32_t cin = continues_previous<C>(vk, shard, c.lane) ? 1u : 0u;
-        const uint32_t nseg = __popc(st) - cin;
-        const uint32_t incl = wave_incl_scan(nseg);
-        total = __builtin_amdgcn_readlane(incl, 63);
-        const uint32_t first = incl - nseg - cin;  // record of the segment before the lane's first start
-#pragma unroll
-        for (int i = 0; i < C::KL; ++i)
-            rec[i] = (__popc(st & ((2u << i) - 1u)) + first) * ((vk >> i) & 1u);
+        // pass A: segment and gap records, shard indices into LDS
+        total = query_records<C>(vk, shard, c.lane, rec);
         if (total <= (uint32_t)kQuerySlots) {
 #pragma unroll
             for (int i = 0; i < C::KL; ++i)
@@ -735,8 +767,7 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
                 wq[2] = w23.x;
                 wq[3] = w23.y;
             }
-            const uint64_t miss = missing_bits<C>(T0, T1, wq);
-            bits = shift_in(bits, __builtin_amdgcn_ballot_w64(miss == 0));  // k-mer i lands at bit KL-1-i
+            bits = shift_in(bits, lanes_present<C>(T0, T1, wq));  // k-mer i lands at bit KL-1-i
             step_fence(D);
         });
         bits = (__builtin_bitreverse32(bits) >> (32 - C::KL)) & vk;

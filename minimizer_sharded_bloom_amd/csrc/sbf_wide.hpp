@@ -170,15 +170,7 @@ __global__ __launch_bounds__(256) void wide_query_kernel(SeqArgs a)
     {
         uint32_t shard[C::KL];
         lane_shards<C>(D, shard);
-        const uint32_t st = run_starts<C>(vk, shard);
-        const uint32_t cin = continues_previous<C>(vk, shard, c.lane) ? 1u : 0u;
-        const uint32_t nseg = __popc(st) - cin;
-        const uint32_t incl = wave_incl_scan(nseg);
-        total = __builtin_amdgcn_readlane(incl, 63);
-        const uint32_t first = incl - nseg - cin;
-#pragma unroll
-        for (int i = 0; i < C::KL; ++i)
-            rec[i] = (__popc(st & ((2u << i) - 1u)) + first) * ((vk >> i) & 1u);
+        total = query_records<C>(vk, shard, c.lane, rec);
         if (total <= (uint32_t)kSlotsW) {
 #pragma unroll
             for (int i = 0; i < C::KL; ++i)
