@@ -119,20 +119,29 @@ CSRC = os.path.join(ROOT, "minimizer_sharded_bloom_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-KERNEL_HEADERS = ("sbf_device.hpp", "sbf_internal.hpp", "sbf_spec.hpp", "sbf_spec_list.hpp", "sbf_wide.hpp")
+# Sources each workload family's kernels are built from: the DNA step's
+# pack/clear kernels and the specialized set at (31,16,28,4), or the alphabet
+# kernels.  A traffic summary is used only while these hash as when it was
+# taken.
+KERNEL_SOURCES = {
+    "dna": ("minimizer_sharded_bloom_amd/csrc/inst_m16.hip", "minimizer_sharded_bloom_amd/csrc/sbf_spec.hpp",
+            "minimizer_sharded_bloom_amd/csrc/sbf_spec_list.hpp", "minimizer_sharded_bloom_amd/csrc/sbf_device.hpp",
+            "minimizer_sharded_bloom_amd/csrc/sbf_internal.hpp", "minimizer_sharded_bloom_amd/csrc/sbf_generic.hip"),
+    "alpha": ("minimizer_sharded_bloom_amd/csrc/sbf_alpha.hip", "minimizer_sharded_bloom_amd/csrc/sbf_device.hpp",
+              "minimizer_sharded_bloom_amd/csrc/sbf_internal.hpp", "minimizer_sharded_bloom_amd/csrc/sbf_generic.hip",
+              "include/sbf.h"),
+}
 
 
-def kernel_sources_sha256() -> str:
-    """Hash of the sources (names and bytes) the device kernels are built
-    from: the .hip files and the headers they include (not the host-only
-    C-ABI, pipeline and reader sources)."""
+def kernel_sources_sha256(family: str = "dna") -> str:
+    """Hash of the sources (names and bytes) that one family's kernels are
+    built from (KERNEL_SOURCES)."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith(".hip") or name in KERNEL_HEADERS:
-            h.update(name.encode() + b"\0")
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for rel in KERNEL_SOURCES[family]:
+        h.update(rel.encode() + b"\0")
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -465,6 +474,7 @@ def main():
         "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
         "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},
         "phase_ms_median": {k2: round(v, 4) for k2, v in phase_med.items()},
+        "kmer_starts": {"insert": nk_g, "query": nk_r, "probe": a.probe_n},
         "valid_kmers": {"insert": vk_g, "query": vk_r},
         "value_valid_gkmers_s": round((vk_g + vk_r + a.probe_n) / (ms_step * 1e-3) / 1e9, 3),
         "insert_valid_gkmers_s": round(vk_g / (phase["insert"] * 1e-3) / 1e9, 3),
@@ -555,7 +565,7 @@ def main_alpha(a, torch, M, S, lib):
     value = total / (ms_step * 1e-3) / 1e9
     ins_rate = nk_g / (phase["insert"] * 1e-3)
     q_rate = nk_r / (phase["query"] * 1e-3)
-    sha = kernel_sources_sha256()
+    sha = kernel_sources_sha256("alpha")
 
     def roof(kind, rate):
         ops = alpha_alu_ops_per_kmer(alpha, kind)
@@ -587,6 +597,7 @@ def main_alpha(a, torch, M, S, lib):
         "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
         "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},
         "phase_ms_median": {k2: round(v, 4) for k2, v in phase_med.items()},
+        "kmer_starts": {"insert": nk_g, "query": nk_r, "probe": a.probe_n},
         "valid_kmers": {"insert": vk_g, "query": vk_r},
         "value_valid_gkmers_s": round((vk_g + vk_r + a.probe_n) / (ms_step * 1e-3) / 1e9, 3),
         "wall_s_timed": round(wall, 3), "gen_s": round(gen_s, 2), "kernel_sources_sha256": sha,
