@@ -64,7 +64,7 @@ FRONT = {
     "validity / run bookkeeping": 2,
 }
 TAIL = {
-    "query": {"(T0|T1) & ~W per half (bitop3), 3 OR reductions, compare, answer bit": 13},
+    "query": {"(T0|T1) & ~W per half (bitop3), one 64-bit compare per word, answer bit": 13},
     "insert": {"T0|T1 and (Wr & keep) | t per half": 16, "record flush share (~0.12 runs/k-mer)": 1.5},
 }
 
