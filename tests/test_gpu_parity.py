@@ -277,3 +277,63 @@ def test_library_first_then_torch():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     p = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=100)
     assert p.returncode == 0 and p.stdout.strip().endswith("ok"), p.stdout + p.stderr
+
+
+def _segments_per_wave(seq: bytes, k: int, m: int, wave: int, n_waves: int) -> list:
+    """Runs of equal minimizer key (low 32 bits of the minimizer hash) that
+    start in each of the first n_waves blocks of `wave` k-mer starts, counted
+    with the oracle's per-k-mer definition (a run entering a block counts
+    there too)."""
+    counts = []
+    prev = None
+    for w in range(n_waves):
+        c = 0
+        for p in range(w * wave, (w + 1) * wave):
+            x = O.pack_kmer(seq[p:p + k])
+            key = None if x is None else O.minimizer_hash(x, k, m) & 0xFFFFFFFF
+            if key is not None and (key != prev or p == w * wave):
+                c += 1
+            prev = key
+        counts.append(c)
+    return counts
+
+
+@pytest.mark.parametrize("m", [17, 21, 22])
+def test_query_waves_at_record_limits(m):
+    """Genome-scale queries at minimizer densities 2/(w+1) whose 2016-k-mer
+    query waves straddle the LDS record slots: m = 17, about 252 segments per
+    wave against 280 slots; m = 21, about 336 against 352, so one launch runs
+    both the LDS path and the per-k-mer path; m = 22, about 367, mostly the
+    per-k-mer path.  Filter words and every query bit match the oracle."""
+    rng = np.random.default_rng(300 + m)
+    params = (31, m, 28, 4)
+    genome = T.random_dna(rng, 300_000)
+    foreign = T.random_dna(rng, 1_000_000)
+    if m == 21:
+        # the input reaches both sides of the 352 slots, with a margin for
+        # the record a wave's idle last lane may add
+        seg = np.array(_segments_per_wave(foreign, 31, m, 2016, (len(foreign) - 30) // 2016))
+        assert (seg < 348).sum() >= 5 and (seg > 356).sum() >= 5, (seg.min(), seg.max())
+    mutated = bytearray(genome)
+    for p in rng.integers(0, len(mutated), 3000):
+        mutated[p] = ord("ACGT"[(("ACGT".index(chr(mutated[p]))) + 1) % 4])
+    g, _ = _run_pair(params, 2**20, [genome], [genome, bytes(mutated), foreign])
+    assert g.specialized
+
+
+def test_query_gaps_at_lane_and_wave_boundaries():
+    """'N' runs of 1, 2, 31 and 40 bases placed at and around lane (32 k-mer
+    starts) and wave (2016) boundaries, so runs of invalid k-mers start, end
+    and continue across lanes and waves; both query widths (32 and 16 k-mers
+    per lane) and an insert of the same text."""
+    rng = np.random.default_rng(401)
+    n = 60_000
+    for params in (MAIN, (31, 16, 20, 4)):
+        a = bytearray(T.random_dna(rng, n))
+        for base in list(range(0, n, 2016)) + list(range(5000, 9000, 32)):
+            off = int(rng.choice([-31, -30, -1, 0, 1, 30, 31]))
+            L = int(rng.choice([1, 2, 31, 40]))
+            p = max(0, base + off)
+            a[p:p + L] = b"N" * min(L, n - p)
+        seq = bytes(a)
+        _run_pair(params, 2**15, [seq[: n // 2]], [seq, seq[1:], seq[31:], seq[2016 + 5:]])
