@@ -437,11 +437,12 @@ constexpr int kWaves = 4;    // waves per 256-thread workgroup
 // (32 per lane) of random sequence holds 2/(w+1) segments per k-mer: about
 // 239 at w = 16 (standard deviation about 8), 269 at w = 14; short reads add
 // one gap record per read but cut the segments there (about 213 per wave for
-// 150-base reads).  280 slots keep
-// a workgroup at 40.5 KB, so four fit in a CU's 160 KB; w <= 14 takes 352
-// slots and three workgroups.  A wave of 1008 k-mers keeps 256.
+// 150-base reads).  280 slots keep a workgroup at 40.5 KB, so four fit in a
+// CU's 160 KB; w <= 14 takes 352 slots and three workgroups.  Waves of 1008
+// k-mers (16 per lane: the query's choice for w <= 11) hold about 168 at
+// w = 11 and 336 at w = 5: 256 slots, or 352 when w <= 7.
 template <class C>
-constexpr int query_slots() { return C::KL == 32 ? (C::W <= 14 ? 352 : 280) : 256; }
+constexpr int query_slots() { return C::KL == 32 ? (C::W <= 14 ? 352 : 280) : (C::W <= 7 ? 352 : 256); }
 
 // NSLOT + 1 records per wave of (shard index, four 64-bit words).  The query
 // numbers its records from 1 (record 0 is unused).  The
@@ -853,15 +854,16 @@ hipError_t launch_probe(const ProbeArgs& a, const Params&)
     return hipGetLastError();
 }
 
-// The query takes 32 k-mers per lane while k-s+1 <= 8: its per-lane work
-// (code loads, halo moves, scan, gather) is then spread over twice the
-// k-mers.  More s-mers per k-mer make the doubling levels too large for 32
-// (over 160 VGPRs), and the insert measures faster at 16.
+// The query takes 32 k-mers per lane while k-s+1 <= 8 and w >= 12: its
+// per-lane work (code loads, halo moves, scan, gather) is then spread over
+// twice the k-mers.  More s-mers per k-mer make the doubling levels too large
+// for 32 (over 160 VGPRs); denser minimizers (w <= 11) would give a 2016-k-mer
+// wave more segments than its LDS slots; and the insert measures faster at 16.
 template <int K, int M, int S, int H>
 KernelSet spec_set()
 {
     using C = Cfg<K, M, S, H>;
-    using CQ = Cfg<K, M, S, H, (K - S + 1 <= 8 ? 32 : 0)>;
+    using CQ = Cfg<K, M, S, H, (K - S + 1 <= 8 && K - M + 1 >= 12 ? 32 : 0)>;
     KernelSet ks;
     ks.insert = &launch_insert<C>;
     ks.query = &launch_query<CQ>;

@@ -298,21 +298,23 @@ def _segments_per_wave(seq: bytes, k: int, m: int, wave: int, n_waves: int) -> l
     return counts
 
 
-@pytest.mark.parametrize("m", [17, 21, 22])
+@pytest.mark.parametrize("m", [17, 21, 27, 28])
 def test_query_waves_at_record_limits(m):
-    """Genome-scale queries at minimizer densities 2/(w+1) whose 2016-k-mer
-    query waves straddle the LDS record slots: m = 17, about 252 segments per
-    wave against 280 slots; m = 21, about 336 against 352, so one launch runs
-    both the LDS path and the per-k-mer path; m = 22, about 367, mostly the
-    per-k-mer path.  Filter words and every query bit match the oracle."""
+    """Genome-scale queries at minimizer densities 2/(w+1) near the query's
+    LDS record slots.  m = 17: about 252 segments per 2016-k-mer wave (32
+    k-mers per lane) against 280 slots.  From w <= 11 on the query takes 16
+    k-mers per lane: m = 21, about 168 per 1008-k-mer wave against 256;
+    m = 27, about 337 against 352, so one launch runs both the LDS path and
+    the per-k-mer path; m = 28, about 404, the per-k-mer path.  Filter words
+    and every query bit match the oracle."""
     rng = np.random.default_rng(300 + m)
     params = (31, m, 28, 4)
     genome = T.random_dna(rng, 300_000)
     foreign = T.random_dna(rng, 1_000_000)
-    if m == 21:
+    if m == 27:
         # the input reaches both sides of the 352 slots, with a margin for
         # the record a wave's idle last lane may add
-        seg = np.array(_segments_per_wave(foreign, 31, m, 2016, (len(foreign) - 30) // 2016))
+        seg = np.array(_segments_per_wave(foreign, 31, m, 1008, (len(foreign) - 30) // 1008))
         assert (seg < 348).sum() >= 5 and (seg > 356).sum() >= 5, (seg.min(), seg.max())
     mutated = bytearray(genome)
     for p in rng.integers(0, len(mutated), 3000):
