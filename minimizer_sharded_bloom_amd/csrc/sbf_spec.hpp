@@ -444,6 +444,12 @@ constexpr int kWaves = 4;    // waves per 256-thread workgroup
 template <class C>
 constexpr int query_slots() { return C::KL == 32 ? (C::W <= 14 ? 352 : 280) : (C::W <= 7 ? 352 : 256); }
 
+// Insert records per wave before records go straight to the filter (four
+// unmerged 64-bit atomics each): 256, or 352 when w <= 8, where a wave of
+// 1008 k-mers holds 2/(w+1) runs per k-mer, 224 at w = 8 and 336 at w = 5.
+template <class C>
+constexpr int insert_slots() { return C::W <= 8 ? 352 : kSlots; }
+
 // NSLOT + 1 records per wave of (shard index, four 64-bit words).  The query
 // numbers its records from 1 (record 0 is unused).  The
 // indices sit in their own array: pass A writes one per k-mer, and at a
@@ -453,7 +459,6 @@ struct WaveLdsN {
     uint32_t idx[kWaves][NSLOT + 1];
     alignas(16) uint64_t words[kWaves][NSLOT + 1][4];  // 32-byte records, 16-byte halves
 };
-using WaveLds = WaveLdsN<kSlots>;
 
 // Gather of a wave's records 1 .. total into LDS: record r is the RB-byte
 // shard (idx[r] & shard_mask) of the filter, copied to words + RB * r.  Each
@@ -577,11 +582,13 @@ __device__ __forceinline__ void global_or_record(uint64_t* __restrict__ filter, 
 // a wave scan gives each run a record slot.  Pass B: each run's sector masks
 // go to its slot (a run continuing the previous lane's last run ORs into that
 // slot).  Flush: four adjacent lanes OR the four words of one record into the
-// filter.  Records past kSlots go straight to the filter from their lane.
+// filter.  Records past the wave's slots go straight to the filter from their
+// lane.
 template <class C>
 __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
 {
-    __shared__ WaveLds lds;
+    constexpr int kInsSlots = insert_slots<C>();
+    __shared__ WaveLdsN<kInsSlots> lds;
     const LaneCtx<C> c = lane_ctx<C>(a.nk);
     if (!c.live)
         return;  // whole wave
@@ -628,7 +635,7 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
                     first[w] = Wr[w];
             } else {
                 const uint32_t slot = base + ridx - cin;
-                if (slot < (uint32_t)kSlots) {
+                if (slot < (uint32_t)kInsSlots) {
                     lds.idx[wv][slot] = shard[i];
 #pragma unroll
                     for (int w = 0; w < 4; ++w)
@@ -644,7 +651,7 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
     // first runs continuing the previous lane: OR into its last record
     if (cin) {
         const uint32_t slot = base - 1u;
-        if (slot < (uint32_t)kSlots) {
+        if (slot < (uint32_t)kInsSlots) {
 #pragma unroll
             for (int w = 0; w < C::NS; ++w)
                 __hip_atomic_fetch_or(&lds.words[wv][slot][w], first[w], __ATOMIC_RELAXED,
@@ -656,7 +663,7 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
     wave_lds_sync();
 
     // flush: lane -> (record, word)
-    const uint32_t T = total < (uint32_t)kSlots ? total : (uint32_t)kSlots;
+    const uint32_t T = total < (uint32_t)kInsSlots ? total : (uint32_t)kInsSlots;
     for (uint32_t r = c.lane; r < 4u * T; r += 64u) {
         const uint32_t rec = r >> 2, q = r & 3u;
         if (q < (uint32_t)C::NS) {
