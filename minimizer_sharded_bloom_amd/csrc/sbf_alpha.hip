@@ -32,6 +32,7 @@
 #include "../../include/sbf.h"
 #include "sbf_device.hpp"
 #include "sbf_internal.hpp"
+#include "sbf_spec.hpp"
 
 namespace sbf {
 namespace {
@@ -444,18 +445,33 @@ KernelSet make_alpha()
     return ks;
 }
 
-// Compile-time instances: the default protein (k=12, m=6, s=10, H=4) and
-// triplet (k=10, m=5, s=8, H=4) parameters and one neighbour of each.
+// Compile-time instances: the insert and query of the DNA kernels
+// (sbf_spec.hpp: 16 symbols per lane, runs gathered once per segment) read
+// the text through their text front end; the probe is this file's.
+template <int A, int K, int M, int S, int H>
+KernelSet make_alpha_spec()
+{
+    using C = Cfg<K, M, S, H, 16, (int)A>;
+    KernelSet ks;
+    ks.insert = &launch_insert<C>;
+    ks.query = &launch_query<C>;
+    ks.probe = &alpha_probe<ACfg<A, K, M, S, H>>;
+    ks.specialized = 1;
+    return ks;
+}
+
+// The default protein (k=12, m=6, s=10, H=4) and triplet (k=10, m=5, s=8,
+// H=4) parameters and one neighbour of each.
 struct AlphaEntry {
     uint32_t alpha, k, m, s, H;
     KernelSet (*make)();
 };
 constexpr uint32_t kP = SBF_ALPHABET_PROTEIN, kT = SBF_ALPHABET_TRIPLET;
 const AlphaEntry kAlphaTable[] = {
-    {kP, 12, 6, 10, 4, &make_alpha<ACfg<kP, 12, 6, 10, 4>>},
-    {kP, 9, 4, 7, 3, &make_alpha<ACfg<kP, 9, 4, 7, 3>>},
-    {kT, 10, 5, 8, 4, &make_alpha<ACfg<kT, 10, 5, 8, 4>>},
-    {kT, 7, 3, 7, 2, &make_alpha<ACfg<kT, 7, 3, 7, 2>>},
+    {kP, 12, 6, 10, 4, &make_alpha_spec<kP, 12, 6, 10, 4>},
+    {kP, 9, 4, 7, 3, &make_alpha_spec<kP, 9, 4, 7, 3>},
+    {kT, 10, 5, 8, 4, &make_alpha_spec<kT, 10, 5, 8, 4>},
+    {kT, 7, 3, 7, 2, &make_alpha_spec<kT, 7, 3, 7, 2>},
 };
 
 }  // namespace

@@ -18,25 +18,6 @@ namespace sbf {
 // one validity word, four bases per 32-bit SIMD-within-a-register step.
 // ---------------------------------------------------------------------------
 
-// Four ASCII bytes (first base in the low byte) -> one code byte with the
-// first base in its top two bits, and four validity bits (bit j = byte j).
-__device__ __forceinline__ void encode_dword(uint32_t w, uint32_t& code_byte, uint32_t& valid4)
-{
-    // A=0x41 C=0x43 G=0x47 T=0x54 (and lower case): ((c>>1)^(c>>2))&3 = 0,1,2,3
-    const uint32_t c = ((w >> 1) ^ (w >> 2)) & 0x03030303u;
-    // c0 + c1<<8 + c2<<16 + c3<<24 times 2^30+2^20+2^10+1 puts c0..c3 at bits
-    // 30,28,26,24 with every cross term below bit 24 and no carry into it
-    code_byte = (c * 0x40100401u) >> 24;
-    // valid iff the byte, lower-cased, is the letter its code stands for
-    const uint32_t expect = __builtin_amdgcn_perm(0x74676361u, 0x74676361u, c);  // "acgt" by code
-    const uint32_t diff = (w | 0x20202020u) ^ expect;
-    // exact zero-byte flags: high bit of byte j set iff byte j of diff is 0
-    const uint32_t t = (diff & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
-    const uint32_t z = ~(t | diff | 0x7F7F7F7Fu);
-    // flags at bits 7,15,23,31 -> bits 21..24 via one multiply
-    valid4 = ((((z >> 7) & 0x01010101u) * 0x00204081u) >> 21) & 0xFu;
-}
-
 // 16 bases (four dwords) -> one code word (first base in bits 31..30) and 16
 // validity bits.
 __device__ __forceinline__ void encode16(uint4 q, uint32_t& code, uint32_t& val)

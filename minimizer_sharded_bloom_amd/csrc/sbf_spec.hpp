@@ -35,23 +35,30 @@
 namespace sbf {
 
 // KL_ = 0: 16 k-mers per lane, or 32 when the halo exceeds 16; a nonzero
-// KL_ (16 or 32) fixes it.
-template <int K_, int M_, int S_, int H_, int KL_ = 0>
+// KL_ (16 or 32) fixes it.  A_ is the input: SBF_ALPHABET_DNA reads packed
+// 2-bit codes and validity bits; SBF_ALPHABET_PROTEIN (5-bit letters) and
+// SBF_ALPHABET_TRIPLET (6-bit codons of three bases) read the ASCII text and
+// pack each lane's symbols in registers ([cuSBF] §IV-A).
+template <int K_, int M_, int S_, int H_, int KL_ = 0, int A_ = 0>
 struct Cfg {
-    static constexpr int k = K_, m = M_, s = S_, H = H_;
+    static constexpr int k = K_, m = M_, s = S_, H = H_, A = A_;
+    static constexpr int B = A_ == 0 ? 2 : (A_ == 1 ? 5 : 6);  // bits per symbol
     static constexpr int W = k - m + 1;    // m-mers per k-mer
     static constexpr int Z = k - s + 1;    // s-mers per k-mer (Findere z+1)
     static constexpr int HALO = (W - 1 > Z - 1) ? W - 1 : Z - 1;
     static constexpr int KL = KL_ ? KL_ : (HALO <= 16 ? 16 : 32);  // k-mers per lane
     static_assert(KL == 16 || KL == 32, "16 or 32 k-mers per lane");
     static_assert(HALO <= KL, "halo must come from the next lane alone");
+    static_assert(A_ == 0 || KL == 16, "text input: 16 symbols per lane");
     static constexpr int LW = 63;                    // working lanes per wave
     static constexpr int KPW = KL * LW;              // k-mers per wave
-    static constexpr int ND = KL / 16 + 2;           // code words per lane
+    // stream words per lane: for DNA KL/16 own code words and two of halo;
+    // for text, enough for every window of the own positions plus one word
+    static constexpr int ND = A_ == 0 ? KL / 16 + 2 : ((KL + (m > s ? m : s) - 1) * B + 31) / 32 + 1;
     static constexpr int NS = H < 4 ? H : 4;         // sectors in use
     static constexpr int NM = KL + W - 1;            // m-mer hashes per lane
     static constexpr int NZ = KL + Z - 1;            // s-mer hashes per lane
-    static_assert(1 <= m && m <= k && k <= 32 && 1 <= s && s <= k && H >= 1, "bad parameters");
+    static_assert(1 <= m && m <= k && k * B <= 64 && 1 <= s && s <= k && H >= 1, "bad parameters");
 };
 
 template <int B, int E, class F>
@@ -65,14 +72,14 @@ __device__ __forceinline__ void static_for(F&& f)
 
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 
-// Window of N bases starting at base j of a packed KK-mer x.
-template <int KK, int N>
+// Window of N symbols of B bits starting at symbol j of a packed KK-mer x.
+template <int KK, int N, int B = 2>
 __device__ __forceinline__ uint64_t sub_bases(uint64_t x, int j)
 {
-    if constexpr (N >= 32)
+    if constexpr (N * B >= 64)
         return x;
     else
-        return (x >> (2 * (KK - N - j))) & ((1ull << (2 * N)) - 1ull);
+        return (x >> (B * (KK - N - j))) & ((1ull << (B * N)) - 1ull);
 }
 
 // 32 bits of the lane's packed base stream starting at bit OFF (OFF compile
@@ -81,23 +88,25 @@ template <int OFF, int NDW>
 __device__ __forceinline__ uint32_t stream_bits32(const uint32_t (&D)[NDW])
 {
     constexpr int a = OFF >> 5, r = OFF & 31;
+    static_assert(a + (r != 0) < NDW, "window past the lane's stream words");
     if constexpr (r == 0)
         return D[a];
     else
         return __builtin_amdgcn_alignbit(D[a], D[a + 1], 32 - r);
 }
 
-// Value of the N bases starting at the lane's base P, first base most
-// significant (N <= 32): one or two funnel shifts and a shift.
-template <int P, int N, int NDW>
+// Value of the N symbols of B bits starting at the lane's symbol P, first
+// symbol most significant (N * B <= 64): one or two funnel shifts and a shift.
+template <int P, int N, int B, int NDW>
 __device__ __forceinline__ uint64_t bases_at(const uint32_t (&D)[NDW])
 {
-    if constexpr (2 * N <= 32) {
-        const uint32_t w = stream_bits32<2 * P>(D);
-        return 2 * N == 32 ? (uint64_t)w : (uint64_t)(w >> (32 - 2 * N));
+    constexpr int OFF = P * B, LEN = N * B;
+    if constexpr (LEN <= 32) {
+        const uint32_t w = stream_bits32<OFF>(D);
+        return LEN == 32 ? (uint64_t)w : (uint64_t)(w >> (32 - LEN));
     } else {
-        const uint32_t lo = stream_bits32<2 * P + 2 * N - 32>(D);
-        const uint32_t hi = stream_bits32<2 * P>(D) >> (64 - 2 * N);
+        const uint32_t lo = stream_bits32<OFF + LEN - 32>(D);
+        const uint32_t hi = LEN == 64 ? stream_bits32<OFF>(D) : stream_bits32<OFF>(D) >> (64 - LEN);
         return ((uint64_t)hi << 32) | lo;
     }
 }
@@ -175,7 +184,7 @@ __device__ __forceinline__ void lane_shards(const uint32_t (&D)[C::ND], uint32_t
     uint64_t hm[NM];
     static_for<0, KL>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        hm[i] = hash_min(bases_at<i, C::m>(D));
+        hm[i] = hash_min(bases_at<i, C::m, C::B>(D));
         if constexpr (i < W - 1)
             hm[KL + i] = from_next_lane(hm[i]);  // lane l+1's position i is this lane's KL+i
     });
@@ -213,18 +222,6 @@ __device__ __forceinline__ void lane_shards(const uint32_t (&D)[C::ND], uint32_t
             }
         }
     }
-}
-
-// s-mer hashes of positions 0 .. KL+Z-2 (own KL, halo from lane+1).
-template <class C>
-__device__ __forceinline__ void lane_smer_hashes(const uint32_t (&D)[C::ND], uint64_t (&hs)[C::NZ])
-{
-#pragma unroll
-    for (int i = 0; i < C::KL; ++i)
-        hs[i] = hash_s(top_bases(stream_window<C::ND>(D, i), C::s));
-#pragma unroll
-    for (int j = 0; j < C::Z - 1; ++j)
-        hs[C::KL + j] = from_next_lane(hs[j]);
 }
 
 // Bit i set iff bits i .. i+KK-1 of v are all set: the zero bits of v are
@@ -266,6 +263,149 @@ __device__ __forceinline__ uint32_t lane_valid(const SeqArgs& a, const LaneCtx<C
     return v & keep;
 }
 
+// Validity bits of a protein dword (four letters, first in the low byte):
+// byte j is valid iff it is an ASCII letter, i.e. c | 0x20 lies in 'a'..'z'.
+// Setting bit 7 of every byte before subtracting keeps the bytes from
+// borrowing from each other; bit j of the result is byte j.
+__device__ __forceinline__ uint32_t letter_valid4(uint32_t w)
+{
+    const uint32_t xh = w | 0xA0A0A0A0u;        // lower case, bit 7 set
+    const uint32_t ge = xh - 0x61616161u;       // bit 7: byte >= 'a'
+    const uint32_t gt = xh - 0x7B7B7B7Bu;       // bit 7: byte > 'z'
+    const uint32_t f = __builtin_amdgcn_bitop3_b32(ge, gt, w, 0x10) & 0x80808080u;  // ge & ~gt & ~w (ASCII)
+    return (((f >> 7) * 0x00204081u) >> 21) & 0xFu;  // bits 7, 15, 23, 31 -> 0..3
+}
+
+// Text front end (protein and triplet filters): the lane's KL = 16 symbols
+// are read from the ASCII text and packed in registers, first symbol most
+// significant, B bits each, as D[0 ..]; the symbols past them come from lane
+// l+1's packed words by DPP, and so do its validity bits.  A protein letter
+// codes as (c - 1) & 31, its place in A..Z in either case; a codon is its
+// three bases' 2-bit codes, first base most significant, so the lane's 48
+// bases packed at 2 bits are its 16 codons at 6 bits.  Returns the valid-k-mer
+// bits of the lane (bit i: k-mer p0+i is valid and < nk).
+template <class C>
+__device__ __forceinline__ uint32_t load_text(const SeqArgs& a, const LaneCtx<C>& c, uint32_t (&D)[C::ND])
+{
+    constexpr int SB = C::A == 2 ? 3 : 1;  // bytes per symbol
+    constexpr int NB = C::KL * SB;         // bytes per lane
+    constexpr int NQ = NB / 16;            // 16-byte loads per lane
+    constexpr int OB = C::KL * C::B;       // own stream bits
+    constexpr int OW = OB / 32, OR = OB % 32;
+    const uint64_t tb = a.nsym * (uint64_t)SB;  // bytes of whole symbols
+    const uint64_t b0 = c.wstart * (uint64_t)SB;
+    const uint64_t avail = tb > b0 ? tb - b0 : 0;
+    const uint32_t nrec = avail < 0xFFFFFFFFull ? (uint32_t)avail : 0xFFFFFFFFu;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.text + (b0 < tb ? b0 : tb)), (short)0,
+                                                      (int)nrec, 0x00020000);
+    const uint32_t off = c.lane * (uint32_t)NB;
+    uint32_t q[4 * NQ];
+    if (avail >= 64ull * NB) {
+        // every byte of the wave lies before the end
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16u * j), 0, 0);
+            q[4 * j] = v.x;
+            q[4 * j + 1] = v.y;
+            q[4 * j + 2] = v.z;
+            q[4 * j + 3] = v.w;
+        }
+    } else {
+        // the wave that reaches the end: byte loads, 0 past the last symbol
+#pragma unroll
+        for (int j = 0; j < 4 * NQ; ++j) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)(off + 4u * j + b), 0, 0) << (8 * b);
+            q[j] = w;
+        }
+    }
+    uint32_t S[OW + (OR ? 1 : 0)];
+    uint32_t own_valid = 0;
+    if constexpr (C::A == 1) {
+#pragma unroll
+        for (int i = 0; i < OW + (OR ? 1 : 0); ++i)
+            S[i] = 0;
+#pragma unroll
+        for (int t = 0; t < 4 * NQ; ++t) {
+            const uint32_t codes = ((q[t] | 0x80808080u) - 0x01010101u) & 0x1F1F1F1Fu;  // (c - 1) & 31 per byte
+            own_valid |= letter_valid4(q[t]) << (4 * t);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int P = 5 * (4 * t + jj), wd = P >> 5, r = P & 31;
+                const uint32_t code = __builtin_amdgcn_ubfe(codes, 8 * jj, 5);
+                if (r + 5 <= 32) {
+                    S[wd] |= code << (27 - r);
+                } else {
+                    S[wd] |= code >> (r + 5 - 32);
+                    S[wd + 1] |= code << (59 - r);
+                }
+            }
+        }
+    } else {
+        uint32_t cb[4 * NQ], nb[4 * NQ];
+#pragma unroll
+        for (int d = 0; d < 4 * NQ; ++d)
+            encode_dword(q[d], cb[d], nb[d]);
+#pragma unroll
+        for (int u = 0; u < OW; ++u)
+            S[u] = (cb[4 * u] << 24) | (cb[4 * u + 1] << 16) | (cb[4 * u + 2] << 8) | cb[4 * u + 3];
+        // codon validity: four codons per three dwords (twelve bases); the
+        // AND of bits 3c .. 3c+2 lands at bit 3c, then bits 0,3,6,9 -> 0..3
+#pragma unroll
+        for (int g = 0; g < 4 * NQ / 3; ++g) {
+            const uint32_t v = nb[3 * g] | (nb[3 * g + 1] << 4) | (nb[3 * g + 2] << 8);
+            uint32_t y = v & (v >> 1) & (v >> 2) & 0x249u;
+            y = (y | (y >> 2)) & 0xC3u;
+            y = (y | (y >> 4)) & 0xFu;
+            own_valid |= y << (4 * g);
+        }
+    }
+    // halo: lane l+1's packed words spliced after the own OB bits
+    constexpr int NSW = OW + (OR ? 1 : 0);  // own stream words
+    uint32_t N[C::ND];
+#pragma unroll
+    for (int t = 0; t < C::ND; ++t)
+        N[t] = 0;
+#pragma unroll
+    for (int t = 0; t < NSW; ++t)
+        N[t] = from_next_lane(S[t]);
+#pragma unroll
+    for (int u = 0; u < OW; ++u)
+        D[u] = S[u];
+#pragma unroll
+    for (int t = 0; t < C::ND - OW; ++t) {
+        if constexpr (OR == 0)
+            D[OW + t] = N[t];
+        else if (t == 0)
+            D[OW] = S[OW] | (N[0] >> OR);
+        else
+            D[OW + t] = __builtin_amdgcn_alignbit(N[t - 1], N[t], OR);
+    }
+    static_assert(C::KL + C::k - 1 <= 32, "validity window");
+    const uint32_t win = own_valid | (from_next_lane(own_valid) << C::KL);
+    const uint32_t v = (uint32_t)valid_starts<C::k>((uint64_t)win);
+    const uint64_t rem = a.nk > c.p0 ? a.nk - c.p0 : 0;
+    uint32_t keep = rem >= (uint64_t)C::KL ? (1u << C::KL) - 1u : (1u << rem) - 1u;
+    if (c.lane >= (uint32_t)C::LW)
+        keep = 0;
+    return v & keep;
+}
+
+// Stream words and valid-k-mer bits of the lane, from packed DNA or text.
+template <class C>
+__device__ __forceinline__ uint32_t lane_input(const SeqArgs& a, const LaneCtx<C>& c, uint32_t (&D)[C::ND])
+{
+    if constexpr (C::A == 0) {
+        load_codes<C>(a, c, D);
+        return lane_valid<C>(a, c);
+    } else {
+        return load_text<C>(a, c, D);
+    }
+}
+
 // Sector masks of one s-mer hash: hash index t sets one bit in word t mod 4.
 template <class C>
 __device__ __forceinline__ void smer_masks(uint64_t h, uint64_t (&mk)[4])
@@ -293,7 +433,7 @@ __device__ __forceinline__ void step_fence(uint32_t (&D)[NDW])
 template <class C, int Q>
 __device__ __forceinline__ uint64_t smer_hash_at(const uint32_t (&D)[C::ND])
 {
-    return hash_s(bases_at<Q, C::s>(D));
+    return hash_s(bases_at<Q, C::s, C::B>(D));
 }
 
 // Streaming Findere masks.  Level l entry e = OR of the sector masks of
@@ -594,10 +734,9 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
         return;  // whole wave
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar LDS bases
     uint32_t D[C::ND];
-    load_codes<C>(a, c, D);
+    const uint32_t vk = lane_input<C>(a, c, D);
     uint32_t shard[C::KL];
     lane_shards<C>(D, shard);
-    const uint32_t vk = lane_valid<C>(a, c);
 
     // pass A: slots
     const uint32_t st = run_starts<C>(vk, shard);
@@ -678,6 +817,35 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
 // window, minimizer over its w m-mers, one shard load, all s-mer masks.  The
 // path for waves whose runs exceed the LDS slots (very short runs); a runtime
 // loop keeps it small.
+// The k-mer starting at the lane's symbol i (a run-time index): the 64
+// stream bits from bit i*B, cut to k symbols.
+template <class C>
+__device__ __forceinline__ uint64_t kmer_at_lane(const uint32_t (&D)[C::ND], int i)
+{
+    uint32_t d0, d1, d2, r;
+    if constexpr (C::A == 0) {
+        const bool hi16 = i >= 16;
+        d0 = hi16 ? D[1] : D[0];
+        d1 = hi16 ? D[2] : D[1];
+        d2 = hi16 ? D[C::ND - 1] : D[2];
+        r = 2u * (uint32_t)(i & 15);
+    } else {
+        const uint32_t off = (uint32_t)i * C::B, wa = off >> 5;
+        r = off & 31u;
+        d0 = d1 = d2 = 0;
+#pragma unroll
+        for (int j = 0; j < C::ND; ++j) {
+            if (wa == (uint32_t)j) {
+                d0 = D[j];
+                d1 = j + 1 < C::ND ? D[j + 1 < C::ND ? j + 1 : j] : 0u;
+                d2 = j + 2 < C::ND ? D[j + 2 < C::ND ? j + 2 : j] : 0u;
+            }
+        }
+    }
+    const uint64_t win = ((uint64_t)funnel_hi(d0, d1, r) << 32) | funnel_hi(d1, d2, r);
+    return C::k * C::B >= 64 ? win : win >> (64 - C::k * C::B);
+}
+
 template <class C>
 __device__ __forceinline__ uint32_t query_lane_direct(const SeqArgs& a, const uint32_t (&D)[C::ND], uint32_t vk)
 {
@@ -685,17 +853,11 @@ __device__ __forceinline__ uint32_t query_lane_direct(const SeqArgs& a, const ui
     for (int i = 0; i < C::KL; ++i) {
         if (!((vk >> i) & 1u))
             continue;
-        const bool hi16 = i >= 16;
-        const uint32_t d0 = hi16 ? D[1] : D[0];
-        const uint32_t d1 = hi16 ? D[2] : D[1];
-        const uint32_t d2 = hi16 ? D[C::ND - 1] : D[2];
-        const uint32_t r = 2u * (uint32_t)(i & 15);
-        const uint64_t win = ((uint64_t)funnel_hi(d0, d1, r) << 32) | funnel_hi(d1, d2, r);
-        const uint64_t x = top_bases(win, C::k);
+        const uint64_t x = kmer_at_lane<C>(D, i);
         uint64_t mn = ~0ull;
 #pragma unroll
         for (int j = 0; j < C::W; ++j) {
-            const uint64_t h = hash_min(sub_bases<C::k, C::m>(x, j));
+            const uint64_t h = hash_min(sub_bases<C::k, C::m, C::B>(x, j));
             mn = h < mn ? h : mn;
         }
         uint64_t w[4];
@@ -704,7 +866,7 @@ __device__ __forceinline__ uint32_t query_lane_direct(const SeqArgs& a, const ui
 #pragma unroll
         for (int j = 0; j < C::Z; ++j) {
             uint64_t mk[4];
-            smer_masks<C>(hash_s(sub_bases<C::k, C::s>(x, j)), mk);
+            smer_masks<C>(hash_s(sub_bases<C::k, C::s, C::B>(x, j)), mk);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 R[q] |= mk[q];
@@ -737,8 +899,7 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
         return;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar LDS bases
     uint32_t D[C::ND];
-    load_codes<C>(a, c, D);
-    const uint32_t vk = lane_valid<C>(a, c);
+    const uint32_t vk = lane_input<C>(a, c, D);
     uint32_t total;
     uint32_t rec[C::KL];
     {
