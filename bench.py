@@ -73,25 +73,20 @@ def alu_ops_per_kmer(kind: str) -> float:
     return float(sum(FRONT.values()) + sum(TAIL[kind].values()))
 
 
-# Other alphabets (one symbol per lane, sliding windows across lanes): the
-# same per-position work as the DNA front end, except that each position
-# decodes its symbol from ASCII and extends its m-mer and s-mer values by one
-# symbol (64-bit shift, OR, mask each) instead of cutting them from packed
-# words.  Itemised in the design doc.
+# Other alphabets: the DNA kernels' work per k-mer start (windows cut from a
+# packed stream, here 5- or 6-bit symbols packed in registers) plus decoding
+# the symbol from ASCII in the kernel's text front end.  Itemised in the design doc.
 ALPHAS = {
     "protein": {"params": (12, 6, 10, 4), "bytes_per_symbol": 1,
-                "decode": {"decode a letter: or, subtract, compare": 3}},
+                "decode": {"letter: SWAR codes, letter test and flag bits over 4 bytes (1/4 each), "
+                           "5-bit field into the packed word": 5.5}},
     "triplet": {"params": (10, 5, 8, 4), "bytes_per_symbol": 3,
-                "decode": {"decode a codon: 3 x (2 shifts, xor, and, compare against acgt) + 2 shift-ors": 17}},
+                "decode": {"codon: SWAR 2-bit codes and validity of its 3 bases (4.25 each), codon flag": 15.75}},
 }
-ALPHA_WINDOWS = {"m-mer and s-mer extended by one symbol (2 x 64-bit shift, or, and)": 8}
 
 
 def alpha_alu_ops_per_kmer(alpha: str, kind: str) -> float:
-    drop = ("m-mer window (funnel shift)", "s-mer window (2 funnel shifts + shift)")
-    front = sum(v for k2, v in FRONT.items() if k2 not in drop)
-    return float(front + sum(ALPHA_WINDOWS.values()) + sum(ALPHAS[alpha]["decode"].values())
-                 + sum(TAIL[kind].values()))
+    return float(sum(FRONT.values()) + sum(ALPHAS[alpha]["decode"].values()) + sum(TAIL[kind].values()))
 
 
 def alpha_bytes_per_kmer(alpha: str, kind: str) -> float:

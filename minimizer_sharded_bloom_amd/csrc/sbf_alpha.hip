@@ -11,11 +11,17 @@
 // place in A..Z; a triplet symbol is the codon at bytes 3j..3j+2 coded
 // 16 c0 + 4 c1 + c2 from the DNA base codes; anything else is invalid.
 //
-// Layout (differs from [cuSBF]'s one-k-mer-per-thread tiles): a wave64 owns
-// 64 consecutive symbol positions, one per lane, read straight from the ASCII
-// text (no packing pass).  The m-mer and s-mer starting at each lane are
-// assembled from neighbouring lanes with DPP moves; h_min and h_s are then
-// computed once per position, not once per k-mer that contains it.  The
+// Two layouts.  The compile-time parameter sets (the table at the end) run
+// the insert and query kernels of sbf_spec.hpp through their text front end:
+// 16 symbols per lane packed in registers, sliding windows inside the lane,
+// each segment's shard gathered once into LDS.  Any other parameters run this
+// file's run-time kernels, and every set runs this file's probe.
+//
+// Run-time layout (differs from [cuSBF]'s one-k-mer-per-thread tiles): a
+// wave64 owns 64 consecutive symbol positions, one per lane, read straight
+// from the ASCII text (no packing pass).  The m-mer and s-mer starting at each
+// lane are assembled from neighbouring lanes with DPP moves; h_min and h_s are
+// then computed once per position, not once per k-mer that contains it.  The
 // minimizer of the k-mer starting at lane l is the minimum of h_min over
 // lanes l .. l+w-1 (w = k-m+1), and its s-mer bits the OR over lanes
 // l .. l+z-1 (z = k-s+1): both are sliding windows across lanes, done by
@@ -23,12 +29,12 @@
 // Lanes l <= 64-k start a complete k-mer, so one wave step yields 65-k
 // k-mers; the rest of the wave is halo.
 //
-// Insert groups consecutive k-mers of one shard into runs (super-k-mers,
-// [cuSBF] §IV-D), ORs each run's masks in an LDS record with LDS atomics and
-// issues one global atomic OR per record word, four adjacent lanes per
-// record.  Query loads each k-mer's 256-bit shard and tests its mask; the
-// wave's answer ballots are appended to a running 64-bit word so every store
-// is a whole, aligned answer word.
+// The run-time insert groups consecutive k-mers of one shard into runs
+// (super-k-mers, [cuSBF] §IV-D), ORs each run's masks in an LDS record with
+// LDS atomics and issues one global atomic OR per record word, four adjacent
+// lanes per record.  The run-time query loads each k-mer's 256-bit shard and
+// tests its mask; the wave's answer ballots are appended to a running 64-bit
+// word so every store is a whole, aligned answer word.
 #include "../../include/sbf.h"
 #include "sbf_device.hpp"
 #include "sbf_internal.hpp"
@@ -192,61 +198,28 @@ __device__ __forceinline__ bool wave_step(const SeqArgs& a, const Params& P, uin
 
     // m-mer and s-mer starting here: symbols of lanes l .. l+max(m,s)-1
     uint64_t hm, vs;
-    if constexpr (C::kStatic) {
-        // 32-bit rolling values of up to P symbols (P * B <= 32); an s-mer of
-        // more than P symbols is its first P and the (s-P)-symbol value that
-        // lane l+P holds
-        constexpr uint32_t P = 32u / Al::B;
-        static_assert(C::kS <= 2 * P && C::kM <= P, "window longer than two 32-bit pieces");
-        constexpr uint32_t S1 = C::kS <= P ? C::kS : P, S2 = C::kS - S1;
-        constexpr uint32_t NR = C::kM > S1 ? C::kM : S1;
-        uint32_t acc = sym, t = sym, am = sym, as1 = sym, as2 = sym;
-#pragma unroll
-        for (uint32_t i = 1; i < NR; ++i) {
-            t = from_next_lane(t);
-            acc = (acc << Al::B) | t;
-            if (i + 1u == C::kM)
-                am = acc;
-            if (i + 1u == S1)
-                as1 = acc;
-            if (i + 1u == S2)
-                as2 = acc;
-        }
-        hm = hash_min32(am);
-        if constexpr (S2 > 0)
-            vs = ((uint64_t)as1 << (Al::B * S2)) | lane_down(as2, P, lane);
-        else
-            vs = as1;
-    } else {
-        const uint32_t nr = m > s ? m : s;
-        uint64_t acc = sym, vm = sym;
-        uint32_t t = sym;
-        vs = sym;
-        for (uint32_t i = 1; i < nr; ++i) {
-            t = from_next_lane(t);
-            acc = (acc << Al::B) | t;
-            if (i + 1u == m)
-                vm = acc;
-            if (i + 1u == s)
-                vs = acc;
-        }
-        hm = hash_min(vm);
+    const uint32_t nr = m > s ? m : s;
+    uint64_t acc = sym, vm = sym;
+    uint32_t t = sym;
+    vs = sym;
+    for (uint32_t i = 1; i < nr; ++i) {
+        t = from_next_lane(t);
+        acc = (acc << Al::B) | t;
+        if (i + 1u == m)
+            vm = acc;
+        if (i + 1u == s)
+            vs = acc;
     }
+    hm = hash_min(vm);
     shard = (uint32_t)window_min(hm, k - m + 1u, lane) & a.shard_mask;
 
     const uint64_t h = hash_s(vs);
     mk[0] = mk[1] = mk[2] = mk[3] = 0;
-    if constexpr (C::kStatic) {
+    for (uint32_t j = 0; j < H; ++j) {
+        const uint64_t bit = 1ull << bit_addr_rt(h, j, H);
 #pragma unroll
-        for (uint32_t j = 0; j < H; ++j)
-            mk[j & 3u] |= 1ull << bit_addr_rt(h, j, H);
-    } else {
-        for (uint32_t j = 0; j < H; ++j) {
-            const uint64_t bit = 1ull << bit_addr_rt(h, j, H);
-#pragma unroll
-            for (uint32_t q = 0; q < 4; ++q)
-                mk[q] |= (j & 3u) == q ? bit : 0ull;
-        }
+        for (uint32_t q = 0; q < 4; ++q)
+            mk[q] |= (j & 3u) == q ? bit : 0ull;
     }
     window_or(mk, k - s + 1u, H, lane);
 
