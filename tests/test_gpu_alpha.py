@@ -86,6 +86,34 @@ def test_alpha_edge_lengths(alpha):
     pair(alpha, params, 2**13, ins, qs)
 
 
+@pytest.mark.parametrize("alpha,params", [(a, p) for a in SPECIALIZED for p in SPECIALIZED[a]])
+def test_alpha_text_front_end_edges(alpha, params):
+    """The compile-time sets read 16 symbols per lane, 1008 k-mer starts per
+    wave, and take byte loads only in the wave that reaches the end of the
+    text (one whose 1024 symbols are not all present): lengths around a lane,
+    a wave and that limit, texts ending at every offset of a lane, invalid
+    symbols at lane edges, triplet texts with stray bytes after the last
+    codon."""
+    k = params[0]
+    rng = np.random.default_rng(11 + sum(params) + len(alpha))
+    lens = [k, k + 1, 15 + k, 16 + k, 17 + k, 1007 + k, 1008 + k, 1009 + k, 1023, 1024, 1025, 1023 + k, 1024 + k,
+            1040 + k, 2015 + k, 2016 + k, 2017 + k, 3024 + k] + [5000 + d for d in range(16)]
+    ins = [text(alpha, rng, L) for L in lens]
+    edge = bytearray(text(alpha, rng, 4000))
+    sb = 3 if alpha == "triplet" else 1
+    for lane_start in range(0, 4000, 16):
+        for d in (-1, 0, 15):
+            p = lane_start + d
+            if 0 <= p < 4000 and rng.random() < 0.3:
+                edge[sb * p] = ord("*" if alpha == "protein" else "N")
+    ins.append(bytes(edge))
+    if alpha == "triplet":
+        ins += [text(alpha, rng, 1024) + b"A", text(alpha, rng, 1008 + k) + b"GT"]
+    qs = [text(alpha, rng, L) for L in lens[::2]] + ins[-4:]
+    g, _ = pair(alpha, params, 2**14, ins, qs)
+    assert g.specialized
+
+
 @pytest.mark.parametrize("alpha", ["protein", "triplet"])
 def test_alpha_host_pipeline(alpha):
     """Host input through the chunked pipeline with tiny chunks (k-1 symbols
