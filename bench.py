@@ -116,15 +116,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # Sources each workload family's kernels are built from: the DNA step's
 # pack/clear kernels and the specialized set at (31,16,28,4), or the alphabet
-# kernels.  A traffic summary is used only while these hash as when it was
+# kernels (their insert and query are sbf_spec.hpp's with a text front end).  A traffic summary is used only while these hash as when it was
 # taken.
 KERNEL_SOURCES = {
     "dna": ("minimizer_sharded_bloom_amd/csrc/inst_m16.hip", "minimizer_sharded_bloom_amd/csrc/sbf_spec.hpp",
             "minimizer_sharded_bloom_amd/csrc/sbf_spec_list.hpp", "minimizer_sharded_bloom_amd/csrc/sbf_device.hpp",
             "minimizer_sharded_bloom_amd/csrc/sbf_internal.hpp", "minimizer_sharded_bloom_amd/csrc/sbf_generic.hip"),
-    "alpha": ("minimizer_sharded_bloom_amd/csrc/sbf_alpha.hip", "minimizer_sharded_bloom_amd/csrc/sbf_device.hpp",
-              "minimizer_sharded_bloom_amd/csrc/sbf_internal.hpp", "minimizer_sharded_bloom_amd/csrc/sbf_generic.hip",
-              "include/sbf.h"),
+    "alpha": ("minimizer_sharded_bloom_amd/csrc/sbf_alpha.hip", "minimizer_sharded_bloom_amd/csrc/sbf_spec.hpp",
+              "minimizer_sharded_bloom_amd/csrc/sbf_device.hpp", "minimizer_sharded_bloom_amd/csrc/sbf_internal.hpp",
+              "minimizer_sharded_bloom_amd/csrc/sbf_generic.hip", "include/sbf.h"),
 }
 
 
