@@ -59,16 +59,25 @@ int fail(int code, const char* what)
     return code;
 }
 
+// A HIP call that fails also leaves its error as the thread's last HIP
+// error, which the launch checks (hipGetLastError after a launch) would
+// report again on a later, unrelated call.  The error is recorded here and
+// then cleared.
 int fail_hip(hipError_t e, const char* what)
 {
     g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    (void)hipGetLastError();
     return e == hipErrorOutOfMemory ? SBF_ENOMEM : SBF_EDEVICE;
 }
 
 void ok() { g_last_error.clear(); }
 
+// Every entry point that launches work comes through here first: an error
+// left behind by an earlier HIP call of the caller's is not this call's, so
+// it is dropped before the call's own launches are checked.
 int set_device(const sbf_t* h)
 {
+    (void)hipGetLastError();
     hipError_t e = hipSetDevice(h->device);
     return e == hipSuccess ? SBF_OK : fail_hip(e, "hipSetDevice");
 }
@@ -151,6 +160,7 @@ int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
         h->ks = sbf::alpha_kernels(P);
     else if (!sbf::find_specialized(P, &h->ks))
         h->ks = sbf::generic_kernels();
+    (void)hipGetLastError();  // an earlier call's error is not this one's (see set_device)
     hipError_t e = hipGetDevice(&h->device);
     if (e != hipSuccess) {
         delete h;
@@ -351,6 +361,7 @@ int sbf_pack(const char* d_ascii, uint64_t len, uint32_t* d_codes, uint32_t* d_v
     }
     if (!d_ascii || !d_codes || !d_valid)
         return fail(SBF_EINVAL, "NULL argument");
+    (void)hipGetLastError();  // an earlier call's error is not this one's (see set_device)
     hipError_t e = sbf::launch_pack(d_ascii, len, d_codes, d_valid, (hipStream_t)stream);
     if (e != hipSuccess)
         return fail_hip(e, "pack launch");

@@ -69,6 +69,7 @@ int sbf_membench_shard_reads(const uint64_t* d_table, uint64_t nshard, uint64_t 
         return SBF_EINVAL;
     if (n == 0)
         return SBF_OK;
+    (void)hipGetLastError();  // report this launch's error, not an earlier call's
     hipLaunchKernelGGL(sbf::shard_reads_kernel, dim3(sbf::grid_for(n)), dim3(256), 0, (hipStream_t)stream, d_table,
                        nshard - 1, n, seed, d_sink);
     return hipGetLastError() == hipSuccess ? SBF_OK : SBF_EDEVICE;
@@ -80,6 +81,7 @@ int sbf_membench_shard_ors(uint64_t* d_table, uint64_t nshard, uint64_t n, uint6
         return SBF_EINVAL;
     if (n == 0)
         return SBF_OK;
+    (void)hipGetLastError();  // report this launch's error, not an earlier call's
     hipLaunchKernelGGL(sbf::shard_ors_kernel, dim3(sbf::grid_for(4 * n)), dim3(256), 0, (hipStream_t)stream, d_table,
                        nshard - 1, n, seed);
     return hipGetLastError() == hipSuccess ? SBF_OK : SBF_EDEVICE;
