@@ -584,9 +584,9 @@ constexpr int kWaves = 4;    // waves per 256-thread workgroup
 template <class C>
 constexpr int query_slots() { return C::KL == 32 ? (C::W <= 14 ? 352 : 280) : (C::W <= 7 ? 352 : 256); }
 
-// Insert records per wave before records go straight to the filter (four
-// unmerged 64-bit atomics each): 256, or 352 when w <= 8, where a wave of
-// 1008 k-mers holds 2/(w+1) runs per k-mer, 224 at w = 8 and 336 at w = 5.
+// Insert records per wave and round (a wave with more runs takes several
+// rounds): 256, or 352 when w <= 8, where a wave of 1008 k-mers holds 2/(w+1)
+// runs per k-mer, 224 at w = 8 and 336 at w = 5.
 template <class C>
 constexpr int insert_slots() { return C::W <= 8 ? 352 : kSlots; }
 
@@ -722,8 +722,8 @@ __device__ __forceinline__ void global_or_record(uint64_t* __restrict__ filter, 
 // a wave scan gives each run a record slot.  Pass B: each run's sector masks
 // go to its slot (a run continuing the previous lane's last run ORs into that
 // slot).  Flush: four adjacent lanes OR the four words of one record into the
-// filter.  Records past the wave's slots go straight to the filter from their
-// lane.
+// filter.  With dense minimizers a wave with more runs than slots does this
+// in rounds of slots.
 template <class C>
 __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
 {
@@ -746,69 +746,84 @@ __global__ __launch_bounds__(256) void sbf_insert_kernel(SeqArgs a)
     const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
     const uint32_t base = incl - nrec;
 
-    // pass B: run masks -> records
-    FindereMasks<C> fm;
-    fm.init(D);
-    uint64_t Wr[4] = {0, 0, 0, 0};
-    uint64_t first[4] = {0, 0, 0, 0};
-    static_for<0, C::KL>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        uint64_t T0[4], T1[4];
-        fm.template step<i>(D, T0, T1);
-        const bool vi = (vk >> i) & 1u;
-        // a run start clears the run masks; an invalid k-mer may add to them,
-        // as it never lies inside a run and the next start clears them again
-        const uint32_t keep = ((st >> i) & 1u) ? 0u : 0xFFFFFFFFu;
-        accumulate_run<C>(Wr, keep, T0, T1);
-        // the run ends here if the next k-mer does not continue it
-        bool ends;
-        if constexpr (i == C::KL - 1)
-            ends = vi;
-        else
-            ends = vi && (((st >> (i + 1)) & 1u) || !((vk >> (i + 1)) & 1u));
-        if (ends) {
-            const uint32_t ridx = __popc(st & ((2u << i) - 1u)) - 1u;
-            if (ridx == 0 && cin) {
+    // Dense minimizers (w <= 8) go in rounds of kInsSlots records: a later
+    // round repeats pass B and keeps the records of its own range, so every
+    // record is flushed merged.  Elsewhere one round serves, and a record
+    // past the slots (a rare wave) goes straight to the filter from its lane;
+    // the rounds would keep pass B's inputs live across the loop, which
+    // costs those kernels about 50 VGPRs.
+    constexpr bool kRounds = C::W <= 8;
+    const uint32_t nrounds = kRounds ? total : (total ? 1u : 0u);
+    for (uint32_t r0 = 0; r0 < nrounds; r0 += (uint32_t)kInsSlots) {
+        if (r0)
+            wave_lds_sync();  // the previous round's flush has read its records
+        // pass B: run masks -> records
+        FindereMasks<C> fm;
+        fm.init(D);
+        uint64_t Wr[4] = {0, 0, 0, 0};
+        uint64_t first[4] = {0, 0, 0, 0};
+        const uint32_t slot0 = base - cin - r0;  // this lane's first own record in this round's slots
+        static_for<0, C::KL>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            uint64_t T0[4], T1[4];
+            fm.template step<i>(D, T0, T1);
+            const bool vi = (vk >> i) & 1u;
+            // a run start clears the run masks; an invalid k-mer may add to
+            // them, as it never lies inside a run and the next start clears
+            // them again
+            const uint32_t keep = ((st >> i) & 1u) ? 0u : 0xFFFFFFFFu;
+            accumulate_run<C>(Wr, keep, T0, T1);
+            // the run ends here if the next k-mer does not continue it
+            bool ends;
+            if constexpr (i == C::KL - 1)
+                ends = vi;
+            else
+                ends = vi && (((st >> (i + 1)) & 1u) || !((vk >> (i + 1)) & 1u));
+            if (ends) {
+                const uint32_t ridx = __popc(st & ((2u << i) - 1u)) - 1u;
+                if (ridx == 0 && cin) {
 #pragma unroll
-                for (int w = 0; w < C::NS; ++w)
-                    first[w] = Wr[w];
-            } else {
-                const uint32_t slot = base + ridx - cin;
-                if (slot < (uint32_t)kInsSlots) {
-                    lds.idx[wv][slot] = shard[i];
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        lds.words[wv][slot][w] = Wr[w];
+                    for (int w = 0; w < C::NS; ++w)
+                        first[w] = Wr[w];
                 } else {
-                    global_or_record<C>(a.filter, shard[i] & a.shard_mask, Wr);
+                    const uint32_t slot = slot0 + ridx;  // below kInsSlots iff in this round
+                    if (slot < (uint32_t)kInsSlots) {
+                        lds.idx[wv][slot] = shard[i];
+#pragma unroll
+                        for (int w = 0; w < 4; ++w)
+                            lds.words[wv][slot][w] = Wr[w];
+                    } else if constexpr (!kRounds) {
+                        global_or_record<C>(a.filter, shard[i] & a.shard_mask, Wr);
+                    }
                 }
             }
-        }
-        step_fence(D);
-    });
-    wave_lds_sync();
-    // first runs continuing the previous lane: OR into its last record
-    if (cin) {
-        const uint32_t slot = base - 1u;
-        if (slot < (uint32_t)kInsSlots) {
+            step_fence(D);
+        });
+        wave_lds_sync();
+        // first runs continuing the previous lane: OR into its last record
+        if (cin) {
+            const uint32_t slot = base - 1u - r0;
+            if (slot < (uint32_t)kInsSlots) {
 #pragma unroll
-            for (int w = 0; w < C::NS; ++w)
-                __hip_atomic_fetch_or(&lds.words[wv][slot][w], first[w], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_WAVEFRONT);
-        } else {
-            global_or_record<C>(a.filter, shard[0] & a.shard_mask, first);
+                for (int w = 0; w < C::NS; ++w)
+                    __hip_atomic_fetch_or(&lds.words[wv][slot][w], first[w], __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WAVEFRONT);
+            } else if constexpr (!kRounds) {
+                global_or_record<C>(a.filter, shard[0] & a.shard_mask, first);
+            }
         }
-    }
-    wave_lds_sync();
+        wave_lds_sync();
 
-    // flush: lane -> (record, word)
-    const uint32_t T = total < (uint32_t)kInsSlots ? total : (uint32_t)kInsSlots;
-    for (uint32_t r = c.lane; r < 4u * T; r += 64u) {
-        const uint32_t rec = r >> 2, q = r & 3u;
-        if (q < (uint32_t)C::NS) {
-            const uint64_t m = lds.words[wv][rec][q];
-            if (m)
-                atomic_or_u64(a.filter + 4ull * (lds.idx[wv][rec] & a.shard_mask) + q, m);
+        // flush: lane -> (record, word)
+        const uint32_t left = total - r0;
+        const uint32_t T = left < (uint32_t)kInsSlots ? left : (uint32_t)kInsSlots;
+        for (uint32_t r = c.lane; r < 4u * T; r += 64u) {
+            const uint32_t rec = r >> 2, q = r & 3u;
+            if (q < (uint32_t)C::NS) {
+                const uint64_t m = lds.words[wv][rec][q];
+                if (m)
+                    atomic_or_u64(a.filter + 4ull * (lds.idx[wv][rec] & a.shard_mask) + q, m);
+            }
         }
     }
 }

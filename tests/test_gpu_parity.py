@@ -298,15 +298,17 @@ def _segments_per_wave(seq: bytes, k: int, m: int, wave: int, n_waves: int) -> l
     return counts
 
 
-@pytest.mark.parametrize("m", [17, 21, 27, 28])
+@pytest.mark.parametrize("m", [17, 21, 27, 28, 31])
 def test_query_waves_at_record_limits(m):
     """Genome-scale queries at minimizer densities 2/(w+1) near the query's
     LDS record slots.  m = 17: about 252 segments per 2016-k-mer wave (32
     k-mers per lane) against 280 slots.  From w <= 11 on the query takes 16
     k-mers per lane: m = 21, about 168 per 1008-k-mer wave against 256;
     m = 27, about 337 against 352, so one launch runs both the LDS path and
-    the per-k-mer path; m = 28, about 404, the per-k-mer path.  Filter words
-    and every query bit match the oracle."""
+    the per-k-mer path; m = 28, about 404, the per-k-mer path.  The insert
+    (1008-k-mer waves, 352 slots at w <= 8) goes through its slots in rounds:
+    one or two at m = 27, two at m = 28, three at m = 31 (every k-mer its own
+    run).  Filter words and every query bit match the oracle."""
     rng = np.random.default_rng(300 + m)
     params = (31, m, 28, 4)
     genome = T.random_dna(rng, 300_000)
