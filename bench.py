@@ -7,12 +7,13 @@ Genomic Sequence Data on Modern GPUs"):
     clear the filter
     pack the genome (ASCII -> 2-bit codes + validity)
     insert every genome k-mer           (Algorithm 1)
-    pack the reads
-    query every read k-mer              (Algorithm 2)
+    query every read k-mer              (Algorithm 2), the query kernel
+                                        decoding the reads' ASCII itself
     false-positive probe of n random k-mers (§V-D)
-at k=31, m=16, s=28, H=4.  Every launch goes to torch's current stream, so
-the torch events recorded between launches time each kernel on the stream it
-runs on.
+at k=31, m=16, s=28, H=4.  (`--query-input packed` packs the reads in a pass
+of their own and queries the packed codes instead.)  Every launch goes to
+torch's current stream, so the torch events recorded between launches time
+each kernel on the stream it runs on.
 
 Prints one JSON line.  `value` = k-mers processed per second over the step
 (genome k-mer starts + read k-mer starts + probe k-mers) / step time.
@@ -65,6 +66,10 @@ FRONT = {
 }
 TAIL = {
     "query": {"(T0|T1) & ~W per half (bitop3), one 64-bit compare per word, answer bit": 13},
+    # a query that decodes its reads from ASCII (one base per k-mer start)
+    "query_text": {"(T0|T1) & ~W per half (bitop3), one 64-bit compare per word, answer bit": 13,
+                   "base from ASCII: 2 shifts + bitop3 code, multiply gather, letter lookup, "
+                   "masked compare, add, flag (8 per 4 bases); 21 gathers per 32 bases": 2.66},
     "insert": {"T0|T1 and (Wr & keep) | t per half": 16, "record flush share (~0.12 runs/k-mer)": 1.5},
 }
 
@@ -105,6 +110,8 @@ def _bytes_per_kmer(kind: str, w: int = K - M_ + 1) -> float:
     also writes its answer bit.  Random minimizers give 2/(w+1) runs per k-mer."""
     runs = 2.0 / (w + 1)
     seq = 0.25 + 0.125
+    if kind == "query_text":  # one ASCII byte per base instead
+        return 1.0 + 0.125 + 32 * runs
     if kind == "query":
         return seq + 0.125 + 32 * runs
     return seq + 64 * runs
@@ -245,6 +252,9 @@ def parse():
     ap.add_argument("--data-cache", default="",
                     help="directory for the generated inputs: saved there (.npy) after generating, memory-mapped "
                          "from there when present (profiled runs then skip the forking long-read generator)")
+    ap.add_argument("--query-input", default="text", choices=["text", "packed"],
+                    help="DNA reads as the query gets them: text (default; sbf_query_seq, whose kernel decodes "
+                         "the ASCII itself) or packed (sbf_pack, then sbf_query_packed)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 256 MiB device copy (elementwise kernel) whose "
                          "FETCH_SIZE/WRITE_SIZE counters scale the filter kernels' counters")
@@ -378,30 +388,42 @@ def main():
     hits = torch.zeros(1, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    names = ["clear", "pack_genome", "insert", "pack_reads", "query", "probe"]
+    text_query = a.query_input == "text"
+    assert not text_query or reads.data_ptr() % 16 == 0, "the ASCII query path needs 16-byte-aligned reads"
+    if text_query:
+        names = ["clear", "pack_genome", "insert", "query", "probe"]
+    else:
+        names = ["clear", "pack_genome", "insert", "pack_reads", "query", "probe"]
 
     def step(events=None):
-        def mark(i):
+        marks = iter(range(len(names) + 1))
+
+        def mark():
+            i = next(marks)
             if events is not None:
                 events[i].record(stream)
-        mark(0)
+        mark()
         M.check(lib.sbf_clear(f.handle, sp), "clear")
-        mark(1)
+        mark()
         M.check(lib.sbf_pack(genome.data_ptr(), LG, g_codes.data_ptr(), g_valid.data_ptr(), sp), "pack")
-        mark(2)
+        mark()
         M.check(lib.sbf_insert_packed(f.handle, g_codes.data_ptr(), g_valid.data_ptr(), LG, sp), "insert")
-        mark(3)
-        M.check(lib.sbf_pack(reads.data_ptr(), LR, r_codes.data_ptr(), r_valid.data_ptr(), sp), "pack")
-        mark(4)
-        M.check(lib.sbf_query_packed(f.handle, r_codes.data_ptr(), r_valid.data_ptr(), LR, out.data_ptr(), sp), "query")
-        mark(5)
+        mark()
+        if text_query:
+            M.check(lib.sbf_query_seq(f.handle, reads.data_ptr(), LR, out.data_ptr(), M.SBF_DEVICE, sp), "query")
+        else:
+            M.check(lib.sbf_pack(reads.data_ptr(), LR, r_codes.data_ptr(), r_valid.data_ptr(), sp), "pack")
+            mark()
+            M.check(lib.sbf_query_packed(f.handle, r_codes.data_ptr(), r_valid.data_ptr(), LR, out.data_ptr(), sp),
+                    "query")
+        mark()
         M.check(lib.sbf_fpr_probe_device(f.handle, a.probe_n, 0x5EED, hits.data_ptr(), sp), "probe")
-        mark(6)
+        mark()
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(a.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(a.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -438,8 +460,9 @@ def main():
     wl = "cfg%d" % a.workload
 
     def roof(kind, rate):
-        alu = rate * alu_ops_per_kmer(kind)
-        mem = rate * _bytes_per_kmer(kind)
+        model = "query_text" if kind == "query" and text_query else kind
+        alu = rate * alu_ops_per_kmer(model)
+        mem = rate * _bytes_per_kmer(model)
         tr = measured_traffic(wl, kind, sha)
         traffic = None if tr is None else tr["bytes"]
         extra = {} if tr is None else {"traffic_fetch": tr["fetch"], "traffic_write": tr["write"],
@@ -447,10 +470,10 @@ def main():
                                        "traffic_per_kmer": tr["bytes"] / (nk_r if kind == "query" else nk_g)}
         return (dict({"bound": "alu", "achieved": alu / 1e12, "peak": ALU_PEAK / 1e12,
                       "unit": "T lane-instr/s", "frac": alu / ALU_PEAK, "traffic": traffic,
-                      "kernel": kind, "per_kmer_ops": alu_ops_per_kmer(kind)}, **extra),
+                      "kernel": kind, "per_kmer_ops": alu_ops_per_kmer(model)}, **extra),
                 dict({"bound": "hbm", "achieved": mem / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                       "frac": mem / HBM_PEAK, "traffic": traffic, "kernel": kind,
-                      "per_kmer_bytes": _bytes_per_kmer(kind)}, **extra))
+                      "per_kmer_bytes": _bytes_per_kmer(model)}, **extra))
 
     dom = "query" if phase["query"] >= phase["insert"] else "insert"
     alu, mem = roof(dom, q_rate if dom == "query" else ins_rate)
@@ -465,7 +488,9 @@ def main():
                    "kmers_per_step": total},
         "roofline": primary, "roofline_other": secondary,
         "insert_gkmers_s": round(ins_rate / 1e9, 3), "query_gkmers_s": round(q_rate / 1e9, 3),
-        "pack_gbases_s": round((LG + LR) / ((phase["pack_genome"] + phase["pack_reads"]) * 1e-3) / 1e9, 3),
+        "pack_gbases_s": round((LG + (0 if text_query else LR))
+                               / ((phase["pack_genome"] + phase.get("pack_reads", 0.0)) * 1e-3) / 1e9, 3),
+        "query_input": a.query_input,
         "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
         "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},
         "phase_ms_median": {k2: round(v, 4) for k2, v in phase_med.items()},

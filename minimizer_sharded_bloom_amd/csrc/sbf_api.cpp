@@ -477,6 +477,14 @@ int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits, u
         ok();
         return SBF_OK;
     }
+    if (h->ks.query_text && ((uintptr_t)seq & 15u) == 0) {
+        // the query kernel reads the ASCII itself (16-byte loads per lane)
+        hipError_t e = h->ks.query_text(text_args(h, seq, len, out_bits, st), h->P);
+        if (e != hipSuccess)
+            return fail_hip(e, "query");
+        ok();
+        return SBF_OK;
+    }
     rc = stage_packed(h, seq, len, st);
     if (rc)
         return rc;

@@ -266,6 +266,9 @@ int run_pipeline(sbf_t* h, Source& src, Sink* sink, hipStream_t user, uint64_t* 
         if (e == hipSuccess && h->P.alpha != SBF_ALPHABET_DNA) {
             const SeqArgs a = text_args(h, hs.d_in[b], have, sink ? hs.d_out[b] : nullptr, s);
             e = sink ? h->ks.query(a, h->P) : h->ks.insert(a, h->P);
+        } else if (e == hipSuccess && sink && h->ks.query_text) {
+            // DNA query read as ASCII by the query kernel itself
+            e = h->ks.query_text(text_args(h, hs.d_in[b], have, hs.d_out[b], s), h->P);
         } else if (e == hipSuccess) {
             e = launch_pack(hs.d_in[b], have, hs.d_codes[b], hs.d_valid[b], s);
             if (e == hipSuccess) {

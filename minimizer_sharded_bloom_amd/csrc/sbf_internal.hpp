@@ -20,6 +20,7 @@ struct SeqArgs {
     hipStream_t stream;
     // Protein and triplet alphabets read the ASCII text itself: symbol j is
     // byte j (protein) or bytes 3j..3j+2 (triplet); nk counts symbol starts.
+    // So does a DNA query through KernelSet::query_text (base j = byte j).
     const char* text;
     uint64_t nsym;
 };
@@ -48,6 +49,9 @@ struct KernelSet {
     SeqLaunch query;
     ProbeLaunch probe;
     int specialized;
+    // DNA query straight from ASCII (SeqArgs.text, nsym = bytes), or null:
+    // the sequence is then packed first and `query` reads the codes
+    SeqLaunch query_text = nullptr;
 };
 
 // One row of a specialization table (see sbf_spec_list.hpp).

@@ -38,23 +38,29 @@ namespace sbf {
 // KL_ (16 or 32) fixes it.  A_ is the input: SBF_ALPHABET_DNA reads packed
 // 2-bit codes and validity bits; SBF_ALPHABET_PROTEIN (5-bit letters) and
 // SBF_ALPHABET_TRIPLET (6-bit codons of three bases) read the ASCII text and
-// pack each lane's symbols in registers ([cuSBF] §IV-A).
+// pack each lane's symbols in registers ([cuSBF] §IV-A); kDnaText reads DNA
+// as ASCII and packs it in registers the same way, so a query of a device
+// sequence needs no separate packing pass.
+constexpr int kDnaText = 3;
+
 template <int K_, int M_, int S_, int H_, int KL_ = 0, int A_ = 0>
 struct Cfg {
     static constexpr int k = K_, m = M_, s = S_, H = H_, A = A_;
-    static constexpr int B = A_ == 0 ? 2 : (A_ == 1 ? 5 : 6);  // bits per symbol
+    static constexpr bool BASES = A_ == 0 || A_ == kDnaText;   // 2-bit bases, 16 per stream word
+    static constexpr int B = BASES ? 2 : (A_ == 1 ? 5 : 6);  // bits per symbol
     static constexpr int W = k - m + 1;    // m-mers per k-mer
     static constexpr int Z = k - s + 1;    // s-mers per k-mer (Findere z+1)
     static constexpr int HALO = (W - 1 > Z - 1) ? W - 1 : Z - 1;
     static constexpr int KL = KL_ ? KL_ : (HALO <= 16 ? 16 : 32);  // k-mers per lane
     static_assert(KL == 16 || KL == 32, "16 or 32 k-mers per lane");
     static_assert(HALO <= KL, "halo must come from the next lane alone");
-    static_assert(A_ == 0 || KL == 16, "text input: 16 symbols per lane");
+    static_assert(BASES || KL == 16, "protein and triplet text: 16 symbols per lane");
+    static_assert(A_ != kDnaText || KL == 32, "DNA text: 32 bases per lane, whose s-mers end within lane l+1");
     static constexpr int LW = 63;                    // working lanes per wave
     static constexpr int KPW = KL * LW;              // k-mers per wave
     // stream words per lane: for DNA KL/16 own code words and two of halo;
     // for text, enough for every window of the own positions plus one word
-    static constexpr int ND = A_ == 0 ? KL / 16 + 2 : ((KL + (m > s ? m : s) - 1) * B + 31) / 32 + 1;
+    static constexpr int ND = BASES ? KL / 16 + 2 : ((KL + (m > s ? m : s) - 1) * B + 31) / 32 + 1;
     static constexpr int NS = H < 4 ? H : 4;         // sectors in use
     static constexpr int NM = KL + W - 1;            // m-mer hashes per lane
     static constexpr int NZ = KL + Z - 1;            // s-mer hashes per lane
@@ -276,14 +282,16 @@ __device__ __forceinline__ uint32_t letter_valid4(uint32_t w)
     return (((f >> 7) * 0x00204081u) >> 21) & 0xFu;  // bits 7, 15, 23, 31 -> 0..3
 }
 
-// Text front end (protein and triplet filters): the lane's KL = 16 symbols
-// are read from the ASCII text and packed in registers, first symbol most
-// significant, B bits each, as D[0 ..]; the symbols past them come from lane
-// l+1's packed words by DPP, and so do its validity bits.  A protein letter
-// codes as (c - 1) & 31, its place in A..Z in either case; a codon is its
-// three bases' 2-bit codes, first base most significant, so the lane's 48
-// bases packed at 2 bits are its 16 codons at 6 bits.  Returns the valid-k-mer
-// bits of the lane (bit i: k-mer p0+i is valid and < nk).
+// Text front end (protein and triplet filters, and DNA text): the lane's KL
+// symbols (16 letters or codons, or 32 bases) are read from the ASCII text
+// and packed in registers, first symbol most significant, B bits each, as
+// D[0 ..]; the symbols past them come from lane l+1's packed words by DPP,
+// and so do its validity bits.  A protein letter codes as (c - 1) & 31, its
+// place in A..Z in either case; a base codes and validates as in the packing
+// pass; a codon is its three bases' 2-bit codes, first base most significant,
+// so the lane's 48 bases packed at 2 bits are its 16 codons at 6 bits.
+// Returns the valid-k-mer bits of the lane (bit i: k-mer p0+i is valid and
+// < nk).
 template <class C>
 __device__ __forceinline__ uint32_t load_text(const SeqArgs& a, const LaneCtx<C>& c, uint32_t (&D)[C::ND])
 {
@@ -344,6 +352,38 @@ __device__ __forceinline__ uint32_t load_text(const SeqArgs& a, const LaneCtx<C>
                 }
             }
         }
+    } else if constexpr (C::A == kDnaText) {
+        // 32 bases in eight dwords.  Per dword: the 2-bit codes c, as in the
+        // packing pass ((b >> 1) ^ (b >> 2)) & 3, gathered by one multiply
+        // into the top byte, first base most significant; and the invalid
+        // bytes at bit 7: a byte is valid iff, with bits 5 (case) and 7
+        // cleared, it equals the letter of its code, and bit 7 is clear.
+        // d7 has bits 5 and 7 of every byte clear, so d7 + 0x7F per byte
+        // sets bit 7 exactly for a nonzero byte and never carries.
+        static_assert(NQ == 2 && OW == 2 && OR == 0, "32 bases per lane");
+        uint32_t P[8], Zi[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            const uint32_t w = q[d];
+            const uint32_t cc = __builtin_amdgcn_bitop3_b32(w >> 1, w >> 2, 0x03030303u, 0x28);  // (x ^ y) & m
+            P[d] = cc * 0x40100401u;  // code of byte j at bits 31-2j .. 30-2j
+            const uint32_t e = __builtin_amdgcn_perm(0x74676361u, 0x74676361u, cc);  // "acgt" by code
+            const uint32_t d7 = __builtin_amdgcn_bitop3_b32(w, 0xA0A0A0A0u, e, 0x12);     // ~k & (w ^ e)
+            Zi[d] = __builtin_amdgcn_bitop3_b32(d7 + 0x7F7F7F7Fu, w, 0x80808080u, 0xA8);  // (x | w) & m
+        }
+        // code words: the top bytes of four products each
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            S[u] = __builtin_amdgcn_perm(P[4 * u], P[4 * u + 1], 0x07030C0Cu) |
+                   __builtin_amdgcn_perm(P[4 * u + 2], P[4 * u + 3], 0x0C0C0703u);
+        // invalid flags of two dwords (bits 3,11,19,27 and 7,15,23,31) times
+        // 1 + 2^7 + 2^14 + 2^21 land in bits 24..31 in base order, every
+        // other partial product below bit 24 and on a bit of its own
+        uint32_t V[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            V[g] = ((Zi[2 * g] >> 4) | Zi[2 * g + 1]) * 0x00204081u;
+        own_valid = ~(__builtin_amdgcn_perm(V[1], V[0], 0x0C0C0703u) | __builtin_amdgcn_perm(V[3], V[2], 0x07030C0Cu));
     } else {
         uint32_t cb[4 * NQ], nb[4 * NQ];
 #pragma unroll
@@ -384,11 +424,18 @@ __device__ __forceinline__ uint32_t load_text(const SeqArgs& a, const LaneCtx<C>
         else
             D[OW + t] = __builtin_amdgcn_alignbit(N[t - 1], N[t], OR);
     }
-    static_assert(C::KL + C::k - 1 <= 32, "validity window");
-    const uint32_t win = own_valid | (from_next_lane(own_valid) << C::KL);
-    const uint32_t v = (uint32_t)valid_starts<C::k>((uint64_t)win);
+    // validity of the own symbols and then lane l+1's
+    uint64_t win;
+    if constexpr (C::KL == 32) {
+        static_assert(C::KL + C::k - 1 <= 64, "validity window");
+        win = own_valid | ((uint64_t)from_next_lane(own_valid) << 32);
+    } else {
+        static_assert(C::KL + C::k - 1 <= 32, "validity window");
+        win = (uint32_t)(own_valid | (from_next_lane(own_valid) << C::KL));
+    }
+    const uint32_t v = (uint32_t)valid_starts<C::k>(win);
     const uint64_t rem = a.nk > c.p0 ? a.nk - c.p0 : 0;
-    uint32_t keep = rem >= (uint64_t)C::KL ? (1u << C::KL) - 1u : (1u << rem) - 1u;
+    uint32_t keep = rem >= (uint64_t)C::KL ? (C::KL == 32 ? 0xFFFFFFFFu : (1u << C::KL) - 1u) : (1u << rem) - 1u;
     if (c.lane >= (uint32_t)C::LW)
         keep = 0;
     return v & keep;
@@ -838,7 +885,7 @@ template <class C>
 __device__ __forceinline__ uint64_t kmer_at_lane(const uint32_t (&D)[C::ND], int i)
 {
     uint32_t d0, d1, d2, r;
-    if constexpr (C::A == 0) {
+    if constexpr (C::BASES) {
         const bool hi16 = i >= 16;
         d0 = hi16 ? D[1] : D[0];
         d1 = hi16 ? D[2] : D[1];
@@ -1042,14 +1089,19 @@ hipError_t launch_probe(const ProbeArgs& a, const Params&)
 // twice the k-mers.  More s-mers per k-mer make the doubling levels too large
 // for 32 (over 160 VGPRs); denser minimizers (w <= 11) would give a 2016-k-mer
 // wave more segments than its LDS slots; and the insert measures faster at 16.
+// At 32 k-mers per lane a query also reads the DNA as ASCII itself, so that a
+// device sequence is packed in registers instead of by a pass of its own.
 template <int K, int M, int S, int H>
 KernelSet spec_set()
 {
     using C = Cfg<K, M, S, H>;
-    using CQ = Cfg<K, M, S, H, (K - S + 1 <= 8 && K - M + 1 >= 12 ? 32 : 0)>;
+    constexpr bool kQ32 = K - S + 1 <= 8 && K - M + 1 >= 12;
+    using CQ = Cfg<K, M, S, H, (kQ32 ? 32 : 0)>;
     KernelSet ks;
     ks.insert = &launch_insert<C>;
     ks.query = &launch_query<CQ>;
+    if constexpr (kQ32)
+        ks.query_text = &launch_query<Cfg<K, M, S, H, 32, kDnaText>>;
     ks.probe = &launch_probe<C>;
     ks.specialized = 1;
     return ks;

@@ -325,6 +325,47 @@ def test_query_waves_at_record_limits(m):
     assert g.specialized
 
 
+@pytest.mark.parametrize("params", [MAIN, (31, 21, 28, 4)])
+def test_query_inputs_agree(params):
+    """A DNA query reads its input three ways: the query kernel decoding the
+    ASCII itself (a 16-byte-aligned device sequence, 32 k-mers per lane),
+    the packing pass and then the packed kernel (an unaligned device
+    sequence, or parameters with 16 k-mers per lane), and sbf_query_packed
+    on codes from sbf_pack.  Every way gives the oracle's bits, on text with
+    lower case, 'N' runs, other letters and bytes with bit 7 set, at lengths
+    around a lane (32 bases) and a wave (2016 k-mers, 2048 bytes read)."""
+    import minimizer_sharded_bloom_amd as M
+    torch = G.torch_cuda()
+    rng = np.random.default_rng(77 + params[1])
+    genome = T.random_dna(rng, 60_000)
+    g = G.gpu_filter(params, 2**18)
+    o = G.oracle_filter(params, 2**18)
+    g.insert_seq(G.to_dev(genome))
+    o.insert_seq(genome)
+    noise = np.frombuffer(b"acgtNNRYn\x00\xc1\xe1@*", dtype=np.uint8)
+    for n in [31, 32, 33, 62, 63, 64, 2015, 2016, 2046, 2047, 2048, 2049, 4095, 4096 + 45, 40_000 + 3]:
+        src = bytearray(genome[rng.integers(0, len(genome) - n):][:n])
+        for p in rng.integers(0, n, max(1, n // 40)):
+            src[p] = int(noise[rng.integers(0, noise.size)])
+        if n > 100:
+            p = int(rng.integers(0, n - 40))
+            src[p:p + 33] = b"N" * 33
+        seq = bytes(src)
+        want = o.query_seq(seq)
+        got = G.dev_bits_to_np(g.query_seq(G.to_dev(seq)))
+        G.assert_words_equal(got, want, "aligned n=%d %s" % (n, params))
+        for off in (1, 5, 15):
+            buf = torch.zeros(n + 16, dtype=torch.uint8, device="cuda")
+            buf[off:off + n] = torch.frombuffer(bytearray(seq), dtype=torch.uint8).cuda()
+            view = buf[off:off + n]
+            assert view.data_ptr() % 16 == off
+            got = G.dev_bits_to_np(g.query_seq(view))
+            G.assert_words_equal(got, want, "offset %d n=%d %s" % (off, n, params))
+        codes, valid = M.pack(G.to_dev(seq))
+        got = G.dev_bits_to_np(g.query_packed(codes, valid, n))
+        G.assert_words_equal(got, want, "packed n=%d %s" % (n, params))
+
+
 def test_query_gaps_at_lane_and_wave_boundaries():
     """'N' runs of 1, 2, 31 and 40 bases placed at and around lane (32 k-mer
     starts) and wave (2016) boundaries, so runs of invalid k-mers start, end
