@@ -214,7 +214,12 @@ int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void
 /*
  * Sequence-native query: one bit per k-mer start into out_bits
  * (ceil((len-k+1)/64) uint64_t words, fully overwritten), which lives where
- * `flags` says (SBF_HOST: synchronizes; SBF_DEVICE: asynchronous).
+ * `flags` says (SBF_HOST: synchronizes; SBF_DEVICE: asynchronous).  Input and
+ * staging as for sbf_insert_seq, except that a DNA filter whose query takes
+ * 32 k-mers per lane (k-s+1 <= 8 and k-m+1 >= 12) reads a 16-byte-aligned
+ * device sequence, and each host chunk, as ASCII in the query kernel itself:
+ * no packing pass and no staging buffer.  The answers are the same for any
+ * alignment.
  */
 int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits,
                   uint32_t flags, void* stream);
