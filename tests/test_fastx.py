@@ -109,6 +109,45 @@ def test_reader_matches_reference(tmp_path, kind, gz):
         assert nrec == len(recs)
 
 
+def test_reader_large_fasta(tmp_path):
+    """A 3 MB FASTA file with random line widths, CRLF and LF lines, comments,
+    blank lines, empty records, a '>' inside a sequence line and one 600 kB
+    record on a single line matches the reference for piece sizes and end
+    capacities that stop calls at every kind of place, and its gzip copy
+    reads the same."""
+    rng = np.random.default_rng(12)
+    parts = []
+    recs = random_records(rng, 2000, max_len=2500, alphabet=b"ACGTacgtNRY")
+    for i, s in enumerate(recs):
+        eol = b"\r\n" if rng.random() < 0.3 else b"\n"
+        parts.append(b">r%d desc >not a header" % i + eol)
+        if rng.random() < 0.1:
+            parts.append(b";comment" + eol)
+        if i == 700:
+            s = bytes(rng.choice(np.frombuffer(b"ACGT", dtype=np.uint8), 600_000))
+            recs[i] = s
+            parts.append(s + eol)
+            continue
+        w = int(rng.integers(1, 200))
+        for a in range(0, len(s), w):
+            parts.append(s[a:a + w] + eol)
+        if rng.random() < 0.1:
+            parts.append(eol * int(rng.integers(1, 4)))
+    parts.append(b"ACG>T\n")  # '>' inside a line is a base of the last record
+    recs[-1] = recs[-1] + b"ACG>T"
+    text = b"\n\n" + b"".join(parts)
+    path = write(tmp_path, "big.fa", text)
+    want, want_ends = R.normalize(text)
+    assert want == b"N".join(recs)
+    for piece, ecap in [(1 << 22, 1 << 16), (1 << 20, 5), (100_003, 1), (65_537, 64), (1 << 22, 1)]:
+        got, ends, nrec = read_all(path, piece, ecap)
+        assert got == want, (piece, ecap)
+        assert ends == want_ends, (piece, ecap)
+        assert nrec == len(recs)
+    gz, gz_ends, _ = read_all(write(tmp_path, "big.fa.gz", text, gz=True), 1 << 22)
+    assert gz == want and gz_ends == want_ends
+
+
 def test_reader_multimember_gzip(tmp_path):
     rng = np.random.default_rng(5)
     a = fasta_text(rng, random_records(rng, 50))
