@@ -340,15 +340,23 @@ __global__ __launch_bounds__(256) void alpha_probe_kernel(ProbeArgs a, Params P)
             const uint64_t hm = hash_min((x >> (B * (k - m - j))) & mmask);
             mn = hm < mn ? hm : mn;
         }
-        uint64_t mk[4] = {0, 0, 0, 0};
+        uint64_t w[4];
+        load_shard(a.filter, (uint32_t)mn & a.shard_mask, w);
+        if constexpr (C::kStatic) {
+            // compile-time H: test the k-mer's bits one by one (a shift each)
+            uint32_t hit = 1u;
 #pragma unroll
-        for (uint32_t j = 0; j + s <= k; ++j) {
-            const uint64_t h = hash_s((x >> (B * (k - s - j))) & smask);
-            if constexpr (C::kStatic) {
+            for (uint32_t j = 0; j + s <= k; ++j) {
+                const uint64_t h = hash_s((x >> (B * (k - s - j))) & smask);
 #pragma unroll
                 for (uint32_t t = 0; t < H; ++t)
-                    mk[t & 3u] |= 1ull << bit_addr_rt(h, t, H);
-            } else {
+                    hit &= (uint32_t)(w[t & 3u] >> bit_addr_rt(h, t, H));
+            }
+            cnt += hit & 1u;
+        } else {
+            uint64_t mk[4] = {0, 0, 0, 0};
+            for (uint32_t j = 0; j + s <= k; ++j) {
+                const uint64_t h = hash_s((x >> (B * (k - s - j))) & smask);
                 for (uint32_t t = 0; t < H; ++t) {
                     const uint64_t bit = 1ull << bit_addr_rt(h, t, H);
 #pragma unroll
@@ -356,10 +364,8 @@ __global__ __launch_bounds__(256) void alpha_probe_kernel(ProbeArgs a, Params P)
                         mk[q] |= (t & 3u) == q ? bit : 0ull;
                 }
             }
+            cnt += covers(w, mk) ? 1u : 0u;
         }
-        uint64_t w[4];
-        load_shard(a.filter, (uint32_t)mn & a.shard_mask, w);
-        cnt += covers(w, mk) ? 1u : 0u;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)

@@ -1031,20 +1031,17 @@ __global__ __launch_bounds__(256) void sbf_probe_kernel(ProbeArgs a)
         }
         uint64_t w[4];
         load_shard(a.filter, (uint32_t)mn & a.shard_mask, w);
-        uint64_t R[4] = {0, 0, 0, 0};
+        // one k-mer with its own shard: test its Z*H bits one by one (a
+        // shift each) rather than build and compare sector masks
+        uint32_t hit = 1u;
 #pragma unroll
         for (int j = 0; j < C::Z; ++j) {
-            uint64_t mk[4];
-            smer_masks<C>(hash_s(sub_bases<C::k, C::s>(x, j)), mk);
+            const uint64_t h = hash_s(sub_bases<C::k, C::s>(x, j));
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                R[q] |= mk[q];
+            for (int t = 0; t < C::H; ++t)
+                hit &= (uint32_t)(w[t & 3] >> bit_addr<C::H>(h, t));
         }
-        uint64_t miss = 0;
-#pragma unroll
-        for (int q = 0; q < C::NS; ++q)
-            miss |= R[q] & ~w[q];
-        cnt += miss == 0;
+        cnt += hit & 1u;
     }
     // wave reduction, one atomic per wave
 #pragma unroll
