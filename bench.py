@@ -40,13 +40,18 @@ if ROOT not in sys.path:
 K, M_, S_, H_ = 31, 16, 28, 4
 METRIC = "insert & query Gk-mers/s (k=31,m=16,s=28,H=4) + fraction of HBM/L2 roofline"
 
-# MI355X ALU peak from unit counts and clock: 256 CUs x 4 SIMDs x 16 lanes;
-# a wave64 VALU instruction occupies a SIMD for 4 clocks, so the chip retires
-# 256 * 64 lane-instructions per clock, 3.93e13 per second at 2.4 GHz -- the
-# fp64 FMA rate (78.6 TFLOP/s).  (A few 2-operand integer ops can issue
-# faster; the kernels' own SQ counters show them issue-bound at this rate.)
+# MI355X ALU peak from unit counts and clock: 256 CUs x 4 SIMDs.  A SIMD
+# issues a wave64 instruction of the two-operand 32-bit kind (logic, add,
+# shift on VGPRs, with at most a literal or inline constant; also bitop3 on
+# three VGPRs) every 2 clocks, 32 lanes per clock, so the chip retires
+# 256 * 4 * 32 lane-instructions per clock: 7.86e13 per second at 2.4 GHz,
+# the fp32 vector rate (157.3 TFLOP/s counting an FMA as two).  64-bit
+# shifts, compares and multiply-adds, 32-bit multiplies, three-input adds
+# and shifts, alignbit, perm, bcnt, DPP moves and any form that reads an
+# SGPR take 4 clocks: half that rate, the fp64 one.  matched_ceilings()
+# measures both rates on the box (sbf_membench_valu).
 CUS, CLOCK_HZ = 256, 2.4e9
-ALU_PEAK = CUS * 64 * CLOCK_HZ  # 3.93e13 lane-instructions/s
+ALU_PEAK = CUS * 4 * 32 * CLOCK_HZ  # 7.86e13 lane-instructions/s
 HBM_PEAK = 8.0e12               # bytes/s
 
 # Algorithmic integer work per k-mer start at (k,m,s,H) = (31,16,28,4), in
@@ -206,7 +211,9 @@ def matched_ceilings(lib, torch, filt, stream, n_ops: int = 1 << 25) -> dict:
     """Random 32-byte shard reads over the filter itself and random 32-byte
     shard OR-updates (four lanes, one 64-bit atomic each) over a scratch table
     of the same size, in G operations/s (median of 3 after one warm-up):
-    the memory ceilings the query / probe and the insert flush can reach."""
+    the memory ceilings the query / probe and the insert flush can reach.
+    Also the VALU issue rate of a 2-clock and a 4-clock instruction form on
+    this box, the two ceilings of the ALU roofline."""
     n_sh = filt.num_shards
     table = lib.sbf_filter_device_ptr(filt.handle)
     scratch = torch.zeros(4 * n_sh, dtype=torch.int64, device="cuda")
@@ -231,6 +238,24 @@ def matched_ceilings(lib, torch, filt, stream, n_ops: int = 1 << 25) -> dict:
         ts.sort()
         out[name] = round(n_ops / (ts[1] * 1e-3) / 1e9, 3)
     del scratch
+    # VALU issue rates of the 2-clock and 4-clock instruction forms, in
+    # T lane-instructions/s (8192 workgroups x 256 lanes x 8 x iters)
+    iters = 2048
+    lane_instr = 8192 * 256 * 8 * iters
+    for name, kind in (("valu_2clk_t_lane_instr_per_s", 0), ("valu_4clk_t_lane_instr_per_s", 1)):
+        ts = []
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = lib.sbf_membench_valu(kind, iters, sink.data_ptr(), sp)
+            e1.record(stream)
+            if rc != 0:
+                raise RuntimeError("%s failed (%d)" % (name, rc))
+            torch.cuda.synchronize()
+            if rep:
+                ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        out[name] = round(lane_instr / (ts[1] * 1e-3) / 1e12, 2)
     return out
 
 

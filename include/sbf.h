@@ -325,6 +325,15 @@ int sbf_membench_shard_reads(const uint64_t* d_table, uint64_t nshard, uint64_t 
  * record.  Modifies the table. */
 int sbf_membench_shard_ors(uint64_t* d_table, uint64_t nshard, uint64_t n, uint64_t seed, void* stream);
 
+/* VALU issue rate: 8192 workgroups of 256 lanes, each lane running `iters`
+ * rounds of eight independent instructions of one form (kind 0: v_xor_b32 on
+ * VGPRs, the two-operand 32-bit logic/add/shift forms; kind 1:
+ * v_mad_u64_u32, a 64-bit form), i.e. 8192 * 256 * 8 * iters lane-
+ * instructions.  Registers only; d_sink (one device word) is written only if
+ * the results hit a fixed value.  Asynchronous on `stream`; the caller times
+ * it.  SBF_EINVAL for a NULL d_sink, kind > 1 or iters outside 1 .. 2^32. */
+int sbf_membench_valu(uint32_t kind, uint64_t iters, uint64_t* d_sink, void* stream);
+
 /* Static text for a return code. */
 const char* sbf_strerror(int code);
 

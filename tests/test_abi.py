@@ -110,3 +110,7 @@ def test_membench_rejects_bad_sizes(lib):
     assert lib.sbf_membench_shard_ors(8, 1000, 10, 1, None) == _lib.SBF_EINVAL
     assert lib.sbf_membench_shard_reads(8, 0, 10, 1, 8, None) == _lib.SBF_EINVAL
     assert lib.sbf_membench_shard_reads(8, 1024, 10, 1, None, None) == _lib.SBF_EINVAL
+    assert lib.sbf_membench_valu(0, 10, None, None) == _lib.SBF_EINVAL
+    assert lib.sbf_membench_valu(2, 10, 8, None) == _lib.SBF_EINVAL
+    assert lib.sbf_membench_valu(1, 0, 8, None) == _lib.SBF_EINVAL
+    assert lib.sbf_membench_valu(1, (1 << 32) + 1, 8, None) == _lib.SBF_EINVAL

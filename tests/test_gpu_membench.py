@@ -1,7 +1,8 @@
 """The matched-ceiling microbenchmarks stay inside the table they are given
 and do what they say: every OR lands in the table (guard words around it stay
 zero), the four words of an updated shard change together, and bad sizes are
-refused before any launch."""
+refused before any launch.  The VALU issue-rate kernels run and leave their
+sink word alone."""
 import numpy as np
 import pytest
 
@@ -31,3 +32,13 @@ def test_membench_stays_in_bounds():
     assert L.sbf_membench_shard_ors(table, 1000, 10, 7, None) == _lib.SBF_EINVAL
     assert L.sbf_membench_shard_reads(table, 0, 10, 7, sink.data_ptr(), None) == _lib.SBF_EINVAL
     assert L.sbf_membench_shard_reads(table, nsh, 10, 7, None, None) == _lib.SBF_EINVAL
+
+
+def test_valu_rate_kernels_run():
+    torch = G.torch_cuda()
+    L = M.lib()
+    sink = torch.zeros(1, dtype=torch.int64, device="cuda")
+    for kind in (0, 1):
+        assert L.sbf_membench_valu(kind, 16, sink.data_ptr(), None) == _lib.SBF_OK
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
