@@ -13,7 +13,9 @@ Genomic Sequence Data on Modern GPUs"):
 at k=31, m=16, s=28, H=4.  (`--query-input packed` packs the reads in a pass
 of their own and queries the packed codes instead.)  Every launch goes to
 torch's current stream, so the torch events recorded between launches time
-each kernel on the stream it runs on.
+each kernel on the stream it runs on.  The defaults (300 warm-up steps, 200
+timed) let the engine clock settle: with 3 warm-up steps and 20 timed ones
+the step measured about 8 % slower on the same box.
 
 Prints one JSON line.  `value` = k-mers processed per second over the step
 (genome k-mer starts + read k-mer starts + probe k-mers) / step time.
@@ -259,11 +261,35 @@ def matched_ceilings(lib, torch, filt, stream, n_ops: int = 1 << 25) -> dict:
     return out
 
 
+def timed_steps(torch, step, n_phases: int, a):
+    """a.warmup untimed steps, then exactly a.steps timed steps between two
+    events on the current stream, bracketed by device synchronizations, with
+    events recorded between the launches of every timed step on the stream
+    the kernels run on.  Returns (ms per step, wall seconds of the timed
+    region, per-step event lists)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(a.warmup):
+        step(None, stream)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_phases + 1)] for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(a.steps):
+        step(evs[i], stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return t_start.elapsed_time(t_end) / a.steps, wall, evs
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="synthetic configuration (default 2: 8 MiB filter, 5 Mbp genome, 2 M reads; "
                          "5: 4 GiB filter, 3 Gbp genome, 1 M long reads)")
@@ -412,7 +438,6 @@ def main():
     out = torch.empty(f.num_answer_words(LR), dtype=torch.int64, device=dev)
     hits = torch.zeros(1, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
     text_query = a.query_input == "text"
     assert not text_query or reads.data_ptr() % 16 == 0, "the ASCII query path needs 16-byte-aligned reads"
     if text_query:
@@ -420,13 +445,14 @@ def main():
     else:
         names = ["clear", "pack_genome", "insert", "pack_reads", "query", "probe"]
 
-    def step(events=None):
+    def step(events, st):
+        sp = st.cuda_stream
         marks = iter(range(len(names) + 1))
 
         def mark():
             i = next(marks)
             if events is not None:
-                events[i].record(stream)
+                events[i].record(st)
         mark()
         M.check(lib.sbf_clear(f.handle, sp), "clear")
         mark()
@@ -445,21 +471,7 @@ def main():
         M.check(lib.sbf_fpr_probe_device(f.handle, a.probe_n, 0x5EED, hits.data_ptr(), sp), "probe")
         mark()
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(a.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(a.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / a.steps
+    ms_step, wall, evs = timed_steps(torch, step, len(names), a)
     phase = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / a.steps for i, n in enumerate(names)}
     phase_med = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
     progress("timed steps done")
@@ -558,13 +570,14 @@ def main_alpha(a, torch, M, S, lib):
     out = torch.empty(f.num_answer_words(LR), dtype=torch.int64, device=dev)
     hits = torch.zeros(1, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
     names = ["clear", "insert", "query", "probe"]
 
-    def step(events=None):
+    def step(events, st):
+        sp = st.cuda_stream
+
         def mark(i):
             if events is not None:
-                events[i].record(stream)
+                events[i].record(st)
         mark(0)
         M.check(lib.sbf_clear(f.handle, sp), "clear")
         mark(1)
@@ -575,21 +588,7 @@ def main_alpha(a, torch, M, S, lib):
         M.check(lib.sbf_fpr_probe_device(f.handle, a.probe_n, 0x5EED, hits.data_ptr(), sp), "probe")
         mark(4)
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(a.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / a.steps
+    ms_step, wall, evs = timed_steps(torch, step, len(names), a)
     phase = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / a.steps for i, n in enumerate(names)}
     import numpy as np
     phase_med = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
