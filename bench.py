@@ -15,7 +15,7 @@ of their own and queries the packed codes instead.)  Every launch goes to
 torch's current stream, so the torch events recorded between launches time
 each kernel on the stream it runs on.  The defaults (300 warm-up steps, 200
 timed) let the engine clock settle: with 3 warm-up steps and 20 timed ones
-the step measured about 8 % slower on the same box.
+the step measured about 8 % slower on the same machine.
 
 Prints one JSON line.  `value` = k-mers processed per second over the step
 (genome k-mer starts + read k-mer starts + probe k-mers) / step time.
@@ -51,7 +51,7 @@ METRIC = "insert & query Gk-mers/s (k=31,m=16,s=28,H=4) + fraction of HBM/L2 roo
 # shifts, compares and multiply-adds, 32-bit multiplies, three-input adds
 # and shifts, alignbit, perm, bcnt, DPP moves and any form that reads an
 # SGPR take 4 clocks: half that rate, the fp64 one.  matched_ceilings()
-# measures both rates on the box (sbf_membench_valu).
+# measures both rates on the machine it runs on (sbf_membench_valu).
 CUS, CLOCK_HZ = 256, 2.4e9
 ALU_PEAK = CUS * 4 * 32 * CLOCK_HZ  # 7.86e13 lane-instructions/s
 HBM_PEAK = 8.0e12               # bytes/s
@@ -59,7 +59,7 @@ HBM_PEAK = 8.0e12               # bytes/s
 # Algorithmic integer work per k-mer start at (k,m,s,H) = (31,16,28,4), in
 # 32-bit VALU instructions, for the sliding formulation (each position hashes
 # one m-mer and one s-mer; the minimizer is a sliding minimum; the Findere
-# mask of a k-mer is one new doubling level per s-mer).  Itemised in the design doc.
+# mask of a k-mer is one new doubling level per s-mer).
 FRONT = {
     "m-mer window (funnel shift)": 1,
     "h_min: 32x64 multiply with folded offset (2 mad_u64), carry move, fold": 4,
@@ -87,7 +87,7 @@ def alu_ops_per_kmer(kind: str) -> float:
 
 # Other alphabets: the DNA kernels' work per k-mer start (windows cut from a
 # packed stream, here 5- or 6-bit symbols packed in registers) plus decoding
-# the symbol from ASCII in the kernel's text front end.  Itemised in the design doc.
+# the symbol from ASCII in the kernel's text front end.
 ALPHAS = {
     "protein": {"params": (12, 6, 10, 4), "bytes_per_symbol": 1,
                 "decode": {"letter: SWAR codes, letter test and flag bits over 4 bytes (1/4 each), "
@@ -215,7 +215,7 @@ def matched_ceilings(lib, torch, filt, stream, n_ops: int = 1 << 25) -> dict:
     of the same size, in G operations/s (median of 3 after one warm-up):
     the memory ceilings the query / probe and the insert flush can reach.
     Also the VALU issue rate of a 2-clock and a 4-clock instruction form on
-    this box, the two ceilings of the ALU roofline."""
+    this machine, the two ceilings of the ALU roofline."""
     n_sh = filt.num_shards
     table = lib.sbf_filter_device_ptr(filt.handle)
     scratch = torch.zeros(4 * n_sh, dtype=torch.int64, device="cuda")
@@ -400,7 +400,7 @@ def cached_workload(S, cfg: int, cache: str) -> dict:
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % a.gpus,
+        print("bench.py measures one GPU only: this library has no multi-GPU path (got --gpus %d)" % a.gpus,
               file=sys.stderr)
         sys.exit(2)
     import numpy as np

@@ -26,9 +26,12 @@ K = 31
 
 
 def progress(msg: str):
-    """Progress line for long tests (stdout is captured by pytest)."""
-    if os.path.isdir("gpurun_out"):
-        with open(os.path.join("gpurun_out", "test_progress.log"), "a") as f:
+    """Progress line for long tests, appended to the file that the
+    SBF_TEST_PROGRESS environment variable names (stdout is captured by
+    pytest)."""
+    path = os.environ.get("SBF_TEST_PROGRESS")
+    if path:
+        with open(path, "a") as f:
             f.write("%.1f %s\n" % (time.time(), msg))
 
 
