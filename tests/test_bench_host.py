@@ -24,3 +24,31 @@ def test_valid_kmer_count():
             for n in (0, 3, 50, 997):
                 t = np.frombuffer(alphabet, dtype=np.uint8)[rng.integers(0, len(alphabet), n)]
                 assert bench.valid_kmer_count(t, k, alpha) == brute(t.tobytes(), k, alpha), (alpha, k, n)
+
+
+def test_roofline_models():
+    """The ALU and byte models of the roofline: 52 front-end instructions per
+    k-mer start, +13 for the query test, +2.66 for decoding ASCII, +17.5 for
+    the insert; 0.375 B of packed input (1 B of ASCII) plus a 32-byte shard
+    per run at 2/(w+1) runs per k-mer; the peak of 256 CUs x 4 SIMDs x 32
+    lanes per clock at 2.4 GHz."""
+    import pytest
+    assert bench.alu_ops_per_kmer("query") == pytest.approx(65.0)
+    assert bench.alu_ops_per_kmer("query_text") == pytest.approx(67.66)
+    assert bench.alu_ops_per_kmer("insert") == pytest.approx(69.5)
+    runs = 2.0 / 17
+    assert bench._bytes_per_kmer("query") == pytest.approx(0.375 + 0.125 + 32 * runs)
+    assert bench._bytes_per_kmer("query_text") == pytest.approx(1.0 + 0.125 + 32 * runs)
+    assert bench._bytes_per_kmer("insert") == pytest.approx(0.375 + 64 * runs)
+    assert bench.ALU_PEAK == pytest.approx(256 * 4 * 32 * 2.4e9)
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says why."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert p.returncode == 2 and "one GPU" in p.stderr, (p.returncode, p.stderr[-500:])
