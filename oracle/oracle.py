@@ -55,6 +55,8 @@ def lib():
         L.osbf_bitaddr.restype = u32
         L.osbf_bitaddr_wide.argtypes = [u64, u32, u32]
         L.osbf_bitaddr_wide.restype = u32
+        L.osbf_minimizer_hashes.argtypes = [p, u64, u32, u32, p]
+        L.osbf_minimizer_hashes.restype = u64
         L.osbf_words_per_shard.argtypes = [p]
         L.osbf_words_per_shard.restype = u32
         L.osbf_probe_kmer.argtypes = [u64, u64, u32]
@@ -201,6 +203,17 @@ def subwindow(x: int, k: int, i: int, w: int) -> int:
 
 def minimizer_hash(x: int, k: int, m: int) -> int:
     return lib().osbf_minimizer_hash(x, k, m)
+
+
+def minimizer_hashes(seq, k: int, m: int) -> np.ndarray:
+    """Minimizer hash of every k-mer start of a DNA text (oracle, one k-mer at
+    a time); 2^64 - 1 where the k-mer is invalid."""
+    arr, ptr = _buf(seq)
+    n = max(0, arr.size - k + 1)
+    out = np.empty(n, dtype=np.uint64)
+    if n:
+        lib().osbf_minimizer_hashes(ptr, arr.size, k, m, out.ctypes.data)
+    return out
 
 
 # ---- filter ----------------------------------------------------------------

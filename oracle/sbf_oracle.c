@@ -242,6 +242,27 @@ uint64_t osbf_minimizer_hash(uint64_t x, unsigned k, unsigned m)
     return best;
 }
 
+/* Minimizer hash of every k-mer start of an ASCII DNA sequence, each from
+ * its own packed k-mer (no sliding): out[p] for p in [0, len-k+1), ~0 for an
+ * invalid k-mer.  Returns the number of valid k-mers.  For density checks of
+ * the minimizer scheme ([cuSBF] §II-B-1) on long random text. */
+uint64_t osbf_minimizer_hashes(const char* seq, uint64_t len, unsigned k, unsigned m, uint64_t* out)
+{
+    uint64_t valid = 0;
+    if (len < k)
+        return 0;
+    for (uint64_t p = 0; p + k <= len; ++p) {
+        uint64_t x;
+        if (osbf_pack_kmer(seq + p, k, &x) == 0) {
+            out[p] = osbf_minimizer_hash(x, k, m);
+            ++valid;
+        } else {
+            out[p] = ~0ull;
+        }
+    }
+    return valid;
+}
+
 osbf* osbf_create(int kind, unsigned k, unsigned m, unsigned s, unsigned H, uint64_t bits)
 {
     return osbf_create_alpha(kind, OSBF_ALPHA_DNA, k, m, s, H, bits);

@@ -75,6 +75,10 @@ uint64_t osbf_subwindow(uint64_t x, unsigned k, unsigned i, unsigned w);
 /* minimizer hash of a packed k-mer: min over its k-m+1 m-mers of h_min */
 uint64_t osbf_minimizer_hash(uint64_t x, unsigned k, unsigned m);
 
+/* minimizer hash of every k-mer start of an ASCII DNA sequence (out[p] for
+ * p < len-k+1, ~0 where the k-mer is invalid); returns the valid count */
+uint64_t osbf_minimizer_hashes(const char* seq, uint64_t len, unsigned k, unsigned m, uint64_t* out);
+
 /* ---- filter ------------------------------------------------------------- */
 
 /* Returns NULL on invalid parameters or allocation failure. */

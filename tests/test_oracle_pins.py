@@ -146,17 +146,28 @@ def test_minimizer_brute_force():
 
 def test_minimizer_density():
     """§II-B-1: random minimizers on random text have density about 2/(w+1);
-    for k = 31, m = 16 the mean super-k-mer is (w+1)/2 = 8.5 k-mers."""
+    for k = 31, m = 16 the mean super-k-mer is (w+1)/2 = 8.5 k-mers.  Over
+    10^7 uniform bases the oracle's density must lie within 2 % of 2/(w+1)
+    (its standard error there is about 0.1 %, so a hash whose minimizers are
+    biased by a few percent fails); a brute-force recount on the first 2000
+    k-mers checks that the batch call is the per-k-mer minimizer."""
     rng = np.random.default_rng(15)
     k, m = 31, 16
     w = k - m + 1
-    seq = T.random_dna(rng, 60000)
-    xs = [O.pack_kmer(seq[p:p + k]) for p in range(len(seq) - k + 1)]
-    mh = np.array([O.minimizer_hash(x, k, m) for x in xs], dtype=np.uint64)
+    seq = T.random_dna(rng, 10_000_000)
+    mh = O.minimizer_hashes(seq, k, m)
+    assert mh.size == len(seq) - k + 1
+    for p in range(0, 2000):
+        assert int(mh[p]) == T.minimizer_hash_str(seq[p:p + k].decode(), m)
     changes = int((mh[1:] != mh[:-1]).sum())
-    density = changes / (len(mh) - 1)
-    assert abs(density - 2 / (w + 1)) < 0.06 * 2 / (w + 1)
-    assert abs(1 / density - (w + 1) / 2) < 0.6
+    density = changes / (mh.size - 1)
+    assert abs(density - 2 / (w + 1)) < 0.02 * 2 / (w + 1)
+    assert abs(1 / density - (w + 1) / 2) < 0.02 * (w + 1) / 2
+    # other window lengths on a shorter piece (2 * 10^6 bases, +-2 %)
+    for kk, mm in ((31, 12), (31, 20), (21, 11)):
+        ww = kk - mm + 1
+        d = float((np.diff(O.minimizer_hashes(seq[:2_000_000], kk, mm)) != 0).mean())
+        assert abs(d - 2 / (ww + 1)) < 0.02 * 2 / (ww + 1), (kk, mm, d)
 
 
 def test_shard_uniformity():
@@ -505,6 +516,36 @@ def test_wide_classic_bloom_eq1():
     assert abs(np.mean(fills) - mean_fill) < 4.5 * np.std(fills) / math.sqrt(trials) + 1e-3
     eq1 = (1 - math.exp(-H * n / 512)) ** H
     assert abs(mean_fill ** H - eq1) / eq1 < 0.05
+
+
+@pytest.mark.parametrize("H,n_keys", [(8, 60), (12, 45)])
+def test_wide_salted_addresses_independent(H, n_keys):
+    """Salted addresses of the wide layout (H > 7: the top 9 bits of
+    h_s * mix((t+1) G), the golden-ratio-derived salt of §IV-G over a 512-bit
+    block).  With one block and s = m = k the filter is a classic 512-bit Bloom
+    filter with H hash functions; if the H addresses of a key are independent
+    and uniform over the block, a random key hits with probability fill^H,
+    fill measured on the block itself.  Correlated salts (an arithmetic
+    progression of addresses), a wrong shift (addresses confined to a few
+    words) or a wrong word index fail this."""
+    rng = np.random.default_rng(36 + H)
+    k, trials, probes = 31, 40, 4000
+    hits, expect = 0, 0.0
+    for tr in range(trials):
+        f = O.OracleFilter(k, k, k, H, 512, kind=O.KIND_WIDE)
+        assert f.num_shards == 1 and f.words_per_shard == 8
+        for x in rng.choice(2**62, n_keys, replace=False):
+            f.insert_kmer(int(x))
+        fill = sum(bin(int(v)).count("1") for v in f.words()) / 512
+        hits += f.fpr_probe(probes, 11000 + 100 * H + tr)
+        expect += probes * fill ** H
+    assert expect > 500
+    assert abs(hits - expect) <= 4.5 * math.sqrt(expect) + 2
+    # every word of the block receives addresses (the 9-bit range is used)
+    f = O.OracleFilter(k, k, k, H, 512, kind=O.KIND_WIDE)
+    for x in rng.choice(2**62, 40, replace=False):
+        f.insert_kmer(int(x))
+    assert all(int(v) != 0 for v in f.words())
 
 
 @pytest.mark.parametrize("k,m,s,H", [(31, 16, 28, 4), (31, 16, 24, 2)])
