@@ -13,12 +13,20 @@ Genomic Sequence Data on Modern GPUs"):
 at k=31, m=16, s=28, H=4.  (`--query-input packed` packs the reads in a pass
 of their own and queries the packed codes instead.)  Every launch goes to
 torch's current stream, so the torch events recorded between launches time
-each kernel on the stream it runs on.  The defaults (300 warm-up steps, 200
-timed) let the engine clock settle: with 3 warm-up steps and 20 timed ones
-the step measured about 8 % slower on the same machine.
+each kernel on the stream it runs on.
 
-Prints one JSON line.  `value` = k-mers processed per second over the step
-(genome k-mer starts + read k-mer starts + probe k-mers) / step time.
+The default workload is configuration 3: a 2^32-bit (512 MiB) filter, out of
+every on-chip cache, a 200 Mbp genome inserted and 20 M reads of 150 bp
+queried.  Before the warm-up steps the step is repeated, untimed, for
+--prewarm-s seconds (default 1.5 s): the engine clock takes a fraction of a
+second of load to settle, and a short run would otherwise time part of that
+ramp.
+
+Prints one JSON line.  `value` = valid k-mers processed per second over the
+step: (valid genome k-mers + valid read k-mers + probe k-mers) / step time,
+where a k-mer is valid when all of its bases are A, C, G or T; positions
+whose k-mer spans a record separator are not counted ("kmer_starts" and the
+*_starts_gkmers_s fields give the rates over all positions).
 
 `--alphabet protein|triplet` times the same step over the protein (k=12,
 m=6, s=10, H=4) or DNA-triplet (k=10, m=5, s=8, H=4) filter on its synthetic
@@ -268,6 +276,13 @@ def timed_steps(torch, step, n_phases: int, a):
     the kernels run on.  Returns (ms per step, wall seconds of the timed
     region, per-step event lists)."""
     stream = torch.cuda.current_stream()
+    t_pre = time.perf_counter()
+    a.prewarm_steps = 0
+    while time.perf_counter() - t_pre < a.prewarm_s:
+        for _ in range(5):
+            step(None, stream)
+        a.prewarm_steps += 5
+        torch.cuda.synchronize()
     for _ in range(a.warmup):
         step(None, stream)
     torch.cuda.synchronize()
@@ -288,11 +303,14 @@ def timed_steps(torch, step, n_phases: int, a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="synthetic configuration (default 2: 8 MiB filter, 5 Mbp genome, 2 M reads; "
-                         "5: 4 GiB filter, 3 Gbp genome, 1 M long reads)")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prewarm-s", type=float, default=1.5,
+                    help="seconds of untimed steps before the warm-up steps, so the engine clock settles")
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                    help="synthetic configuration (default 3: 512 MiB filter, 200 Mbp genome, 20 M reads; "
+                         "2: 8 MiB filter, 5 Mbp genome, 2 M reads; 5: 4 GiB filter, 3 Gbp genome, "
+                         "1 M long reads)")
     ap.add_argument("--alphabet", default="dna", choices=["dna", "protein", "triplet"],
                     help="dna (default, --workload applies) or the protein / DNA-triplet workload")
     ap.add_argument("--probe-n", type=int, default=10_000_000)
@@ -487,11 +505,12 @@ def main():
         del src, dst
 
     nk_g, nk_r = LG - K + 1, LR - K + 1
-    total = nk_g + nk_r + a.probe_n
-    value = total / (ms_step * 1e-3) / 1e9
     vk_g, vk_r = valid_kmer_count(genome_h, K), valid_kmer_count(reads_h, K)
-    ins_rate = nk_g / (phase["insert"] * 1e-3)
-    q_rate = nk_r / (phase["query"] * 1e-3)
+    total = vk_g + vk_r + a.probe_n
+    value = total / (ms_step * 1e-3) / 1e9
+    # rates over valid k-mers (the roofline's numerator counts only these)
+    ins_rate = vk_g / (phase["insert"] * 1e-3)
+    q_rate = vk_r / (phase["query"] * 1e-3)
 
     sha = kernel_sources_sha256()
     wl = "cfg%d" % a.workload
@@ -504,17 +523,25 @@ def main():
         traffic = None if tr is None else tr["bytes"]
         extra = {} if tr is None else {"traffic_fetch": tr["fetch"], "traffic_write": tr["write"],
                                        "traffic_source": tr["source"],
-                                       "traffic_per_kmer": tr["bytes"] / (nk_r if kind == "query" else nk_g)}
+                                       "traffic_per_valid_kmer": tr["bytes"] / (vk_r if kind == "query" else vk_g)}
         return (dict({"bound": "alu", "achieved": alu / 1e12, "peak": ALU_PEAK / 1e12,
                       "unit": "T lane-instr/s", "frac": alu / ALU_PEAK, "traffic": traffic,
-                      "kernel": kind, "per_kmer_ops": alu_ops_per_kmer(model)}, **extra),
+                      "kernel": kind, "per_valid_kmer_ops": alu_ops_per_kmer(model),
+                      "ms_per_launch": phase[kind]}, **extra),
                 dict({"bound": "hbm", "achieved": mem / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                       "frac": mem / HBM_PEAK, "traffic": traffic, "kernel": kind,
-                      "per_kmer_bytes": _bytes_per_kmer(model)}, **extra))
+                      "per_valid_kmer_bytes": _bytes_per_kmer(model), "ms_per_launch": phase[kind]}, **extra))
+
+    def binding(kind, rate):
+        """The two ceilings of one kernel, the binding one (higher fraction)
+        first."""
+        alu, mem = roof(kind, rate)
+        return (alu, mem) if alu["frac"] >= mem["frac"] else (mem, alu)
 
     dom = "query" if phase["query"] >= phase["insert"] else "insert"
-    alu, mem = roof(dom, q_rate if dom == "query" else ins_rate)
-    primary, secondary = (alu, mem) if alu["frac"] >= mem["frac"] else (mem, alu)
+    primary, secondary = binding(dom, q_rate if dom == "query" else ins_rate)
+    other = "insert" if dom == "query" else "query"
+    other_primary, _ = binding(other, ins_rate if other == "insert" else q_rate)
 
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "Gk-mers/s", "n_gpus": 1, "steps": a.steps,
@@ -522,9 +549,13 @@ def main():
         "vs_baseline": None, "dtype": "u64", "data": "synthetic",
         "config": {"workload": wl, "k": K, "m": M_, "s": S_, "H": H_, "filter_bits": w["bits"],
                    "genome_bases": LG, "read_bases": LR, "probe_kmers": a.probe_n,
-                   "kmers_per_step": total},
-        "roofline": primary, "roofline_other": secondary,
+                   "valid_kmers_per_step": total},
+        "roofline": primary, "roofline_other": secondary, "roofline_" + other: other_primary,
         "insert_gkmers_s": round(ins_rate / 1e9, 3), "query_gkmers_s": round(q_rate / 1e9, 3),
+        "insert_starts_gkmers_s": round(nk_g / (phase["insert"] * 1e-3) / 1e9, 3),
+        "query_starts_gkmers_s": round(nk_r / (phase["query"] * 1e-3) / 1e9, 3),
+        "value_starts_gkmers_s": round((nk_g + nk_r + a.probe_n) / (ms_step * 1e-3) / 1e9, 3),
+        "prewarm": {"seconds": a.prewarm_s, "steps": a.prewarm_steps},
         "pack_gbases_s": round((LG + (0 if text_query else LR))
                                / ((phase["pack_genome"] + phase.get("pack_reads", 0.0)) * 1e-3) / 1e9, 3),
         "query_input": a.query_input,
@@ -533,9 +564,6 @@ def main():
         "phase_ms_median": {k2: round(v, 4) for k2, v in phase_med.items()},
         "kmer_starts": {"insert": nk_g, "query": nk_r, "probe": a.probe_n},
         "valid_kmers": {"insert": vk_g, "query": vk_r},
-        "value_valid_gkmers_s": round((vk_g + vk_r + a.probe_n) / (ms_step * 1e-3) / 1e9, 3),
-        "insert_valid_gkmers_s": round(vk_g / (phase["insert"] * 1e-3) / 1e9, 3),
-        "query_valid_gkmers_s": round(vk_r / (phase["query"] * 1e-3) / 1e9, 3),
         "wall_s_timed": round(wall, 3), "gen_s": round(gen_s, 2),
         "kernel_sources_sha256": sha,
     }
@@ -543,8 +571,9 @@ def main():
         # runs per k-mer for random minimizers, 2/(w+1): the insert's record
         # flushes and the query's shard reads, set against the matched ceilings
         runs = 2.0 / (K - M_ + 2)
-        ceilings["insert_records_est_g_per_s"] = round(ins_rate * runs / 1e9, 3)
-        ceilings["insert_frac_of_or_ceiling"] = round(ins_rate * runs / 1e9 / ceilings["shard_ors_g_per_s"], 3)
+        ceilings["insert_records_est_g_per_s"] = round(nk_g / (phase["insert"] * 1e-3) * runs / 1e9, 3)
+        ceilings["insert_frac_of_or_ceiling"] = round(ceilings["insert_records_est_g_per_s"]
+                                                      / ceilings["shard_ors_g_per_s"], 3)
         res["matched_ceilings"] = ceilings
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
@@ -605,10 +634,10 @@ def main_alpha(a, torch, M, S, lib):
 
     nk_g, nk_r = f.num_symbols(LG) - k + 1, f.num_symbols(LR) - k + 1
     vk_g, vk_r = valid_kmer_count(w["insert"], k, alpha), valid_kmer_count(w["queries"][0], k, alpha)
-    total = nk_g + nk_r + a.probe_n
+    total = vk_g + vk_r + a.probe_n
     value = total / (ms_step * 1e-3) / 1e9
-    ins_rate = nk_g / (phase["insert"] * 1e-3)
-    q_rate = nk_r / (phase["query"] * 1e-3)
+    ins_rate = vk_g / (phase["insert"] * 1e-3)
+    q_rate = vk_r / (phase["query"] * 1e-3)
     sha = kernel_sources_sha256("alpha")
 
     def roof(kind, rate):
@@ -618,12 +647,14 @@ def main_alpha(a, torch, M, S, lib):
         traffic = None if tr is None else tr["bytes"]
         extra = {} if tr is None else {"traffic_fetch": tr["fetch"], "traffic_write": tr["write"],
                                        "traffic_source": tr["source"],
-                                       "traffic_per_kmer": tr["bytes"] / (nk_r if kind == "query" else nk_g)}
+                                       "traffic_per_valid_kmer": tr["bytes"] / (vk_r if kind == "query" else vk_g)}
         return (dict({"bound": "alu", "achieved": alu / 1e12, "peak": ALU_PEAK / 1e12, "unit": "T lane-instr/s",
-                      "frac": alu / ALU_PEAK, "traffic": traffic, "kernel": kind, "per_kmer_ops": ops}, **extra),
+                      "frac": alu / ALU_PEAK, "traffic": traffic, "kernel": kind, "per_valid_kmer_ops": ops,
+                      "ms_per_launch": phase[kind]}, **extra),
                 dict({"bound": "hbm", "achieved": mem / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                       "frac": mem / HBM_PEAK, "traffic": traffic, "kernel": kind,
-                      "per_kmer_bytes": alpha_bytes_per_kmer(alpha, kind)}, **extra))
+                      "per_valid_kmer_bytes": alpha_bytes_per_kmer(alpha, kind), "ms_per_launch": phase[kind]},
+                     **extra))
 
     dom = "query" if phase["query"] >= phase["insert"] else "insert"
     alu, mem = roof(dom, q_rate if dom == "query" else ins_rate)
@@ -635,21 +666,25 @@ def main_alpha(a, torch, M, S, lib):
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u64", "data": "synthetic",
         "config": {"workload": alpha, "k": k, "m": m, "s": s, "H": H, "filter_bits": w["bits"],
-                   "insert_bytes": LG, "query_bytes": LR, "probe_kmers": a.probe_n, "kmers_per_step": total},
+                   "insert_bytes": LG, "query_bytes": LR, "probe_kmers": a.probe_n, "valid_kmers_per_step": total},
         "roofline": primary, "roofline_other": secondary,
         "insert_gkmers_s": round(ins_rate / 1e9, 3), "query_gkmers_s": round(q_rate / 1e9, 3),
+        "insert_starts_gkmers_s": round(nk_g / (phase["insert"] * 1e-3) / 1e9, 3),
+        "query_starts_gkmers_s": round(nk_r / (phase["query"] * 1e-3) / 1e9, 3),
+        "value_starts_gkmers_s": round((nk_g + nk_r + a.probe_n) / (ms_step * 1e-3) / 1e9, 3),
+        "prewarm": {"seconds": a.prewarm_s, "steps": a.prewarm_steps},
         "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
         "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},
         "phase_ms_median": {k2: round(v, 4) for k2, v in phase_med.items()},
         "kmer_starts": {"insert": nk_g, "query": nk_r, "probe": a.probe_n},
         "valid_kmers": {"insert": vk_g, "query": vk_r},
-        "value_valid_gkmers_s": round((vk_g + vk_r + a.probe_n) / (ms_step * 1e-3) / 1e9, 3),
         "wall_s_timed": round(wall, 3), "gen_s": round(gen_s, 2), "kernel_sources_sha256": sha,
     }
     if ceilings is not None:
         runs = 2.0 / (k - m + 2)
-        ceilings["insert_records_est_g_per_s"] = round(ins_rate * runs / 1e9, 3)
-        ceilings["insert_frac_of_or_ceiling"] = round(ins_rate * runs / 1e9 / ceilings["shard_ors_g_per_s"], 3)
+        ceilings["insert_records_est_g_per_s"] = round(nk_g / (phase["insert"] * 1e-3) * runs / 1e9, 3)
+        ceilings["insert_frac_of_or_ceiling"] = round(ceilings["insert_records_est_g_per_s"]
+                                                      / ceilings["shard_ors_g_per_s"], 3)
         res["matched_ceilings"] = ceilings
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, (k, m, s, H), alpha)

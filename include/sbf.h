@@ -144,30 +144,55 @@ int sbf_create_wide(sbf_t** out, uint32_t k, uint32_t m, uint32_t s, uint32_t H,
 int sbf_create_alphabet(sbf_t** out, uint32_t alphabet, uint32_t k, uint32_t m, uint32_t s, uint32_t H,
                         uint64_t bits);
 
-/* Free a filter and its buffers (synchronizes the device). NULL is a no-op. */
+/*
+ * Free a filter and its buffers (synchronizes the device).  NULL is a no-op.
+ * Not an operation of the method: [cuSBF] §IV-A describes the filter as a
+ * device object built from (k, m, s, H) and a size, and says nothing of its
+ * release; here the handle owns its device memory until this call.
+ * Errors: SBF_EDEVICE if the synchronization reports an earlier failure (the
+ * memory is freed all the same).
+ */
 int sbf_destroy(sbf_t* h);
 
-/* Zero the filter, asynchronously on `stream`. */
+/*
+ * Zero the filter, asynchronously on `stream`: the empty filter of [cuSBF]
+ * §IV-B (every bit of every shard 0), as sbf_create leaves it.  The page
+ * defines no clear; a filter is refilled by clearing and inserting again.
+ * Errors: SBF_EINVAL for a NULL handle, SBF_EDEVICE if the launch fails.
+ */
 int sbf_clear(sbf_t* h, void* stream);
 
-/* Parameters and sizes of a filter into a caller-owned struct. */
+/*
+ * Parameters and sizes of a filter into a caller-owned struct: (k, m, s, H)
+ * of [cuSBF] §IV-A and the shard count after the rounding to a power of two
+ * of §IV-B (the page fixes the sizes; it defines no call that reports them).
+ * Host only, no device work.  Errors: SBF_EINVAL for a NULL argument.
+ */
 int sbf_info(const sbf_t* h, sbf_info_t* out);
 
 /*
  * Copy the raw filter words (uint64_t[W*N], shard j = words Wj..Wj+W-1, W =
- * words_per_shard) to dst.  flags = SBF_HOST: dst is host memory,
- * synchronizes; SBF_DEVICE: device memory, asynchronous on `stream`.
- * SBF_EINVAL if bytes < 8 * W * N.
+ * words_per_shard) to dst: the bit array in the shard and sector layout of
+ * [cuSBF] §IV-B (word 4j+q is sector q of shard j; the page defines the
+ * layout, not a copy of it -- this exists for inspection and parity checks).
+ * flags = SBF_HOST: dst is host memory, synchronizes; SBF_DEVICE: device
+ * memory, asynchronous on `stream`.  The caller owns dst.  SBF_EINVAL for a
+ * NULL argument, other flags, or bytes < 8 * W * N; SBF_EDEVICE if the copy
+ * fails.
  */
 int sbf_copy_filter(const sbf_t* h, void* dst, uint64_t bytes, uint32_t flags, void* stream);
 
 /*
- * Device pointer to the filter words (owned by the handle, valid until
- * sbf_destroy), or NULL for a NULL handle.
+ * Device pointer to the filter words in the layout of sbf_copy_filter
+ * ([cuSBF] §IV-B; the page defines no such accessor).  Owned by the handle,
+ * valid until sbf_destroy; writing through it changes the filter.  NULL for a
+ * NULL handle; no device work, no error code.
  */
 const uint64_t* sbf_filter_device_ptr(const sbf_t* h);
 
-/* Number of uint32_t words of the packed codes and validity of len bases. */
+/* Number of uint32_t words of the packed codes and validity of len bases, in
+ * the packed layout above (2 bits per base, [cuSBF] §IV-A; the storage order
+ * is this library's).  Host only; NULL outputs are skipped. */
 void sbf_packed_words(uint64_t len, uint64_t* code_words, uint64_t* valid_words);
 
 /*
@@ -225,7 +250,8 @@ int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits,
                   uint32_t flags, void* stream);
 
 /*
- * Chunk size of the host pipeline, in k-mer starts (rounded up to a multiple
+ * Chunk size of the host pipeline ([cuSBF] §IV-G host staging; the page gives
+ * no chunk size), in k-mer starts (rounded up to a multiple
  * of 64; 64 <= chunk_bases <= 2^34; default 2^26).  Each of the three slots
  * holds chunk_bases + 64 bytes of pinned input, the same on the device, its
  * packed form and chunk_bases/64 + 1 answer words (pinned and device).
@@ -260,10 +286,12 @@ int sbf_fastx_open(sbf_fastx_t** out, const char* path);
 int sbf_fastx_read(sbf_fastx_t* r, char* buf, uint64_t cap, uint64_t* len,
                    uint64_t* ends, uint64_t ends_cap, uint64_t* n_ends);
 
-/* Records started so far (0 for NULL). */
+/* Records started so far (0 for NULL).  Reader bookkeeping, not defined by
+ * the page. */
 uint64_t sbf_fastx_records(const sbf_fastx_t* r);
 
-/* Close a reader; NULL is a no-op. */
+/* Close a reader and free its buffers; NULL is a no-op (not defined by the
+ * page). */
 int sbf_fastx_close(sbf_fastx_t* r);
 
 typedef struct sbf_fastx_stats {
@@ -334,10 +362,12 @@ int sbf_membench_shard_ors(uint64_t* d_table, uint64_t nshard, uint64_t n, uint6
  * it.  SBF_EINVAL for a NULL d_sink, kind > 1 or iters outside 1 .. 2^32. */
 int sbf_membench_valu(uint32_t kind, uint64_t iters, uint64_t* d_sink, void* stream);
 
-/* Static text for a return code. */
+/* Static text for a return code (error reporting is this library's; the page
+ * states none). */
 const char* sbf_strerror(int code);
 
-/* Text of the calling thread's last error ("" if none). */
+/* Text of the calling thread's last error ("" if none); valid until the
+ * thread's next call into the library. */
 const char* sbf_last_error(void);
 
 #ifdef __cplusplus

@@ -44,6 +44,20 @@ def _is_device_tensor(x) -> bool:
     return isinstance(x, torch.Tensor) and x.is_cuda
 
 
+def _device_bytes(seq, stream):
+    """A contiguous 1-D view of a CUDA uint8 tensor.  A non-contiguous input
+    is copied; the copy is recorded on `stream` so the caching allocator does
+    not reuse it while the asynchronous call may still read it there."""
+    torch = _torch()
+    if seq.dtype != torch.uint8:
+        raise TypeError("expected a CUDA uint8 tensor of ASCII bytes, got %s" % (seq.dtype,))
+    a = seq.contiguous().view(-1)
+    if not seq.is_contiguous() and stream is not None:
+        st = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(_stream_ptr(stream))
+        a.record_stream(st)
+    return a
+
+
 def _host_bytes(seq) -> np.ndarray:
     if isinstance(seq, str):
         seq = seq.encode("ascii")
@@ -175,7 +189,7 @@ class SuperBloomFilter:
         """Insert every valid k-mer of an ASCII sequence: a CUDA uint8 tensor
         (asynchronous) or host bytes / str / numpy (synchronizes)."""
         if _is_device_tensor(seq):
-            a = seq.contiguous().view(-1)
+            a = _device_bytes(seq, stream)
             check(lib().sbf_insert_seq(self._h, a.data_ptr(), a.numel(), SBF_DEVICE, _stream_ptr(stream)),
                   "sbf_insert_seq")
         else:
@@ -187,7 +201,7 @@ class SuperBloomFilter:
         tensor of bit words (asynchronous); host input a numpy uint64 array."""
         if _is_device_tensor(seq):
             torch = _torch()
-            a = seq.contiguous().view(-1)
+            a = _device_bytes(seq, stream)
             nw = self.num_answer_words(a.numel())
             if out is None:
                 out = torch.empty(max(nw, 1), dtype=torch.int64, device=a.device)

@@ -4,10 +4,8 @@ GPUs", §V: out-of-cache filters, the (s, m, H) sweep and the blocked Bloom
 comparison, a genome-scale filter).
 
 The oracle side uses the threaded drivers of oracle/sbf_oracle.c (the same
-per-k-mer definition, k-mer starts split over threads) and, for the 4 GiB
-filter of configuration 5, the shard-sampled driver: the words of every shard
-s with (s & 63) == 13 are compared exactly, and every read k-mer mapped to
-one of them is answered by both sides.
+per-k-mer definition, k-mer starts split over threads); every filter word is
+compared, the 4 GiB filter of configuration 5 included.
 """
 import os
 import time
@@ -49,15 +47,26 @@ def _full_filter_parity(params, bits, genome, kind="sbf", mt=True):
     return g, o
 
 
-def test_config3_full():
-    """512 MiB filter (out of every cache): the 200 Mbp genome's filter
-    words all match; query bits match on every k-mer of the first 200 k reads
-    and on 1 M sampled positions of all 20 M reads; probe counts match."""
+@pytest.fixture(scope="module")
+def cfg3():
+    """Configuration 3 once per module: the 200 Mbp genome inserted into the
+    512 MiB filter on both sides, and the GPU's answers for the 20 M reads."""
     w = S.workload(3)
     progress("config 3 generated")
     g, o = _full_filter_parity(MAIN, w["bits"], w["insert"])
     reads = w["queries"][0]
+    progress("config 3 gpu query of %d bases" % reads.size)
     got = G.dev_bits_to_np(g.query_seq(G.to_dev(reads)))
+    yield {"w": w, "g": g, "o": o, "reads": reads, "got": got}
+    g.close()
+    o.close()
+
+
+def test_config3_full(cfg3):
+    """512 MiB filter (out of every cache): the 200 Mbp genome's filter
+    words all match; query bits match on every k-mer of the first 200 k reads
+    and on 1 M sampled positions of all 20 M reads; probe counts match."""
+    g, o, reads, got = cfg3["g"], cfg3["o"], cfg3["reads"], cfg3["got"]
     nk = reads.size - K + 1
     head = 200_000 * 151
     want_head = o.query_seq_mt(reads[:head])
@@ -66,6 +75,65 @@ def test_config3_full():
     assert (T.bits_of(got, nk)[pos.astype(np.int64)] == o.query_positions(reads, pos)).all()
     progress("config 3 query checked")
     assert g.fpr_probe(1_000_000, 0x5EED) == o.fpr_probe(1_000_000, 0x5EED)
+
+
+def _bit_slice(words: np.ndarray, start: int, n: int) -> np.ndarray:
+    """Bits [start, start + n) of LSB-first uint64 words, as LSB-first words
+    (bits past n zero)."""
+    nw = (n + 63) // 64
+    base, off = divmod(start, 64)
+    w = np.zeros(nw + 1, dtype=np.uint64)
+    avail = min(nw + 1, words.size - base)
+    w[:avail] = words[base:base + avail]
+    if off:
+        out = (w[:nw] >> np.uint64(off)) | (w[1:nw + 1] << np.uint64(64 - off))
+    else:
+        out = w[:nw].copy()
+    if n % 64:
+        out[-1] &= np.uint64((1 << (n % 64)) - 1)
+    return out
+
+
+def test_query_beyond_2e32_starts(cfg3):
+    """One query launch of more than 2^32 k-mer starts (the size of the
+    genome-scale query, [cuSBF] §V-F): the configuration-3 reads twice,
+    joined by one 'N' -- 6.04 G bases -- against the configuration-3 filter.
+    The first copy's answers equal the single-copy answers (checked against
+    the oracle in test_config3_full); the k k-mers that span the joining 'N'
+    answer 0; the second copy's answers, which start at bit L + 1 (past 2^32
+    for most of them), equal the first copy's word for word after the shift;
+    and 200 k seeded positions past 2^32 equal the oracle's own answers for
+    the same k-mers."""
+    torch = G.torch_cuda()
+    g, o, reads, got = cfg3["g"], cfg3["o"], cfg3["reads"], cfg3["got"]
+    L = reads.size
+    nk = L - K + 1
+    one = G.to_dev(reads)
+    sep = torch.tensor([ord("N")], dtype=torch.uint8, device=one.device)
+    two = torch.cat([one, sep, one])
+    del one
+    assert two.numel() == 2 * L + 1 and two.numel() - K + 1 > 2**32
+    assert two.data_ptr() % 16 == 0  # the kernel reads the ASCII itself
+    progress("query of %d bases in one launch" % two.numel())
+    res = G.dev_bits_to_np(g.query_seq(two))
+    del two
+    torch.cuda.synchronize()
+    nk2 = 2 * L + 1 - K + 1
+    assert res.size == (nk2 + 63) // 64
+    progress("doubled query done")
+    G.assert_words_equal(_bit_slice(res, 0, nk), _bit_slice(got, 0, nk), "first copy")
+    assert not _bit_slice(res, nk, K).any(), "k-mers across the separator"
+    G.assert_words_equal(_bit_slice(res, L + 1, nk), _bit_slice(got, 0, nk), "second copy (bit offset L + 1)")
+    if nk2 % 64:
+        assert int(res[-1]) >> (nk2 % 64) == 0, "bits past the last k-mer start"
+    # the oracle on seeded positions past 2^32 (the same k-mers of the reads)
+    rng = np.random.default_rng(97)
+    pos = rng.integers(2**32, nk2, 200_000).astype(np.uint64)
+    bits = (res[(pos >> np.uint64(6)).astype(np.int64)] >> (pos & np.uint64(63))) & np.uint64(1)
+    want = o.query_positions(reads, pos - np.uint64(L + 1))
+    assert (bits.astype(np.uint8) == want).all()
+    assert want.sum() > 1000
+    progress("doubled query checked")
 
 
 @pytest.mark.parametrize("kind,params", [("sbf", MAIN), ("bbf", (31, 0, 0, 4))])
@@ -97,36 +165,31 @@ def test_config4_sweep_points():
         assert g.fpr_probe(300_000, s * m * H) == o.fpr_probe(300_000, s * m * H)
 
 
-def test_config5_sampled():
-    """2^35-bit (4 GiB) filter, 3 Gbp genome with 'N' runs: the words of every
-    shard s with (s & 63) == 13 equal the oracle's (shard-sampled insert); on
-    the seeded 1% long-read subsample every k-mer mapped to those shards has
-    the oracle's answer; the genome's first 100 Mbp query exactly their valid
-    k-mers (no false negatives, invalid k-mers false)."""
+def test_config5_full():
+    """2^35-bit (4 GiB) filter, 3 Gbp genome with 'N' runs ([cuSBF] §V-F,
+    genome-scale filters): every word of the filter equals the oracle's
+    (threaded per-k-mer insert); every k-mer of the seeded 1% long-read
+    subsample has the oracle's answer; the genome's first 100 Mbp query
+    exactly their valid k-mers (no false negatives, invalid k-mers false)."""
     bits = S.CONFIG_BITS[5]
     genome = S.genome_with_n_runs(S.CONFIG_GENOME[5])
     progress("config 5 genome generated")
     g = G.gpu_filter(MAIN, bits)
     g.insert_seq(G.to_dev(genome))
+    words = g.words()
     progress("config 5 gpu insert done")
-    words = g.words().reshape(-1, 4)
     o = G.oracle_filter(MAIN, bits)
-    o.insert_seq_sampled_mt(genome, 63, 13)
-    progress("config 5 oracle sampled insert done")
-    want = o.words().reshape(-1, 4)
-    sel = np.arange(13, want.shape[0], 64)
-    G.assert_words_equal(words[sel].reshape(-1), want[sel].reshape(-1), "config 5 sampled shards")
-    assert want[sel].any()
-    del words, want
+    o.insert_seq_mt(genome)
+    progress("config 5 oracle insert done")
+    ow = np.ctypeslib.as_array(O_words_ptr(o), shape=(words.size,))
+    G.assert_words_equal(words, ow, "config 5 filter")
+    assert (words != 0).mean() > 0.5
+    del words, ow
     # queries: the seeded 1% subsample (one batch of 10 k long reads)
     reads = S.long_read_batch(genome, S.long_read_subsample_batch())
-    progress("config 5 subsample reads generated")
+    progress("config 5 subsample reads generated (%d bases)" % reads.size)
     got = G.dev_bits_to_np(g.query_seq(G.to_dev(reads)))
-    ans, checked = o.query_seq_sampled_mt(reads, 63, 13)
-    nk = reads.size - K + 1
-    cb = T.bits_of(checked, nk).astype(bool)
-    assert cb.sum() > 100_000
-    assert (T.bits_of(got, nk)[cb] == T.bits_of(ans, nk)[cb]).all()
+    G.assert_words_equal(got, o.query_seq_mt(reads), "config 5 subsample query")
     # no false negatives on the genome itself, invalid k-mers answer false
     head = genome[:100_000_000]
     hb = T.bits_of(G.dev_bits_to_np(g.query_seq(G.to_dev(head))), head.size - K + 1)
@@ -134,3 +197,11 @@ def test_config5_sampled():
     bad = (cum[K:] - cum[:-K]) > 0
     assert (hb == ~bad).all()
     progress("config 5 checked")
+    g.close()
+    o.close()
+
+
+def O_words_ptr(o):
+    """The oracle filter's own word array (no 4 GiB copy)."""
+    from oracle import oracle as O
+    return O.lib().osbf_words(o._h)
