@@ -323,6 +323,23 @@ int sbf_query_fastx(sbf_t* h, const char* path, uint64_t* hits, uint64_t* kmers,
                     sbf_fastx_stats_t* stats);
 
 /*
+ * Allocation-free insert of a device sequence, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same result as sbf_insert_seq with
+ * SBF_DEVICE, asynchronous on `stream`, but the packed codes and validity go
+ * to a static device array of the library (24 MiB per device, held until the
+ * process ends) instead of the handle's staging buffers, and the call makes
+ * no allocation of any kind.  DNA filters: len <= 2^26 bases, larger len is
+ * SBF_EINVAL (split the input into pieces overlapping by k-1 bases); protein
+ * and triplet filters read the text directly and take any length.
+ * All calls on one device share that array: two calls that may overlap on
+ * one device (other streams, other handles, other threads) race and must be
+ * serialized by the caller.  len < k is a no-op.  Errors: SBF_EINVAL (NULL
+ * handle or sequence, len over the limit), SBF_EDEVICE.
+ */
+int sbf_insert_seq_noalloc(sbf_t* h, const char* d_seq, uint64_t len, void* stream);
+
+/*
  * False-positive probe ([cuSBF] §V-D): query n k-mers drawn on the device
  * from the SplitMix64 stream seeded with `seed` (k-mer i = output i shifted
  * right by 64-2k) and store the number of positives in *hits (host).

@@ -55,6 +55,7 @@ SIGNATURES = {
     "sbf_insert_packed": (_int, [_p, _p, _p, _u64, _p]),
     "sbf_query_packed": (_int, [_p, _p, _p, _u64, _p, _p]),
     "sbf_insert_seq": (_int, [_p, _p, _u64, _u32, _p]),
+    "sbf_insert_seq_noalloc": (_int, [_p, _p, _u64, _p]),
     "sbf_query_seq": (_int, [_p, _p, _u64, _p, _u32, _p]),
     "sbf_fpr_probe": (_int, [_p, _u64, _u64, ctypes.POINTER(_u64)]),
     "sbf_fpr_probe_device": (_int, [_p, _u64, _u64, _p, _p]),

@@ -5,6 +5,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -49,7 +50,23 @@ bool find_specialized(const Params& p, KernelSet* out)
 
 namespace {
 thread_local std::string g_last_error;
+
+// Packed staging of sbf_insert_seq_noalloc, for callers that cannot allocate:
+// the code words of up to kNoAllocMaxBases bases, then their validity words
+// (24 MiB).  Each device the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never a
+// device address: kernels get the address that hipGetSymbolAddress returns
+// for the current device (noalloc_scratch below).
+constexpr uint64_t kNoAllocMaxBases = 1ull << 26;
+constexpr uint64_t kNoAllocCodeWords = kNoAllocMaxBases / 16;   // 16 bases per code word
+constexpr uint64_t kNoAllocValidWords = kNoAllocMaxBases / 32;  // 32 bases per validity word
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, null until resolved
 }  // namespace
+
+static __device__ __align__(256) uint32_t scratch[kNoAllocCodeWords + kNoAllocValidWords];
 
 namespace sbf {
 
@@ -80,6 +97,26 @@ int set_device(const sbf_t* h)
     (void)hipGetLastError();
     hipError_t e = hipSetDevice(h->device);
     return e == hipSuccess ? SBF_OK : fail_hip(e, "hipSetDevice");
+}
+
+// Device address of `device`'s copy of the static scratch array, resolved
+// once per device with that device current (it must be current here).  Called
+// when a filter is created on the device, and again by the allocation-free
+// entry point if that did not succeed.
+int noalloc_scratch(int device, uint32_t** out)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return fail(SBF_EDEVICE, "device index beyond the static scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return fail_hip(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[device] = static_cast<uint32_t*>(p);
+    }
+    *out = g_scratch_ptr[device];
+    return SBF_OK;
 }
 
 uint64_t code_words(uint64_t len) { return (len + 15) / 16; }
@@ -186,6 +223,10 @@ int create_impl(sbf_t** out, const sbf::Params& P, uint64_t bits)
         delete h;
         return fail_hip(e, "zeroing the filter");
     }
+    // set-up of the allocation-free insert on this device; a failure here
+    // only matters to that entry point, which resolves again and reports it
+    uint32_t* unused = nullptr;
+    (void)sbf::noalloc_scratch(h->device, &unused);
     *out = h;
     ok();
     return SBF_OK;
@@ -492,6 +533,46 @@ int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits, u
     hipError_t e = h->ks.query(a, h->P);
     if (e != hipSuccess)
         return fail_hip(e, "query");
+    ok();
+    return SBF_OK;
+}
+
+int sbf_insert_seq_noalloc(sbf_t* h, const char* d_seq, uint64_t len, void* stream)
+{
+    if (!h)
+        return fail(SBF_EINVAL, "handle is NULL");
+    if (symbols_of(h, len) < h->P.k) {
+        ok();
+        return SBF_OK;
+    }
+    if (!d_seq)
+        return fail(SBF_EINVAL, "seq is NULL");
+    if (h->P.alpha == SBF_ALPHABET_DNA && len > kNoAllocMaxBases)
+        return fail(SBF_EINVAL, "sbf_insert_seq_noalloc: len exceeds 2^26 bases, the size of its static staging");
+    int rc = set_device(h);
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (h->P.alpha != SBF_ALPHABET_DNA) {
+        // protein and triplet kernels read the text itself: no staging
+        e = h->ks.insert(text_args(h, d_seq, len, nullptr, st), h->P);
+    } else {
+        uint32_t* base = nullptr;
+        rc = noalloc_scratch(h->device, &base);
+        if (rc)
+            return rc;
+        // The pack writes every code and validity word that the insert reads
+        // (its buffer ranges end at ceil(len/16) and ceil(len/32) words), so
+        // nothing left by an earlier call needs clearing.
+        uint32_t* codes = base;
+        uint32_t* valid = base + kNoAllocCodeWords;
+        e = sbf::launch_pack(d_seq, len, codes, valid, st);
+        if (e == hipSuccess)
+            e = h->ks.insert(seq_args(h, codes, valid, len, nullptr, st), h->P);
+    }
+    if (e != hipSuccess)
+        return fail_hip(e, "insert");
     ok();
     return SBF_OK;
 }
