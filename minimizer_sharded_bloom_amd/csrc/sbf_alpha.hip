@@ -130,55 +130,6 @@ __device__ __forceinline__ bool covers(const uint64_t (&w)[4], const uint64_t (&
     return ((~w[0] & mk[0]) | (~w[1] & mk[1]) | (~w[2] & mk[2]) | (~w[3] & mk[3])) == 0;
 }
 
-// Value of lane l+d in lane l for a wave-uniform d >= 1 (lanes past 63 read
-// garbage; only halo lanes look there).
-__device__ __forceinline__ uint32_t lane_down(uint32_t v, uint32_t d, uint32_t lane)
-{
-    if (d == 1u)
-        return from_next_lane(v);
-    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((lane + d) << 2), (int)v);
-}
-
-__device__ __forceinline__ uint64_t lane_down(uint64_t v, uint32_t d, uint32_t lane)
-{
-    return ((uint64_t)lane_down((uint32_t)(v >> 32), d, lane) << 32) | lane_down((uint32_t)v, d, lane);
-}
-
-// min over lanes l .. l+w-1 (1 <= w <= 64)
-__device__ __forceinline__ uint64_t window_min(uint64_t v, uint32_t w, uint32_t lane)
-{
-    uint32_t span = 1;
-#pragma unroll
-    while (2u * span <= w) {
-        const uint64_t o = lane_down(v, span, lane);
-        v = o < v ? o : v;
-        span *= 2u;
-    }
-    if (span < w) {
-        const uint64_t o = lane_down(v, w - span, lane);
-        v = o < v ? o : v;
-    }
-    return v;
-}
-
-// OR over lanes l .. l+z-1 of the four sector masks (words q >= H stay 0)
-__device__ __forceinline__ void window_or(uint64_t (&mk)[4], uint32_t z, uint32_t H, uint32_t lane)
-{
-    const uint32_t nq = H < 4u ? H : 4u;
-    uint32_t span = 1;
-#pragma unroll
-    while (2u * span <= z) {
-#pragma unroll
-        for (uint32_t q = 0; q < nq; ++q)
-            mk[q] |= lane_down(mk[q], span, lane);
-        span *= 2u;
-    }
-    if (span < z)
-#pragma unroll
-        for (uint32_t q = 0; q < nq; ++q)
-            mk[q] |= lane_down(mk[q], z - span, lane);
-}
-
 // One wave step over symbol positions base .. base+63: for the k-mer that
 // starts at this lane, its shard, its four sector masks and whether it is
 // to be processed (complete within the wave, every symbol valid, start

@@ -24,6 +24,8 @@ const SpecEntry* spec_table_slice_m_b(size_t* n);
 const SpecEntry* spec_table_slice_m_c(size_t* n);
 const SpecEntry* spec_table_slice_h(size_t* n);
 const SpecEntry* spec_table_wide(size_t* n);
+const SpecEntry* spec_table_grid_best_a(size_t* n);
+const SpecEntry* spec_table_grid_best_b(size_t* n);
 
 bool find_specialized(const Params& p, KernelSet* out)
 {
@@ -33,7 +35,8 @@ bool find_specialized(const Params& p, KernelSet* out)
     static const TableFn tables[] = {spec_table_m12,       spec_table_m16,       spec_table_m20,
                                      spec_table_extra,     spec_table_slice_s_a, spec_table_slice_s_b,
                                      spec_table_slice_m_a, spec_table_slice_m_b, spec_table_slice_m_c,
-                                     spec_table_slice_h,   spec_table_wide};
+                                     spec_table_slice_h,   spec_table_wide,      spec_table_grid_best_a,
+                                     spec_table_grid_best_b};
     for (TableFn fn : tables) {
         size_t n = 0;
         const SpecEntry* t = fn(&n);

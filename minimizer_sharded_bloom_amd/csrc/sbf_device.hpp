@@ -220,6 +220,66 @@ __device__ __forceinline__ uint64_t from_next_lane(uint64_t v)
     return ((uint64_t)from_next_lane((uint32_t)(v >> 32)) << 32) | from_next_lane((uint32_t)v);
 }
 
+// Raw buffer over the 32-bit words [w0, n) of an array, w0 wave-uniform: a
+// read past the end returns 0 through the buffer range check, so lane loads
+// need no bounds branches.  Descriptor word 3: 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t word_buffer(const uint32_t* a, uint64_t n, uint64_t w0)
+{
+    const uint64_t b = w0 < n ? w0 : n;
+    const uint64_t bytes = (n - b) * 4ull;
+    const uint32_t nrec = bytes < 0xFFFFFFFFull ? (uint32_t)bytes : 0xFFFFFFFFu;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a + b), (short)0, (int)nrec, 0x00020000);
+}
+
+// Value of lane l+d in lane l for a wave-uniform d >= 1 (lanes past 63 read
+// garbage; only halo lanes look there).
+__device__ __forceinline__ uint32_t lane_down(uint32_t v, uint32_t d, uint32_t lane)
+{
+    if (d == 1u)
+        return from_next_lane(v);
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((lane + d) << 2), (int)v);
+}
+
+__device__ __forceinline__ uint64_t lane_down(uint64_t v, uint32_t d, uint32_t lane)
+{
+    return ((uint64_t)lane_down((uint32_t)(v >> 32), d, lane) << 32) | lane_down((uint32_t)v, d, lane);
+}
+
+// min over lanes l .. l+w-1 (1 <= w <= 64)
+__device__ __forceinline__ uint64_t window_min(uint64_t v, uint32_t w, uint32_t lane)
+{
+    uint32_t span = 1;
+#pragma unroll
+    while (2u * span <= w) {
+        const uint64_t o = lane_down(v, span, lane);
+        v = o < v ? o : v;
+        span *= 2u;
+    }
+    if (span < w) {
+        const uint64_t o = lane_down(v, w - span, lane);
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+// OR over lanes l .. l+z-1 of the four sector masks (words q >= H stay 0)
+__device__ __forceinline__ void window_or(uint64_t (&mk)[4], uint32_t z, uint32_t H, uint32_t lane)
+{
+    const uint32_t nq = H < 4u ? H : 4u;
+    uint32_t span = 1;
+#pragma unroll
+    while (2u * span <= z) {
+#pragma unroll
+        for (uint32_t q = 0; q < nq; ++q)
+            mk[q] |= lane_down(mk[q], span, lane);
+        span *= 2u;
+    }
+    if (span < z)
+#pragma unroll
+        for (uint32_t q = 0; q < nq; ++q)
+            mk[q] |= lane_down(mk[q], z - span, lane);
+}
+
 // LDS written by some lanes of this wave becomes visible to all its lanes.
 __device__ __forceinline__ void wave_lds_sync()
 {

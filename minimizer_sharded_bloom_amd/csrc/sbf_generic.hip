@@ -268,6 +268,209 @@ __global__ __launch_bounds__(256) void generic_probe_kernel(ProbeArgs a, Params 
         atomicAdd(a.hits, (unsigned long long)cnt);
 }
 
+// ---------------------------------------------------------------------------
+// Run-time sliding kernels of the Super Bloom filter (any k, m, s, H that has
+// no compiled set).  A wave step covers 64 consecutive positions, one per
+// lane: lane l reads the packed bases p .. p+31 (p = base + l) from the code
+// words and hashes the m-mer and the s-mer starting at p once; the k-mer
+// starting at p takes the minimum h_min over lanes l .. l+w-1 (its w = k-m+1
+// m-mers, [cuSBF] Algorithm 1) and the OR of the s-mer sector masks over
+// lanes l .. l+z-1 (its z = k-s+1 s-mers), both by cross-lane doubling.  The
+// lanes l < E = 65 - max(w, z) start a complete k-mer, so one step yields E
+// k-mers and the rest of the wave is halo.  Every position is hashed once
+// per step instead of w + z times per k-mer as in the per-k-mer kernels.
+// ---------------------------------------------------------------------------
+
+// k-mer starts per wave task: whole answer words, so tasks never share one.
+constexpr uint64_t kSlideTask = 2048;
+
+// Shard key (low 32 bits of the minimizer hash) and sector masks of the k-mer
+// starting at this lane's position; true if it is to be processed (a start
+// lane, before `end`, every base valid).  HC > 0 fixes H at compile time (the
+// bit-address loop unrolls); HC = 0 takes it from P.  Code and validity words
+// come through raw buffers based at the step's first word, so reads past the
+// end of the sequence return 0 without a bounds branch.
+template <int HC>
+__device__ __forceinline__ bool slide_step(const SeqArgs& a, const Params& P, uint64_t base, uint64_t end,
+                                           uint32_t lane, uint32_t E, uint32_t& key, uint64_t (&mk)[4])
+{
+    const uint32_t k = P.k, m = P.m, s = P.s, H = HC ? (uint32_t)HC : P.H;
+    const uint64_t p = base + lane;
+    // bases p .. p+31, first in the top bits
+    const auto rc = word_buffer(a.codes, a.ncw, base >> 4);
+    const uint32_t o = (((uint32_t)(base & 15u) + lane) >> 4) * 4u;
+    const uint32_t d0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, (int)o, 0, 0);
+    const uint32_t d1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, (int)(o + 4u), 0, 0);
+    const uint32_t d2 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, (int)(o + 8u), 0, 0);
+    const uint32_t r = 2u * (uint32_t)(p & 15u);
+    const uint64_t win = ((uint64_t)funnel_hi(d0, d1, r) << 32) | funnel_hi(d1, d2, r);
+    // validity bits p .. p+63
+    const auto rv = word_buffer(a.valid, a.nvw, base >> 5);
+    const uint32_t vb = (uint32_t)(base & 31u) + lane;
+    const uint32_t vo = (vb >> 5) * 4u, voff = vb & 31u;
+    const uint32_t v0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, (int)vo, 0, 0);
+    const uint32_t v1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, (int)(vo + 4u), 0, 0);
+    const uint32_t v2 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, (int)(vo + 8u), 0, 0);
+    const uint64_t vwin = ((uint64_t)__builtin_amdgcn_alignbit(v2, v1, voff) << 32) | __builtin_amdgcn_alignbit(v1, v0, voff);
+    const uint64_t need = k >= 64u ? ~0ull : ((1ull << k) - 1ull);
+
+    const uint64_t vm = m >= 32u ? win : win >> (64u - 2u * m);
+    const uint64_t vs = s >= 32u ? win : win >> (64u - 2u * s);
+    key = (uint32_t)window_min(hash_min(vm), k - m + 1u, lane);
+    const uint64_t h = hash_s(vs);
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q)
+        mk[q] = 0;
+    if constexpr (HC > 0) {
+#pragma unroll
+        for (int t = 0; t < HC; ++t)
+            mk[t & 3] |= 1ull << bit_addr<HC>(h, t);
+    } else {
+        for (uint32_t t0 = 0; t0 < H; t0 += 4u) {
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q)
+                if (t0 + q < H)
+                    mk[q] |= 1ull << bit_addr_rt(h, t0 + q, H);
+        }
+    }
+    window_or(mk, k - s + 1u, H, lane);
+    return lane < E && p < end && (vwin & need) == need;
+}
+
+// Step length: E = 65 - max(w, z) k-mers per wave step.
+__device__ __forceinline__ uint32_t slide_yield(const Params& P)
+{
+    const uint32_t w = P.k - P.m + 1u, z = P.k - P.s + 1u;
+    return 65u - (w > z ? w : z);
+}
+
+// Insert: consecutive valid k-mers of one shard key within a step form a run
+// ([cuSBF] §IV-D super-k-mers); each run ORs its k-mers' masks into an LDS
+// record with LDS atomics, and four adjacent lanes OR one record's words
+// into the filter (one merged request per run).
+template <int HC>
+__global__ __launch_bounds__(256) void slide_insert_kernel(SeqArgs a, Params P)
+{
+    __shared__ uint64_t rec_mk[4][64][4];
+    __shared__ uint32_t rec_sh[4][64];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t E = slide_yield(P);
+    const uint64_t ntasks = (a.nk + kSlideTask - 1) / kSlideTask;
+    const uint64_t wstride = (uint64_t)gridDim.x * 4u;
+    const uint64_t le = lane == 63u ? ~0ull : (2ull << lane) - 1ull;  // lanes 0 .. lane
+    for (uint64_t task = (uint64_t)blockIdx.x * 4u + wv; task < ntasks; task += wstride) {
+        const uint64_t t0 = task * kSlideTask;
+        const uint64_t t1 = t0 + kSlideTask < a.nk ? t0 + kSlideTask : a.nk;
+        for (uint64_t base = t0; base < t1; base += E) {
+            uint32_t key;
+            uint64_t mk[4];
+            const bool kv = slide_step<HC>(a, P, base, t1, lane, E, key, mk);
+            const uint32_t pkey = from_prev_lane(key);
+            const uint32_t pkv = from_prev_lane(kv ? 1u : 0u);  // lane 0 reads 0
+            const bool head = kv && !(pkv && pkey == key);
+            const uint64_t HB = __ballot(head);
+            const uint32_t nrec = (uint32_t)__popcll(HB);
+            if (nrec == 0)
+                continue;
+            const uint32_t r = (uint32_t)__popcll(HB & le) - 1u;  // this k-mer's run (valid lanes)
+            reinterpret_cast<ulonglong2*>(rec_mk[wv][lane])[0] = ulonglong2{0, 0};
+            reinterpret_cast<ulonglong2*>(rec_mk[wv][lane])[1] = ulonglong2{0, 0};
+            wave_lds_sync();
+            if (kv) {
+#pragma unroll
+                for (uint32_t q = 0; q < 4; ++q)
+                    if (mk[q])
+                        __hip_atomic_fetch_or(&rec_mk[wv][r][q], mk[q], __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_WAVEFRONT);
+                if (head)
+                    rec_sh[wv][r] = key & a.shard_mask;
+            }
+            wave_lds_sync();
+            // flush: lane -> (record lane/4 + 16 j, word lane & 3)
+            const uint32_t q = lane & 3u;
+            for (uint32_t rr = lane >> 2; rr < nrec; rr += 16u) {
+                const uint64_t m = rec_mk[wv][rr][q];
+                if (m)
+                    atomic_or_u64(a.filter + 4ull * rec_sh[wv][rr] + q, m);
+            }
+            wave_lds_sync();  // the next step rewrites the records
+        }
+    }
+}
+
+// Query: each processed k-mer loads its 256-bit shard (the lanes of a run
+// load the same line, which one wave load serves once) and tests its masks;
+// the step's answer ballot (E bits) is appended to a running 64-bit word so
+// each store is one whole, aligned answer word.
+template <int HC>
+__global__ __launch_bounds__(256) void slide_query_kernel(SeqArgs a, Params P)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t E = slide_yield(P);
+    const uint64_t ntasks = (a.nk + kSlideTask - 1) / kSlideTask;
+    const uint64_t wstride = (uint64_t)gridDim.x * 4u;
+    for (uint64_t task = (uint64_t)blockIdx.x * 4u + wv; task < ntasks; task += wstride) {
+        const uint64_t t0 = task * kSlideTask;
+        const uint64_t t1 = t0 + kSlideTask < a.nk ? t0 + kSlideTask : a.nk;
+        uint64_t acc = 0;         // answers not yet stored, first at bit 0
+        uint32_t nb = 0;          // how many (< 64)
+        uint64_t word = t0 >> 6;  // answer word they belong to
+        for (uint64_t base = t0; base < t1; base += E) {
+            uint32_t key;
+            uint64_t mk[4];
+            bool pres = slide_step<HC>(a, P, base, t1, lane, E, key, mk);
+            if (pres) {
+                uint64_t w[4];
+                load_shard(a.filter, key & a.shard_mask, w);
+                pres = ((~w[0] & mk[0]) | (~w[1] & mk[1]) | (~w[2] & mk[2]) | (~w[3] & mk[3])) == 0;
+            }
+            const uint64_t bits = __ballot(pres);  // bits 0 .. E-1
+            acc |= bits << nb;
+            const uint64_t spill = nb ? bits >> (64u - nb) : 0ull;
+            nb += E;
+            if (nb >= 64u) {
+                if (lane == 0)
+                    a.out[word] = acc;
+                ++word;
+                acc = spill;
+                nb -= 64u;
+            }
+        }
+        // the task's last, partial word (never the next task's first)
+        if (nb && (word << 6) < t1 && lane == 0)
+            a.out[word] = acc;
+    }
+}
+
+// Kernel of the sliding family for this H: compile-time H for 1 .. 16,
+// run-time above.
+#define SBF_SLIDE_KERNEL(NAME)                                                                  \
+    static void (*NAME##_for(uint32_t H))(SeqArgs, Params)                                      \
+    {                                                                                           \
+        switch (H) {                                                                            \
+        case 1: return NAME<1>;   case 2: return NAME<2>;   case 3: return NAME<3>;             \
+        case 4: return NAME<4>;   case 5: return NAME<5>;   case 6: return NAME<6>;             \
+        case 7: return NAME<7>;   case 8: return NAME<8>;   case 9: return NAME<9>;             \
+        case 10: return NAME<10>; case 11: return NAME<11>; case 12: return NAME<12>;           \
+        case 13: return NAME<13>; case 14: return NAME<14>; case 15: return NAME<15>;           \
+        case 16: return NAME<16>; default: return NAME<0>;                                     \
+        }                                                                                       \
+    }
+SBF_SLIDE_KERNEL(slide_insert_kernel)
+SBF_SLIDE_KERNEL(slide_query_kernel)
+#undef SBF_SLIDE_KERNEL
+
+static uint32_t slide_blocks(uint64_t nk)
+{
+    const uint64_t tasks = (nk + kSlideTask - 1) / kSlideTask;
+    uint64_t b = (tasks + 3) / 4;
+    if (b > 16384)
+        b = 16384;
+    return (uint32_t)(b ? b : 1);
+}
+
 static uint32_t grid_for(uint64_t n)
 {
     uint64_t b = (n + 255) / 256;
@@ -276,15 +479,24 @@ static uint32_t grid_for(uint64_t n)
     return (uint32_t)(b ? b : 1);
 }
 
+// The Super Bloom filter takes the sliding kernels; the blocked Bloom
+// comparator and the wide-block variant the per-k-mer ones.
 static hipError_t gen_insert(const SeqArgs& a, const Params& P)
 {
-    hipLaunchKernelGGL(generic_insert_kernel, dim3(grid_for(a.nk)), dim3(256), 0, a.stream, a, P);
+    if (P.kind == 0)
+        hipLaunchKernelGGL(slide_insert_kernel_for(P.H), dim3(slide_blocks(a.nk)), dim3(256), 0, a.stream, a, P);
+    else
+        hipLaunchKernelGGL(generic_insert_kernel, dim3(grid_for(a.nk)), dim3(256), 0, a.stream, a, P);
     return hipGetLastError();
 }
 
 static hipError_t gen_query(const SeqArgs& a, const Params& P)
 {
-    hipLaunchKernelGGL(generic_query_kernel, dim3(grid_for((a.nk + 63) & ~63ull)), dim3(256), 0, a.stream, a, P);
+    if (P.kind == 0)
+        hipLaunchKernelGGL(slide_query_kernel_for(P.H), dim3(slide_blocks(a.nk)), dim3(256), 0, a.stream, a, P);
+    else
+        hipLaunchKernelGGL(generic_query_kernel, dim3(grid_for((a.nk + 63) & ~63ull)), dim3(256), 0, a.stream, a,
+                           P);
     return hipGetLastError();
 }
 

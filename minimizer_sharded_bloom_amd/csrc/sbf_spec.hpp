@@ -142,17 +142,6 @@ __device__ __forceinline__ LaneCtx<C> lane_ctx(uint64_t nk_pad)
     return c;
 }
 
-// Raw buffer over the 32-bit words [w0, n) of an array, w0 wave-uniform: a
-// read past the end returns 0 through the buffer range check, so lane loads
-// need no bounds branches.  Descriptor word 3: 32-bit data format.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t word_buffer(const uint32_t* a, uint64_t n, uint64_t w0)
-{
-    const uint64_t b = w0 < n ? w0 : n;
-    const uint64_t bytes = (n - b) * 4ull;
-    const uint32_t nrec = bytes < 0xFFFFFFFFull ? (uint32_t)bytes : 0xFFFFFFFFu;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a + b), (short)0, (int)nrec, 0x00020000);
-}
-
 // Packed code words of the lane: KL/16 own words and two more for the halo
 // (0 past the end of the sequence).  KPW is a multiple of 16, so the wave's
 // first k-mer starts a code word.

@@ -29,6 +29,13 @@
 #define SBF_SLICE_M_C(X) X(31, 25, 28, 4) X(31, 26, 28, 4) X(31, 27, 28, 4) X(31, 28, 28, 4) X(31, 29, 28, 4) X(31, 30, 28, 4) X(31, 31, 28, 4)
 #define SBF_SLICE_H(X) X(31, 16, 28, 1) X(31, 16, 28, 5) X(31, 16, 28, 8) X(31, 16, 28, 16)
 
+// The lowest-FPR block of the two-dimensional (s, m) grid at H = 4 on
+// genome-like input (s = 23..26, m = 21..23; the grid's map puts its
+// minimum there, several times below (28, 16, 4)), split in two for
+// parallel builds.
+#define SBF_GRID_BEST_A(X) X(31, 21, 23, 4) X(31, 22, 23, 4) X(31, 23, 23, 4) X(31, 21, 24, 4) X(31, 22, 24, 4) X(31, 23, 24, 4)
+#define SBF_GRID_BEST_B(X) X(31, 21, 25, 4) X(31, 22, 25, 4) X(31, 23, 25, 4) X(31, 21, 26, 4) X(31, 22, 26, 4) X(31, 23, 26, 4)
+
 // Wide-block variant (512-bit blocks, whole-block addressing): the operating
 // point and its neighbours in s, H and m.
 #define SBF_WIDE(X)                                                                                               \

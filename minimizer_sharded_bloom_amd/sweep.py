@@ -11,9 +11,13 @@ at the same budget for H in {2,3,4,6}, and the wide-block variant (512-bit
 blocks, whole-block addressing; §V-D) at ten points around (28, 16, 4).  Prints one JSON line per point and a
 summary table.  With --grid: the slices of the wider grid (Fig. 4) through
 the operating point -- s = 16..31 at (m, H) = (16, 4), m = 8..31 at
-(s, H) = (28, 4), H in {1,2,3,4,5,6,8,12,16} at (m, s) = (16, 28).
+(s, H) = (28, 4), H in {1,2,3,4,5,6,8,12,16} at (m, s) = (16, 28).  With
+--grid2d: the whole two-dimensional grid of Fig. 4, s = 16..31 x m = 8..31,
+at each H in --h-values (default 4, 8, 12, 16; H > 10 takes the salted bit
+address).  Points outside the compiled parameter sets run on the generic
+per-k-mer kernels; each row says which.
 
-    python -m minimizer_sharded_bloom_amd.sweep [--probe-n N] [--reps R] [--grid]
+    python -m minimizer_sharded_bloom_amd.sweep [--probe-n N] [--reps R] [--grid | --grid2d]
 """
 from __future__ import annotations
 
@@ -34,10 +38,13 @@ M_VALUES = (12, 16, 20)
 H_VALUES = (2, 3, 4, 6)
 
 
-def _time_ms(torch, stream, fn, reps):
-    """Median kernel time of fn() over reps runs, events on `stream`."""
+def _time_ms(torch, stream, fn, reps, before=None):
+    """Median kernel time of fn() over reps runs, events on `stream`;
+    before(), if given, runs ahead of each timed run outside the events."""
     ts = []
     for _ in range(reps):
+        if before is not None:
+            before()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -48,7 +55,8 @@ def _time_ms(torch, stream, fn, reps):
     return float(np.median(ts))
 
 
-def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, grid: bool = False, out=sys.stdout):
+def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, grid: bool = False, out=sys.stdout,
+        grid2d: bool = False, h_values=(4, 8, 12, 16)):
     import torch
 
     torch.cuda.set_device(0)
@@ -75,11 +83,10 @@ def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, grid: bool
         out_bits = torch.empty(max(1, f.num_answer_words(LR)), dtype=torch.int64, device=dev)
 
         def ins():
-            check(L.sbf_clear(f.handle, sp), "clear")
             check(L.sbf_insert_packed(f.handle, gc.data_ptr(), gv.data_ptr(), LG, sp), "insert")
 
-        # clear + insert timed together; clear is one 128 MiB fill (~0.03 ms)
-        t_ins = _time_ms(torch, stream, ins, reps)
+        # each timed insert starts from a cleared filter; the clear is not timed
+        t_ins = _time_ms(torch, stream, ins, reps, before=lambda: check(L.sbf_clear(f.handle, sp), "clear"))
         t_q = _time_ms(torch, stream, lambda: check(
             L.sbf_query_packed(f.handle, rc.data_ptr(), rv.data_ptr(), LR, out_bits.data_ptr(), sp), "query"), reps)
         t_p = _time_ms(torch, stream, lambda: check(
@@ -93,6 +100,13 @@ def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, grid: bool
         rows.append(row)
         print(json.dumps(row), file=out, flush=True)
 
+    if grid2d:
+        for H in h_values:
+            for s in range(16, 32):
+                for m in range(8, 32):
+                    with SuperBloomFilter(K, m, s, H, BITS) as f:
+                        point(f, {"kind": "grid2d", "s": s, "m": m, "H": H})
+        return rows
     if grid:
         for kind, pts in (("slice_s", [(16, s, 4) for s in range(16, 32)]),
                           ("slice_m", [(m, 28, 4) for m in range(8, 32)]),
@@ -116,6 +130,30 @@ def run(probe_n: int = 10_000_000, reps: int = 3, seed: int = 0x5EED, grid: bool
     return rows
 
 
+def grid_tables(rows) -> str:
+    """Two-dimensional maps (rows s, columns m) per H of the FPR and of the
+    insert and query rates, from --grid2d rows; '*' marks the points served
+    by compiled (specialized) kernels."""
+    out = []
+    for H in sorted({r["H"] for r in rows}):
+        rs = {(r["s"], r["m"]): r for r in rows if r["H"] == H}
+        ms = sorted({m for _, m in rs})
+        ss = sorted({s for s, _ in rs})
+        for key, title, fmt in (("fpr", "FPR on 10^7 random 31-mers", "%.2g"),
+                                ("insert_gkmers_s", "insert Gk-mers/s (k-mer starts)", "%.0f"),
+                                ("query_gkmers_s", "query Gk-mers/s (k-mer starts)", "%.0f")):
+            out.append("\nH = %d: %s ('*' = compiled kernel set)\n" % (H, title))
+            out.append("| s \\ m | " + " | ".join(str(m) for m in ms) + " |")
+            out.append("|---|" + "---:|" * len(ms))
+            for s_ in ss:
+                cells = []
+                for m in ms:
+                    r = rs.get((s_, m))
+                    cells.append("" if r is None else (fmt % r[key]) + ("*" if r["specialized"] else ""))
+                out.append("| %d | " % s_ + " | ".join(cells) + " |")
+    return "\n".join(out)
+
+
 def table(rows) -> str:
     lines = ["| kind | s | m | H | insert Gk-mers/s | query Gk-mers/s | FPR (random 31-mers) | specialized |",
              "|---|---|---|---|---:|---:|---:|---|"]
@@ -132,8 +170,12 @@ if __name__ == "__main__":
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--grid", action="store_true",
                     help="instead: the s-, m- and H-slices through (s, m, H) = (28, 16, 4)")
+    ap.add_argument("--grid2d", action="store_true",
+                    help="instead: the full s = 16..31 x m = 8..31 grid at each H of --h-values")
+    ap.add_argument("--h-values", default="4,8,12,16", help="H values of --grid2d (comma-separated)")
     a = ap.parse_args()
     t0 = time.time()
-    rows = run(a.probe_n, a.reps, grid=a.grid)
-    print(table(rows))
+    rows = run(a.probe_n, a.reps, grid=a.grid, grid2d=a.grid2d,
+               h_values=tuple(int(x) for x in a.h_values.split(",")))
+    print(grid_tables(rows) if a.grid2d else table(rows))
     print("sweep wall time %.1f s" % (time.time() - t0), file=sys.stderr)

@@ -187,12 +187,14 @@ def test_sweep_instantiations(m):
 GRID_SLICES = ([(31, 16, s, 4) for s in (16, 17, 18, 19, 20, 21, 22, 23, 25, 27, 29, 31)]
                + [(31, m, 28, 4) for m in (8, 9, 10, 11, 13, 14, 15, 17, 18, 19, 21, 22, 23, 24, 25, 26, 27, 28,
                                           29, 30, 31)]
-               + [(31, 16, 28, H) for H in (1, 5, 8, 16)])
+               + [(31, 16, 28, H) for H in (1, 5, 8, 16)]
+               + [(31, m, s, 4) for s in (23, 24, 25, 26) for m in (21, 22, 23)])
 
 
 def test_grid_slices():
-    """Every set of the s-, m- and H-slices through the operating point is
-    specialized and bit-exact on a short genome, reads and probes."""
+    """Every set of the s-, m- and H-slices through the operating point, and
+    of the lowest-FPR block of the (s, m) grid, is specialized and bit-exact
+    on a short genome, reads and probes."""
     genome = S.genome_with_repeats(30000, seed_genome=90)
     reads = S.short_read_set(genome, 200)
     gs = S.to_ascii(genome)
@@ -382,3 +384,48 @@ def test_query_gaps_at_lane_and_wave_boundaries():
             a[p:p + L] = b"N" * min(L, n - p)
         seq = bytes(a)
         _run_pair(params, 2**15, [seq[: n // 2]], [seq, seq[1:], seq[31:], seq[2016 + 5:]])
+
+
+SLIDE_PARAMS = [(32, 1, 32, 3), (32, 32, 1, 5), (31, 24, 27, 4), (20, 7, 11, 9), (31, 19, 22, 12), (2, 1, 2, 1),
+                (31, 17, 24, 8)]
+
+
+@pytest.mark.parametrize("params", SLIDE_PARAMS)
+def test_sliding_kernels(params):
+    """Parameter sets without a compiled set run the run-time sliding
+    kernels: 65 - max(w, z) k-mers per wave step (33 at w = 32 or z = 32),
+    tasks of 2048 k-mer starts.  Filter words and every answer bit equal the
+    oracle's on noisy input whose lengths straddle the step and task
+    boundaries, on a poly-A run across steps and tasks, all-'N' and 'N'
+    every 37 bases, over several inserts into one filter."""
+    k, m, s, H = params
+    w, z = k - m + 1, k - s + 1
+    E = 65 - max(w, z)
+    rng = np.random.default_rng(61 + sum(params))
+    lens = [0, 1, k - 1, k, k + 1, E + k - 1, E + k, 2048 + k - 2, 2048 + k - 1, 2048 + k, 4096 + E + k, 100_003]
+    ins = [_noisy(rng, L) for L in lens[:6]] + [b"A" * 6000, _noisy(rng, 30_000)]
+    every37 = bytearray(T.random_dna(rng, 9000))
+    for i in range(0, len(every37), 37):
+        every37[i] = ord("N")
+    qs = [_noisy(rng, L) for L in lens] + [b"A" * 6000, b"N" * 500, bytes(every37)] + ins[-2:]
+    g, _ = _run_pair(params, 2**16, ins, qs)
+    assert not g.specialized
+
+
+def test_sliding_kernels_many_tasks():
+    """A 140 Mbp insert and a 20 Mbp query on a run-time parameter set: more
+    tasks than the grid's waves (the grid-stride loop); full filter and every
+    answer bit against the threaded oracle."""
+    params = (31, 24, 27, 4)
+    codes = S.genome_with_repeats(140_000_000, seed_genome=21)
+    genome = S.to_ascii(codes)
+    reads = S.short_read_set(codes, 130_000)  # half sampled from this genome
+    del codes
+    g = G.gpu_filter(params, 2**30)
+    o = G.oracle_filter(params, 2**30)
+    assert not g.specialized
+    g.insert_seq(G.to_dev(genome))
+    o.insert_seq_mt(genome)
+    G.assert_words_equal(g.words(), o.words(), "sliding insert, 140 Mbp")
+    got = G.dev_bits_to_np(g.query_seq(G.to_dev(reads)))
+    G.assert_words_equal(got, o.query_seq_mt(reads), "sliding query, 20 Mbp")
