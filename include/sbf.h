@@ -370,6 +370,16 @@ int sbf_membench_shard_reads(const uint64_t* d_table, uint64_t nshard, uint64_t 
  * record.  Modifies the table. */
 int sbf_membench_shard_ors(uint64_t* d_table, uint64_t nshard, uint64_t n, uint64_t seed, void* stream);
 
+/* Random 32-byte OR-updates of each operation's shard, four adjacent lanes
+ * with one 64-bit update each, in the form `mode` selects: bits 0-1 = 0 a
+ * device-scope atomic OR (as sbf_membench_shard_ors), 1 a workgroup-scope
+ * atomic OR, 2 a plain load, OR and store (not atomic: concurrent updates of
+ * one word can be lost; it measures a rate, not a filter); bit 2 confines the
+ * shards of workgroup b to the eighth of the table numbered b mod 8 (needs
+ * nshard >= 8).  Modifies the table.  SBF_EINVAL for other modes. */
+int sbf_membench_shard_rmw(uint64_t* d_table, uint64_t nshard, uint64_t n, uint64_t seed, uint32_t mode,
+                           void* stream);
+
 /* VALU issue rate: 8192 workgroups of 256 lanes, each lane running `iters`
  * rounds of eight independent instructions of one form (kind 0: v_xor_b32 on
  * VGPRs, the two-operand 32-bit logic/add/shift forms; kind 1:

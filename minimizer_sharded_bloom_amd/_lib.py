@@ -68,6 +68,7 @@ SIGNATURES = {
     "sbf_query_fastx": (_int, [_p, ctypes.c_char_p, _p, _p, _u64, ctypes.POINTER(SbfFastxStats)]),
     "sbf_membench_shard_reads": (_int, [_p, _u64, _u64, _u64, _p, _p]),
     "sbf_membench_shard_ors": (_int, [_p, _u64, _u64, _u64, _p]),
+    "sbf_membench_shard_rmw": (_int, [_p, _u64, _u64, _u64, _u32, _p]),
     "sbf_membench_valu": (_int, [_u32, _u64, _p, _p]),
     "sbf_strerror": (ctypes.c_char_p, [_int]),
     "sbf_last_error": (ctypes.c_char_p, []),

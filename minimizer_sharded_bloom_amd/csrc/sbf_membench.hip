@@ -82,6 +82,33 @@ __global__ __launch_bounds__(256) void shard_ors_kernel(uint64_t* __restrict__ t
     }
 }
 
+// Random 32-byte OR-updates in one of several forms (four adjacent lanes per
+// operation, lane q updates word q): MODE 0 a 64-bit atomic OR at device
+// scope, 1 the same at workgroup scope, 2 a plain load, OR and store (not
+// atomic: concurrent updates of one word may be lost; a rate only).  PART
+// confines the shards of workgroup b to the eighth of the table numbered
+// b mod 8, the eighth its XCD would own under round-robin dispatch.
+template <int MODE, bool PART>
+__global__ __launch_bounds__(256) void shard_rmw_kernel(uint64_t* __restrict__ table, uint64_t mask, uint64_t n,
+                                                        uint64_t seed)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * (blockDim.x / 4u);
+    const uint32_t q = threadIdx.x & 3u;
+    const uint64_t part = (mask + 1u) / 8u;
+    for (uint64_t j = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) / 4u; j < n; j += stride) {
+        const uint64_t h = op_hash(seed, j);
+        const uint64_t shard = PART ? (blockIdx.x % 8u) * part + (h & (part - 1u)) : (h & mask);
+        uint64_t* p = table + 4u * shard + q;
+        const uint64_t v = 1ull << ((h >> 58) ^ q);
+        if constexpr (MODE == 0)
+            __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else if constexpr (MODE == 1)
+            __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        else
+            *p = *p | v;
+    }
+}
+
 uint32_t grid_for(uint64_t threads)
 {
     uint64_t b = (threads + 255) / 256;
@@ -136,6 +163,30 @@ int sbf_membench_shard_ors(uint64_t* d_table, uint64_t nshard, uint64_t n, uint6
     (void)hipGetLastError();  // report this launch's error, not an earlier call's
     hipLaunchKernelGGL(sbf::shard_ors_kernel, dim3(sbf::grid_for(4 * n)), dim3(256), 0, (hipStream_t)stream, d_table,
                        nshard - 1, n, seed);
+    return hipGetLastError() == hipSuccess ? SBF_OK : SBF_EDEVICE;
+}
+
+int sbf_membench_shard_rmw(uint64_t* d_table, uint64_t nshard, uint64_t n, uint64_t seed, uint32_t mode,
+                           void* stream)
+{
+    const uint32_t form = mode & 3u;
+    const bool part = (mode & 4u) != 0;
+    if (!d_table || !sbf::pow2(nshard) || form > 2u || (mode & ~7u) || (part && nshard < 8))
+        return SBF_EINVAL;
+    if (n == 0)
+        return SBF_OK;
+    (void)hipGetLastError();  // report this launch's error, not an earlier call's
+    const dim3 grid(sbf::grid_for(4 * n)), block(256);
+    hipStream_t st = (hipStream_t)stream;
+    const uint64_t mask = nshard - 1;
+    switch (mode) {
+    case 0: hipLaunchKernelGGL((sbf::shard_rmw_kernel<0, false>), grid, block, 0, st, d_table, mask, n, seed); break;
+    case 1: hipLaunchKernelGGL((sbf::shard_rmw_kernel<1, false>), grid, block, 0, st, d_table, mask, n, seed); break;
+    case 2: hipLaunchKernelGGL((sbf::shard_rmw_kernel<2, false>), grid, block, 0, st, d_table, mask, n, seed); break;
+    case 4: hipLaunchKernelGGL((sbf::shard_rmw_kernel<0, true>), grid, block, 0, st, d_table, mask, n, seed); break;
+    case 5: hipLaunchKernelGGL((sbf::shard_rmw_kernel<1, true>), grid, block, 0, st, d_table, mask, n, seed); break;
+    default: hipLaunchKernelGGL((sbf::shard_rmw_kernel<2, true>), grid, block, 0, st, d_table, mask, n, seed); break;
+    }
     return hipGetLastError() == hipSuccess ? SBF_OK : SBF_EDEVICE;
 }
 

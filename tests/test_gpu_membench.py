@@ -42,3 +42,41 @@ def test_valu_rate_kernels_run():
         assert L.sbf_membench_valu(kind, 16, sink.data_ptr(), None) == _lib.SBF_OK
     torch.cuda.synchronize()
     assert int(sink.item()) == 0
+
+
+def test_update_forms_stay_in_bounds():
+    """sbf_membench_shard_rmw in every form stays inside its table; the
+    device-scope atomic form sets the same words as sbf_membench_shard_ors
+    for the same seed, the other whole-table forms a subset of them; the
+    partitioned forms touch every eighth of the table; bad modes and sizes
+    are refused."""
+    torch = G.torch_cuda()
+    L = M.lib()
+    nsh, guard, n = 1 << 10, 4096, 3000
+    ref = torch.zeros(4 * nsh, dtype=torch.int64, device="cuda")
+    assert L.sbf_membench_shard_ors(ref.data_ptr(), nsh, n, 11, None) == _lib.SBF_OK
+    torch.cuda.synchronize()
+    want = ref.cpu().numpy().view(np.uint64)
+    for mode in (0, 1, 2, 4, 5, 6):
+        buf = torch.zeros(4 * nsh + 2 * guard, dtype=torch.int64, device="cuda")
+        table = buf.data_ptr() + 8 * guard
+        assert L.sbf_membench_shard_rmw(table, nsh, n, 11, mode, None) == _lib.SBF_OK
+        torch.cuda.synchronize()
+        h = buf.cpu().numpy().view(np.uint64)
+        assert not h[:guard].any() and not h[guard + 4 * nsh:].any(), mode
+        sh = h[guard:guard + 4 * nsh]
+        if mode == 0:
+            assert (sh == want).all(), mode
+        elif mode in (1, 2):
+            # workgroup scope is atomic only within a workgroup, and a plain
+            # update not at all: bits may be lost, never invented
+            assert not (sh & ~want).any(), mode
+            assert sh.any(), mode
+        else:
+            eighths = sh.reshape(8, -1).any(axis=1)
+            assert eighths.all(), mode
+    table = ref.data_ptr()
+    for bad in (3, 7, 8, 16):
+        assert L.sbf_membench_shard_rmw(table, nsh, 10, 1, bad, None) == _lib.SBF_EINVAL
+    assert L.sbf_membench_shard_rmw(table, 4, 10, 1, 4, None) == _lib.SBF_EINVAL
+    assert L.sbf_membench_shard_rmw(table, 1000, 10, 1, 0, None) == _lib.SBF_EINVAL
