@@ -93,6 +93,35 @@ def alu_ops_per_kmer(kind: str) -> float:
     return float(sum(FRONT.values()) + sum(TAIL[kind].values()))
 
 
+# How many of those instructions are of the forms that issue every 4 clocks,
+# half the rate of the simple two-operand 32-bit forms (measured on the
+# device: 64-bit shifts, compares and multiply-adds, 32-bit multiplies,
+# alignbit, perm, v_cndmask, VOPC compares, DPP moves and anything reading an
+# SGPR; xor/or/and/bitop3/shift-by-immediate on VGPRs issue every 2).  Per
+# item of FRONT and TAIL, in the same order: the m-mer window is one
+# alignbit; h_min two 64-bit multiply-adds (plus a move and a fold xor);
+# the sliding minimum's 64-bit compares and selects all; the shard mask reads
+# an SGPR; the s-mer window two alignbits; h_s its 64-bit add of G, three
+# 64-bit shifts and both multiplies (2 mul_lo + mad_u64 + add3 each); the bit
+# masks four 64-bit shifts; the doubling ORs none; the run bookkeeping a
+# compare and a carry-in add.
+FRONT_4CLK = (1, 2, 9, 1, 2, 12, 4, 0, 2)
+TAIL_4CLK = {
+    "query": (5,),                 # four 64-bit compares and the carry-in add; the bitop3s issue every 2
+    "query_text": (5, 0.91),       # + per base: the multiply and perm of the code gather, perms of the flags
+    "insert": (0, 1.5),            # ORs and bitop3s every 2; the record flush's atomics and address math
+}
+
+
+def alu_issue_slots_per_kmer(kind: str) -> float:
+    """The algorithmic instructions of alu_ops_per_kmer in 2-clock issue
+    slots: a 4-clock form occupies two.  Against the same peak (one slot =
+    one lane-instruction of the 2-clock forms) this is the share of the
+    VALU's issue capacity the algorithm itself needs."""
+    assert len(FRONT_4CLK) == len(FRONT) and len(TAIL_4CLK[kind]) == len(TAIL[kind])
+    return alu_ops_per_kmer(kind) + float(sum(FRONT_4CLK) + sum(TAIL_4CLK[kind]))
+
+
 # Other alphabets: the DNA kernels' work per k-mer start (windows cut from a
 # packed stream, here 5- or 6-bit symbols packed in registers) plus decoding
 # the symbol from ASCII in the kernel's text front end.
@@ -524,10 +553,12 @@ def main():
         extra = {} if tr is None else {"traffic_fetch": tr["fetch"], "traffic_write": tr["write"],
                                        "traffic_source": tr["source"],
                                        "traffic_per_valid_kmer": tr["bytes"] / (vk_r if kind == "query" else vk_g)}
+        slots = rate * alu_issue_slots_per_kmer(model)
         return (dict({"bound": "alu", "achieved": alu / 1e12, "peak": ALU_PEAK / 1e12,
                       "unit": "T lane-instr/s", "frac": alu / ALU_PEAK, "traffic": traffic,
                       "kernel": kind, "per_valid_kmer_ops": alu_ops_per_kmer(model),
-                      "ms_per_launch": phase[kind]}, **extra),
+                      "per_valid_kmer_issue_slots": alu_issue_slots_per_kmer(model),
+                      "issue_slot_frac": slots / ALU_PEAK, "ms_per_launch": phase[kind]}, **extra),
                 dict({"bound": "hbm", "achieved": mem / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                       "frac": mem / HBM_PEAK, "traffic": traffic, "kernel": kind,
                       "per_valid_kmer_bytes": _bytes_per_kmer(model), "ms_per_launch": phase[kind]}, **extra))

@@ -41,6 +41,10 @@ def test_roofline_models():
     assert bench._bytes_per_kmer("query_text") == pytest.approx(1.0 + 0.125 + 32 * runs)
     assert bench._bytes_per_kmer("insert") == pytest.approx(0.375 + 64 * runs)
     assert bench.ALU_PEAK == pytest.approx(256 * 4 * 32 * 2.4e9)
+    # issue slots: every 4-clock form counts twice
+    assert bench.alu_issue_slots_per_kmer("query") == pytest.approx(65.0 + 33 + 5)
+    assert bench.alu_issue_slots_per_kmer("query_text") == pytest.approx(67.66 + 33 + 5.91)
+    assert bench.alu_issue_slots_per_kmer("insert") == pytest.approx(69.5 + 33 + 1.5)
 
 
 def test_more_than_one_gpu_is_refused():
