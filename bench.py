@@ -216,6 +216,18 @@ def measured_traffic(workload: str, kernel: str, sha: str):
     return None
 
 
+def filter_level(nbytes: int) -> str:
+    """Where a filter of nbytes lives once warm: within the 4 MB L2 of one
+    XCD ("l2": every XCD sees the whole filter), within the 256 MB MALL
+    ("mall"), else HBM ("hbm"); the memory fraction is against the 8 TB/s
+    HBM peak in every case, and is only a bound for "hbm"."""
+    if nbytes <= 4 << 20:
+        return "l2"
+    if nbytes <= 256 << 20:
+        return "mall"
+    return "hbm"
+
+
 def valid_kmer_count(text, k: int, alpha: str = "dna", chunk: int = 3 << 26) -> int:
     """k-mer starts whose k symbols are all valid (positions with an invalid
     symbol, e.g. a record separator, are not): the throughput count of valid
@@ -561,7 +573,8 @@ def main():
                       "issue_slot_frac": slots / ALU_PEAK, "ms_per_launch": phase[kind]}, **extra),
                 dict({"bound": "hbm", "achieved": mem / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                       "frac": mem / HBM_PEAK, "traffic": traffic, "kernel": kind,
-                      "per_valid_kmer_bytes": _bytes_per_kmer(model), "ms_per_launch": phase[kind]}, **extra))
+                      "per_valid_kmer_bytes": _bytes_per_kmer(model), "ms_per_launch": phase[kind],
+                      "filter_resides": filter_level(w["bits"] // 8)}, **extra))
 
     def binding(kind, rate):
         """The two ceilings of one kernel, the binding one (higher fraction)

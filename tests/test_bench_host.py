@@ -56,3 +56,14 @@ def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120, cwd=root)
     assert p.returncode == 2 and "one GPU" in p.stderr, (p.returncode, p.stderr[-500:])
+
+
+def test_filter_level():
+    """The memory row names the level the filter lives in: 1 MiB in one
+    XCD's L2, 8 MiB (configuration 2) and 128 MiB in the MALL, 512 MiB
+    (configuration 3) and 4 GiB (configuration 5) in HBM."""
+    assert bench.filter_level(1 << 20) == "l2"
+    assert bench.filter_level(8 << 20) == "mall"
+    assert bench.filter_level(128 << 20) == "mall"
+    assert bench.filter_level(512 << 20) == "hbm"
+    assert bench.filter_level(4 << 30) == "hbm"
