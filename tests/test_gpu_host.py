@@ -31,6 +31,25 @@ def test_host_pipeline_chunks(chunk):
     G.assert_words_equal(got, o.query_seq(reads), "host query, chunk %d" % chunk)
 
 
+@pytest.mark.parametrize("params", [(31, 24, 27, 4), (25, 9, 20, 12)])
+def test_host_pipeline_runtime_parameters(params):
+    """Parameter sets without a compiled set (run-time sliding kernels)
+    through the chunked host pipeline, with chunks that are not multiples of
+    a wave step: filter words and every answer bit equal the oracle's."""
+    g = S.to_ascii(S.genome_with_repeats(400_000, seed_genome=23))
+    reads = S.short_read_set(S.genome_with_repeats(400_000, seed_genome=23), 4_000)
+    for chunk in (64, 5000, 1 << 20):
+        f = G.gpu_filter(params, 2**20)
+        assert not f.specialized
+        f.set_staging(chunk)
+        o = G.oracle_filter(params, 2**20)
+        f.insert_seq(g.tobytes())
+        o.insert_seq(g)
+        G.assert_words_equal(f.words(), o.words(), "host insert %s, chunk %d" % (params, chunk))
+        G.assert_words_equal(f.query_seq(reads.tobytes()), o.query_seq(reads),
+                             "host query %s, chunk %d" % (params, chunk))
+
+
 @pytest.mark.parametrize("extra", [-1, 0, 1, 63, 64, 65])
 def test_host_pipeline_boundary_lengths(extra):
     """Lengths around whole chunks: n chunks of 4096 k-mer starts + k - 1 + extra."""
