@@ -103,7 +103,9 @@ struct Alphabet<SBF_ALPHABET_TRIPLET> {
 
 // Parameters of one kernel instance: compile-time (K, M, S, H nonzero, every
 // loop unrolled and every mask index static) or, with zeros, taken from the
-// run-time Params (the same code with run-time loops).
+// run-time Params (the same code with run-time loops).  A run-time instance
+// can still fix H alone (K = M = S = 0, H nonzero), so that the bit-address
+// and mask loop unrolls with static word indices.
 template <int A, int K, int M, int S, int H>
 struct ACfg {
     static constexpr int kAlpha = A;
@@ -166,6 +168,7 @@ __device__ __forceinline__ bool wave_step(const SeqArgs& a, const Params& P, uin
 
     const uint64_t h = hash_s(vs);
     mk[0] = mk[1] = mk[2] = mk[3] = 0;
+#pragma unroll
     for (uint32_t j = 0; j < H; ++j) {
         const uint64_t bit = 1ull << bit_addr_rt(h, j, H);
 #pragma unroll
@@ -404,6 +407,32 @@ const AlphaEntry kAlphaTable[] = {
     {kT, 7, 3, 7, 2, &make_alpha_spec<kT, 7, 3, 7, 2>},
 };
 
+// Run-time kernels of one alphabet, with H fixed at compile time for
+// 1 <= H <= 16 and taken at run time above.
+template <uint32_t A>
+KernelSet alpha_runtime(uint32_t H)
+{
+    switch (H) {
+    case 1: return make_alpha<ACfg<A, 0, 0, 0, 1>>();
+    case 2: return make_alpha<ACfg<A, 0, 0, 0, 2>>();
+    case 3: return make_alpha<ACfg<A, 0, 0, 0, 3>>();
+    case 4: return make_alpha<ACfg<A, 0, 0, 0, 4>>();
+    case 5: return make_alpha<ACfg<A, 0, 0, 0, 5>>();
+    case 6: return make_alpha<ACfg<A, 0, 0, 0, 6>>();
+    case 7: return make_alpha<ACfg<A, 0, 0, 0, 7>>();
+    case 8: return make_alpha<ACfg<A, 0, 0, 0, 8>>();
+    case 9: return make_alpha<ACfg<A, 0, 0, 0, 9>>();
+    case 10: return make_alpha<ACfg<A, 0, 0, 0, 10>>();
+    case 11: return make_alpha<ACfg<A, 0, 0, 0, 11>>();
+    case 12: return make_alpha<ACfg<A, 0, 0, 0, 12>>();
+    case 13: return make_alpha<ACfg<A, 0, 0, 0, 13>>();
+    case 14: return make_alpha<ACfg<A, 0, 0, 0, 14>>();
+    case 15: return make_alpha<ACfg<A, 0, 0, 0, 15>>();
+    case 16: return make_alpha<ACfg<A, 0, 0, 0, 16>>();
+    default: return make_alpha<ACfg<A, 0, 0, 0, 0>>();
+    }
+}
+
 }  // namespace
 
 KernelSet alpha_kernels(const Params& P)
@@ -411,7 +440,7 @@ KernelSet alpha_kernels(const Params& P)
     for (const AlphaEntry& e : kAlphaTable)
         if (e.alpha == P.alpha && e.k == P.k && e.m == P.m && e.s == P.s && e.H == P.H)
             return e.make();
-    return P.alpha == SBF_ALPHABET_TRIPLET ? make_alpha<ACfg<kT, 0, 0, 0, 0>>() : make_alpha<ACfg<kP, 0, 0, 0, 0>>();
+    return P.alpha == SBF_ALPHABET_TRIPLET ? alpha_runtime<kT>(P.H) : alpha_runtime<kP>(P.H);
 }
 
 }  // namespace sbf
