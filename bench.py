@@ -355,7 +355,7 @@ def parse():
     ap.add_argument("--alphabet", default="dna", choices=["dna", "protein", "triplet"],
                     help="dna (default, --workload applies) or the protein / DNA-triplet workload")
     ap.add_argument("--probe-n", type=int, default=10_000_000)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline in seconds (0 disables it)")
     ap.add_argument("--no-membench", dest="membench", action="store_false",
                     help="skip the matched-ceiling microbenchmarks (random shard reads / OR-updates) run after timing")
