@@ -727,7 +727,7 @@ __device__ __forceinline__ bool continues_previous(uint32_t vk, const uint32_t (
 // whose answers the validity bits clear.
 template <class C>
 __device__ __forceinline__ uint32_t query_records(uint32_t vk, const uint32_t (&shard)[C::KL], uint32_t lane,
-                                                  uint32_t (&rec)[C::KL])
+                                                  uint32_t (&rec)[C::KL], uint32_t& gs_out, uint32_t& first_out)
 {
     constexpr uint32_t all = C::KL == 32 ? 0xFFFFFFFFu : (1u << C::KL) - 1u;
     const uint32_t st = run_starts<C>(vk, shard);
@@ -742,7 +742,27 @@ __device__ __forceinline__ uint32_t query_records(uint32_t vk, const uint32_t (&
 #pragma unroll
     for (int i = 0; i < C::KL; ++i)
         rec[i] = __popc(gs & ((2u << i) - 1u)) + first;
+    gs_out = gs;
+    first_out = first;
     return __builtin_amdgcn_readlane(incl, 63);
+}
+
+// Gap records point at shard 0.  The k-mers of a gap wrote the keys of
+// invalid windows to it; each of those would cost the gather a line from
+// HBM, while shard 0 stays in L2 after its first load.  The answers of a gap
+// are cleared by the validity bits whatever its record holds.  Runs after the
+// k-mers' own writes (LDS writes of one wave land in program order).
+template <class C>
+__device__ __forceinline__ void point_gaps_at_shard0(uint32_t* idx, uint32_t vk, uint32_t gs, uint32_t first)
+{
+    constexpr uint32_t all = C::KL == 32 ? 0xFFFFFFFFu : (1u << C::KL) - 1u;
+    const uint32_t g = ~vk & all;
+    uint32_t gst = g & ~(g << 1);  // first k-mer of each gap piece in the lane
+    while (gst) {
+        const uint32_t b = (uint32_t)__builtin_ctz(gst);
+        idx[__popc(gs & ((2u << b) - 1u)) + first] = 0u;
+        gst &= gst - 1u;
+    }
 }
 
 template <class C>
@@ -957,11 +977,13 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
         uint32_t shard[C::KL];
         lane_shards<C>(D, shard);
         // pass A: segment and gap records, shard indices into LDS
-        total = query_records<C>(vk, shard, c.lane, rec);
+        uint32_t gs, first;
+        total = query_records<C>(vk, shard, c.lane, rec, gs, first);
         if (total <= (uint32_t)kQuerySlots) {
 #pragma unroll
             for (int i = 0; i < C::KL; ++i)
                 lds.idx[wv][rec[i]] = shard[i];
+            point_gaps_at_shard0<C>(lds.idx[wv], vk, gs, first);
         }
     }
     uint32_t bits;

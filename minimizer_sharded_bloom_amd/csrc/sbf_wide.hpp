@@ -170,11 +170,13 @@ __global__ __launch_bounds__(256) void wide_query_kernel(SeqArgs a)
     {
         uint32_t shard[C::KL];
         lane_shards<C>(D, shard);
-        total = query_records<C>(vk, shard, c.lane, rec);
+        uint32_t gs, first;
+        total = query_records<C>(vk, shard, c.lane, rec, gs, first);
         if (total <= (uint32_t)kSlotsW) {
 #pragma unroll
             for (int i = 0; i < C::KL; ++i)
                 lds.idx[wv][rec[i]] = shard[i];
+            point_gaps_at_shard0<C>(lds.idx[wv], vk, gs, first);
         }
     }
     uint32_t bits;
