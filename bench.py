@@ -10,8 +10,11 @@ Genomic Sequence Data on Modern GPUs"):
     query every read k-mer              (Algorithm 2), the query kernel
                                         decoding the reads' ASCII itself
     false-positive probe of n random k-mers (§V-D)
-at k=31, m=16, s=28, H=4.  (`--query-input packed` packs the reads in a pass
-of their own and queries the packed codes instead.)  Every launch goes to
+at k=31, m=16, s=28, H=4.  The reads of workloads 2-4 all have 150 bases:
+they are queried read by read (sbf_query_reads), so no lane works on the
+starts that straddle two reads.  (`--query-input text` queries them as one
+'N'-joined sequence instead, `--query-input packed` packs that sequence in a
+pass of its own and queries the packed codes.)  Every launch goes to
 torch's current stream, so the torch events recorded between launches time
 each kernel on the stream it runs on.
 
@@ -362,9 +365,11 @@ def parse():
     ap.add_argument("--data-cache", default="",
                     help="directory for the generated inputs: saved there (.npy) after generating, memory-mapped "
                          "from there when present (profiled runs then skip the forking long-read generator)")
-    ap.add_argument("--query-input", default="text", choices=["text", "packed"],
-                    help="DNA reads as the query gets them: text (default; sbf_query_seq, whose kernel decodes "
-                         "the ASCII itself) or packed (sbf_pack, then sbf_query_packed)")
+    ap.add_argument("--query-input", default="auto", choices=["auto", "reads", "text", "packed"],
+                    help="DNA reads as the query gets them: reads (sbf_query_reads, the per-read query of the "
+                         "equal-length reads of workloads 2-4), text (sbf_query_seq of the reads joined by 'N', "
+                         "whose kernel decodes the ASCII itself) or packed (sbf_pack, then sbf_query_packed); "
+                         "auto (default) = reads where the workload's reads have one length, else text")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 256 MiB device copy (elementwise kernel) whose "
                          "FETCH_SIZE/WRITE_SIZE counters scale the filter kernels' counters")
@@ -497,8 +502,18 @@ def main():
     out = torch.empty(f.num_answer_words(LR), dtype=torch.int64, device=dev)
     hits = torch.zeros(1, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
-    text_query = a.query_input == "text"
-    assert not text_query or reads.data_ptr() % 16 == 0, "the ASCII query path needs 16-byte-aligned reads"
+    # workloads 2-4 query reads of one length joined by one 'N'; workload 5's
+    # long reads vary in length
+    fixed_reads = a.workload in (2, 3, 4)
+    qin = a.query_input if a.query_input != "auto" else ("reads" if fixed_reads else "text")
+    if qin == "reads":
+        assert fixed_reads, "--query-input reads needs equal-length reads (workloads 2-4)"
+        RL, RS = S.READ_LEN, S.READ_LEN + 1
+        n_reads = (LR + 1) // RS
+        assert (n_reads - 1) * RS + RL == LR, "reads are not %d bases at a stride of %d" % (RL, RS)
+        rout = torch.empty(n_reads * f.read_answer_words(RL), dtype=torch.int32, device=dev)
+    text_query = qin in ("text", "reads")  # no packing pass for the reads
+    assert qin != "text" or reads.data_ptr() % 16 == 0, "the ASCII query path needs 16-byte-aligned reads"
     if text_query:
         names = ["clear", "pack_genome", "insert", "query", "probe"]
     else:
@@ -519,7 +534,9 @@ def main():
         mark()
         M.check(lib.sbf_insert_packed(f.handle, g_codes.data_ptr(), g_valid.data_ptr(), LG, sp), "insert")
         mark()
-        if text_query:
+        if qin == "reads":
+            M.check(lib.sbf_query_reads(f.handle, reads.data_ptr(), n_reads, RL, RS, rout.data_ptr(), sp), "query")
+        elif text_query:
             M.check(lib.sbf_query_seq(f.handle, reads.data_ptr(), LR, out.data_ptr(), M.SBF_DEVICE, sp), "query")
         else:
             M.check(lib.sbf_pack(reads.data_ptr(), LR, r_codes.data_ptr(), r_valid.data_ptr(), sp), "pack")
@@ -602,7 +619,7 @@ def main():
         "prewarm": {"seconds": a.prewarm_s, "steps": a.prewarm_steps},
         "pack_gbases_s": round((LG + (0 if text_query else LR))
                                / ((phase["pack_genome"] + phase.get("pack_reads", 0.0)) * 1e-3) / 1e9, 3),
-        "query_input": a.query_input,
+        "query_input": qin,
         "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
         "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},
         "phase_ms_median": {k2: round(v, 4) for k2, v in phase_med.items()},

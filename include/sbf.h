@@ -250,6 +250,31 @@ int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits,
                   uint32_t flags, void* stream);
 
 /*
+ * Per-read query of a device batch of n_reads equal-length DNA reads
+ * ([cuSBF] §IV-E, Algorithm 2, on the read sets of §V-A; the page queries
+ * records joined by an invalid separator, §IV-F, and so spends work on the
+ * k-1 starts per record that straddle two records; here no read's work
+ * crosses into the next).  Read r is the read_len bytes at
+ * d_reads + r * stride (stride >= read_len when n_reads > 1, at most 2^25;
+ * the bytes between reads never enter an answer).  Each read has
+ * nkr = read_len - k + 1 k-mers and gets rch = ceil(nkr / 32) uint32_t words
+ * of d_out (device, n_reads * rch words, fully overwritten): read r's k-mer
+ * 32j + i is bit i of word rch * r + j, 1 iff present (every s-mer hits, as
+ * in sbf_query_seq); k-mers with a non-ACGT base answer 0, and so do the bits
+ * past nkr.  The answers equal sbf_query_seq's bits r * stride + i of the
+ * batch queried as one sequence, for i < nkr.  Asynchronous on `stream`.  A
+ * DNA filter whose query takes 32 k-mers per lane (as in sbf_query_seq) runs
+ * a per-read kernel with no staging; any other DNA filter queries the batch
+ * as one sequence into a handle-owned answer buffer (grown on demand, which
+ * synchronizes `stream`) and cuts the reads' words out of it.  n_reads = 0 or
+ * read_len < k is a no-op.  Errors: SBF_EINVAL (NULL handle or pointer,
+ * stride < read_len, stride > 2^25, n_reads * rch >= 2^32), SBF_EUNSUPPORTED
+ * (protein and triplet filters), SBF_ENOMEM, SBF_EDEVICE.
+ */
+int sbf_query_reads(sbf_t* h, const char* d_reads, uint64_t n_reads, uint32_t read_len,
+                    uint64_t stride, uint32_t* d_out, void* stream);
+
+/*
  * Chunk size of the host pipeline ([cuSBF] §IV-G host staging; the page gives
  * no chunk size), in k-mer starts (rounded up to a multiple
  * of 64; 64 <= chunk_bases <= 2^34; default 2^26).  Each of the three slots

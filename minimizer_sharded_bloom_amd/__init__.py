@@ -217,6 +217,33 @@ class SuperBloomFilter:
                   "sbf_query_seq")
         return res
 
+    def read_answer_words(self, read_len: int) -> int:
+        """uint32 answer words per read of sbf_query_reads: ceil((read_len - k + 1) / 32)."""
+        nkr = read_len - self.k + 1
+        return (nkr + 31) // 32 if nkr > 0 else 0
+
+    def query_reads(self, reads, n_reads: int, read_len: int, stride: int = None, out=None, stream=None):
+        """Per-read query of n_reads equal-length reads in a device uint8
+        tensor (read r = bytes r*stride .. r*stride + read_len - 1; stride
+        defaults to read_len + 1, reads joined by one separator).  Returns an
+        int32 CUDA tensor (n_reads, ceil((read_len - k + 1) / 32)): k-mer
+        32j + i of read r at bit i of [r, j] (asynchronous)."""
+        torch = _torch()
+        if stride is None:
+            stride = read_len + 1
+        a = _device_bytes(reads, stream)
+        need = (n_reads - 1) * stride + read_len if n_reads else 0
+        if a.numel() < need:
+            raise ValueError("reads holds %d bytes; %d reads of %d at stride %d need %d"
+                             % (a.numel(), n_reads, read_len, stride, need))
+        rch = self.read_answer_words(read_len)
+        if out is None:
+            out = torch.empty((n_reads, rch), dtype=torch.int32, device=a.device)
+        if n_reads and rch:
+            check(lib().sbf_query_reads(self._h, a.data_ptr(), n_reads, read_len, stride, out.data_ptr(),
+                                        _stream_ptr(stream)), "sbf_query_reads")
+        return out
+
     # ---- packed (device-resident) calls ---------------------------------------
     def insert_packed(self, codes, valid, length: int, stream=None):
         check(lib().sbf_insert_packed(self._h, codes.data_ptr(), valid.data_ptr(), length, _stream_ptr(stream)),

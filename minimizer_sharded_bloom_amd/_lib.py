@@ -57,6 +57,7 @@ SIGNATURES = {
     "sbf_insert_seq": (_int, [_p, _p, _u64, _u32, _p]),
     "sbf_insert_seq_noalloc": (_int, [_p, _p, _u64, _p]),
     "sbf_query_seq": (_int, [_p, _p, _u64, _p, _u32, _p]),
+    "sbf_query_reads": (_int, [_p, _p, _u64, _u32, _u64, _p, _p]),
     "sbf_fpr_probe": (_int, [_p, _u64, _u64, ctypes.POINTER(_u64)]),
     "sbf_fpr_probe_device": (_int, [_p, _u64, _u64, _p, _p]),
     "sbf_set_staging": (_int, [_p, _u64]),

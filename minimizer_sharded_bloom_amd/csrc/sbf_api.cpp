@@ -64,6 +64,10 @@ constexpr uint64_t kNoAllocMaxBases = 1ull << 26;
 constexpr uint64_t kNoAllocCodeWords = kNoAllocMaxBases / 16;   // 16 bases per code word
 constexpr uint64_t kNoAllocValidWords = kNoAllocMaxBases / 32;  // 32 bases per validity word
 
+// sbf_query_reads: the per-read kernel addresses a wave's bytes with 32-bit
+// offsets from its first read, at most 65 strides away
+constexpr uint64_t kReadsMaxStride = 1ull << 25;
+
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 uint32_t* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, null until resolved
@@ -264,6 +268,28 @@ int grow_packed(sbf_t* h, uint64_t len, hipStream_t st)
     return SBF_OK;
 }
 
+// Answer words of a read batch queried as one sequence.
+int grow_rbits(sbf_t* h, uint64_t words, hipStream_t st)
+{
+    if (h->rbits_cap >= words)
+        return SBF_OK;
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return fail_hip(e, "answer staging");
+    if (h->d_rbits)
+        (void)hipFree(h->d_rbits);
+    h->d_rbits = nullptr;
+    h->rbits_cap = 0;
+    const uint64_t n = words + words / 4 + 64;
+    e = hipMalloc(reinterpret_cast<void**>(&h->d_rbits), 8 * n);
+    if (e != hipSuccess) {
+        h->d_rbits = nullptr;
+        return fail_hip(e, "hipMalloc(answer staging)");
+    }
+    h->rbits_cap = n;
+    return SBF_OK;
+}
+
 // Pack a device-resident sequence into the handle's staging buffers.
 int stage_packed(sbf_t* h, const char* d_seq, uint64_t len, hipStream_t st)
 {
@@ -320,6 +346,8 @@ int sbf_destroy(sbf_t* h)
         (void)hipFree(h->d_codes);
     if (h->d_valid)
         (void)hipFree(h->d_valid);
+    if (h->d_rbits)
+        (void)hipFree(h->d_rbits);
     sbf::free_host_staging(h->host);
     delete h;
     if (e != hipSuccess)
@@ -536,6 +564,57 @@ int sbf_query_seq(sbf_t* h, const char* seq, uint64_t len, uint64_t* out_bits, u
     hipError_t e = h->ks.query(a, h->P);
     if (e != hipSuccess)
         return fail_hip(e, "query");
+    ok();
+    return SBF_OK;
+}
+
+int sbf_query_reads(sbf_t* h, const char* d_reads, uint64_t n_reads, uint32_t read_len, uint64_t stride,
+                    uint32_t* d_out, void* stream)
+{
+    if (!h)
+        return fail(SBF_EINVAL, "handle is NULL");
+    if (h->P.alpha != SBF_ALPHABET_DNA)
+        return fail(SBF_EUNSUPPORTED, "sbf_query_reads: DNA filters only (query protein or triplet text with sbf_query_seq)");
+    if (n_reads == 0 || read_len < h->P.k) {
+        ok();
+        return SBF_OK;
+    }
+    if (!d_reads || !d_out)
+        return fail(SBF_EINVAL, "NULL argument");
+    if (n_reads > 1 && stride < read_len)
+        return fail(SBF_EINVAL, "sbf_query_reads: stride is less than read_len");
+    if (stride > kReadsMaxStride)
+        return fail(SBF_EINVAL, "sbf_query_reads: stride exceeds 2^25 bytes");
+    const uint32_t nkr = read_len - h->P.k + 1;  // k-mers per read
+    const uint32_t rch = (nkr + 31) / 32;        // answer words per read
+    if (n_reads > 0xFFFFFFFFull / rch)
+        return fail(SBF_EINVAL, "sbf_query_reads: the batch has 2^32 or more answer words; split it");
+    int rc = set_device(h);
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const uint64_t nbytes = (n_reads - 1) * stride + read_len;
+    hipError_t e;
+    if (h->ks.query_reads) {
+        sbf::SeqArgs a = text_args(h, d_reads, nbytes, reinterpret_cast<uint64_t*>(d_out), st);
+        a.nk = n_reads * rch;
+        a.stride = stride;
+        a.rlen = read_len;
+        a.rchunks = rch;
+        e = h->ks.query_reads(a, h->P);
+    } else {
+        // the batch as one sequence, then each read's answers cut out of it
+        const uint64_t nbw = (nbytes - h->P.k + 1 + 63) / 64;
+        rc = grow_rbits(h, nbw, st);
+        if (rc)
+            return rc;
+        rc = sbf_query_seq(h, d_reads, nbytes, h->d_rbits, SBF_DEVICE, stream);
+        if (rc)
+            return rc;
+        e = sbf::launch_reads_remap(h->d_rbits, nbw, n_reads, stride, nkr, rch, d_out, st);
+    }
+    if (e != hipSuccess)
+        return fail_hip(e, "query_reads");
     ok();
     return SBF_OK;
 }

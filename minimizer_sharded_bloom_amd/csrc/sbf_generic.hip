@@ -99,6 +99,39 @@ hipError_t launch_fill_zero(uint64_t* p, uint64_t nwords, hipStream_t st)
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void reads_remap_kernel(const uint64_t* __restrict__ bits, uint64_t nbw, uint64_t n,
+                                                          uint64_t stride, uint32_t nkr, uint32_t rch,
+                                                          uint32_t* __restrict__ out)
+{
+    const uint64_t total = n * rch;
+    const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total; g += step) {
+        const uint64_t r = g / rch, j = g - r * rch;
+        const uint64_t b = r * stride + 32u * j;  // bit of the read's k-mer 32j
+        const uint64_t w = b >> 6;
+        const uint32_t sh = (uint32_t)(b & 63u);
+        uint64_t v = bits[w] >> sh;
+        if (sh > 32u && w + 1 < nbw)
+            v |= bits[w + 1] << (64u - sh);
+        const uint32_t left = nkr - 32u * (uint32_t)j;
+        out[g] = (uint32_t)v & (left >= 32u ? 0xFFFFFFFFu : (1u << left) - 1u);
+    }
+}
+
+hipError_t launch_reads_remap(const uint64_t* bits, uint64_t nbw, uint64_t n, uint64_t stride, uint32_t nkr,
+                              uint32_t rch, uint32_t* out, hipStream_t st)
+{
+    const uint64_t total = n * rch;
+    if (total == 0)
+        return hipSuccess;
+    uint64_t blocks = (total + 255) / 256;
+    if (blocks > 65536)
+        blocks = 65536;
+    hipLaunchKernelGGL(reads_remap_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, bits, nbw, n, stride, nkr, rch,
+                       out);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Generic per-k-mer kernels (runtime k, m, s, H; SBF and BBF).
 // ---------------------------------------------------------------------------

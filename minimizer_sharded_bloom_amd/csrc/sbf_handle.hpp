@@ -44,6 +44,10 @@ struct sbf_handle {
     uint32_t* d_codes;
     uint32_t* d_valid;
     uint64_t packed_cap;  // bases
+    // answers of a read batch queried as one sequence (sbf_query_reads
+    // without a per-read kernel)
+    uint64_t* d_rbits;
+    uint64_t rbits_cap;  // words
     unsigned long long* d_hits;
     sbf::HostStaging host;
 };

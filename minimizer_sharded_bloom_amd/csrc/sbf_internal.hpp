@@ -23,6 +23,13 @@ struct SeqArgs {
     // So does a DNA query through KernelSet::query_text (base j = byte j).
     const char* text;
     uint64_t nsym;
+    // Per-read DNA query (KernelSet::query_reads): read r is the rlen bytes
+    // at text + r * stride, nsym the bytes from text to the last read's end,
+    // nk the batch's chunks (rchunks = ceil((rlen - k + 1) / 32) per read),
+    // out the answer words (uint32_t[nk]).
+    uint64_t stride;
+    uint32_t rlen;
+    uint32_t rchunks;
 };
 
 // Arguments of one false-positive probe launch.
@@ -52,6 +59,10 @@ struct KernelSet {
     // DNA query straight from ASCII (SeqArgs.text, nsym = bytes), or null:
     // the sequence is then packed first and `query` reads the codes
     SeqLaunch query_text = nullptr;
+    // Per-read DNA query of a batch of equal-length reads (SeqArgs.stride,
+    // rlen, rchunks), or null: sbf_query_reads then queries the batch as one
+    // sequence and cuts each read's answers out of it
+    SeqLaunch query_reads = nullptr;
 };
 
 // One row of a specialization table (see sbf_spec_list.hpp).
@@ -71,5 +82,12 @@ KernelSet alpha_kernels(const Params& P);
 // Small utility launches.
 hipError_t launch_pack(const char* ascii, uint64_t len, uint32_t* codes, uint32_t* valid, hipStream_t st);
 hipError_t launch_fill_zero(uint64_t* p, uint64_t nwords, hipStream_t st);
+// Answers of a batch of n equal-length reads (read r at byte r * stride,
+// nkr = len - k + 1 k-mers each) cut out of the answers of the batch queried
+// as one sequence (bits: one bit per k-mer start, nbw words): read r gets
+// words rch * r .. rch * r + rch - 1 of out, k-mer 32j + i at bit i of word
+// j, 0 past its last k-mer.
+hipError_t launch_reads_remap(const uint64_t* bits, uint64_t nbw, uint64_t n, uint64_t stride, uint32_t nkr,
+                              uint32_t rch, uint32_t* out, hipStream_t st);
 
 }  // namespace sbf

@@ -40,13 +40,17 @@ namespace sbf {
 // SBF_ALPHABET_TRIPLET (6-bit codons of three bases) read the ASCII text and
 // pack each lane's symbols in registers ([cuSBF] §IV-A); kDnaText reads DNA
 // as ASCII and packs it in registers the same way, so a query of a device
-// sequence needs no separate packing pass.
+// sequence needs no separate packing pass.  kDnaReads is the per-read query
+// of a batch of equal-length DNA reads: a lane takes 32 k-mer starts of one
+// read and reads all 62 bases they span itself (no halo from lane l+1).
 constexpr int kDnaText = 3;
+constexpr int kDnaReads = 4;
 
 template <int K_, int M_, int S_, int H_, int KL_ = 0, int A_ = 0>
 struct Cfg {
     static constexpr int k = K_, m = M_, s = S_, H = H_, A = A_;
-    static constexpr bool BASES = A_ == 0 || A_ == kDnaText;   // 2-bit bases, 16 per stream word
+    static constexpr bool BASES = A_ == 0 || A_ == kDnaText || A_ == kDnaReads;  // 2-bit bases, 16 per word
+    static constexpr bool OWN_HALO = A_ == kDnaReads;  // the lane hashes the positions past its own
     static constexpr int B = BASES ? 2 : (A_ == 1 ? 5 : 6);  // bits per symbol
     static constexpr int W = k - m + 1;    // m-mers per k-mer
     static constexpr int Z = k - s + 1;    // s-mers per k-mer (Findere z+1)
@@ -56,11 +60,14 @@ struct Cfg {
     static_assert(HALO <= KL, "halo must come from the next lane alone");
     static_assert(BASES || KL == 16, "protein and triplet text: 16 symbols per lane");
     static_assert(A_ != kDnaText || KL == 32, "DNA text: 32 bases per lane, whose s-mers end within lane l+1");
+    static_assert(A_ != kDnaReads || KL == 32, "DNA reads: 32 k-mers per lane, 64 bases in four stream words");
     static constexpr int LW = 63;                    // working lanes per wave
     static constexpr int KPW = KL * LW;              // k-mers per wave
-    // stream words per lane: for DNA KL/16 own code words and two of halo;
-    // for text, enough for every window of the own positions plus one word
-    static constexpr int ND = BASES ? KL / 16 + 2 : ((KL + (m > s ? m : s) - 1) * B + 31) / 32 + 1;
+    // stream words per lane: for DNA KL/16 own code words and two of halo
+    // (per-read query: its 64 bases and a zero word, which the 32-bit window
+    // of its last m-mer may reach); for text, enough for every window of the
+    // own positions plus one word
+    static constexpr int ND = A_ == kDnaReads ? 5 : BASES ? KL / 16 + 2 : ((KL + (m > s ? m : s) - 1) * B + 31) / 32 + 1;
     static constexpr int NS = H < 4 ? H : 4;         // sectors in use
     static constexpr int NM = KL + W - 1;            // m-mer hashes per lane
     static constexpr int NZ = KL + Z - 1;            // s-mer hashes per lane
@@ -180,8 +187,12 @@ __device__ __forceinline__ void lane_shards(const uint32_t (&D)[C::ND], uint32_t
     static_for<0, KL>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         hm[i] = hash_min(bases_at<i, C::m, C::B>(D));
-        if constexpr (i < W - 1)
-            hm[KL + i] = from_next_lane(hm[i]);  // lane l+1's position i is this lane's KL+i
+        if constexpr (i < W - 1) {
+            if constexpr (C::OWN_HALO)
+                hm[KL + i] = hash_min(bases_at<KL + i, C::m, C::B>(D));
+            else
+                hm[KL + i] = from_next_lane(hm[i]);  // lane l+1's position i is this lane's KL+i
+        }
     });
     if constexpr (W == 1) {
 #pragma unroll
@@ -271,6 +282,40 @@ __device__ __forceinline__ uint32_t letter_valid4(uint32_t w)
     return (((f >> 7) * 0x00204081u) >> 21) & 0xFu;  // bits 7, 15, 23, 31 -> 0..3
 }
 
+// 32 DNA bases in eight dwords of ASCII (first base in the low byte of q[0])
+// -> two stream words, first base most significant, and the returned
+// validity bits (bit j: base j).  Per dword: the 2-bit codes c, as in the
+// packing pass ((b >> 1) ^ (b >> 2)) & 3, gathered by one multiply into the
+// top byte, first base most significant; and the invalid bytes at bit 7: a
+// byte is valid iff, with bits 5 (case) and 7 cleared, it equals the letter
+// of its code, and bit 7 is clear.  d7 has bits 5 and 7 of every byte clear,
+// so d7 + 0x7F per byte sets bit 7 exactly for a nonzero byte and never
+// carries.
+__device__ __forceinline__ uint32_t decode_dna32(const uint32_t* q, uint32_t& S0, uint32_t& S1)
+{
+    uint32_t P[8], Zi[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+        const uint32_t w = q[d];
+        const uint32_t cc = __builtin_amdgcn_bitop3_b32(w >> 1, w >> 2, 0x03030303u, 0x28);  // (x ^ y) & m
+        P[d] = cc * 0x40100401u;  // code of byte j at bits 31-2j .. 30-2j
+        const uint32_t e = __builtin_amdgcn_perm(0x74676361u, 0x74676361u, cc);  // "acgt" by code
+        const uint32_t d7 = __builtin_amdgcn_bitop3_b32(w, 0xA0A0A0A0u, e, 0x12);     // ~k & (w ^ e)
+        Zi[d] = __builtin_amdgcn_bitop3_b32(d7 + 0x7F7F7F7Fu, w, 0x80808080u, 0xA8);  // (x | w) & m
+    }
+    // code words: the top bytes of four products each
+    S0 = __builtin_amdgcn_perm(P[0], P[1], 0x07030C0Cu) | __builtin_amdgcn_perm(P[2], P[3], 0x0C0C0703u);
+    S1 = __builtin_amdgcn_perm(P[4], P[5], 0x07030C0Cu) | __builtin_amdgcn_perm(P[6], P[7], 0x0C0C0703u);
+    // invalid flags of two dwords (bits 3,11,19,27 and 7,15,23,31) times
+    // 1 + 2^7 + 2^14 + 2^21 land in bits 24..31 in base order, every
+    // other partial product below bit 24 and on a bit of its own
+    uint32_t V[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        V[g] = ((Zi[2 * g] >> 4) | Zi[2 * g + 1]) * 0x00204081u;
+    return ~(__builtin_amdgcn_perm(V[1], V[0], 0x0C0C0703u) | __builtin_amdgcn_perm(V[3], V[2], 0x07030C0Cu));
+}
+
 // Text front end (protein and triplet filters, and DNA text): the lane's KL
 // symbols (16 letters or codons, or 32 bases) are read from the ASCII text
 // and packed in registers, first symbol most significant, B bits each, as
@@ -342,37 +387,8 @@ __device__ __forceinline__ uint32_t load_text(const SeqArgs& a, const LaneCtx<C>
             }
         }
     } else if constexpr (C::A == kDnaText) {
-        // 32 bases in eight dwords.  Per dword: the 2-bit codes c, as in the
-        // packing pass ((b >> 1) ^ (b >> 2)) & 3, gathered by one multiply
-        // into the top byte, first base most significant; and the invalid
-        // bytes at bit 7: a byte is valid iff, with bits 5 (case) and 7
-        // cleared, it equals the letter of its code, and bit 7 is clear.
-        // d7 has bits 5 and 7 of every byte clear, so d7 + 0x7F per byte
-        // sets bit 7 exactly for a nonzero byte and never carries.
         static_assert(NQ == 2 && OW == 2 && OR == 0, "32 bases per lane");
-        uint32_t P[8], Zi[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            const uint32_t w = q[d];
-            const uint32_t cc = __builtin_amdgcn_bitop3_b32(w >> 1, w >> 2, 0x03030303u, 0x28);  // (x ^ y) & m
-            P[d] = cc * 0x40100401u;  // code of byte j at bits 31-2j .. 30-2j
-            const uint32_t e = __builtin_amdgcn_perm(0x74676361u, 0x74676361u, cc);  // "acgt" by code
-            const uint32_t d7 = __builtin_amdgcn_bitop3_b32(w, 0xA0A0A0A0u, e, 0x12);     // ~k & (w ^ e)
-            Zi[d] = __builtin_amdgcn_bitop3_b32(d7 + 0x7F7F7F7Fu, w, 0x80808080u, 0xA8);  // (x | w) & m
-        }
-        // code words: the top bytes of four products each
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            S[u] = __builtin_amdgcn_perm(P[4 * u], P[4 * u + 1], 0x07030C0Cu) |
-                   __builtin_amdgcn_perm(P[4 * u + 2], P[4 * u + 3], 0x0C0C0703u);
-        // invalid flags of two dwords (bits 3,11,19,27 and 7,15,23,31) times
-        // 1 + 2^7 + 2^14 + 2^21 land in bits 24..31 in base order, every
-        // other partial product below bit 24 and on a bit of its own
-        uint32_t V[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-            V[g] = ((Zi[2 * g] >> 4) | Zi[2 * g + 1]) * 0x00204081u;
-        own_valid = ~(__builtin_amdgcn_perm(V[1], V[0], 0x0C0C0703u) | __builtin_amdgcn_perm(V[3], V[2], 0x07030C0Cu));
+        own_valid = decode_dna32(q, S[0], S[1]);
     } else {
         uint32_t cb[4 * NQ], nb[4 * NQ];
 #pragma unroll
@@ -456,12 +472,14 @@ __device__ __forceinline__ void smer_masks(uint64_t h, uint64_t (&mk)[4])
 
 // Ordering point between the unrolled steps of a pass: the packed bases pass
 // through an empty asm, so no hash of a later step can be computed before it
-// (which would keep every hash live at once).
-template <int NDW>
+// (which would keep every hash live at once).  The first N words (all by
+// default) pass; a constant word left out stays a constant.
+template <int N = 0, int NDW>
 __device__ __forceinline__ void step_fence(uint32_t (&D)[NDW])
 {
+    constexpr int n = N > 0 && N < NDW ? N : NDW;
 #pragma unroll
-    for (int j = 0; j < NDW; ++j)
+    for (int j = 0; j < n; ++j)
         asm volatile("" : "+v"(D[j])::"memory");
 }
 
@@ -497,7 +515,10 @@ struct FindereMasks {
         });
         static_for<0, Z - 1>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
-            halo[q] = from_next_lane(head[q]);
+            if constexpr (C::OWN_HALO)
+                halo[q] = smer_hash_at<C, C::KL + q>(D);
+            else
+                halo[q] = from_next_lane(head[q]);
         });
     }
 
@@ -725,16 +746,22 @@ __device__ __forceinline__ bool continues_previous(uint32_t vk, const uint32_t (
 // shard index into its own record with no branch and no validity test: a
 // segment's k-mers all carry its shard, and a gap's record holds some index
 // whose answers the validity bits clear.
-template <class C>
+// With GAPS false (the per-read query, whose lanes end in the invalid starts
+// past their read's last k-mer) only a gap that opens a lane gets a record
+// of its own, one that continues no other lane's; every other gap shares the
+// record of the segment before it.  The k-mers must then write their records
+// last k-mer first, so that the segment's own first k-mer writes last.
+template <class C, bool GAPS = true>
 __device__ __forceinline__ uint32_t query_records(uint32_t vk, const uint32_t (&shard)[C::KL], uint32_t lane,
                                                   uint32_t (&rec)[C::KL], uint32_t& gs_out, uint32_t& first_out)
 {
     constexpr uint32_t all = C::KL == 32 ? 0xFFFFFFFFu : (1u << C::KL) - 1u;
     const uint32_t st = run_starts<C>(vk, shard);
-    const uint32_t gs = (st | (~vk & ((vk << 1) | 1u))) & all;  // plus gap starts
+    const uint32_t gs = GAPS ? (st | (~vk & ((vk << 1) | 1u))) & all  // plus gap starts
+                             : st | (~vk & 1u);                       // plus a gap that opens the lane
     const uint32_t prev_valid = from_prev_lane((vk >> (C::KL - 1)) & 1u);
     const uint32_t prev_shard = from_prev_lane(shard[C::KL - 1]);
-    const bool cont = lane > 0 && ((vk & 1u) ? (prev_valid && shard[0] == prev_shard) : !prev_valid);
+    const bool cont = lane > 0 && ((vk & 1u) ? (prev_valid && shard[0] == prev_shard) : (GAPS && !prev_valid));
     const uint32_t cin = cont ? 1u : 0u;
     const uint32_t n = __popc(gs) - cin;
     const uint32_t incl = wave_incl_scan(n);
@@ -898,7 +925,7 @@ __device__ __forceinline__ uint64_t kmer_at_lane(const uint32_t (&D)[C::ND], int
         const bool hi16 = i >= 16;
         d0 = hi16 ? D[1] : D[0];
         d1 = hi16 ? D[2] : D[1];
-        d2 = hi16 ? D[C::ND - 1] : D[2];
+        d2 = hi16 ? D[C::ND > 3 ? 3 : C::ND - 1] : D[2];  // i >= 16 only when KL = 32 (ND >= 4)
         r = 2u * (uint32_t)(i & 15);
     } else {
         const uint32_t off = (uint32_t)i * C::B, wa = off >> 5;
@@ -951,26 +978,20 @@ __device__ __forceinline__ uint32_t query_lane_direct(const SeqArgs& a, const ui
     return bits;
 }
 
-// Query ([cuSBF] Algorithm 2).  Pass A: shards, validity, and per k-mer the
-// LDS record of its segment (a run of one shard) or gap (a run of invalid
+// Query ([cuSBF] Algorithm 2) of one lane's KL k-mers, given its stream
+// words D and valid-k-mer bits vk.  Pass A: shards and per k-mer the LDS
+// record of its segment (a run of one shard) or gap (a run of invalid
 // k-mers), numbered from 1 across the wave.  Every k-mer writes its shard
 // index to its record: all k-mers of a segment carry the same shard, so no
 // write needs a branch.  Gather: the wave loads every record's 32-byte shard
 // into LDS at once, two lanes per shard.  Pass B (straight-line): k-mer i
 // reads the words of its record and is present iff every bit of its Findere
-// mask R_i is set: (R_i & W) == R_i; invalid k-mers answer 0.
-template <class C>
-__global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
+// mask R_i is set: (R_i & W) == R_i; invalid k-mers answer 0.  Returns the
+// answer bits (bit i: k-mer i).
+template <class C, bool GAPS, int NSLOT>
+__device__ __forceinline__ uint32_t query_lane(const SeqArgs& a, uint32_t (&D)[C::ND], uint32_t vk,
+                                               uint32_t lane, int wv, WaveLdsN<NSLOT>& lds)
 {
-    constexpr int kQuerySlots = query_slots<C>();
-    __shared__ WaveLdsN<kQuerySlots> lds;
-    const uint64_t nk_pad = round64(a.nk);
-    const LaneCtx<C> c = lane_ctx<C>(nk_pad);
-    if (!c.live)
-        return;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar LDS bases
-    uint32_t D[C::ND];
-    const uint32_t vk = lane_input<C>(a, c, D);
     uint32_t total;
     uint32_t rec[C::KL];
     {
@@ -978,19 +999,26 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
         lane_shards<C>(D, shard);
         // pass A: segment and gap records, shard indices into LDS
         uint32_t gs, first;
-        total = query_records<C>(vk, shard, c.lane, rec, gs, first);
-        if (total <= (uint32_t)kQuerySlots) {
+        total = query_records<C, GAPS>(vk, shard, lane, rec, gs, first);
+        if (total <= (uint32_t)NSLOT) {
+            if constexpr (GAPS) {
 #pragma unroll
-            for (int i = 0; i < C::KL; ++i)
-                lds.idx[wv][rec[i]] = shard[i];
-            point_gaps_at_shard0<C>(lds.idx[wv], vk, gs, first);
+                for (int i = 0; i < C::KL; ++i)
+                    lds.idx[wv][rec[i]] = shard[i];
+                point_gaps_at_shard0<C>(lds.idx[wv], vk, gs, first);
+            } else {
+                // last k-mer first: a segment's first k-mer writes its record last
+#pragma unroll
+                for (int i = C::KL - 1; i >= 0; --i)
+                    lds.idx[wv][rec[i]] = shard[i];
+            }
         }
     }
     uint32_t bits;
-    if (total <= (uint32_t)kQuerySlots) {
+    if (total <= (uint32_t)NSLOT) {
         wave_lds_sync();
-        gather_records<32, kQuerySlots>(a.filter, a.shard_mask, lds.idx[wv], reinterpret_cast<char*>(&lds.words[wv][0][0]),
-                                        total, c.lane);
+        gather_records<32, NSLOT>(a.filter, a.shard_mask, lds.idx[wv], reinterpret_cast<char*>(&lds.words[wv][0][0]),
+                                  total, lane);
         wave_lds_sync();
 
         // pass B
@@ -1010,18 +1038,122 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
                 wq[3] = w23.y;
             }
             bits = shift_in(bits, lanes_present<C>(T0, T1, wq));  // k-mer i lands at bit KL-1-i
-            step_fence(D);
+            step_fence<C::OWN_HALO ? 4 : 0>(D);  // the per-read query's zero word stays a constant
         });
         bits = (__builtin_bitreverse32(bits) >> (32 - C::KL)) & vk;
     } else {
         bits = query_lane_direct<C>(a, D, vk);
     }
+    return bits;
+}
+
+// Query of a sequence: each lane answers KL consecutive k-mer starts.
+template <class C>
+__global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
+{
+    constexpr int kQuerySlots = query_slots<C>();
+    __shared__ WaveLdsN<kQuerySlots> lds;
+    const uint64_t nk_pad = round64(a.nk);
+    const LaneCtx<C> c = lane_ctx<C>(nk_pad);
+    if (!c.live)
+        return;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar LDS bases
+    uint32_t D[C::ND];
+    const uint32_t vk = lane_input<C>(a, c, D);
+    const uint32_t bits = query_lane<C, true>(a, D, vk, c.lane, wv, lds);
     if (c.lane < (uint32_t)C::LW && c.p0 < nk_pad) {
         if constexpr (C::KL == 16)
             reinterpret_cast<uint16_t*>(a.out)[c.p0 >> 4] = (uint16_t)bits;
         else
             reinterpret_cast<uint32_t*>(a.out)[c.p0 >> 5] = bits;
     }
+}
+
+// Per-read query input.  Lane g of the launch (g = 64 * wave + lane) takes
+// chunk c = g mod R of read r = g / R: the k-mer starts 32c .. 32c+31 of the
+// read.  It loads the 64 bytes from base 32c of the read (the 62 its k-mers
+// span, and two more) itself, as four stream words; nothing comes from lane
+// l+1.  Reads start anywhere: the lane loads the 17 aligned dwords around its
+// bytes and shifts them into place.  Returns the lane's valid-k-mer bits:
+// k-mer 32c+i is valid iff its k bases are and it is one of the read's
+// len - k + 1 k-mers.
+template <class C>
+__device__ __forceinline__ uint32_t reads_input(const SeqArgs& a, uint64_t g0, uint32_t lane, uint32_t (&D)[C::ND])
+{
+    static_assert(C::ND == 5, "64 bases per lane and a zero word");
+    // the batch holds fewer than 2^32 chunks and stride <= 2^25 bytes, so a
+    // wave's bytes lie within 65 strides of its first (host checks)
+    const uint32_t R = a.rchunks;
+    const uint32_t g = (uint32_t)g0 + lane;
+    const uint32_t r = g / R, c = g - r * R;
+    const uint32_t r0 = (uint32_t)g0 / R, c0 = (uint32_t)g0 - r0 * R;  // the wave's first chunk
+    // byte addresses relative to the dword below the wave's first byte
+    const uintptr_t first = reinterpret_cast<uintptr_t>(a.text) + (uint64_t)r0 * a.stride + 32u * c0;
+    const char* base = reinterpret_cast<const char*>(first & ~(uintptr_t)3);
+    const uint64_t end = reinterpret_cast<uintptr_t>(a.text) + a.nsym - reinterpret_cast<uintptr_t>(base);
+    const uint32_t nrec = end < 0xFFFFFFFFull ? (uint32_t)end : 0xFFFFFFFFu;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)nrec, 0x00020000);
+    const uint32_t lb = (uint32_t)(reinterpret_cast<uintptr_t>(a.text) + (uint64_t)r * a.stride + 32u * c -
+                                   reinterpret_cast<uintptr_t>(base));
+    const uint32_t o = lb & ~3u, sh = lb & 3u;
+    uint32_t q[17];
+    const bool whole = __builtin_amdgcn_ballot_w64(o + 68u > nrec) == 0;  // wave-uniform
+    if (whole) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(o + 16u * j), 0, 0);
+            q[4 * j] = v.x;
+            q[4 * j + 1] = v.y;
+            q[4 * j + 2] = v.z;
+            q[4 * j + 3] = v.w;
+        }
+        q[16] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (int)(o + 64u), 0, 0);
+    } else {
+        // a wave that reaches the end of the batch: byte loads, 0 past it
+#pragma unroll
+        for (int j = 0; j < 17; ++j) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)(o + 4u * j + b), 0, 0) << (8 * b);
+            q[j] = w;
+        }
+    }
+    uint32_t w[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        w[j] = __builtin_amdgcn_alignbyte(q[j + 1], q[j], sh);
+    const uint32_t v0 = decode_dna32(w, D[0], D[1]);
+    const uint32_t v1 = decode_dna32(w + 8, D[2], D[3]);
+    D[4] = 0;
+    const uint32_t v = (uint32_t)valid_starts<C::k>(v0 | ((uint64_t)v1 << 32));
+    const uint32_t left = a.rlen - (uint32_t)C::k + 1u - 32u * c;  // the read's k-mers from 32c on
+    uint32_t keep = left >= 32u ? 0xFFFFFFFFu : (1u << left) - 1u;
+    if (g >= a.nk)
+        keep = 0;
+    return v & keep;
+}
+
+// Per-read query of a batch of equal-length reads (lanes as in reads_input).
+// A lane's k-mers all lie in one read, so no lane spends work on the starts
+// that straddle two reads; the answers of read r are 32-bit words R*r ..
+// R*r + R-1, k-mer 32j + i at bit i of word j, 0 past the read's last k-mer.
+template <class C>
+__global__ __launch_bounds__(256) void sbf_query_reads_kernel(SeqArgs a)
+{
+    constexpr int kQuerySlots = query_slots<C>();
+    __shared__ WaveLdsN<kQuerySlots> lds;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t g0 = ((uint64_t)blockIdx.x * 4u + (uint32_t)wv) * 64u;
+    if (g0 >= a.nk)
+        return;
+    const uint32_t lane = threadIdx.x & 63u;
+    uint32_t D[C::ND];
+    const uint32_t vk = reads_input<C>(a, g0, lane, D);
+    const uint32_t bits = query_lane<C, false>(a, D, vk, lane, wv, lds);
+    if (g0 + lane < a.nk)
+        reinterpret_cast<uint32_t*>(a.out)[g0 + lane] = bits;
 }
 
 // [cuSBF] §V-D: n uniformly random k-mers from the SplitMix64 stream, each
@@ -1080,6 +1212,15 @@ hipError_t launch_query(const SeqArgs& a, const Params&)
     return hipGetLastError();
 }
 
+// a.nk counts the batch's chunks (R per read), one lane each
+template <class C>
+hipError_t launch_query_reads(const SeqArgs& a, const Params&)
+{
+    const uint64_t blocks = (a.nk + 255) / 256;
+    hipLaunchKernelGGL(sbf_query_reads_kernel<C>, dim3((uint32_t)blocks), dim3(256), 0, a.stream, a);
+    return hipGetLastError();
+}
+
 template <class C>
 hipError_t launch_probe(const ProbeArgs& a, const Params&)
 {
@@ -1108,8 +1249,10 @@ KernelSet spec_set()
     KernelSet ks;
     ks.insert = &launch_insert<C>;
     ks.query = &launch_query<CQ>;
-    if constexpr (kQ32)
+    if constexpr (kQ32) {
         ks.query_text = &launch_query<Cfg<K, M, S, H, 32, kDnaText>>;
+        ks.query_reads = &launch_query_reads<Cfg<K, M, S, H, 32, kDnaReads>>;
+    }
     ks.probe = &launch_probe<C>;
     ks.specialized = 1;
     return ks;

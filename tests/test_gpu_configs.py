@@ -73,6 +73,48 @@ def test_config3_full(cfg3):
     assert g.fpr_probe(1_000_000, 0x5EED) == o.fpr_probe(1_000_000, 0x5EED)
 
 
+def test_config3_reads(cfg3):
+    """The per-read query of configuration 3's 20 M reads (150 bases at a
+    stride of 151, one launch of the per-read kernel): every answer word
+    equals the bits that the one-sequence query gave the same k-mers (checked
+    against the oracle in test_config3_full), and 200 k seeded k-mers equal
+    the oracle's own answers."""
+    torch = G.torch_cuda()
+    g, o, reads, got = cfg3["g"], cfg3["o"], cfg3["reads"], cfg3["got"]
+    L, stride = S.READ_LEN, S.READ_LEN + 1
+    n = (reads.size + 1) // stride
+    assert (n - 1) * stride + L == reads.size
+    progress("config 3 per-read query of %d reads" % n)
+    res = g.query_reads(G.to_dev(reads), n, L, stride)
+    torch.cuda.synchronize()
+    res = res.cpu().numpy().view(np.uint32)
+    nkr = L - K + 1
+    R = (nkr + 31) // 32
+    assert res.shape == (n, R)
+    # the same bits cut out of the one-sequence answers, read by read
+    b = (np.arange(n, dtype=np.uint64)[:, None] * np.uint64(stride) + np.uint64(32) * np.arange(R, dtype=np.uint64)[None, :])
+    w = (b >> np.uint64(6)).astype(np.int64)
+    sh = b & np.uint64(63)
+    g2 = np.concatenate([got, np.zeros(1, dtype=np.uint64)])
+    v = g2[w] >> sh
+    hi = sh > np.uint64(32)
+    v[hi] |= g2[w[hi] + 1] << (np.uint64(64) - sh[hi])
+    left = nkr - 32 * np.arange(R)
+    mask = np.where(left >= 32, 0xFFFFFFFF, (1 << np.minimum(left, 31)) - 1).astype(np.uint64)
+    want = (v & mask[None, :]).astype(np.uint32)
+    bad = np.argwhere(res != want)
+    assert bad.size == 0, "per-read words differ: %d; first %s got %#x want %#x" % (
+        bad.shape[0], bad[0], int(res[tuple(bad[0])]), int(want[tuple(bad[0])]))
+    progress("config 3 per-read query equals the one-sequence query")
+    rng = np.random.default_rng(98)
+    r = rng.integers(0, n, 200_000)
+    i = rng.integers(0, nkr, 200_000)
+    bits = (res[r, i // 32] >> (i % 32).astype(np.uint32)) & 1
+    want1 = o.query_positions(reads, (r * stride + i).astype(np.uint64))
+    assert (bits.astype(np.uint8) == want1).all()
+    assert want1.sum() > 1000
+
+
 def _bit_slice(words: np.ndarray, start: int, n: int) -> np.ndarray:
     """Bits [start, start + n) of LSB-first uint64 words, as LSB-first words
     (bits past n zero)."""
