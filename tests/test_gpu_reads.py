@@ -15,10 +15,11 @@ from tests import helpers as T
 
 pytestmark = pytest.mark.gpu
 
-# (params, kind): the first four have a compiled 32-k-mer query (per-read
-# kernel; m = 8 and 12 reach furthest past a lane's own bases), the rest go
-# through the one-sequence path
-FAST = [((31, 16, 28, 4), "sbf"), ((31, 20, 24, 2), "sbf"), ((31, 12, 28, 4), "sbf"), ((31, 8, 28, 4), "sbf")]
+# (params, kind): the first five have a compiled 32-k-mer query (per-read
+# kernel; m = 8 and 12 reach furthest past a lane's own bases, k = 32 spans
+# 63 of its 64 bases), the rest go through the one-sequence path
+FAST = [((31, 16, 28, 4), "sbf"), ((31, 20, 24, 2), "sbf"), ((31, 12, 28, 4), "sbf"), ((31, 8, 28, 4), "sbf"),
+        ((32, 16, 28, 4), "sbf")]
 SLOW = [((31, 24, 27, 4), "sbf"), ((31, 0, 0, 4), "bbf"), ((31, 16, 28, 4), "wide")]
 
 
