@@ -5,8 +5,8 @@ One step = one pass of the whole path over one batch of device-resident
 synthetic input (the method of "cuSBF: A Minimizer-Aware Bloom Filter for
 Genomic Sequence Data on Modern GPUs"):
     clear the filter
-    pack the genome (ASCII -> 2-bit codes + validity)
-    insert every genome k-mer           (Algorithm 1)
+    insert every genome k-mer           (Algorithm 1), the insert kernel
+                                        decoding the genome's ASCII itself
     query every read k-mer              (Algorithm 2), the query kernel
                                         decoding the reads' ASCII itself
     false-positive probe of n random k-mers (§V-D)
@@ -14,7 +14,8 @@ at k=31, m=16, s=28, H=4.  The reads of workloads 2-4 all have 150 bases:
 they are queried read by read (sbf_query_reads), so no lane works on the
 starts that straddle two reads.  (`--query-input text` queries them as one
 'N'-joined sequence instead, `--query-input packed` packs that sequence in a
-pass of its own and queries the packed codes.)  Every launch goes to
+pass of its own and queries the packed codes; `--insert-input packed` packs
+the genome in a pass of its own before the insert.)  Every launch goes to
 torch's current stream, so the torch events recorded between launches time
 each kernel on the stream it runs on.
 
@@ -89,6 +90,10 @@ TAIL = {
                    "base from ASCII: 2 shifts + bitop3 code, multiply gather, letter lookup, "
                    "masked compare, add, flag (8 per 4 bases); 21 gathers per 32 bases": 2.66},
     "insert": {"T0|T1 and (Wr & keep) | t per half": 16, "record flush share (~0.12 runs/k-mer)": 1.5},
+    # an insert that decodes its genome from ASCII, the same per base
+    "insert_text": {"T0|T1 and (Wr & keep) | t per half": 16, "record flush share (~0.12 runs/k-mer)": 1.5,
+                    "base from ASCII: 2 shifts + bitop3 code, multiply gather, letter lookup, "
+                    "masked compare, add, flag (8 per 4 bases); 21 gathers per 32 bases": 2.66},
 }
 
 
@@ -113,6 +118,7 @@ TAIL_4CLK = {
     "query": (5,),                 # four 64-bit compares and the carry-in add; the bitop3s issue every 2
     "query_text": (5, 0.91),       # + per base: the multiply and perm of the code gather, perms of the flags
     "insert": (0, 1.5),            # ORs and bitop3s every 2; the record flush's atomics and address math
+    "insert_text": (0, 1.5, 0.91),
 }
 
 
@@ -161,6 +167,8 @@ def _bytes_per_kmer(kind: str, w: int = K - M_ + 1) -> float:
         return 1.0 + 0.125 + 32 * runs
     if kind == "query":
         return seq + 0.125 + 32 * runs
+    if kind == "insert_text":
+        return 1.0 + 64 * runs
     return seq + 64 * runs
 
 
@@ -370,6 +378,9 @@ def parse():
                          "equal-length reads of workloads 2-4), text (sbf_query_seq of the reads joined by 'N', "
                          "whose kernel decodes the ASCII itself) or packed (sbf_pack, then sbf_query_packed); "
                          "auto (default) = reads where the workload's reads have one length, else text")
+    ap.add_argument("--insert-input", default="text", choices=["text", "packed"],
+                    help="DNA genome as the insert gets it: text (default; sbf_insert_seq, whose kernel decodes "
+                         "the ASCII itself) or packed (sbf_pack, then sbf_insert_packed)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run one plain 256 MiB device copy (elementwise kernel) whose "
                          "FETCH_SIZE/WRITE_SIZE counters scale the filter kernels' counters")
@@ -514,10 +525,10 @@ def main():
         rout = torch.empty(n_reads * f.read_answer_words(RL), dtype=torch.int32, device=dev)
     text_query = qin in ("text", "reads")  # no packing pass for the reads
     assert qin != "text" or reads.data_ptr() % 16 == 0, "the ASCII query path needs 16-byte-aligned reads"
-    if text_query:
-        names = ["clear", "pack_genome", "insert", "query", "probe"]
-    else:
-        names = ["clear", "pack_genome", "insert", "pack_reads", "query", "probe"]
+    text_insert = a.insert_input == "text"
+    assert not text_insert or genome.data_ptr() % 16 == 0, "the ASCII insert path needs a 16-byte-aligned genome"
+    names = (["clear"] + ([] if text_insert else ["pack_genome"]) + ["insert"]
+             + ([] if text_query else ["pack_reads"]) + ["query", "probe"])
 
     def step(events, st):
         sp = st.cuda_stream
@@ -530,9 +541,12 @@ def main():
         mark()
         M.check(lib.sbf_clear(f.handle, sp), "clear")
         mark()
-        M.check(lib.sbf_pack(genome.data_ptr(), LG, g_codes.data_ptr(), g_valid.data_ptr(), sp), "pack")
-        mark()
-        M.check(lib.sbf_insert_packed(f.handle, g_codes.data_ptr(), g_valid.data_ptr(), LG, sp), "insert")
+        if text_insert:
+            M.check(lib.sbf_insert_seq(f.handle, genome.data_ptr(), LG, M.SBF_DEVICE, sp), "insert")
+        else:
+            M.check(lib.sbf_pack(genome.data_ptr(), LG, g_codes.data_ptr(), g_valid.data_ptr(), sp), "pack")
+            mark()
+            M.check(lib.sbf_insert_packed(f.handle, g_codes.data_ptr(), g_valid.data_ptr(), LG, sp), "insert")
         mark()
         if qin == "reads":
             M.check(lib.sbf_query_reads(f.handle, reads.data_ptr(), n_reads, RL, RS, rout.data_ptr(), sp), "query")
@@ -574,7 +588,7 @@ def main():
     wl = "cfg%d" % a.workload
 
     def roof(kind, rate):
-        model = "query_text" if kind == "query" and text_query else kind
+        model = kind + ("_text" if (text_query if kind == "query" else text_insert) else "")
         alu = rate * alu_ops_per_kmer(model)
         mem = rate * _bytes_per_kmer(model)
         tr = measured_traffic(wl, kind, sha)
@@ -617,8 +631,10 @@ def main():
         "query_starts_gkmers_s": round(nk_r / (phase["query"] * 1e-3) / 1e9, 3),
         "value_starts_gkmers_s": round((nk_g + nk_r + a.probe_n) / (ms_step * 1e-3) / 1e9, 3),
         "prewarm": {"seconds": a.prewarm_s, "steps": a.prewarm_steps},
-        "pack_gbases_s": round((LG + (0 if text_query else LR))
-                               / ((phase["pack_genome"] + phase.get("pack_reads", 0.0)) * 1e-3) / 1e9, 3),
+        "pack_gbases_s": (round(((0 if text_insert else LG) + (0 if text_query else LR))
+                                / ((phase.get("pack_genome", 0.0) + phase.get("pack_reads", 0.0)) * 1e-3) / 1e9, 3)
+                          if not (text_insert and text_query) else None),
+        "insert_input": a.insert_input,
         "query_input": qin,
         "probe_gkmers_s": round(a.probe_n / (phase["probe"] * 1e-3) / 1e9, 3),
         "phase_ms": {k2: round(v, 4) for k2, v in phase.items()},

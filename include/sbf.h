@@ -230,9 +230,12 @@ int sbf_query_packed(sbf_t* h, const uint32_t* d_codes, const uint32_t* d_valid,
  * work on `stream`
  * and the call synchronizes.  SBF_DEVICE: `seq` is device memory; packing
  * goes to the handle's staging buffer and the call is asynchronous on
- * `stream`.  Staging buffers grow on demand (growing synchronizes `stream`)
- * and stay allocated until sbf_destroy.  Protein and triplet filters read the
- * text itself (no packing; chunks overlap by k-1 symbols).
+ * `stream`, except that a DNA filter with a compiled parameter set reads a
+ * 16-byte-aligned device sequence as ASCII in the insert kernel itself (no
+ * packing pass, no staging; the same filter for any alignment).  Staging
+ * buffers grow on demand (growing synchronizes `stream`) and stay allocated
+ * until sbf_destroy.  Protein and triplet filters read the text itself (no
+ * packing; chunks overlap by k-1 symbols).
  */
 int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void* stream);
 

@@ -513,6 +513,14 @@ int sbf_insert_seq(sbf_t* h, const char* seq, uint64_t len, uint32_t flags, void
         ok();
         return SBF_OK;
     }
+    if (h->ks.insert_text && ((uintptr_t)seq & 15u) == 0) {
+        // the insert kernel reads the ASCII itself (16-byte loads per lane)
+        hipError_t e = h->ks.insert_text(text_args(h, seq, len, nullptr, st), h->P);
+        if (e != hipSuccess)
+            return fail_hip(e, "insert");
+        ok();
+        return SBF_OK;
+    }
     rc = stage_packed(h, seq, len, st);
     if (rc)
         return rc;

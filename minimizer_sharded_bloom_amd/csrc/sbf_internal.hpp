@@ -59,6 +59,8 @@ struct KernelSet {
     // DNA query straight from ASCII (SeqArgs.text, nsym = bytes), or null:
     // the sequence is then packed first and `query` reads the codes
     SeqLaunch query_text = nullptr;
+    // DNA insert straight from ASCII (SeqArgs.text, nsym = bytes), or null
+    SeqLaunch insert_text = nullptr;
     // Per-read DNA query of a batch of equal-length reads (SeqArgs.stride,
     // rlen, rchunks), or null: sbf_query_reads then queries the batch as one
     // sequence and cuts each read's answers out of it

@@ -39,8 +39,8 @@ namespace sbf {
 // 2-bit codes and validity bits; SBF_ALPHABET_PROTEIN (5-bit letters) and
 // SBF_ALPHABET_TRIPLET (6-bit codons of three bases) read the ASCII text and
 // pack each lane's symbols in registers ([cuSBF] §IV-A); kDnaText reads DNA
-// as ASCII and packs it in registers the same way, so a query of a device
-// sequence needs no separate packing pass.  kDnaReads is the per-read query
+// as ASCII and packs it in registers the same way, so an insert or query of
+// a device sequence needs no separate packing pass.  kDnaReads is the per-read query
 // of a batch of equal-length DNA reads: a lane takes 32 k-mer starts of one
 // read and reads all 62 bases they span itself (no halo from lane l+1).
 constexpr int kDnaText = 3;
@@ -59,7 +59,8 @@ struct Cfg {
     static_assert(KL == 16 || KL == 32, "16 or 32 k-mers per lane");
     static_assert(HALO <= KL, "halo must come from the next lane alone");
     static_assert(BASES || KL == 16, "protein and triplet text: 16 symbols per lane");
-    static_assert(A_ != kDnaText || KL == 32, "DNA text: 32 bases per lane, whose s-mers end within lane l+1");
+    // DNA text at 32 k-mers per lane takes lane l+1's bases by DPP, and its
+    // s-mers end within them; at 16 a lane loads its 48 bases itself
     static_assert(A_ != kDnaReads || KL == 32, "DNA reads: 32 k-mers per lane, 64 bases in four stream words");
     static constexpr int LW = 63;                    // working lanes per wave
     static constexpr int KPW = KL * LW;              // k-mers per wave
@@ -316,6 +317,75 @@ __device__ __forceinline__ uint32_t decode_dna32(const uint32_t* q, uint32_t& S0
     return ~(__builtin_amdgcn_perm(V[1], V[0], 0x0C0C0703u) | __builtin_amdgcn_perm(V[3], V[2], 0x07030C0Cu));
 }
 
+// 16 DNA bases in four dwords of ASCII -> one stream word and 16 validity
+// bits, as half of decode_dna32.
+__device__ __forceinline__ uint32_t decode_dna16(const uint32_t* q, uint32_t& S0)
+{
+    uint32_t P[4], Zi[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t w = q[d];
+        const uint32_t cc = __builtin_amdgcn_bitop3_b32(w >> 1, w >> 2, 0x03030303u, 0x28);
+        P[d] = cc * 0x40100401u;
+        const uint32_t e = __builtin_amdgcn_perm(0x74676361u, 0x74676361u, cc);
+        const uint32_t d7 = __builtin_amdgcn_bitop3_b32(w, 0xA0A0A0A0u, e, 0x12);
+        Zi[d] = __builtin_amdgcn_bitop3_b32(d7 + 0x7F7F7F7Fu, w, 0x80808080u, 0xA8);
+    }
+    S0 = __builtin_amdgcn_perm(P[0], P[1], 0x07030C0Cu) | __builtin_amdgcn_perm(P[2], P[3], 0x0C0C0703u);
+    const uint32_t V0 = ((Zi[0] >> 4) | Zi[1]) * 0x00204081u;
+    const uint32_t V1 = ((Zi[2] >> 4) | Zi[3]) * 0x00204081u;
+    return ~__builtin_amdgcn_perm(V1, V0, 0x0C0C0703u) & 0xFFFFu;
+}
+
+// DNA text at 16 k-mers per lane: the lane loads the 48 bytes from its first
+// base (three aligned 16-byte loads; neighbouring lanes' loads overlap and
+// meet in the caches) and decodes them into its three stream words: its 16
+// bases and the 32 that its k-mers reach past them.  Returns the lane's
+// valid-k-mer bits, as lane_valid does for packed input.
+template <class C>
+__device__ __forceinline__ uint32_t load_dna_text16(const SeqArgs& a, const LaneCtx<C>& c, uint32_t (&D)[C::ND])
+{
+    static_assert(C::KL == 16 && C::ND == 3 && C::KL + C::k - 1 <= 48, "16 k-mers, 48 bases per lane");
+    const uint64_t tb = a.nsym;
+    const uint64_t b0 = c.wstart;  // a multiple of 16 (KPW = 1008)
+    const uint64_t avail = tb > b0 ? tb - b0 : 0;
+    const uint32_t nrec = avail < 0xFFFFFFFFull ? (uint32_t)avail : 0xFFFFFFFFu;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.text + (b0 < tb ? b0 : tb)), (short)0,
+                                                      (int)nrec, 0x00020000);
+    const uint32_t off = 16u * c.lane;
+    uint32_t q[12];
+    if (avail >= 63ull * 16 + 48) {
+        // every byte of the wave lies before the end
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16u * j), 0, 0);
+            q[4 * j] = v.x;
+            q[4 * j + 1] = v.y;
+            q[4 * j + 2] = v.z;
+            q[4 * j + 3] = v.w;
+        }
+    } else {
+        // the wave that reaches the end: byte loads, 0 past the last base
+#pragma unroll
+        for (int j = 0; j < 12; ++j) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)(off + 4u * j + b), 0, 0) << (8 * b);
+            q[j] = w;
+        }
+    }
+    const uint32_t v0 = decode_dna32(q, D[0], D[1]);
+    const uint32_t v1 = decode_dna16(q + 8, D[2]);
+    const uint32_t v = (uint32_t)valid_starts<C::k>(v0 | ((uint64_t)v1 << 32));
+    const uint64_t rem = a.nk > c.p0 ? a.nk - c.p0 : 0;
+    uint32_t keep = rem >= 16u ? 0xFFFFu : (1u << rem) - 1u;
+    if (c.lane >= (uint32_t)C::LW)
+        keep = 0;
+    return v & keep;
+}
+
 // Text front end (protein and triplet filters, and DNA text): the lane's KL
 // symbols (16 letters or codons, or 32 bases) are read from the ASCII text
 // and packed in registers, first symbol most significant, B bits each, as
@@ -453,6 +523,8 @@ __device__ __forceinline__ uint32_t lane_input(const SeqArgs& a, const LaneCtx<C
     if constexpr (C::A == 0) {
         load_codes<C>(a, c, D);
         return lane_valid<C>(a, c);
+    } else if constexpr (C::A == kDnaText && C::KL == 16) {
+        return load_dna_text16<C>(a, c, D);
     } else {
         return load_text<C>(a, c, D);
     }
@@ -1248,6 +1320,7 @@ KernelSet spec_set()
     using CQ = Cfg<K, M, S, H, (kQ32 ? 32 : 0)>;
     KernelSet ks;
     ks.insert = &launch_insert<C>;
+    ks.insert_text = &launch_insert<Cfg<K, M, S, H, 0, kDnaText>>;
     ks.query = &launch_query<CQ>;
     if constexpr (kQ32) {
         ks.query_text = &launch_query<Cfg<K, M, S, H, 32, kDnaText>>;

@@ -358,6 +358,51 @@ def test_query_inputs_agree(params):
         G.assert_words_equal(got, want, "packed n=%d %s" % (n, params))
 
 
+@pytest.mark.parametrize("params", [MAIN, (31, 12, 28, 4), (31, 20, 24, 2)])
+def test_insert_inputs_agree(params):
+    """A DNA insert reads its input three ways: the insert kernel decoding
+    the ASCII itself (a 16-byte-aligned device sequence; 16 k-mers per lane
+    load their 48 bases each, 32 per lane take lane l+1's by DPP), the
+    packing pass and then the packed kernel (an unaligned device sequence),
+    and sbf_insert_packed on codes from sbf_pack.  Every way gives the
+    oracle's filter words, on text with lower case, 'N' runs, other letters
+    and bytes with bit 7 set, at lengths around a lane and a wave (1008 and
+    2016 k-mer starts) and over many waves."""
+    import minimizer_sharded_bloom_amd as M
+    torch = G.torch_cuda()
+    rng = np.random.default_rng(78 + params[1])
+    noise = np.frombuffer(b"acgtNNRYn\x00\xc1\xe1@*", dtype=np.uint8)
+    for n in [31, 46, 47, 48, 62, 63, 1007 + 30, 1008 + 30, 1009 + 30, 1056, 2016 + 30, 2047, 2048, 2049,
+              4096 + 45, 300_000 + 3]:
+        src = bytearray(T.random_dna(rng, n))
+        for p in rng.integers(0, n, max(1, n // 40)):
+            src[p] = int(noise[rng.integers(0, noise.size)])
+        if n > 100:
+            p = int(rng.integers(0, n - 40))
+            src[p:p + 33] = b"N" * 33
+        seq = bytes(src)
+        o = G.oracle_filter(params, 2**14)
+        o.insert_seq(seq)
+        want = o.words()
+        o.close()
+        g = G.gpu_filter(params, 2**14)
+        g.insert_seq(G.to_dev(seq))
+        G.assert_words_equal(g.words(), want, "aligned n=%d %s" % (n, params))
+        for off in (1, 7):
+            g.clear()
+            buf = torch.zeros(n + 16, dtype=torch.uint8, device="cuda")
+            buf[off:off + n] = torch.frombuffer(bytearray(seq), dtype=torch.uint8).cuda()
+            view = buf[off:off + n]
+            assert view.data_ptr() % 16 == off
+            g.insert_seq(view)
+            G.assert_words_equal(g.words(), want, "offset %d n=%d %s" % (off, n, params))
+        g.clear()
+        codes, valid = M.pack(G.to_dev(seq))
+        g.insert_packed(codes, valid, n)
+        G.assert_words_equal(g.words(), want, "packed n=%d %s" % (n, params))
+        g.close()
+
+
 def test_query_gaps_at_lane_and_wave_boundaries():
     """'N' runs of 1, 2, 31 and 40 bases placed at and around lane (32 k-mer
     starts) and wave (2016) boundaries, so runs of invalid k-mers start, end
