@@ -6,9 +6,13 @@
 //  - Lane l < 63 owns the KL consecutive k-mers starting at
 //    p0 = wave_start + KL * l; lane 63 only computes hashes for lane 62's halo.
 //  - Every lane loads its packed bases (KL/16 + 2 words, coalesced across the
-//    wave) and computes the m-mer hash and the s-mer hash of its own KL
-//    positions exactly once; the w-1 m-mer hashes and k-s s-mer hashes past
-//    its range come from lane l+1 through a lane shift.
+//    wave), or decodes them from ASCII, and computes the m-mer hash and the
+//    s-mer hash of its own KL positions exactly once; the w-1 m-mer hashes
+//    and k-s s-mer hashes past its range come from lane l+1 through a lane
+//    shift.
+//  - The per-read query (sbf_query_reads_kernel) instead gives each lane 32
+//    k-mers of one read of a batch and lets it hash the positions past them
+//    itself, since lane l+1 may hold another read.
 //  - Minimizer: a sliding-window minimum over the w m-mer hashes (van Herk /
 //    Gil-Werman block prefix and suffix minima, block = w).
 //  - Runs: consecutive valid k-mers of a lane with one shard ([cuSBF] §IV-D,
