@@ -61,6 +61,7 @@ def test_null_handles(lib):
     assert lib.sbf_query_seq(None, None, 10, None, _lib.SBF_HOST, None) == _lib.SBF_EINVAL
     assert lib.sbf_insert_packed(None, None, None, 10, None) == _lib.SBF_EINVAL
     assert lib.sbf_query_packed(None, None, None, 10, None, None) == _lib.SBF_EINVAL
+    assert lib.sbf_query_reads(None, None, 4, 150, 151, None, None) == _lib.SBF_EINVAL
     hits = ctypes.c_uint64()
     assert lib.sbf_fpr_probe(None, 1, 1, ctypes.byref(hits)) == _lib.SBF_EINVAL
     assert lib.sbf_info(None, None) == _lib.SBF_EINVAL

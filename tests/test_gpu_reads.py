@@ -110,6 +110,32 @@ def test_reads_match_oracle(params, kind):
     o.close()
 
 
+def test_reads_with_gaps():
+    """Reads with runs of 'N' (gaps that open, cut and end lanes, and reads
+    that are all 'N'), where the per-read kernel's gap-free record numbering
+    and last-k-mer-first writes decide which key each record holds."""
+    params = (31, 16, 28, 4)
+    rng = np.random.default_rng(9)
+    n, L, stride = 500, 150, 151
+    buf = _noisy_reads(rng, n, L, stride, rate=0.0)
+    for r in range(n):
+        kind = r % 5
+        row = buf[r * stride:r * stride + L]
+        if kind == 0:
+            row[:] = ord("N")
+        elif kind in (1, 2):
+            p = int(rng.integers(0, L - 40))
+            row[p:p + int(rng.integers(1, 40))] = ord("N")
+        elif kind == 3:
+            for p in rng.integers(0, L, 3):
+                row[p] = ord("n")
+    g, o = _filters(params, "sbf", rng, buf)
+    want = _check(g, o, params, buf, n, L, stride, 0, "gaps")
+    assert not want[::5].any(), "all-'N' reads have no hits"
+    g.close()
+    o.close()
+
+
 def test_reads_fill_the_batch_end():
     """The last wave's reads end at the last byte of the device buffer (the
     kernel's byte-load path), for every residue of the batch size mod 4."""
