@@ -573,21 +573,28 @@ __device__ __forceinline__ uint64_t smer_hash_at(const uint32_t (&D)[C::ND])
 // level is never stored: step<I>() hashes the s-mers new at k-mer I (all of
 // 0..Z-1 at I = 0, then I+Z-1), builds the new entries of levels 0..T-1 and
 // returns R_I = T0 | T1.  The first Z-1 own hashes and the Z-1 halo hashes of
-// lane l+1 are computed by init(); every other hash in the step that first
-// needs it, so few hashes are live at once.
-template <class C>
+// lane l+1 are computed by init(), and so are the next NPRE own hashes (the
+// query computes them while its shard gather is in flight); every other hash
+// in the step that first needs it, so few hashes are live at once.
+template <class C, int NPRE = 0>
 struct FindereMasks {
     static constexpr int NZ = C::NZ, Z = C::Z, TOP = ilog2c(Z), NLV = TOP > 0 ? TOP : 1;
     static constexpr int NH = Z > 1 ? Z - 1 : 1;
+    static constexpr int NP = NPRE < C::KL - (Z - 1) ? NPRE : C::KL - (Z - 1);  // own positions Z-1 .. Z-2+NP
     uint64_t L[NLV][NZ][4];
     uint64_t head[NH];  // own hashes of positions 0 .. Z-2
     uint64_t halo[NH];  // hashes of positions KL .. KL+Z-2 (lane l+1's head)
+    uint64_t pre[NP > 0 ? NP : 1];
 
     __device__ __forceinline__ void init(const uint32_t (&D)[C::ND])
     {
         static_for<0, Z - 1>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
             head[q] = smer_hash_at<C, q>(D);
+        });
+        static_for<0, NP>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            pre[q] = smer_hash_at<C, Z - 1 + q>(D);
         });
         static_for<0, Z - 1>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
@@ -603,10 +610,26 @@ struct FindereMasks {
     {
         if constexpr (Q < Z - 1)
             return head[Q];
+        else if constexpr (Q < Z - 1 + NP)
+            return pre[Q - (Z - 1)];
         else if constexpr (Q < C::KL)
             return smer_hash_at<C, Q>(D);
         else
             return halo[Q - C::KL];
+    }
+
+    // The hashes computed so far pass through an empty asm: a volatile asm
+    // after this call (the gather's wait) cannot be moved above them.
+    __device__ __forceinline__ void pin()
+    {
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+            asm volatile("" : "+v"(head[j]));
+            asm volatile("" : "+v"(halo[j]));
+        }
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+            asm volatile("" : "+v"(pre[j]));
     }
 
     template <int I>
@@ -741,7 +764,7 @@ struct WaveLdsN {
 // the last record loads nothing.  idx holds NSLOT + 1 entries and words
 // NSLOT + 1 records; total <= NSLOT.  The loads are complete when this
 // returns.
-template <int RB, int NSLOT>
+template <int RB, int NSLOT, bool WAIT = true>
 __device__ __forceinline__ void gather_records(const uint64_t* __restrict__ filter, uint32_t shard_mask,
                                                const uint32_t* idx, char* words, uint32_t total, uint32_t lane)
 {
@@ -772,7 +795,8 @@ __device__ __forceinline__ void gather_records(const uint64_t* __restrict__ filt
                                                  words + RB * (1 + RPG * (g0 + j)), 16, 0, 0);
         }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (WAIT)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Inclusive prefix sum over the wave: DPP row shifts by 1, 2, 4 and 8 sum
@@ -1064,6 +1088,18 @@ __device__ __forceinline__ uint32_t query_lane_direct(const SeqArgs& a, const ui
 // reads the words of its record and is present iff every bit of its Findere
 // mask R_i is set: (R_i & W) == R_i; invalid k-mers answer 0.  Returns the
 // answer bits (bit i: k-mer i).
+// s-mer hashes of pass B that the query computes before waiting for its
+// gather (each holds two VGPRs from then to its step).  Where w <= 16,
+// k-s+1 <= 4 and H <= 4 (the operating point (31,16,28,4) among them) eight,
+// or four where the lane also hashes its own halo, fit the kernels' 128
+// VGPRs: 1.5 % off the query out of every cache, 0.5 % at 512 MiB.  Larger
+// windows, more s-mers or more hashes would lose a wave per SIMD to them.
+template <class C>
+constexpr int kQueryPreHashes()
+{
+    return (C::W <= 16 && C::Z <= 4 && C::H <= 4) ? (C::OWN_HALO ? 4 : 8) : 0;
+}
+
 template <class C, bool GAPS, int NSLOT>
 __device__ __forceinline__ uint32_t query_lane(const SeqArgs& a, uint32_t (&D)[C::ND], uint32_t vk,
                                                uint32_t lane, int wv, WaveLdsN<NSLOT>& lds)
@@ -1093,13 +1129,16 @@ __device__ __forceinline__ uint32_t query_lane(const SeqArgs& a, uint32_t (&D)[C
     uint32_t bits;
     if (total <= (uint32_t)NSLOT) {
         wave_lds_sync();
-        gather_records<32, NSLOT>(a.filter, a.shard_mask, lds.idx[wv], reinterpret_cast<char*>(&lds.words[wv][0][0]),
-                                  total, lane);
+        gather_records<32, NSLOT, false>(a.filter, a.shard_mask, lds.idx[wv],
+                                         reinterpret_cast<char*>(&lds.words[wv][0][0]), total, lane);
+        // the first s-mer hashes of pass B while the gather is in flight
+        FindereMasks<C, kQueryPreHashes<C>()> fm;
+        fm.init(D);
+        fm.pin();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         wave_lds_sync();
 
         // pass B
-        FindereMasks<C> fm;
-        fm.init(D);
         bits = 0;
         static_for<0, C::KL>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
