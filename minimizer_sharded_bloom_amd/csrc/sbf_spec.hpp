@@ -1131,6 +1131,7 @@ __device__ __forceinline__ uint32_t query_lane(const SeqArgs& a, uint32_t (&D)[C
         wave_lds_sync();
         gather_records<32, NSLOT, false>(a.filter, a.shard_mask, lds.idx[wv],
                                          reinterpret_cast<char*>(&lds.words[wv][0][0]), total, lane);
+        __builtin_amdgcn_s_setprio(0);
         // the first s-mer hashes of pass B while the gather is in flight
         FindereMasks<C, kQueryPreHashes<C>()> fm;
         fm.init(D);
@@ -1174,6 +1175,7 @@ __global__ __launch_bounds__(256) void sbf_query_kernel(SeqArgs a)
         return;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar LDS bases
     uint32_t D[C::ND];
+    __builtin_amdgcn_s_setprio(1);  // pass A first: its gather is what the other waves wait on
     const uint32_t vk = lane_input<C>(a, c, D);
     const uint32_t bits = query_lane<C, true>(a, D, vk, c.lane, wv, lds);
     if (c.lane < (uint32_t)C::LW && c.p0 < nk_pad) {
@@ -1265,6 +1267,7 @@ __global__ __launch_bounds__(256) void sbf_query_reads_kernel(SeqArgs a)
         return;
     const uint32_t lane = threadIdx.x & 63u;
     uint32_t D[C::ND];
+    __builtin_amdgcn_s_setprio(1);  // pass A first: its gather is what the other waves wait on
     const uint32_t vk = reads_input<C>(a, g0, lane, D);
     const uint32_t bits = query_lane<C, false>(a, D, vk, lane, wv, lds);
     if (g0 + lane < a.nk)
