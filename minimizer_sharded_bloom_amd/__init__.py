@@ -231,6 +231,9 @@ class SuperBloomFilter:
         torch = _torch()
         if stride is None:
             stride = read_len + 1
+        if not _is_device_tensor(reads):
+            raise TypeError("query_reads takes a CUDA uint8 tensor (device memory); "
+                            "copy host reads to the device first")
         a = _device_bytes(reads, stream)
         need = (n_reads - 1) * stride + read_len if n_reads else 0
         if a.numel() < need:
