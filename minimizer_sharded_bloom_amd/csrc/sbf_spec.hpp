@@ -296,18 +296,21 @@ __device__ __forceinline__ uint32_t letter_valid4(uint32_t w)
 // of its code, and bit 7 is clear.  d7 has bits 5 and 7 of every byte clear,
 // so d7 + 0x7F per byte sets bit 7 exactly for a nonzero byte and never
 // carries.
+__device__ __forceinline__ void dna_dword(uint32_t w, uint32_t& P, uint32_t& Zi)
+{
+    const uint32_t cc = __builtin_amdgcn_bitop3_b32(w >> 1, w >> 2, 0x03030303u, 0x28);  // (x ^ y) & m
+    P = cc * 0x40100401u;  // code of byte j at bits 31-2j .. 30-2j
+    const uint32_t e = __builtin_amdgcn_perm(0x74676361u, 0x74676361u, cc);  // "acgt" by code
+    const uint32_t d7 = __builtin_amdgcn_bitop3_b32(w, 0xA0A0A0A0u, e, 0x12);     // ~k & (w ^ e)
+    Zi = __builtin_amdgcn_bitop3_b32(d7 + 0x7F7F7F7Fu, w, 0x80808080u, 0xA8);     // (x | w) & m
+}
+
 __device__ __forceinline__ uint32_t decode_dna32(const uint32_t* q, uint32_t& S0, uint32_t& S1)
 {
     uint32_t P[8], Zi[8];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-        const uint32_t w = q[d];
-        const uint32_t cc = __builtin_amdgcn_bitop3_b32(w >> 1, w >> 2, 0x03030303u, 0x28);  // (x ^ y) & m
-        P[d] = cc * 0x40100401u;  // code of byte j at bits 31-2j .. 30-2j
-        const uint32_t e = __builtin_amdgcn_perm(0x74676361u, 0x74676361u, cc);  // "acgt" by code
-        const uint32_t d7 = __builtin_amdgcn_bitop3_b32(w, 0xA0A0A0A0u, e, 0x12);     // ~k & (w ^ e)
-        Zi[d] = __builtin_amdgcn_bitop3_b32(d7 + 0x7F7F7F7Fu, w, 0x80808080u, 0xA8);  // (x | w) & m
-    }
+    for (int d = 0; d < 8; ++d)
+        dna_dword(q[d], P[d], Zi[d]);
     // code words: the top bytes of four products each
     S0 = __builtin_amdgcn_perm(P[0], P[1], 0x07030C0Cu) | __builtin_amdgcn_perm(P[2], P[3], 0x0C0C0703u);
     S1 = __builtin_amdgcn_perm(P[4], P[5], 0x07030C0Cu) | __builtin_amdgcn_perm(P[6], P[7], 0x0C0C0703u);
@@ -327,14 +330,8 @@ __device__ __forceinline__ uint32_t decode_dna16(const uint32_t* q, uint32_t& S0
 {
     uint32_t P[4], Zi[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const uint32_t w = q[d];
-        const uint32_t cc = __builtin_amdgcn_bitop3_b32(w >> 1, w >> 2, 0x03030303u, 0x28);
-        P[d] = cc * 0x40100401u;
-        const uint32_t e = __builtin_amdgcn_perm(0x74676361u, 0x74676361u, cc);
-        const uint32_t d7 = __builtin_amdgcn_bitop3_b32(w, 0xA0A0A0A0u, e, 0x12);
-        Zi[d] = __builtin_amdgcn_bitop3_b32(d7 + 0x7F7F7F7Fu, w, 0x80808080u, 0xA8);
-    }
+    for (int d = 0; d < 4; ++d)
+        dna_dword(q[d], P[d], Zi[d]);
     S0 = __builtin_amdgcn_perm(P[0], P[1], 0x07030C0Cu) | __builtin_amdgcn_perm(P[2], P[3], 0x0C0C0703u);
     const uint32_t V0 = ((Zi[0] >> 4) | Zi[1]) * 0x00204081u;
     const uint32_t V1 = ((Zi[2] >> 4) | Zi[3]) * 0x00204081u;
