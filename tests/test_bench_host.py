@@ -29,22 +29,26 @@ def test_valid_kmer_count():
 def test_roofline_models():
     """The ALU and byte models of the roofline: 52 front-end instructions per
     k-mer start, +13 for the query test, +2.66 for decoding ASCII, +17.5 for
-    the insert; 0.375 B of packed input (1 B of ASCII) plus a 32-byte shard
+    the insert (and 2.66 more from ASCII); 0.375 B of packed input (1 B of
+    ASCII) plus a 32-byte shard
     per run at 2/(w+1) runs per k-mer; the peak of 256 CUs x 4 SIMDs x 32
     lanes per clock at 2.4 GHz."""
     import pytest
     assert bench.alu_ops_per_kmer("query") == pytest.approx(65.0)
     assert bench.alu_ops_per_kmer("query_text") == pytest.approx(67.66)
     assert bench.alu_ops_per_kmer("insert") == pytest.approx(69.5)
+    assert bench.alu_ops_per_kmer("insert_text") == pytest.approx(69.5 + 2.66)
     runs = 2.0 / 17
     assert bench._bytes_per_kmer("query") == pytest.approx(0.375 + 0.125 + 32 * runs)
     assert bench._bytes_per_kmer("query_text") == pytest.approx(1.0 + 0.125 + 32 * runs)
     assert bench._bytes_per_kmer("insert") == pytest.approx(0.375 + 64 * runs)
+    assert bench._bytes_per_kmer("insert_text") == pytest.approx(1.0 + 64 * runs)
     assert bench.ALU_PEAK == pytest.approx(256 * 4 * 32 * 2.4e9)
     # issue slots: every 4-clock form counts twice
     assert bench.alu_issue_slots_per_kmer("query") == pytest.approx(65.0 + 33 + 5)
     assert bench.alu_issue_slots_per_kmer("query_text") == pytest.approx(67.66 + 33 + 5.91)
     assert bench.alu_issue_slots_per_kmer("insert") == pytest.approx(69.5 + 33 + 1.5)
+    assert bench.alu_issue_slots_per_kmer("insert_text") == pytest.approx(72.16 + 33 + 2.41)
 
 
 def test_more_than_one_gpu_is_refused():
