@@ -58,6 +58,17 @@ def _device_bytes(seq, stream):
     return a
 
 
+def _check_out(out, words: int, dtype, device):
+    """A caller-supplied output tensor must be a contiguous device tensor of
+    `dtype` with room for `words` elements on the input's device."""
+    if not _is_device_tensor(out) or out.dtype != dtype or not out.is_contiguous():
+        raise TypeError("out must be a contiguous CUDA %s tensor" % (dtype,))
+    if out.device != device:
+        raise ValueError("out is on %s, the input on %s" % (out.device, device))
+    if out.numel() < words:
+        raise ValueError("out holds %d elements; %d are needed" % (out.numel(), words))
+
+
 def _host_bytes(seq) -> np.ndarray:
     if isinstance(seq, str):
         seq = seq.encode("ascii")
@@ -205,6 +216,8 @@ class SuperBloomFilter:
             nw = self.num_answer_words(a.numel())
             if out is None:
                 out = torch.empty(max(nw, 1), dtype=torch.int64, device=a.device)
+            else:
+                _check_out(out, nw, torch.int64, a.device)
             if nw:
                 check(lib().sbf_query_seq(self._h, a.data_ptr(), a.numel(), out.data_ptr(), SBF_DEVICE,
                                           _stream_ptr(stream)), "sbf_query_seq")
@@ -242,6 +255,8 @@ class SuperBloomFilter:
         rch = self.read_answer_words(read_len)
         if out is None:
             out = torch.empty((n_reads, rch), dtype=torch.int32, device=a.device)
+        else:
+            _check_out(out, n_reads * rch, torch.int32, a.device)
         if n_reads and rch:
             check(lib().sbf_query_reads(self._h, a.data_ptr(), n_reads, read_len, stride, out.data_ptr(),
                                         _stream_ptr(stream)), "sbf_query_reads")
@@ -257,6 +272,8 @@ class SuperBloomFilter:
         nw = self.num_answer_words(length)
         if out is None:
             out = torch.empty(max(nw, 1), dtype=torch.int64, device=codes.device)
+        else:
+            _check_out(out, nw, torch.int64, codes.device)
         if nw:
             check(lib().sbf_query_packed(self._h, codes.data_ptr(), valid.data_ptr(), length, out.data_ptr(),
                                          _stream_ptr(stream)), "sbf_query_packed")

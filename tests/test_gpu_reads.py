@@ -170,6 +170,15 @@ def test_reads_errors_and_noops():
     assert C.sbf_query_reads(h, buf.data_ptr(), 4, 30, 151, out.data_ptr(), None) == _lib.SBF_OK
     torch.cuda.synchronize()
     assert int((out != -1).sum()) == 0
+    # the binding checks a caller's output tensor before any call
+    with pytest.raises(ValueError):
+        g.query_reads(buf, 4, 150, 151, out=torch.empty(15, dtype=torch.int32, device="cuda"))
+    with pytest.raises(TypeError):
+        g.query_reads(buf, 4, 150, 151, out=torch.empty(16, dtype=torch.int64, device="cuda"))
+    with pytest.raises(TypeError):
+        g.query_reads(buf.cpu(), 4, 150, 151)
+    with pytest.raises(ValueError):
+        g.query_seq(buf, out=torch.empty(1, dtype=torch.int64, device="cuda"))
     g.close()
     p = G.gpu_filter((11, 5, 9, 3), 2**14, "protein")
     assert C.sbf_query_reads(p._h, buf.data_ptr(), 4, 150, 151, out.data_ptr(), None) == _lib.SBF_EUNSUPPORTED
