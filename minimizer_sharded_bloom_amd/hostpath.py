@@ -5,7 +5,8 @@ transfer), plus FASTA/FASTQ files end to end (§IV-A, §IV-G).
 
 On the configuration-3 workload (200 Mbp genome, 2^32-bit filter, 20 M reads
 of 150 bp), at k=31, m=16, s=28, H=4:
-  device   sequence already in HBM: pack + insert / pack + query
+  device   sequence already in HBM: insert / query, each kernel decoding
+           the ASCII itself
   host     sequence in pageable host memory: the chunked pinned pipeline
   fasta    the genome as a FASTA file (plain, then gzip) through sbf_insert_fastx
   fastq    2 M of the reads as a FASTQ file through sbf_query_fastx
