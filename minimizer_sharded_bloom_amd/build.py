@@ -21,7 +21,7 @@ ARCH = os.environ.get("SBF_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["inst_grid_best_a.hip", "inst_grid_best_b.hip", "inst_wide.hip", "inst_slice_s_a.hip", "inst_slice_s_b.hip", "inst_slice_m_a.hip", "inst_slice_m_b.hip",
            "inst_slice_m_c.hip", "inst_slice_h.hip", "inst_m16.hip", "inst_m12.hip", "inst_m20.hip", "inst_extra.hip",
-           "sbf_alpha.hip", "sbf_generic.hip", "sbf_membench.hip", "sbf_api.cpp", "sbf_host.cpp", "sbf_fastx.cpp"]
+           "sbf_alpha.hip", "sbf_generic.hip", "sbf_membench.hip", "sbf_api.cpp", "sbf_host.cpp", "sbf_fastx.cpp", "sbf_bgzf.cpp"]
 
 
 def hipcc() -> str:

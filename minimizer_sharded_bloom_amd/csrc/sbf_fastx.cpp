@@ -15,9 +15,12 @@
 //          quality lines until as many quality bytes as bases were read (so
 //          a quality line may itself start with '@').
 // gzip (also multi-member) and plain files are read through zlib's gzread,
-// which passes plain data through unchanged.
+// which passes plain data through unchanged; BGZF files (gzip members of at
+// most 64 KiB that state their own size) are inflated by several threads at
+// once (sbf_bgzf.cpp).
 #include <zlib.h>
 
+#include <cstdio>
 #include <cstring>
 #include <new>
 #include <string>
@@ -37,7 +40,9 @@ enum class State { line_start, skip_line, seq, qual };
 
 struct FastxReader {
     gzFile f = nullptr;
+    BgzfReader* bg = nullptr;  // set for BGZF input, which bypasses gzread
     std::vector<char> in;
+    const char* inp = nullptr;  // current input span: in.data() or a BGZF batch
     size_t pos = 0, lim = 0;
     bool eof = false, finished = false;
     Fmt fmt = Fmt::unknown;
@@ -55,6 +60,19 @@ struct FastxReader {
     {
         if (eof)
             return 0;
+        if (bg) {
+            const char* p = nullptr;
+            size_t n = 0;
+            if (bgzf_next(bg, &p, &n, &error))
+                return -1;
+            inp = p;
+            pos = 0;
+            lim = n;
+            if (n == 0)
+                eof = true;
+            return 0;
+        }
+        inp = in.data();
         const int got = gzread(f, in.data(), (unsigned)in.size());
         if (got < 0) {
             int zerr = 0;
@@ -145,7 +163,7 @@ int fastx_read(FastxReader* r, char* buf, uint64_t cap, uint64_t* len, uint64_t*
                 break;
             }
         }
-        const char* p = r->in.data() + r->pos;
+        const char* p = r->inp + r->pos;
         const size_t avail = r->lim - r->pos;
         switch (r->state) {
         case State::line_start: {
@@ -262,6 +280,25 @@ out:
 
 FastxReader* fastx_open(const char* path, std::string* err)
 {
+    unsigned char head[18];
+    size_t nhead = 0;
+    if (FILE* fp = std::fopen(path, "rb")) {
+        nhead = std::fread(head, 1, sizeof head, fp);
+        std::fclose(fp);
+    }
+    if (bgzf_detect(head, nhead)) {
+        BgzfReader* bg = bgzf_open(path, err);
+        if (!bg)
+            return nullptr;
+        FastxReader* r = new (std::nothrow) FastxReader();
+        if (!r) {
+            bgzf_close(bg);
+            *err = "host allocation failed";
+            return nullptr;
+        }
+        r->bg = bg;
+        return r;
+    }
     gzFile f = gzopen(path, "rb");
     if (!f) {
         *err = std::string("cannot open ") + path;
@@ -292,6 +329,8 @@ void fastx_close(FastxReader* r)
         return;
     if (r->f)
         gzclose(r->f);
+    if (r->bg)
+        bgzf_close(r->bg);
     delete r;
 }
 

@@ -8,7 +8,8 @@ of 150 bp), at k=31, m=16, s=28, H=4:
   device   sequence already in HBM: insert / query, each kernel decoding
            the ASCII itself
   host     sequence in pageable host memory: the chunked pinned pipeline
-  fasta    the genome as a FASTA file (plain, then gzip) through sbf_insert_fastx
+  fasta    the genome as a FASTA file (plain, gzip, then BGZF, whose members the
+           reader inflates on several threads) through sbf_insert_fastx
   fastq    2 M of the reads as a FASTQ file through sbf_query_fastx
 and the raw host-to-device copy rate from pinned memory.  One JSON line per
 measurement, then a table.
@@ -107,19 +108,22 @@ def run(reps: int = 3, tmp: str = "/tmp", chunk: int | None = None, sweep=None, 
     # FASTA / FASTQ files
     fa = os.path.join(tmp, "sbf_hostpath_genome.fa")
     fagz = fa + ".gz"
+    fabgz = fa + ".bgz"
     fq = os.path.join(tmp, "sbf_hostpath_reads.fq")
     t0 = time.perf_counter()
     fa_bytes = S.fasta_bytes(genome)
     fa_bytes.tofile(fa)
     with gzip.open(fagz, "wb", compresslevel=1) as g:
         g.write(fa_bytes.tobytes())
+    with open(fabgz, "wb") as g:
+        g.write(S.bgzf_bytes(fa_bytes.tobytes(), level=1))
     nreads = 2_000_000
     r2d = reads[: nreads * (S.READ_LEN + 1)].reshape(nreads, S.READ_LEN + 1)[:, : S.READ_LEN]
     S.fastq_bytes(np.ascontiguousarray(r2d)).tofile(fq)
     emit(what="files_written", seconds=time.perf_counter() - t0, fasta_bytes=os.path.getsize(fa),
-         fasta_gz_bytes=os.path.getsize(fagz), fastq_bytes=os.path.getsize(fq))
+         fasta_gz_bytes=os.path.getsize(fagz), fasta_bgzf_bytes=os.path.getsize(fabgz), fastq_bytes=os.path.getsize(fq))
     try:
-        for path, label in ((fa, "fasta_insert"), (fagz, "fasta_gz_insert")):
+        for path, label in ((fa, "fasta_insert"), (fagz, "fasta_gz_insert"), (fabgz, "fasta_bgzf_insert")):
             best = None
             for _ in range(reps):
                 f.clear()
@@ -138,7 +142,7 @@ def run(reps: int = 3, tmp: str = "/tmp", chunk: int | None = None, sweep=None, 
         emit(what="fastq_query", gkmers_s=nk_q / best["total_seconds"] / 1e9,
              file_mbytes_s=os.path.getsize(fq) / best["total_seconds"] / 1e6, **best)
     finally:
-        for p in (fa, fagz, fq):
+        for p in (fa, fagz, fabgz, fq):
             if os.path.exists(p):
                 os.remove(p)
     f.close()

@@ -361,14 +361,59 @@ def split_records(stream: np.ndarray) -> list:
     return np.split(stream, cuts + 1) if cuts.size else [stream]
 
 
-def write_fasta(path: str, records, width: int = 60, gz: bool = False, crlf: bool = False,
+def bgzf_bytes(data: bytes, block: int = 0xFF00, level: int = 6, eof: bool = True) -> bytes:
+    """`data` as a BGZF file (the blocked gzip of the SAM/BAM format
+    specification, section 4.1): gzip members of at most `block` input bytes,
+    each with the extra subfield 'BC' that holds the member's total size minus
+    one, then (if eof) the empty end-of-file member."""
+    import struct
+    import zlib
+    assert 0 < block <= 0xFF00
+    pieces = [data[a:a + block] for a in range(0, len(data), block)] + ([b""] if eof else [])
+    out = []
+    for piece in pieces:
+        z = zlib.compressobj(level, zlib.DEFLATED, -15)
+        cdata = z.compress(piece) + z.flush()
+        bsize = 12 + 6 + len(cdata) + 8 - 1
+        assert bsize < 1 << 16
+        out.append(b"\x1f\x8b\x08\x04" + struct.pack("<IBBH", 0, 0, 255, 6) + b"BC" + struct.pack("<HH", 2, bsize)
+                   + cdata + struct.pack("<II", zlib.crc32(piece), len(piece)))
+    return b"".join(out)
+
+
+class _Sink:
+    """A binary file that is written plain, gzip (gz=True) or BGZF
+    (gz="bgzf"; assembled in memory and written on close)."""
+
+    def __init__(self, path: str, gz):
+        import gzip
+        self.path, self.bgzf, self.parts = path, gz == "bgzf", []
+        self.f = None if self.bgzf else (gzip.open(path, "wb") if gz else open(path, "wb"))
+
+    def write(self, b: bytes) -> None:
+        if self.bgzf:
+            self.parts.append(b)
+        else:
+            self.f.write(b)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        if self.bgzf:
+            with open(self.path, "wb") as f:
+                f.write(bgzf_bytes(b"".join(self.parts)))
+        else:
+            self.f.close()
+
+
+def write_fasta(path: str, records, width: int = 60, gz=False, crlf: bool = False,
                 names: str = "read") -> None:
     """FASTA file of the given records (uint8 arrays or bytes, trailing 'N'
-    separators stripped) with `width`-base lines; gzip if gz."""
-    import gzip
+    separators stripped) with `width`-base lines; gzip if gz is True, BGZF if
+    gz == "bgzf"."""
     eol = b"\r\n" if crlf else b"\n"
-    opener = gzip.open if gz else open
-    with opener(path, "wb") as f:
+    with _Sink(path, gz) as f:
         for i, r in enumerate(records):
             s = bytes(r).rstrip(b"N")
             f.write(b">%s_%d length=%d" % (names.encode(), i, len(s)) + eol)
@@ -376,13 +421,11 @@ def write_fasta(path: str, records, width: int = 60, gz: bool = False, crlf: boo
                 f.write(s[a:a + width] + eol)
 
 
-def write_fastq(path: str, records, gz: bool = False, seed_qual: int = 12) -> None:
+def write_fastq(path: str, records, gz=False, seed_qual: int = 12) -> None:
     """FASTQ file (4-line records) of the given records with random quality
-    strings (Phred+33 '!'..'J', seeded)."""
-    import gzip
+    strings (Phred+33 '!'..'J', seeded); gzip or BGZF as for write_fasta."""
     rng = np.random.default_rng(seed_qual)
-    opener = gzip.open if gz else open
-    with opener(path, "wb") as f:
+    with _Sink(path, gz) as f:
         for i, r in enumerate(records):
             s = bytes(r).rstrip(b"N")
             q = (rng.integers(33, 75, len(s), dtype=np.uint8)).tobytes()

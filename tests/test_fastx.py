@@ -1,8 +1,8 @@
 """The library's FASTA/FASTQ reader (host code, no GPU) against the reference
 normalization in tests/fastx_ref.py: records joined by one 'N', line breaks
 and whitespace removed ([cuSBF] §IV-A input forms, §IV-F separators), for
-plain and gzip files, multi-line records, CRLF, comments, empty records and
-FASTQ quality lines that start with '@'."""
+plain, gzip and BGZF files, multi-line records, CRLF, comments, empty records
+and FASTQ quality lines that start with '@'."""
 import ctypes
 import gzip
 import os
@@ -159,6 +159,81 @@ def test_reader_multimember_gzip(tmp_path):
     assert got == want and ends == want_ends
 
 
+def test_bgzf_writer_is_gzip():
+    """The test writer's BGZF files are gzip files that Python's own decoder
+    reads back, and the end-of-file member is the 28-byte empty block."""
+    data = bytes(np.random.default_rng(1).integers(0, 256, 300_000, dtype=np.uint8))
+    for block in (1, 999, 0xFF00):
+        assert gzip.decompress(S.bgzf_bytes(data[:50_000] if block == 1 else data, block=block)) == \
+            (data[:50_000] if block == 1 else data)
+    assert len(S.bgzf_bytes(b"")) == 28
+
+
+@pytest.mark.parametrize("block,level", [(0xFF00, 6), (4093, 1), (1, 0)])
+def test_reader_bgzf(tmp_path, block, level):
+    """BGZF input (members inflated in parallel, several batches of members)
+    reads exactly as the plain file, for full 64 KiB blocks, odd block sizes
+    that cut lines and records anywhere, and one-byte blocks."""
+    rng = np.random.default_rng(block)
+    recs = random_records(rng, 3000 if block > 1 else 300, max_len=3000)
+    text = fasta_text(rng, recs, comments=True) + fastq_text(rng, [])
+    want, want_ends = R.normalize(text)
+    p = tmp_path / "x.fa.bgz"
+    p.write_bytes(S.bgzf_bytes(text, block=block, level=level))
+    for piece, ecap in [(1 << 20, 1 << 16), (4099, 7)]:
+        got, ends, nrec = read_all(str(p), piece, ecap)
+        assert got == want and ends == want_ends and nrec == len(recs), (piece, ecap)
+
+
+def test_reader_bgzf_many_batches(tmp_path):
+    """A 20 MB FASTQ file stored uncompressed in BGZF members spans three 8 MiB
+    batches of compressed input, so members are cut by the batch ends; with
+    empty members between the others and no end-of-file member it reads as
+    the plain file."""
+    recs = list(S.to_ascii(S.random_reads(120_000, 80, seed=3)))
+    plain = tmp_path / "r.fq"
+    S.write_fastq(str(plain), recs)
+    text = plain.read_bytes()
+    assert len(text) > 2 * (8 << 20)
+    members = S.bgzf_bytes(text, block=30011, level=0, eof=False)
+    empty = S.bgzf_bytes(b"", eof=True)
+    # an empty member after every 100th one
+    cut, parts, o = 0, [], 0
+    import struct
+    while o < len(members):
+        size = struct.unpack_from("<H", members, o + 16)[0] + 1
+        parts.append(members[o:o + size])
+        cut += 1
+        if cut % 100 == 0:
+            parts.append(empty)
+        o += size
+    p = tmp_path / "r.fq.bgz"
+    p.write_bytes(b"".join(parts))
+    got, ends, nrec = read_all(str(p), 1 << 22)
+    want, want_ends, _ = read_all(str(plain), 1 << 22)
+    assert got == want == b"N".join(r.tobytes() for r in recs) and ends == want_ends and nrec == 120_000
+
+
+def test_reader_bgzf_errors(tmp_path):
+    """Damaged BGZF files end with SBF_EIO: a CRC-32 that does not match, a
+    wrong ISIZE, a file cut inside a member, and a plain gzip member after
+    BGZF ones."""
+    rng = np.random.default_rng(8)
+    text = fasta_text(rng, random_records(rng, 500))
+    good = bytearray(S.bgzf_bytes(text, block=5000))
+    bad_crc = bytearray(good)
+    bad_crc[-28 - 8] ^= 1  # CRC of the last data member
+    bad_isize = bytearray(good)
+    bad_isize[-28 - 4] ^= 1
+    cases = {"crc": bytes(bad_crc), "isize": bytes(bad_isize), "cut": bytes(good[:-28 - 100]),
+             "mixed": bytes(good[:-28]) + gzip.compress(b">x\nACGT\n")}
+    assert read_all(write(tmp_path, "good", bytes(good)))[0] == R.normalize(text)[0]
+    for name, data in cases.items():
+        with pytest.raises(M.SbfError) as e:
+            read_all(write(tmp_path, name, data))
+        assert e.value.code == _lib.SBF_EIO, name
+
+
 def test_reader_synthetic_writers(tmp_path):
     """write_fasta / write_fastq of generated reads read back as the reads
     joined by 'N'."""
@@ -168,6 +243,7 @@ def test_reader_synthetic_writers(tmp_path):
     assert len(recs) == 200
     for name, fn in [("r.fa", lambda p: S.write_fasta(p, recs, width=70)),
                      ("r.fa.gz", lambda p: S.write_fasta(p, recs, gz=True, crlf=True)),
+                     ("r.fa.bgz", lambda p: S.write_fasta(p, recs, gz="bgzf")),
                      ("r.fq", lambda p: S.write_fastq(p, recs))]:
         p = str(tmp_path / name)
         fn(p)

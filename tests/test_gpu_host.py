@@ -77,7 +77,8 @@ def _record_counts(stream: bytes, ends, o):
 
 
 @pytest.mark.parametrize("fmt,gz,chunk", [("fasta", False, 1 << 27), ("fasta", True, 4096), ("fastq", False, 1000),
-                                          ("fastq", True, 1 << 16)])
+                                          ("fastq", True, 1 << 16), ("fasta", "bgzf", 1 << 16),
+                                          ("fastq", "bgzf", 4096)])
 def test_fastx_insert_and_query(tmp_path, fmt, gz, chunk):
     genome = S.genome_with_repeats(400_000, seed_genome=31)
     # the genome cut into contigs of mixed length, and reads from it
