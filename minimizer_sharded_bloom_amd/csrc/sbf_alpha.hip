@@ -164,7 +164,7 @@ __device__ __forceinline__ bool wave_step(const SeqArgs& a, const Params& P, uin
             vs = acc;
     }
     hm = hash_min(vm);
-    shard = (uint32_t)window_min(hm, k - m + 1u, lane) & a.shard_mask;
+    shard = (uint32_t)window_min(hm, lane_window(k - m + 1u, lane), lane) & a.shard_mask;
 
     const uint64_t h = hash_s(vs);
     mk[0] = mk[1] = mk[2] = mk[3] = 0;
@@ -175,7 +175,7 @@ __device__ __forceinline__ bool wave_step(const SeqArgs& a, const Params& P, uin
         for (uint32_t q = 0; q < 4; ++q)
             mk[q] |= (j & 3u) == q ? bit : 0ull;
     }
-    window_or(mk, k - s + 1u, H, lane);
+    window_or(mk, lane_window(k - s + 1u, lane), H, lane);
 
     // k-mer l is valid iff symbols l .. l+k-1 are (bits past lane 63 are 0)
     const uint64_t kv = run_and_rt(V, k);

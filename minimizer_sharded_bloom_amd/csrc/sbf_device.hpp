@@ -231,53 +231,81 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t word_buffer(const uint32_t* a,
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a + b), (short)0, (int)nrec, 0x00020000);
 }
 
-// Value of lane l+d in lane l for a wave-uniform d >= 1 (lanes past 63 read
-// garbage; only halo lanes look there).
-__device__ __forceinline__ uint32_t lane_down(uint32_t v, uint32_t d, uint32_t lane)
+// Plan of a minimum or an OR over lanes l .. l+n-1 (1 <= n <= 64, n
+// wave-uniform): doubling steps over spans 1, 2, 4, ... while twice the span
+// still fits in n (2^levels <= n), then one step over the remaining
+// n - 2^levels lanes.  Made once per kernel or step from n, so the steps
+// themselves are straight-line code with one uniform branch each (none when
+// n is a compile-time constant).  Lanes past 63 read garbage; only halo
+// lanes look there.
+struct LaneWindow {
+    uint32_t levels;    // doubling steps (spans 1 .. 2^(levels-1))
+    uint32_t rem;       // lanes of the last step, 0 for none
+    uint32_t rem_addr;  // ds_bpermute byte address of lane l + rem
+};
+
+__device__ __forceinline__ LaneWindow lane_window(uint32_t n, uint32_t lane)
 {
-    if (d == 1u)
-        return from_next_lane(v);
-    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((lane + d) << 2), (int)v);
+    LaneWindow w;
+    w.levels = 31u - (uint32_t)__builtin_clz(n);
+    w.rem = n - (1u << w.levels);
+    w.rem_addr = (lane + w.rem) << 2;
+    return w;
 }
 
-__device__ __forceinline__ uint64_t lane_down(uint64_t v, uint32_t d, uint32_t lane)
+// Value of the lane whose ds_bpermute byte address is addr.
+__device__ __forceinline__ uint64_t lane_at(uint64_t v, uint32_t addr)
 {
-    return ((uint64_t)lane_down((uint32_t)(v >> 32), d, lane) << 32) | lane_down((uint32_t)v, d, lane);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)addr, (int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)addr, (int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
-// min over lanes l .. l+w-1 (1 <= w <= 64)
-__device__ __forceinline__ uint64_t window_min(uint64_t v, uint32_t w, uint32_t lane)
+// min over lanes l .. l+n-1 of v
+__device__ __forceinline__ uint64_t window_min(uint64_t v, const LaneWindow& W, uint32_t lane)
 {
-    uint32_t span = 1;
-#pragma unroll
-    while (2u * span <= w) {
-        const uint64_t o = lane_down(v, span, lane);
+    if (W.levels >= 1u) {
+        const uint64_t o = from_next_lane(v);  // span 1 by DPP
         v = o < v ? o : v;
-        span *= 2u;
     }
-    if (span < w) {
-        const uint64_t o = lane_down(v, w - span, lane);
+#pragma unroll
+    for (uint32_t j = 1; j < 6; ++j)
+        if (W.levels > j) {
+            const uint64_t o = lane_at(v, (lane + (1u << j)) << 2);
+            v = o < v ? o : v;
+        }
+    if (W.rem) {
+        const uint64_t o = lane_at(v, W.rem_addr);
         v = o < v ? o : v;
     }
     return v;
 }
 
-// OR over lanes l .. l+z-1 of the four sector masks (words q >= H stay 0)
-__device__ __forceinline__ void window_or(uint64_t (&mk)[4], uint32_t z, uint32_t H, uint32_t lane)
+// OR over lanes l .. l+n-1 of the four sector masks (words q >= H stay 0)
+__device__ __forceinline__ void window_or(uint64_t (&mk)[4], const LaneWindow& W, uint32_t H, uint32_t lane)
 {
     const uint32_t nq = H < 4u ? H : 4u;
-    uint32_t span = 1;
+    if (W.levels >= 1u) {
 #pragma unroll
-    while (2u * span <= z) {
-#pragma unroll
-        for (uint32_t q = 0; q < nq; ++q)
-            mk[q] |= lane_down(mk[q], span, lane);
-        span *= 2u;
+        for (uint32_t q = 0; q < 4; ++q)
+            if (q < nq)
+                mk[q] |= from_next_lane(mk[q]);
     }
-    if (span < z)
 #pragma unroll
-        for (uint32_t q = 0; q < nq; ++q)
-            mk[q] |= lane_down(mk[q], z - span, lane);
+    for (uint32_t j = 1; j < 6; ++j)
+        if (W.levels > j) {
+            const uint32_t addr = (lane + (1u << j)) << 2;
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q)
+                if (q < nq)
+                    mk[q] |= lane_at(mk[q], addr);
+        }
+    if (W.rem) {
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q)
+            if (q < nq)
+                mk[q] |= lane_at(mk[q], W.rem_addr);
+    }
 }
 
 // LDS written by some lanes of this wave becomes visible to all its lanes.

@@ -301,6 +301,55 @@ __global__ __launch_bounds__(256) void generic_probe_kernel(ProbeArgs a, Params 
         atomicAdd(a.hits, (unsigned long long)cnt);
 }
 
+// FPR probe of a Super Bloom filter with run-time k, m, s ([cuSBF] §V-D:
+// random k-mers, each answered on its own).  HC > 0 fixes H at compile time,
+// so each s-mer's bits go to static words; HC = 0 takes H from P.  The m-mers
+// and s-mers are cut from the k-mer by a running 2-bit shift, last first, so
+// no window needs a shift by a run-time amount.
+template <int HC>
+__global__ __launch_bounds__(256) void sbf_probe_rt_kernel(ProbeArgs a, Params P)
+{
+    const uint32_t k = P.k, m = P.m, s = P.s, H = HC ? (uint32_t)HC : P.H;
+    const uint64_t mmask = m >= 32u ? ~0ull : (1ull << (2u * m)) - 1ull;
+    const uint64_t smask = s >= 32u ? ~0ull : (1ull << (2u * s)) - 1ull;
+    const uint32_t w = k - m + 1u, z = k - s + 1u;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    uint32_t cnt = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += stride) {
+        const uint64_t x = splitmix_fin(a.seed + (i + 1) * kGolden) >> (64 - 2 * k);
+        uint64_t mn = ~0ull, y = x;
+        for (uint32_t j = 0; j < w; ++j, y >>= 2) {
+            const uint64_t h = hash_min(y & mmask);
+            mn = h < mn ? h : mn;
+        }
+        uint64_t mk[4] = {0, 0, 0, 0};
+        y = x;
+        for (uint32_t j = 0; j < z; ++j, y >>= 2) {
+            const uint64_t h = hash_s(y & smask);
+            if constexpr (HC > 0) {
+#pragma unroll
+                for (int t = 0; t < HC; ++t)
+                    mk[t & 3] |= 1ull << bit_addr<HC>(h, t);
+            } else {
+                for (uint32_t t0 = 0; t0 < H; t0 += 4u) {
+#pragma unroll
+                    for (uint32_t q = 0; q < 4; ++q)
+                        if (t0 + q < H)
+                            mk[q] |= 1ull << bit_addr_rt(h, t0 + q, H);
+                }
+            }
+        }
+        uint64_t sw[4];
+        load_shard(a.filter, (uint32_t)mn & a.shard_mask, sw);
+        cnt += ((~sw[0] & mk[0]) | (~sw[1] & mk[1]) | (~sw[2] & mk[2]) | (~sw[3] & mk[3])) == 0;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        cnt += __shfl_xor(cnt, off);
+    if ((threadIdx.x & 63u) == 0 && cnt)
+        atomicAdd(a.hits, (unsigned long long)cnt);
+}
+
 // ---------------------------------------------------------------------------
 // Run-time sliding kernels of the Super Bloom filter (any k, m, s, H that has
 // no compiled set).  A wave step covers 64 consecutive positions, one per
@@ -317,39 +366,66 @@ __global__ __launch_bounds__(256) void generic_probe_kernel(ProbeArgs a, Params 
 // k-mer starts per wave task: whole answer words, so tasks never share one.
 constexpr uint64_t kSlideTask = 2048;
 
+// What a wave keeps for one task of the sliding kernels: raw buffers over the
+// code and validity words from the task's first ones (a read past the end of
+// the sequence returns 0 through the buffer range check, so lane loads need
+// no bounds branches), and the plans of the minimizer's and the Findere
+// mask's cross-lane windows.
+struct SlideTask {
+    __amdgpu_buffer_rsrc_t rc, rv;
+    uint64_t wc0, wv0;  // first code and validity word of the buffers
+    LaneWindow wm, wz;  // over w = k-m+1 and z = k-s+1 lanes
+
+    __device__ __forceinline__ SlideTask(const SeqArgs& a, const Params& P, uint64_t t0, uint32_t lane)
+        : rc(word_buffer(a.codes, a.ncw, t0 >> 4)), rv(word_buffer(a.valid, a.nvw, t0 >> 5)), wc0(t0 >> 4),
+          wv0(t0 >> 5), wm(lane_window(P.k - P.m + 1u, lane)), wz(lane_window(P.k - P.s + 1u, lane))
+    {
+    }
+};
+
+// The words a lane reads for one wave step: code words holding its bases
+// p .. p+31 and validity words holding bits p .. p+63.  Loaded one step
+// ahead, so the loads of step i+1 are in flight while step i computes.
+struct SlideWords {
+    uint32_t d0, d1, d2, v0, v1, v2;
+};
+
+__device__ __forceinline__ SlideWords slide_load(const SlideTask& T, uint64_t base, uint32_t lane)
+{
+    SlideWords W;
+    const uint32_t o = ((uint32_t)((base >> 4) - T.wc0) + (((uint32_t)(base & 15u) + lane) >> 4)) * 4u;
+    W.d0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(T.rc, (int)o, 0, 0);
+    W.d1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(T.rc, (int)(o + 4u), 0, 0);
+    W.d2 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(T.rc, (int)(o + 8u), 0, 0);
+    const uint32_t vo = ((uint32_t)((base >> 5) - T.wv0) + (((uint32_t)(base & 31u) + lane) >> 5)) * 4u;
+    W.v0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(T.rv, (int)vo, 0, 0);
+    W.v1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(T.rv, (int)(vo + 4u), 0, 0);
+    W.v2 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(T.rv, (int)(vo + 8u), 0, 0);
+    return W;
+}
+
 // Shard key (low 32 bits of the minimizer hash) and sector masks of the k-mer
-// starting at this lane's position; true if it is to be processed (a start
-// lane, before `end`, every base valid).  HC > 0 fixes H at compile time (the
-// bit-address loop unrolls); HC = 0 takes it from P.  Code and validity words
-// come through raw buffers based at the step's first word, so reads past the
-// end of the sequence return 0 without a bounds branch.
+// starting at this lane's position, from the step's words; true if it is to
+// be processed (a start lane, before `end`, every base valid).  HC > 0 fixes
+// H at compile time (the bit-address loop unrolls); HC = 0 takes it from P.
 template <int HC>
-__device__ __forceinline__ bool slide_step(const SeqArgs& a, const Params& P, uint64_t base, uint64_t end,
-                                           uint32_t lane, uint32_t E, uint32_t& key, uint64_t (&mk)[4])
+__device__ __forceinline__ bool slide_step(const Params& P, const SlideTask& T, const SlideWords& D, uint64_t base,
+                                           uint64_t end, uint32_t lane, uint32_t E, uint32_t& key, uint64_t (&mk)[4])
 {
     const uint32_t k = P.k, m = P.m, s = P.s, H = HC ? (uint32_t)HC : P.H;
     const uint64_t p = base + lane;
     // bases p .. p+31, first in the top bits
-    const auto rc = word_buffer(a.codes, a.ncw, base >> 4);
-    const uint32_t o = (((uint32_t)(base & 15u) + lane) >> 4) * 4u;
-    const uint32_t d0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, (int)o, 0, 0);
-    const uint32_t d1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, (int)(o + 4u), 0, 0);
-    const uint32_t d2 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, (int)(o + 8u), 0, 0);
     const uint32_t r = 2u * (uint32_t)(p & 15u);
-    const uint64_t win = ((uint64_t)funnel_hi(d0, d1, r) << 32) | funnel_hi(d1, d2, r);
+    const uint64_t win = ((uint64_t)funnel_hi(D.d0, D.d1, r) << 32) | funnel_hi(D.d1, D.d2, r);
     // validity bits p .. p+63
-    const auto rv = word_buffer(a.valid, a.nvw, base >> 5);
-    const uint32_t vb = (uint32_t)(base & 31u) + lane;
-    const uint32_t vo = (vb >> 5) * 4u, voff = vb & 31u;
-    const uint32_t v0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, (int)vo, 0, 0);
-    const uint32_t v1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, (int)(vo + 4u), 0, 0);
-    const uint32_t v2 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, (int)(vo + 8u), 0, 0);
-    const uint64_t vwin = ((uint64_t)__builtin_amdgcn_alignbit(v2, v1, voff) << 32) | __builtin_amdgcn_alignbit(v1, v0, voff);
+    const uint32_t voff = ((uint32_t)(base & 31u) + lane) & 31u;
+    const uint64_t vwin = ((uint64_t)__builtin_amdgcn_alignbit(D.v2, D.v1, voff) << 32) |
+                          __builtin_amdgcn_alignbit(D.v1, D.v0, voff);
     const uint64_t need = k >= 64u ? ~0ull : ((1ull << k) - 1ull);
 
     const uint64_t vm = m >= 32u ? win : win >> (64u - 2u * m);
     const uint64_t vs = s >= 32u ? win : win >> (64u - 2u * s);
-    key = (uint32_t)window_min(hash_min(vm), k - m + 1u, lane);
+    key = (uint32_t)window_min(hash_min(vm), T.wm, lane);
     const uint64_t h = hash_s(vs);
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q)
@@ -366,7 +442,7 @@ __device__ __forceinline__ bool slide_step(const SeqArgs& a, const Params& P, ui
                     mk[q] |= 1ull << bit_addr_rt(h, t0 + q, H);
         }
     }
-    window_or(mk, k - s + 1u, H, lane);
+    window_or(mk, T.wz, H, lane);
     return lane < E && p < end && (vwin & need) == need;
 }
 
@@ -389,16 +465,21 @@ __global__ __launch_bounds__(256) void slide_insert_kernel(SeqArgs a, Params P)
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t E = slide_yield(P);
+    const uint32_t H = HC ? (uint32_t)HC : P.H, nq = H < 4u ? H : 4u;  // words a record can set
     const uint64_t ntasks = (a.nk + kSlideTask - 1) / kSlideTask;
     const uint64_t wstride = (uint64_t)gridDim.x * 4u;
     const uint64_t le = lane == 63u ? ~0ull : (2ull << lane) - 1ull;  // lanes 0 .. lane
     for (uint64_t task = (uint64_t)blockIdx.x * 4u + wv; task < ntasks; task += wstride) {
         const uint64_t t0 = task * kSlideTask;
         const uint64_t t1 = t0 + kSlideTask < a.nk ? t0 + kSlideTask : a.nk;
+        const SlideTask T(a, P, t0, lane);
+        SlideWords D = slide_load(T, t0, lane);
         for (uint64_t base = t0; base < t1; base += E) {
+            const SlideWords cur = D;
+            D = slide_load(T, base + E, lane);  // the next step's words (past the task: unused)
             uint32_t key;
             uint64_t mk[4];
-            const bool kv = slide_step<HC>(a, P, base, t1, lane, E, key, mk);
+            const bool kv = slide_step<HC>(P, T, cur, base, t1, lane, E, key, mk);
             const uint32_t pkey = from_prev_lane(key);
             const uint32_t pkv = from_prev_lane(kv ? 1u : 0u);  // lane 0 reads 0
             const bool head = kv && !(pkv && pkey == key);
@@ -413,20 +494,22 @@ __global__ __launch_bounds__(256) void slide_insert_kernel(SeqArgs a, Params P)
             if (kv) {
 #pragma unroll
                 for (uint32_t q = 0; q < 4; ++q)
-                    if (mk[q])
+                    if (q < nq)  // every s-mer sets a bit in each word below H
                         __hip_atomic_fetch_or(&rec_mk[wv][r][q], mk[q], __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_WAVEFRONT);
                 if (head)
                     rec_sh[wv][r] = key & a.shard_mask;
             }
             wave_lds_sync();
-            // flush: lane -> (record lane/4 + 16 j, word lane & 3)
+            // flush: lane -> (record lane/4 + 16 j, word lane & 3); words
+            // q >= H of every record are 0 and skipped
             const uint32_t q = lane & 3u;
-            for (uint32_t rr = lane >> 2; rr < nrec; rr += 16u) {
-                const uint64_t m = rec_mk[wv][rr][q];
-                if (m)
-                    atomic_or_u64(a.filter + 4ull * rec_sh[wv][rr] + q, m);
-            }
+            if (q < nq)
+                for (uint32_t rr = lane >> 2; rr < nrec; rr += 16u) {
+                    const uint32_t sh = rec_sh[wv][rr];
+                    const uint64_t m = rec_mk[wv][rr][q];
+                    atomic_or_u64(a.filter + 4ull * sh + q, m);
+                }
             wave_lds_sync();  // the next step rewrites the records
         }
     }
@@ -450,10 +533,14 @@ __global__ __launch_bounds__(256) void slide_query_kernel(SeqArgs a, Params P)
         uint64_t acc = 0;         // answers not yet stored, first at bit 0
         uint32_t nb = 0;          // how many (< 64)
         uint64_t word = t0 >> 6;  // answer word they belong to
+        const SlideTask T(a, P, t0, lane);
+        SlideWords D = slide_load(T, t0, lane);
         for (uint64_t base = t0; base < t1; base += E) {
+            const SlideWords cur = D;
+            D = slide_load(T, base + E, lane);  // the next step's words (past the task: unused)
             uint32_t key;
             uint64_t mk[4];
-            bool pres = slide_step<HC>(a, P, base, t1, lane, E, key, mk);
+            bool pres = slide_step<HC>(P, T, cur, base, t1, lane, E, key, mk);
             if (pres) {
                 uint64_t w[4];
                 load_shard(a.filter, key & a.shard_mask, w);
@@ -477,10 +564,10 @@ __global__ __launch_bounds__(256) void slide_query_kernel(SeqArgs a, Params P)
     }
 }
 
-// Kernel of the sliding family for this H: compile-time H for 1 .. 16,
+// Kernel of a run-time family for this H: compile-time H for 1 .. 16,
 // run-time above.
-#define SBF_SLIDE_KERNEL(NAME)                                                                  \
-    static void (*NAME##_for(uint32_t H))(SeqArgs, Params)                                      \
+#define SBF_SLIDE_KERNEL(NAME, ARGS)                                                            \
+    static void (*NAME##_for(uint32_t H))(ARGS, Params)                                         \
     {                                                                                           \
         switch (H) {                                                                            \
         case 1: return NAME<1>;   case 2: return NAME<2>;   case 3: return NAME<3>;             \
@@ -491,8 +578,9 @@ __global__ __launch_bounds__(256) void slide_query_kernel(SeqArgs a, Params P)
         case 16: return NAME<16>; default: return NAME<0>;                                     \
         }                                                                                       \
     }
-SBF_SLIDE_KERNEL(slide_insert_kernel)
-SBF_SLIDE_KERNEL(slide_query_kernel)
+SBF_SLIDE_KERNEL(slide_insert_kernel, SeqArgs)
+SBF_SLIDE_KERNEL(slide_query_kernel, SeqArgs)
+SBF_SLIDE_KERNEL(sbf_probe_rt_kernel, ProbeArgs)
 #undef SBF_SLIDE_KERNEL
 
 static uint32_t slide_blocks(uint64_t nk)
@@ -540,7 +628,10 @@ static hipError_t gen_probe(const ProbeArgs& a, const Params& P)
     uint64_t b = (a.n + 255) / 256;
     if (b > 8192)
         b = 8192;
-    hipLaunchKernelGGL(generic_probe_kernel, dim3((uint32_t)b), dim3(256), 0, a.stream, a, P);
+    if (P.kind == 0)
+        hipLaunchKernelGGL(sbf_probe_rt_kernel_for(P.H), dim3((uint32_t)b), dim3(256), 0, a.stream, a, P);
+    else
+        hipLaunchKernelGGL(generic_probe_kernel, dim3((uint32_t)b), dim3(256), 0, a.stream, a, P);
     return hipGetLastError();
 }
 

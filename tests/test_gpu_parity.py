@@ -155,9 +155,14 @@ def test_blocked_bloom(kind, params):
 
 
 @pytest.mark.parametrize("kind,params,n", [("sbf", MAIN, 300000), ("sbf", (9, 5, 6, 3), 100000),
-                                           ("sbf", (17, 9, 13, 7), 50000), ("bbf", (31, 0, 0, 4), 200000)])
+                                           ("sbf", (17, 9, 13, 7), 50000), ("sbf", (31, 17, 26, 4), 100000),
+                                           ("sbf", (25, 14, 25, 11), 50000), ("sbf", (12, 12, 6, 64), 50000),
+                                           ("sbf", (32, 32, 1, 1), 50000), ("sbf", (1, 1, 1, 3), 20000),
+                                           ("bbf", (31, 0, 0, 4), 200000)])
 def test_fpr_probe(kind, params, n):
-    """a7: probe hit counts equal the oracle's on the same SplitMix64 stream."""
+    """a7: probe hit counts equal the oracle's on the same SplitMix64 stream,
+    for compiled sets and for run-time ones (compile-time H from 1 to 16, and
+    H = 64 read at run time)."""
     rng = np.random.default_rng(71)
     g = G.gpu_filter(params, 2**15, kind)
     o = G.oracle_filter(params, 2**15, kind)
