@@ -15,9 +15,15 @@
 // Every member is checked: the header fields that make it BGZF, a
 // consistent block size, an inflate that ends exactly at the trailer with
 // ISIZE bytes, and the CRC-32 of the output.  A member that fails any check,
-// or bytes at the end that do not form a whole member, end the stream with an
-// error after the data before it.
+// or a member cut by the end of the file, ends the stream with an error after
+// the data before it.  A later gzip member that is not BGZF (another gzip
+// file appended) hands the rest of the file to zlib's gzread, which the
+// reader thread runs itself; bytes after the last member that do not start
+// a gzip header are ignored, as zlib ignores them.
 #include <zlib.h>
+
+#include <fcntl.h>
+#include <unistd.h>
 
 #include <condition_variable>
 #include <cstdio>
@@ -70,7 +76,8 @@ struct Member {
     uint32_t isize, crc;
 };
 
-constexpr size_t kChunk = 1u << 20;  // compressed bytes per chunk (whole members)
+constexpr size_t kChunk = 1u << 20;      // compressed bytes per chunk (whole members)
+constexpr unsigned kTailChunk = 4u << 20;  // output bytes per chunk past the BGZF members
 
 }  // namespace
 
@@ -93,6 +100,8 @@ struct BgzfReader {
     };
 
     FILE* fp = nullptr;
+    uint64_t foff = 0;       // file offset of the next byte fp returns
+    int64_t tail_at = -1;    // offset of the first member that is not BGZF, once met
     std::vector<Slot> ring;
     std::vector<size_t> queue;  // slots waiting for a worker, oldest first
     size_t qhead = 0;
@@ -124,8 +133,9 @@ struct BgzfReader {
             std::fclose(fp);
     }
 
-    // Cut the next chunk into s: whole members until about kChunk bytes or the
-    // end of the file.  Returns false with s.err set on a bad or cut member.
+    // Cut the next chunk into s: whole members until about kChunk bytes, the
+    // end of the file (eof) or a member that is not BGZF (tail_at set).
+    // Returns false with s.err set on a bad or cut member.
     bool cut(Slot& s, bool& eof)
     {
         s.in.clear();
@@ -135,35 +145,50 @@ struct BgzfReader {
         s.err.clear();
         unsigned char hdr[12];
         while (s.in.size() < kChunk) {
+            const uint64_t mstart = foff;
             const size_t got = std::fread(hdr, 1, sizeof hdr, fp);
-            if (got == 0 && !std::ferror(fp)) {
-                eof = true;
+            foff += got;
+            if (std::ferror(fp)) {
+                s.err = "read error";
+                return false;
+            }
+            if (got == 0 || hdr[0] != 0x1f || (got > 1 && hdr[1] != 0x8b)) {
+                eof = true;  // the end, or trailing bytes that are not gzip
                 return true;
             }
             if (got < sizeof hdr) {
-                s.err = std::ferror(fp) ? "read error" : "BGZF: truncated member at the end of the file";
+                s.err = "BGZF: truncated member at the end of the file";
                 return false;
+            }
+            if (hdr[2] != 8 || hdr[3] != 4) {
+                tail_at = (int64_t)mstart;  // a gzip member without an extra field
+                return true;
             }
             const size_t o = s.in.size();
             const uint32_t xl = le16(hdr + 10);
             s.in.resize(o + 12 + xl);
             std::memcpy(s.in.data() + o, hdr, 12);
-            if (std::fread(s.in.data() + o + 12, 1, xl, fp) != xl) {
+            const size_t gx = std::fread(s.in.data() + o + 12, 1, xl, fp);
+            foff += gx;
+            if (gx != xl) {
                 s.err = "BGZF: truncated member at the end of the file";
                 return false;
             }
             uint32_t xl2 = 0;
             const size_t sz = member_size(s.in.data() + o, 12 + xl, &xl2);
             if (sz == 0) {
-                s.err = "BGZF: a member without the 'BC' block-size field";
-                return false;
+                s.in.resize(o);
+                tail_at = (int64_t)mstart;  // a gzip member without the 'BC' field
+                return true;
             }
             if (sz < 12 + (size_t)xl + 8) {
                 s.err = "BGZF: block size smaller than its header and trailer";
                 return false;
             }
             s.in.resize(o + sz);
-            if (std::fread(s.in.data() + o + 12 + xl, 1, sz - 12 - xl, fp) != sz - 12 - xl) {
+            const size_t gd = std::fread(s.in.data() + o + 12 + xl, 1, sz - 12 - xl, fp);
+            foff += gd;
+            if (gd != sz - 12 - xl) {
                 s.err = "BGZF: truncated member at the end of the file";
                 return false;
             }
@@ -245,7 +270,63 @@ struct BgzfReader {
             cv_consumer.notify_all();
             if (!ok)
                 return;
+            if (tail_at >= 0) {
+                tail_loop();
+                return;
+            }
         }
+    }
+
+    // The file from tail_at on, through zlib's gzread (sequential), in
+    // chunks of up to kTailChunk bytes; an empty last chunk marks the end.
+    void tail_loop()
+    {
+        gzFile gz = nullptr;
+        const int fd = ::dup(::fileno(fp));
+        if (fd >= 0 && ::lseek(fd, (off_t)tail_at, SEEK_SET) == (off_t)tail_at)
+            gz = ::gzdopen(fd, "rb");
+        if (!gz && fd >= 0)
+            ::close(fd);
+        for (bool end = false; !end;) {
+            Slot* s;
+            {
+                std::unique_lock<std::mutex> g(mu);
+                cv_reader.wait(g, [&] { return stop || wpos - rpos < ring.size(); });
+                if (stop)
+                    break;
+                s = &ring[wpos % ring.size()];
+            }
+            s->mem.clear();
+            s->err.clear();
+            int n = -1;
+            if (!gz) {
+                s->err = "cannot reopen the file for its gzip members";
+            } else {
+                try {
+                    if (s->out.size() < kTailChunk)
+                        s->out.resize(kTailChunk);
+                    n = ::gzread(gz, s->out.data(), kTailChunk);
+                    if (n < 0) {
+                        int zerr = 0;
+                        const char* msg = ::gzerror(gz, &zerr);
+                        s->err = std::string("read error: ") + (msg ? msg : "?");
+                    }
+                } catch (const std::bad_alloc&) {
+                    s->err = "host allocation failed";
+                }
+            }
+            end = n <= 0;
+            {
+                std::lock_guard<std::mutex> g(mu);
+                s->out_len = n > 0 ? (size_t)n : 0;
+                s->st = n < 0 ? St::failed : St::done;
+                s->last = end;
+                ++wpos;
+            }
+            cv_consumer.notify_all();
+        }
+        if (gz)
+            ::gzclose(gz);
     }
 
     void work_loop()

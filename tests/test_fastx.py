@@ -214,10 +214,28 @@ def test_reader_bgzf_many_batches(tmp_path):
     assert got == want == b"N".join(r.tobytes() for r in recs) and ends == want_ends and nrec == 120_000
 
 
+def test_reader_bgzf_mixed_and_trailing(tmp_path):
+    """A BGZF file followed by plain gzip members (another gzip file
+    appended) reads as the whole text, the part after the BGZF members
+    through gzread; bytes after the last member that are not gzip are
+    ignored, as zlib ignores them."""
+    rng = np.random.default_rng(4)
+    a = fasta_text(rng, random_records(rng, 800))
+    b = fasta_text(rng, random_records(rng, 300))
+    c = fasta_text(rng, random_records(rng, 200))
+    bg = S.bgzf_bytes(a, block=3000)
+    for name, data, text in [("mixed", bg + gzip.compress(b), a + b),
+                             ("mixed_then_bgzf", bg[:-28] + gzip.compress(b) + S.bgzf_bytes(c, block=777), a + b + c),
+                             ("trailing", bg + b"garbage that is not gzip\n", a)]:
+        got, ends, nrec = read_all(write(tmp_path, name, data), 4099, 7)
+        want, want_ends = R.normalize(text)
+        assert got == want and ends == want_ends, name
+        assert read_all(write(tmp_path, name + ".gz_ref", gzip.compress(text)))[0] == want
+
+
 def test_reader_bgzf_errors(tmp_path):
     """Damaged BGZF files end with SBF_EIO: a CRC-32 that does not match, a
-    wrong ISIZE, a file cut inside a member, and a plain gzip member after
-    BGZF ones."""
+    wrong ISIZE, a file cut inside a member."""
     rng = np.random.default_rng(8)
     text = fasta_text(rng, random_records(rng, 500))
     good = bytearray(S.bgzf_bytes(text, block=5000))
@@ -225,8 +243,7 @@ def test_reader_bgzf_errors(tmp_path):
     bad_crc[-28 - 8] ^= 1  # CRC of the last data member
     bad_isize = bytearray(good)
     bad_isize[-28 - 4] ^= 1
-    cases = {"crc": bytes(bad_crc), "isize": bytes(bad_isize), "cut": bytes(good[:-28 - 100]),
-             "mixed": bytes(good[:-28]) + gzip.compress(b">x\nACGT\n")}
+    cases = {"crc": bytes(bad_crc), "isize": bytes(bad_isize), "cut": bytes(good[:-28 - 100])}
     assert read_all(write(tmp_path, "good", bytes(good)))[0] == R.normalize(text)[0]
     for name, data in cases.items():
         with pytest.raises(M.SbfError) as e:
