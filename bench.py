@@ -239,11 +239,13 @@ def filter_level(nbytes: int) -> str:
     return "hbm"
 
 
-def valid_kmer_count(text, k: int, alpha: str = "dna", chunk: int = 3 << 26) -> int:
+def valid_kmer_count(text, k: int, alpha: str = "dna", chunk: int = 3 << 26, segments: bool = False):
     """k-mer starts whose k symbols are all valid (positions with an invalid
     symbol, e.g. a record separator, are not): the throughput count of valid
     k-mers, next to the count of k-mer starts.  Counted chunk by chunk, with
-    the valid run that crosses a chunk boundary carried over."""
+    the valid run that crosses a chunk boundary carried over.  With
+    segments=True also the number of maximal stretches of valid symbols that
+    hold at least one k-mer, as (count, segments)."""
     import numpy as np
 
     ok = np.zeros(256, dtype=bool)
@@ -253,7 +255,7 @@ def valid_kmer_count(text, k: int, alpha: str = "dna", chunk: int = 3 << 26) -> 
         ok[list(b"ACGTacgt")] = True
     sb = 3 if alpha == "triplet" else 1
     n_sym = text.size // sb
-    total, cur = 0, 0
+    total, cur, nseg = 0, 0, 0
     for lo in range(0, n_sym, chunk):
         hi = min(n_sym, lo + chunk)
         v = ok[text[lo * sb:hi * sb]]
@@ -264,9 +266,14 @@ def valid_kmer_count(text, k: int, alpha: str = "dna", chunk: int = 3 << 26) -> 
             cur += hi - lo
             continue
         total += max(0, cur + int(bad[0]) - k + 1)
-        total += int(np.maximum(np.diff(bad) - k, 0).sum())
+        nseg += cur + int(bad[0]) >= k
+        gaps = np.diff(bad) - 1  # stretches between invalid symbols
+        total += int(np.maximum(gaps - k + 1, 0).sum())
+        nseg += int((gaps >= k).sum())
         cur = hi - lo - 1 - int(bad[-1])
-    return total + max(0, cur - k + 1)
+    total += max(0, cur - k + 1)
+    nseg += cur >= k
+    return (total, int(nseg)) if segments else total
 
 
 def matched_ceilings(lib, torch, filt, stream, n_ops: int = 1 << 25) -> dict:
@@ -577,7 +584,8 @@ def main():
         del src, dst
 
     nk_g, nk_r = LG - K + 1, LR - K + 1
-    vk_g, vk_r = valid_kmer_count(genome_h, K), valid_kmer_count(reads_h, K)
+    (vk_g, seg_g), (vk_r, seg_r) = (valid_kmer_count(genome_h, K, segments=True),
+                                    valid_kmer_count(reads_h, K, segments=True))
     total = vk_g + vk_r + a.probe_n
     value = total / (ms_step * 1e-3) / 1e9
     # rates over valid k-mers (the roofline's numerator counts only these)
@@ -645,12 +653,19 @@ def main():
         "kernel_sources_sha256": sha,
     }
     if ceilings is not None:
-        # runs per k-mer for random minimizers, 2/(w+1): the insert's record
-        # flushes and the query's shard reads, set against the matched ceilings
+        # runs of random minimizers: a stretch of n valid k-mers holds
+        # 1 + (n-1) 2/(w+1) of them on average; one record flush per run for
+        # the insert, one shard read per run for the query, set against the
+        # matched ceilings
         runs = 2.0 / (K - M_ + 2)
-        ceilings["insert_records_est_g_per_s"] = round(nk_g / (phase["insert"] * 1e-3) * runs / 1e9, 3)
+        rec_g = vk_g * runs + seg_g * (1.0 - runs)
+        rec_r = vk_r * runs + seg_r * (1.0 - runs)
+        ceilings["insert_records_est_g_per_s"] = round(rec_g / (phase["insert"] * 1e-3) / 1e9, 3)
         ceilings["insert_frac_of_or_ceiling"] = round(ceilings["insert_records_est_g_per_s"]
                                                       / ceilings["shard_ors_g_per_s"], 3)
+        ceilings["query_shard_reads_est_g_per_s"] = round(rec_r / (phase["query"] * 1e-3) / 1e9, 3)
+        ceilings["query_frac_of_read_ceiling"] = round(ceilings["query_shard_reads_est_g_per_s"]
+                                                       / ceilings["shard_reads_g_per_s"], 3)
         res["matched_ceilings"] = ceilings
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
@@ -710,7 +725,8 @@ def main_alpha(a, torch, M, S, lib):
         del src, dst
 
     nk_g, nk_r = f.num_symbols(LG) - k + 1, f.num_symbols(LR) - k + 1
-    vk_g, vk_r = valid_kmer_count(w["insert"], k, alpha), valid_kmer_count(w["queries"][0], k, alpha)
+    (vk_g, seg_g), (vk_r, seg_r) = (valid_kmer_count(w["insert"], k, alpha, segments=True),
+                                    valid_kmer_count(w["queries"][0], k, alpha, segments=True))
     total = vk_g + vk_r + a.probe_n
     value = total / (ms_step * 1e-3) / 1e9
     ins_rate = vk_g / (phase["insert"] * 1e-3)
@@ -758,10 +774,15 @@ def main_alpha(a, torch, M, S, lib):
         "wall_s_timed": round(wall, 3), "gen_s": round(gen_s, 2), "kernel_sources_sha256": sha,
     }
     if ceilings is not None:
-        runs = 2.0 / (k - m + 2)
-        ceilings["insert_records_est_g_per_s"] = round(nk_g / (phase["insert"] * 1e-3) * runs / 1e9, 3)
+        runs = 2.0 / (k - m + 2)  # as in main()
+        rec_g = vk_g * runs + seg_g * (1.0 - runs)
+        rec_r = vk_r * runs + seg_r * (1.0 - runs)
+        ceilings["insert_records_est_g_per_s"] = round(rec_g / (phase["insert"] * 1e-3) / 1e9, 3)
         ceilings["insert_frac_of_or_ceiling"] = round(ceilings["insert_records_est_g_per_s"]
                                                       / ceilings["shard_ors_g_per_s"], 3)
+        ceilings["query_shard_reads_est_g_per_s"] = round(rec_r / (phase["query"] * 1e-3) / 1e9, 3)
+        ceilings["query_frac_of_read_ceiling"] = round(ceilings["query_shard_reads_est_g_per_s"]
+                                                       / ceilings["shard_reads_g_per_s"], 3)
         res["matched_ceilings"] = ceilings
     if a.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, (k, m, s, H), alpha)

@@ -26,6 +26,30 @@ def test_valid_kmer_count():
                 assert bench.valid_kmer_count(t, k, alpha) == brute(t.tobytes(), k, alpha), (alpha, k, n)
 
 
+def test_valid_segments():
+    """The maximal valid stretches holding a k-mer (the run-count estimate's
+    per-stretch term), against a brute-force scan, also when the stretches
+    cross the counting chunks."""
+    rng = np.random.default_rng(4)
+
+    def brute_seg(text, k):
+        n = cur = 0
+        for c in text + b"N":
+            if T.valid_str(chr(c)):
+                cur += 1
+            else:
+                n += cur >= k
+                cur = 0
+        return n
+
+    for k in (1, 2, 5, 12):
+        for n in (0, 3, 50, 997, 4000):
+            t = np.frombuffer(b"ACGTacgtN\n", dtype=np.uint8)[rng.integers(0, 10, n)]
+            for chunk in (7, 64, 3 << 26):
+                got = bench.valid_kmer_count(t, k, chunk=chunk, segments=True)
+                assert got == (bench.valid_kmer_count(t, k), brute_seg(t.tobytes(), k)), (k, n, chunk)
+
+
 def test_roofline_models():
     """The ALU and byte models of the roofline: 52 front-end instructions per
     k-mer start, +13 for the query test, +2.66 for decoding ASCII, +17.5 for
