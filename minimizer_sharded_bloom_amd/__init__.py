@@ -94,7 +94,7 @@ def pack(ascii_dev, stream=None):
     torch = _torch()
     if not _is_device_tensor(ascii_dev) or ascii_dev.dtype != torch.uint8:
         raise TypeError("pack expects a CUDA uint8 tensor")
-    a = ascii_dev.contiguous().view(-1)
+    a = _device_bytes(ascii_dev, stream)
     cw, vw = packed_words(a.numel())
     codes = torch.empty(max(cw, 1), dtype=torch.int32, device=a.device)
     valid = torch.empty(max(vw, 1), dtype=torch.int32, device=a.device)
