@@ -190,9 +190,10 @@ __global__ __launch_bounds__(256) void alpha_insert_kernel(SeqArgs a, Params P)
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t S = 65u - C::k(P);  // k-mers per wave step
+    const uint32_t nq = C::h(P) < 4u ? C::h(P) : 4u;  // words a record can set
     const uint64_t ntasks = (a.nk + kTask - 1) / kTask;
     const uint64_t wstride = (uint64_t)gridDim.x * 4u;
-    const uint64_t le = (2ull << lane) - 1ull;  // lanes 0 .. lane
+    const uint64_t le = lane == 63u ? ~0ull : (2ull << lane) - 1ull;  // lanes 0 .. lane
     for (uint64_t task = (uint64_t)blockIdx.x * 4u + wv; task < ntasks; task += wstride) {
         const uint64_t t0 = task * kTask;
         const uint64_t t1 = t0 + kTask < a.nk ? t0 + kTask : a.nk;
@@ -209,26 +210,29 @@ __global__ __launch_bounds__(256) void alpha_insert_kernel(SeqArgs a, Params P)
             if (nrec == 0)
                 continue;
             const uint32_t r = (uint32_t)__popcll(HB & le) - 1u;  // this k-mer's run (valid lanes)
+            const bool issue = gather_run_quads(mk, nq, kv, __ballot(kv), HB, le, lane);
             reinterpret_cast<ulonglong2*>(rec_mk[wv][lane])[0] = ulonglong2{0, 0};
             reinterpret_cast<ulonglong2*>(rec_mk[wv][lane])[1] = ulonglong2{0, 0};
             wave_lds_sync();
-            if (kv) {
+            if (issue) {
 #pragma unroll
                 for (uint32_t q = 0; q < 4; ++q)
-                    if (mk[q])
+                    if (q < nq)  // every s-mer sets a bit in each word below H
                         __hip_atomic_fetch_or(&rec_mk[wv][r][q], mk[q], __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_WAVEFRONT);
                 if (head)
                     rec_sh[wv][r] = shard;
             }
             wave_lds_sync();
-            // flush: lane -> (record lane/4 + 16 j, word lane & 3)
+            // flush: lane -> (record lane/4 + 16 j, word lane & 3); words
+            // q >= H of every record are 0 and skipped
             const uint32_t q = lane & 3u;
-            for (uint32_t rr = lane >> 2; rr < nrec; rr += 16u) {
-                const uint64_t m = rec_mk[wv][rr][q];
-                if (m)
-                    atomic_or_u64(a.filter + 4ull * rec_sh[wv][rr] + q, m);
-            }
+            if (q < nq)
+                for (uint32_t rr = lane >> 2; rr < nrec; rr += 16u) {
+                    const uint32_t sh = rec_sh[wv][rr];
+                    const uint64_t m = rec_mk[wv][rr][q];
+                    atomic_or_u64(a.filter + 4ull * sh + q, m);
+                }
             wave_lds_sync();  // the next step rewrites the records
         }
     }

@@ -308,6 +308,31 @@ __device__ __forceinline__ void window_or(uint64_t (&mk)[4], const LaneWindow& W
     }
 }
 
+// Before the k-mers of a run OR their masks into the run's LDS record: a
+// k-mer takes the masks of lane l+1 and then of the pair at lane l+2 where
+// its run goes on that far (DPP moves), and only the k-mers at offsets 0, 4,
+// 8 ... from their run's head go on to OR into the record.  A quarter as many
+// lanes then meet on each record, whose LDS atomics serialize.  KV and HB are
+// the wave's ballots of valid k-mers and run heads, le the mask of lanes
+// 0 .. lane; words q >= nq are left alone.  Returns whether this lane ORs.
+__device__ __forceinline__ bool gather_run_quads(uint64_t (&mk)[4], uint32_t nq, bool kv, uint64_t KV, uint64_t HB,
+                                                 uint64_t le, uint32_t lane)
+{
+    const uint64_t cont = KV & ~HB;  // valid k-mers that continue the run of lane l-1
+    const bool same1 = kv && lane < 63u && ((cont >> (lane + 1u)) & 1ull);
+    const bool same2 = same1 && lane < 62u && ((cont >> (lane + 2u)) & 1ull);
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q)
+        if (q < nq) {
+            const uint64_t n1 = from_next_lane(mk[q]);
+            mk[q] |= same1 ? n1 : 0ull;
+            const uint64_t n2 = from_next_lane(from_next_lane(mk[q]));
+            mk[q] |= same2 ? n2 : 0ull;
+        }
+    const uint32_t hp = 63u - (uint32_t)__builtin_clzll((HB & le) | 1ull);  // this run's head lane
+    return kv && ((lane - hp) & 3u) == 0u;
+}
+
 // LDS written by some lanes of this wave becomes visible to all its lanes.
 __device__ __forceinline__ void wave_lds_sync()
 {

@@ -488,10 +488,11 @@ __global__ __launch_bounds__(256) void slide_insert_kernel(SeqArgs a, Params P)
             if (nrec == 0)
                 continue;
             const uint32_t r = (uint32_t)__popcll(HB & le) - 1u;  // this k-mer's run (valid lanes)
+            const bool issue = gather_run_quads(mk, nq, kv, __ballot(kv), HB, le, lane);
             reinterpret_cast<ulonglong2*>(rec_mk[wv][lane])[0] = ulonglong2{0, 0};
             reinterpret_cast<ulonglong2*>(rec_mk[wv][lane])[1] = ulonglong2{0, 0};
             wave_lds_sync();
-            if (kv) {
+            if (issue) {
 #pragma unroll
                 for (uint32_t q = 0; q < 4; ++q)
                     if (q < nq)  // every s-mer sets a bit in each word below H
