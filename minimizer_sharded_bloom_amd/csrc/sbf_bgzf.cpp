@@ -306,10 +306,14 @@ struct BgzfReader {
                     if (s->out.size() < kTailChunk)
                         s->out.resize(kTailChunk);
                     n = ::gzread(gz, s->out.data(), kTailChunk);
+                    int zerr = Z_OK;
+                    const char* msg = ::gzerror(gz, &zerr);
                     if (n < 0) {
-                        int zerr = 0;
-                        const char* msg = ::gzerror(gz, &zerr);
                         s->err = std::string("read error: ") + (msg ? msg : "?");
+                    } else if (n == 0 && zerr == Z_BUF_ERROR) {
+                        // the end of the input inside a gzip member
+                        s->err = "truncated gzip data (the file ends inside a member)";
+                        n = -1;
                     }
                 } catch (const std::bad_alloc&) {
                     s->err = "host allocation failed";

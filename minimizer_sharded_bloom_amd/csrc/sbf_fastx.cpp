@@ -82,8 +82,17 @@ struct FastxReader {
         }
         pos = 0;
         lim = (size_t)got;
-        if (got == 0)
+        if (got == 0) {
+            // gzread reports a file that ends inside a gzip member as the end
+            // of the input, with Z_BUF_ERROR left in gzerror
+            int zerr = Z_OK;
+            gzerror(f, &zerr);
+            if (zerr == Z_BUF_ERROR) {
+                error = "truncated gzip data (the file ends inside a member)";
+                return -1;
+            }
             eof = true;
+        }
         return 0;
     }
 

@@ -243,12 +243,28 @@ def test_reader_bgzf_errors(tmp_path):
     bad_crc[-28 - 8] ^= 1  # CRC of the last data member
     bad_isize = bytearray(good)
     bad_isize[-28 - 4] ^= 1
-    cases = {"crc": bytes(bad_crc), "isize": bytes(bad_isize), "cut": bytes(good[:-28 - 100])}
+    cases = {"crc": bytes(bad_crc), "isize": bytes(bad_isize), "cut": bytes(good[:-28 - 100]),
+             # a gzip member after the BGZF ones, cut before its end (read by gzread)
+             "cut_tail": bytes(good[:-28]) + gzip.compress(b">x\nACGTACGT\n" * 50)[:-12]}
     assert read_all(write(tmp_path, "good", bytes(good)))[0] == R.normalize(text)[0]
     for name, data in cases.items():
         with pytest.raises(M.SbfError) as e:
             read_all(write(tmp_path, name, data))
         assert e.value.code == _lib.SBF_EIO, name
+
+
+def test_reader_truncated_gzip(tmp_path):
+    """A gzip file cut inside its member is an error, not a shorter input:
+    gzread reports such an end as the end of the file, and the reader checks
+    gzerror for it."""
+    rng = np.random.default_rng(6)
+    text = fasta_text(rng, random_records(rng, 200))
+    full = gzip.compress(text)
+    assert read_all(write(tmp_path, "full.gz", full))[0] == R.normalize(text)[0]
+    for cut in (8, 100, len(full) // 2):
+        with pytest.raises(M.SbfError) as e:
+            read_all(write(tmp_path, "cut%d.gz" % cut, full[:-cut]))
+        assert e.value.code == _lib.SBF_EIO, cut
 
 
 def test_reader_synthetic_writers(tmp_path):
