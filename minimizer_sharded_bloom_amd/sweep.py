@@ -14,8 +14,8 @@ the operating point -- s = 16..31 at (m, H) = (16, 4), m = 8..31 at
 (s, H) = (28, 4), H in {1,2,3,4,5,6,8,12,16} at (m, s) = (16, 28).  With
 --grid2d: the whole two-dimensional grid of Fig. 4, s = 16..31 x m = 8..31,
 at each H in --h-values (default 4, 8, 12, 16; H > 10 takes the salted bit
-address).  Points outside the compiled parameter sets run on the generic
-per-k-mer kernels; each row says which.
+address).  Points outside the compiled parameter sets run on the run-time
+kernels (sliding insert and query, run-time probe); each row says which.
 
     python -m minimizer_sharded_bloom_amd.sweep [--probe-n N] [--reps R] [--grid | --grid2d]
 """
