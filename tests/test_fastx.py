@@ -267,6 +267,47 @@ def test_reader_truncated_gzip(tmp_path):
         assert e.value.code == _lib.SBF_EIO, cut
 
 
+def test_reader_mutated_texts(tmp_path):
+    """Seeded random edits (deleted, inserted and replaced bytes among
+    '@+>;', line breaks, CR, spaces and bases) of small FASTA and FASTQ
+    files, read plain, as gzip and as BGZF with small blocks: the reader
+    returns the reference normalization whenever the reference accepts the
+    text, and SBF_EIO whenever it refuses it."""
+    import random
+    rng = np.random.default_rng(17)
+    pr = random.Random(17)
+    for it in range(300):
+        recs = random_records(rng, int(rng.integers(1, 6)), max_len=50)
+        if pr.random() < 0.5:
+            text = fasta_text(rng, recs, crlf=pr.random() < 0.3, comments=True)
+        else:
+            text = fastq_text(rng, recs, multiline=pr.random() < 0.5)
+        b = bytearray(text)
+        for _ in range(pr.randint(1, 4)):
+            op, pos = pr.random(), pr.randrange(len(b) + 1)
+            if op < 0.33 and b:
+                del b[min(pos, len(b) - 1)]
+            elif op < 0.66:
+                b.insert(pos, pr.choice(b"@+>;\n\r ACGTN!I\t"))
+            elif b:
+                b[min(pos, len(b) - 1)] = pr.choice(b"@+>;\n\r ACGTN!I")
+        data = bytes(b)
+        try:
+            want = R.normalize(data)
+        except (AssertionError, ValueError):
+            want = None
+        wrap = it % 3
+        raw = data if wrap == 0 else gzip.compress(data) if wrap == 1 else S.bgzf_bytes(data, block=pr.choice([5, 64, 500]))
+        path = write(tmp_path, "m%d" % it, raw)
+        try:
+            got = read_all(path, 1 << 12, 16)
+            got = (got[0], got[1])
+        except M.SbfError as e:
+            assert e.code == _lib.SBF_EIO
+            got = None
+        assert got == want, (it, data)
+
+
 def test_reader_synthetic_writers(tmp_path):
     """write_fasta / write_fastq of generated reads read back as the reads
     joined by 'N'."""
